@@ -1,0 +1,395 @@
+// Tiled MFMA GEMM mainloop for gfx950: C[M,N] = sum_k A[m,k] * B[n,k].
+//
+// Each operand is staged through LDS in 128-byte rows (64 bf16 or 32 fp32 of
+// K) with the XOR swizzle of swz().  The global -> register prefetch of tile
+// k+1 overlaps the MFMAs of tile k (two LDS buffers, one barrier per K tile).
+// Operand kinds:
+//   OP_BF16_K  bf16, [rows][K] (K contiguous), optional row gather list
+//   OP_BF16_T  bf16, [K][rows] (rows contiguous), optional K gather list;
+//              transposed into LDS with 16-bit writes
+//   OP_F32S_K  fp32 [rows][K], split into bf16 hi and lo tiles
+//   OP_F32S_T  fp32 [K][rows], split into bf16 hi and lo tiles
+//   OP_F32_K   fp32 [rows][K] fed to fp32 MFMA (fp32 workloads)
+//   OP_F32_T   fp32 [K][rows] fed to fp32 MFMA
+// A split operand costs two MFMAs (hi and lo) per fragment; B is always exact
+// in its type.  K-contiguous kinds need K % 64 == 0 (bf16) / 32 (fp32);
+// transposed kinds zero-fill past K and read whole row blocks, so the caller
+// launches them only on matrices whose row count is a multiple of the block.
+#pragma once
+#include "common.hpp"
+
+namespace twell {
+
+enum OpKind { OP_BF16_K = 0, OP_BF16_T = 1, OP_F32S_K = 2, OP_F32S_T = 3, OP_F32_K = 4, OP_F32_T = 5 };
+
+struct Operand {
+  const void* ptr;
+  int64_t ld;          // elements between consecutive rows (K kinds) or K steps (T kinds)
+  const int* gather;   // K kinds: row index list; T kinds: K index list; may be null
+  int nrows;           // rows that exist (K kinds clamp to nrows-1)
+};
+
+template <int KIND> struct KindInfo;
+template <> struct KindInfo<OP_BF16_K> { static constexpr bool split = false, f32mma = false, trans = false; static constexpr int esz = 2; };
+template <> struct KindInfo<OP_BF16_T> { static constexpr bool split = false, f32mma = false, trans = true;  static constexpr int esz = 2; };
+template <> struct KindInfo<OP_F32S_K> { static constexpr bool split = true,  f32mma = false, trans = false; static constexpr int esz = 4; };
+template <> struct KindInfo<OP_F32S_T> { static constexpr bool split = true,  f32mma = false, trans = true;  static constexpr int esz = 4; };
+template <> struct KindInfo<OP_F32_K>  { static constexpr bool split = false, f32mma = true,  trans = false; static constexpr int esz = 4; };
+template <> struct KindInfo<OP_F32_T>  { static constexpr bool split = false, f32mma = true,  trans = true;  static constexpr int esz = 4; };
+
+// K elements per LDS row (= per K tile).
+template <int KIND> constexpr int ktile() { return KindInfo<KIND>::f32mma ? 32 : 64; }
+
+// ------------------------------------------------------------------ loaders
+// Each loader moves one K tile of a ROWS-row operand block from global memory
+// into registers (load) and from registers into the swizzled LDS tile(s)
+// (store).  Thread tid owns a fixed set of 16-byte chunks.
+
+template <int KIND, int ROWS, int NTH> struct Loader;
+
+// bf16 or fp32, K contiguous: 8 chunks of 16 bytes per row.
+template <int KIND, int ROWS, int NTH>
+struct LoaderK {
+  static constexpr int ESZ = KindInfo<KIND>::esz;
+  static constexpr int CH = ROWS * 8 / NTH;
+  static_assert(CH * NTH == ROWS * 8, "tile rows must divide the thread count");
+  const char* rowp[CH];
+  uint4 r[CH];
+  __device__ void init(const Operand& op, int row0, int tid) {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      int id = tid + q * NTH;
+      int gr = min(row0 + (id >> 3), op.nrows - 1);
+      if (op.gather) gr = op.gather[gr];
+      rowp[q] = (const char*)op.ptr + ((int64_t)gr * op.ld) * ESZ + (id & 7) * 16;
+    }
+  }
+  __device__ void load(int k0, int /*K*/) {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) r[q] = *(const uint4*)(rowp[q] + (int64_t)k0 * ESZ);
+  }
+  __device__ void store(char* lds, char* /*lds_lo*/, int tid) const {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      int id = tid + q * NTH;
+      *(uint4*)(lds + swz(id >> 3, id & 7)) = r[q];
+    }
+  }
+};
+template <int ROWS, int NTH> struct Loader<OP_BF16_K, ROWS, NTH> : LoaderK<OP_BF16_K, ROWS, NTH> {};
+template <int ROWS, int NTH> struct Loader<OP_F32_K, ROWS, NTH> : LoaderK<OP_F32_K, ROWS, NTH> {};
+
+// bf16, [K][rows]: a chunk is 8 consecutive rows at one k.  Within a wave,
+// lanes cover 8 k x 8 row-chunks so both the global read (128 contiguous
+// bytes per k) and the transposed LDS writes are conflict free.
+template <int ROWS, int NTH>
+struct Loader<OP_BF16_T, ROWS, NTH> {
+  static_assert(ROWS % 64 == 0, "transposed operand block must be a multiple of 64 rows");
+  static constexpr int CH = 64 * ROWS / 8 / NTH;
+  static_assert(CH * NTH == 64 * ROWS / 8, "bad thread count");
+  const uint16_t* base;
+  int64_t ld;
+  const int* gather;
+  int row0;
+  uint4 r[CH];
+  __device__ static void coords(int id, int& k, int& rc) {
+    const int rch = ROWS / 64;
+    int rest = id >> 6;
+    rc = (rest % rch) * 8 + ((id >> 3) & 7);
+    k = (rest / rch) * 8 + (id & 7);
+  }
+  __device__ void init(const Operand& op, int row0_, int /*tid*/) {
+    base = (const uint16_t*)op.ptr; ld = op.ld; gather = op.gather; row0 = row0_;
+  }
+  __device__ void load(int k0, int K) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      int k, rc;
+      coords(tid + q * NTH, k, rc);
+      int gk = k0 + k;
+      if (gk < K) {
+        if (gather) gk = gather[gk];
+        r[q] = *(const uint4*)(base + (int64_t)gk * ld + row0 + rc * 8);
+      } else {
+        r[q] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ void store(char* lds, char* /*lds_lo*/, int tid) const {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      int k, rc;
+      coords(tid + q * NTH, k, rc);
+      const uint32_t w[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint16_t v = (uint16_t)(w[i >> 1] >> ((i & 1) * 16));
+        *(uint16_t*)(lds + swz(rc * 8 + i, k >> 3) + ((k & 7) << 1)) = v;
+      }
+    }
+  }
+};
+
+// fp32 [rows][K] split into bf16 hi/lo tiles: 16 chunks of 4 floats per row.
+template <int ROWS, int NTH>
+struct Loader<OP_F32S_K, ROWS, NTH> {
+  static constexpr int CH = ROWS * 16 / NTH;
+  static_assert(CH * NTH == ROWS * 16, "bad thread count");
+  const char* rowp[CH];
+  uint4 r[CH];
+  __device__ void init(const Operand& op, int row0, int tid) {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      int id = tid + q * NTH;
+      int gr = min(row0 + (id >> 4), op.nrows - 1);
+      if (op.gather) gr = op.gather[gr];
+      rowp[q] = (const char*)op.ptr + (int64_t)gr * op.ld * 4 + (id & 15) * 16;
+    }
+  }
+  __device__ void load(int k0, int /*K*/) {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) r[q] = *(const uint4*)(rowp[q] + (int64_t)k0 * 4);
+  }
+  __device__ void store(char* lds_hi, char* lds_lo, int tid) const {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      int id = tid + q * NTH;
+      int row = id >> 4, c4 = id & 15;
+      uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+      split_bf16(__uint_as_float(r[q].x), h0, l0);
+      split_bf16(__uint_as_float(r[q].y), h1, l1);
+      split_bf16(__uint_as_float(r[q].z), h2, l2);
+      split_bf16(__uint_as_float(r[q].w), h3, l3);
+      int off = swz(row, c4 >> 1) + (c4 & 1) * 8;
+      *(uint2*)(lds_hi + off) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+      *(uint2*)(lds_lo + off) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+    }
+  }
+};
+
+// fp32 [K][rows] split into bf16 hi/lo tiles: a chunk is 4 rows at one k.
+template <int ROWS, int NTH>
+struct Loader<OP_F32S_T, ROWS, NTH> {
+  static_assert(ROWS % 32 == 0, "bad rows");
+  static constexpr int CH = 64 * ROWS / 4 / NTH;
+  static_assert(CH * NTH == 64 * ROWS / 4, "bad thread count");
+  const float* base;
+  int64_t ld;
+  const int* gather;
+  int row0;
+  uint4 r[CH];
+  __device__ static void coords(int id, int& k, int& rc) {
+    const int rch = ROWS / 32;
+    int rest = id >> 6;
+    rc = (rest % rch) * 8 + ((id >> 3) & 7);
+    k = (rest / rch) * 8 + (id & 7);
+  }
+  __device__ void init(const Operand& op, int row0_, int /*tid*/) {
+    base = (const float*)op.ptr; ld = op.ld; gather = op.gather; row0 = row0_;
+  }
+  __device__ void load(int k0, int K) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      int k, rc;
+      coords(tid + q * NTH, k, rc);
+      int gk = k0 + k;
+      if (gk < K) {
+        if (gather) gk = gather[gk];
+        r[q] = *(const uint4*)(base + (int64_t)gk * ld + row0 + rc * 4);
+      } else {
+        r[q] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ void store(char* lds_hi, char* lds_lo, int tid) const {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      int k, rc;
+      coords(tid + q * NTH, k, rc);
+      const uint32_t w[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t h, l;
+        split_bf16(__uint_as_float(w[i]), h, l);
+        int off = swz(rc * 4 + i, k >> 3) + ((k & 7) << 1);
+        *(uint16_t*)(lds_hi + off) = (uint16_t)h;
+        *(uint16_t*)(lds_lo + off) = (uint16_t)l;
+      }
+    }
+  }
+};
+
+// fp32 [K][rows] for fp32 MFMA: a chunk is 4 rows at one k; K tile is 32.
+template <int ROWS, int NTH>
+struct Loader<OP_F32_T, ROWS, NTH> {
+  static_assert(ROWS % 32 == 0, "bad rows");
+  static constexpr int CH = 32 * ROWS / 4 / NTH;
+  static_assert(CH * NTH == 32 * ROWS / 4, "bad thread count");
+  const float* base;
+  int64_t ld;
+  const int* gather;
+  int row0;
+  uint4 r[CH];
+  __device__ static void coords(int id, int& k, int& rc) {
+    const int rch = ROWS / 32;
+    int rest = id >> 6;
+    rc = (rest % rch) * 8 + ((id >> 3) & 7);
+    k = (rest / rch) * 8 + (id & 7);
+  }
+  __device__ void init(const Operand& op, int row0_, int /*tid*/) {
+    base = (const float*)op.ptr; ld = op.ld; gather = op.gather; row0 = row0_;
+  }
+  __device__ void load(int k0, int K) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      int k, rc;
+      coords(tid + q * NTH, k, rc);
+      int gk = k0 + k;
+      if (gk < K) {
+        if (gather) gk = gather[gk];
+        r[q] = *(const uint4*)(base + (int64_t)gk * ld + row0 + rc * 4);
+      } else {
+        r[q] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ void store(char* lds, char* /*lds_lo*/, int tid) const {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      int k, rc;
+      coords(tid + q * NTH, k, rc);
+      const uint32_t w[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *(uint32_t*)(lds + swz(rc * 4 + i, k >> 2) + ((k & 3) << 2)) = w[i];
+    }
+  }
+};
+
+// ------------------------------------------------------------------ mainloop
+
+template <int BM_, int BN_, int WM_, int WN_, int AKIND, int BKIND, int NB_ = 1>
+struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NB = NB_;
+  static constexpr int NTH = WM * WN * WAVE;
+  static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  static_assert(TM >= 1 && TN >= 1, "wave tile must hold whole 32x32 blocks");
+  static constexpr bool ASPLIT = KindInfo<AKIND>::split;
+  static constexpr bool F32MMA = KindInfo<AKIND>::f32mma;
+  static_assert(KindInfo<BKIND>::f32mma == F32MMA, "A and B must both be fp32 or both bf16");
+  static_assert(!KindInfo<BKIND>::split, "B operand is never split");
+  static constexpr int KT = ktile<AKIND>();
+  static constexpr int A_BYTES = BM * 128;
+  static constexpr int B_BYTES = BN * 128;
+  static constexpr int STAGE = A_BYTES * (ASPLIT ? 2 : 1) + B_BYTES * NB;
+  static constexpr int LDS_BYTES = 2 * STAGE;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static constexpr int A_KIND = AKIND, B_KIND = BKIND;
+};
+
+template <class Cfg>
+struct GemmTile {
+  static constexpr int TM = Cfg::TM, TN = Cfg::TN, NB = Cfg::NB, NTH = Cfg::NTH;
+  f32x16 acc[NB][TM][TN];
+
+  // Multiply the MxN block at (m0, n0) over K; LDS is Cfg::LDS_BYTES.
+  __device__ void run(const Operand& A, const Operand* B, int m0, int n0, int K, char* lds) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wr = (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
+    const int wc = (wave % Cfg::WN) * (Cfg::BN / Cfg::WN);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[b][i][j][e] = 0.f;
+
+    Loader<Cfg::A_KIND, Cfg::BM, NTH> la;
+    Loader<Cfg::B_KIND, Cfg::BN, NTH> lb[NB];
+    la.init(A, m0, tid);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) lb[b].init(B[b], n0, tid);
+
+    const int nk = (K + Cfg::KT - 1) / Cfg::KT;
+    auto stage_ptr = [&](int s) { return lds + s * Cfg::STAGE; };
+    auto a_hi = [&](int s) { return stage_ptr(s); };
+    auto a_lo = [&](int s) { return stage_ptr(s) + Cfg::A_BYTES; };
+    auto b_ptr = [&](int s, int b) {
+      return stage_ptr(s) + Cfg::A_BYTES * (Cfg::ASPLIT ? 2 : 1) + b * Cfg::B_BYTES;
+    };
+
+    if (nk > 0) {
+      la.load(0, K);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) lb[b].load(0, K);
+      la.store(a_hi(0), a_lo(0), tid);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) lb[b].store(b_ptr(0, b), nullptr, tid);
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        la.load((kt + 1) * Cfg::KT, K);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) lb[b].load((kt + 1) * Cfg::KT, K);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ch = 2 * kk + (lane >> 5);
+        uint4 fa[TM], fal[Cfg::ASPLIT ? TM : 1], fb[NB][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          fa[i] = *(const uint4*)(a_hi(cur) + swz(wr + i * 32 + (lane & 31), ch));
+          if constexpr (Cfg::ASPLIT)
+            fal[i] = *(const uint4*)(a_lo(cur) + swz(wr + i * 32 + (lane & 31), ch));
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            fb[b][j] = *(const uint4*)(b_ptr(cur, b) + swz(wc + j * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              if constexpr (Cfg::F32MMA) {
+                acc[b][i][j] = mfma32_f32(fa[i], fb[b][j], acc[b][i][j]);
+              } else {
+                acc[b][i][j] = mfma32(fa[i], fb[b][j], acc[b][i][j]);
+                if constexpr (Cfg::ASPLIT) acc[b][i][j] = mfma32(fal[i], fb[b][j], acc[b][i][j]);
+              }
+            }
+      }
+      if (more) {
+        la.store(a_hi(cur ^ 1), a_lo(cur ^ 1), tid);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) lb[b].store(b_ptr(cur ^ 1, b), nullptr, tid);
+      }
+      __syncthreads();
+    }
+  }
+
+  // Row (within the block) and column of accumulator element e of block (i, j).
+  __device__ static int row_of(int i, int e) {
+    const int wave = threadIdx.x >> 6;
+    return (wave / Cfg::WN) * (Cfg::BM / Cfg::WM) + i * 32 + mfma32_row(threadIdx.x & 63, e);
+  }
+  __device__ static int col_of(int j) {
+    const int wave = threadIdx.x >> 6;
+    return (wave % Cfg::WN) * (Cfg::BN / Cfg::WN) + j * 32 + (threadIdx.x & 31);
+  }
+};
+
+}  // namespace twell

@@ -1,0 +1,51 @@
+// Internal host-side interface between the C-ABI entry points and the kernel
+// translation units.  Not part of the public header.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace twell {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+// Device view of a TwELL matrix (all pointers device memory).
+struct TwellView {
+  int T, F, NT, NR;
+  uint8_t* cnt;     // [T][NT]
+  uint8_t* width;   // [NR][NT]
+  void* val;        // [NR][NT][64][16]
+  uint8_t* idx;     // [NR][NT][64][16]
+  uint64_t* mask;   // [T][NT] or null
+};
+
+// Gate GEMM g = x.WgT^T + bg, h = ReLU(g), packed into TwELL in the epilogue
+// (values fp32).  row_skip (optional, u8 [T]) marks rows whose mask must be
+// stored as empty for the consumers (never used by the gate itself).
+hipError_t launch_gate_twell(int in_dt, const void* x, const void* WgT, const void* bg,
+                             int T, int d, int F, const TwellView& out, hipStream_t s);
+
+// Standalone pack of a [T][F] matrix with leading dimension ldg.
+hipError_t launch_pack(const void* G, int gdt, int64_t ldg, const TwellView& out, hipStream_t s);
+// Unpack to a dense [T][F] matrix with leading dimension ldh (value dtype vdt).
+hipError_t launch_unpack(const TwellView& in, int vdt, void* H, int64_t ldh, hipStream_t s);
+
+// Sparse up-projection times gate on the TwELL pattern:
+//   a[t,n] = h[t,n] * (x_t . WuT[n]) for every stored (t, n), written into
+//   aval (same layout as the TwELL values, fp32; may alias the h values).
+// Rows with skip[t] != 0 are left untouched.
+hipError_t launch_sddmm_up(int in_dt, const void* x, const void* WuT, int T, int d, int F,
+                           const TwellView& h, float* aval, const uint8_t* skip, hipStream_t s);
+
+// Sparse down-projection: y_t = sum over stored n of a[t,n] * Wd[n]
+// (out_dt fp32 or bf16).  Rows with skip[t] != 0 are not written.
+hipError_t launch_spmm_down(int in_dt, int out_dt, const float* aval, const void* Wd, int T,
+                            int d, int F, const TwellView& pat, void* y, const uint8_t* skip,
+                            hipStream_t s);
+
+// Dense baseline: act = ReLU(x.WgT^T + bg) * (x.WuT^T) in bf16 (fused dual GEMM),
+// then y = act.Wd.  act is a [T][F] bf16 workspace.
+hipError_t launch_dense_fwd(const void* x, const void* WgT, const void* bg, const void* WuT,
+                            const void* Wd, int T, int d, int F, void* act, int out_dt, void* y,
+                            hipStream_t s);
+
+}  // namespace twell

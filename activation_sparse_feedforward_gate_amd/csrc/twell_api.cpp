@@ -1,0 +1,272 @@
+// C-ABI entry points of libtwell: argument checks on the host, then kernel
+// launches on the caller's stream.  No allocation, no synchronisation.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <initializer_list>
+
+#include "../../include/twell.h"
+#include "internal.hpp"
+
+using namespace twell;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+twell_status fail(twell_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+twell_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TWELL_OK;
+  return fail(TWELL_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+constexpr int GPU_R = 16, GPU_C = 64;
+
+// Carves consecutive 256-byte aligned regions out of a workspace.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off = round_up(off + bytes, 256);
+    return p;
+  }
+};
+
+void mat_parts(int64_t T, int64_t F, int64_t R, int64_t C, twell_dtype v, size_t parts[5]) {
+  const int64_t NR = (T + R - 1) / R, NT = (F + C - 1) / C;
+  parts[0] = (size_t)(T * NT);
+  parts[1] = (size_t)(NR * NT);
+  parts[2] = (size_t)(NR * NT * C * R) * (v == TWELL_F32 ? 4 : 2);
+  parts[3] = (size_t)(NR * NT * C * R);
+  parts[4] = (size_t)(T * NT) * 8;
+}
+
+twell_status check_shape(const twell_ffn_shape* sh) {
+  if (!sh) return fail(TWELL_EINVAL, "shape is NULL");
+  if (sh->T < 0 || sh->d <= 0 || sh->F <= 0) return fail(TWELL_EINVAL, "bad shape T=%d d=%d F=%d", sh->T, sh->d, sh->F);
+  if ((sh->in_dt != TWELL_F32 && sh->in_dt != TWELL_BF16) || (sh->out_dt != TWELL_F32 && sh->out_dt != TWELL_BF16))
+    return fail(TWELL_EINVAL, "bad dtype");
+  if (sh->d % 64 != 0 || sh->F % 64 != 0)
+    return fail(TWELL_EUNSUPPORTED, "GPU path needs d %% 64 == 0 and F %% 64 == 0 (d=%d F=%d)", sh->d, sh->F);
+  if (sh->F > 65472) return fail(TWELL_EUNSUPPORTED, "F=%d too large (max 65472)", sh->F);
+  return TWELL_OK;
+}
+
+twell_status check_mat(const twell_mat* m, bool need_mask) {
+  if (!m) return fail(TWELL_EINVAL, "twell_mat is NULL");
+  if (m->T < 0 || m->F <= 0) return fail(TWELL_EINVAL, "bad twell_mat shape T=%d F=%d", m->T, m->F);
+  if (m->R != GPU_R || m->C != GPU_C)
+    return fail(TWELL_EUNSUPPORTED, "GPU TwELL tiles are 16 x 64 (got %d x %d)", m->R, m->C);
+  if (m->F % GPU_C != 0) return fail(TWELL_EUNSUPPORTED, "F=%d is not a multiple of 64", m->F);
+  if (m->vdtype != TWELL_F32 && m->vdtype != TWELL_BF16) return fail(TWELL_EINVAL, "bad value dtype");
+  if (m->T > 0 && (!m->cnt || !m->width || !m->val || !m->idx))
+    return fail(TWELL_EINVAL, "twell_mat array is NULL");
+  if (need_mask && m->T > 0 && !m->mask) return fail(TWELL_EINVAL, "twell_mat mask is required here");
+  if (!aligned16(m->val) || !aligned16(m->mask)) return fail(TWELL_EINVAL, "twell_mat arrays must be 16-byte aligned");
+  return TWELL_OK;
+}
+
+TwellView view_of(const twell_mat* m) {
+  TwellView v;
+  v.T = m->T; v.F = m->F; v.NT = m->F / GPU_C; v.NR = (m->T + GPU_R - 1) / GPU_R;
+  v.cnt = m->cnt; v.width = m->width; v.val = m->val; v.idx = m->idx; v.mask = m->mask;
+  return v;
+}
+
+// Workspace of the inference forward: one TwELL (fp32 values, with mask).
+struct FwdWs {
+  TwellView h;
+};
+
+size_t fwd_layout(const twell_ffn_shape* sh, void* ws, FwdWs* out) {
+  size_t parts[5];
+  mat_parts(sh->T, sh->F, GPU_R, GPU_C, TWELL_F32, parts);
+  Carver c(ws);
+  TwellView v;
+  v.T = sh->T; v.F = sh->F; v.NT = sh->F / GPU_C; v.NR = (sh->T + GPU_R - 1) / GPU_R;
+  v.cnt = (uint8_t*)c.take(parts[0]);
+  v.width = (uint8_t*)c.take(parts[1]);
+  v.val = c.take(parts[2]);
+  v.idx = (uint8_t*)c.take(parts[3]);
+  v.mask = (uint64_t*)c.take(parts[4]);
+  if (out) out->h = v;
+  return c.off;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t twell_mat_bytes(int32_t T, int32_t F, int32_t R, int32_t C, twell_dtype vdtype, size_t parts[5]) {
+  size_t p[5] = {0, 0, 0, 0, 0};
+  if (T >= 0 && F > 0 && R > 0 && C > 0) mat_parts(T, F, R, C, vdtype, p);
+  if (parts) memcpy(parts, p, sizeof(p));
+  return p[0] + p[1] + p[2] + p[3] + p[4];
+}
+
+twell_status twell_pack(const void* G, twell_dtype gdtype, int64_t ldg, twell_mat* out, hipStream_t stream) {
+  twell_status st = check_mat(out, false);
+  if (st) return st;
+  if (gdtype != out->vdtype) return fail(TWELL_EINVAL, "twell_pack stores bit copies: vdtype must equal the dtype of G");
+  if (ldg < out->F) return fail(TWELL_EINVAL, "ldg=%lld < F=%d", (long long)ldg, out->F);
+  if (out->T == 0) return TWELL_OK;
+  if (!G) return fail(TWELL_EINVAL, "G is NULL");
+  return hip_status(launch_pack(G, gdtype == TWELL_BF16 ? DT_BF16 : DT_F32, ldg, view_of(out), stream), "twell_pack");
+}
+
+twell_status twell_unpack(const twell_mat* in, void* H, int64_t ldh, hipStream_t stream) {
+  twell_status st = check_mat(in, false);
+  if (st) return st;
+  if (ldh < in->F) return fail(TWELL_EINVAL, "ldh=%lld < F=%d", (long long)ldh, in->F);
+  if (in->T == 0) return TWELL_OK;
+  if (!H) return fail(TWELL_EINVAL, "H is NULL");
+  return hip_status(launch_unpack(view_of(in), in->vdtype == TWELL_BF16 ? DT_BF16 : DT_F32, H, ldh, stream),
+                    "twell_unpack");
+}
+
+size_t twell_ffn_fwd_workspace(const twell_ffn_shape* sh, int32_t training) {
+  if (!sh || check_shape(sh) != TWELL_OK) return 0;
+  (void)training;
+  return fwd_layout(sh, nullptr, nullptr);
+}
+
+twell_status twell_ffn_fwd(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
+                           const void* WuT, const void* Wd, void* y, twell_mat* saved_h,
+                           int32_t dense_row_threshold, void* ws, size_t ws_bytes, hipStream_t stream) {
+  twell_status st = check_shape(sh);
+  if (st) return st;
+  if (sh->T > 0 && (!x || !WgT || !WuT || !Wd || !y)) return fail(TWELL_EINVAL, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(WgT) || !aligned16(WuT) || !aligned16(Wd) || !aligned16(y) || !aligned16(bg))
+    return fail(TWELL_EINVAL, "tensors must be 16-byte aligned");
+  if (saved_h) {
+    st = check_mat(saved_h, true);
+    if (st) return st;
+    if (saved_h->T != sh->T || saved_h->F != sh->F || saved_h->vdtype != TWELL_F32)
+      return fail(TWELL_EINVAL, "saved_h must be T x F with fp32 values");
+  }
+  if (dense_row_threshold >= 0)
+    return fail(TWELL_EUNSUPPORTED, "the hybrid forward (dense_row_threshold >= 0) is not built yet");
+  const size_t need = fwd_layout(sh, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (sh->T == 0) return TWELL_OK;
+
+  FwdWs w;
+  fwd_layout(sh, ws, &w);
+  const int in_dt = sh->in_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
+  const int out_dt = sh->out_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
+  TwellView h = w.h;
+  float* aval = (float*)w.h.val;             // a overwrites h in place
+  if (saved_h) {
+    h = view_of(saved_h);                    // h is kept for the backward pass
+    aval = (float*)w.h.val;
+  }
+  hipError_t e = launch_gate_twell(in_dt, x, WgT, bg, sh->T, sh->d, sh->F, h, stream);
+  if (e != hipSuccess) return hip_status(e, "gate GEMM");
+  e = launch_sddmm_up(in_dt, x, WuT, sh->T, sh->d, sh->F, h, aval, nullptr, stream);
+  if (e != hipSuccess) return hip_status(e, "sparse up-projection");
+  e = launch_spmm_down(in_dt, out_dt, aval, Wd, sh->T, sh->d, sh->F, h, y, nullptr, stream);
+  return hip_status(e, "sparse down-projection");
+}
+
+static twell_status check_tensors(const twell_ffn_shape* sh, std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs) {
+    if (sh->T > 0 && !p) return fail(TWELL_EINVAL, "NULL tensor argument");
+    if (!aligned16(p)) return fail(TWELL_EINVAL, "tensors must be 16-byte aligned");
+  }
+  return TWELL_OK;
+}
+
+static twell_status check_h(const twell_ffn_shape* sh, const twell_mat* h) {
+  twell_status st = check_mat(h, true);
+  if (st) return st;
+  if (h->T != sh->T || h->F != sh->F || h->vdtype != TWELL_F32)
+    return fail(TWELL_EINVAL, "TwELL matrix must be T x F (T=%d F=%d) with fp32 values", sh->T, sh->F);
+  return TWELL_OK;
+}
+
+twell_status twell_gate_pack(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
+                             twell_mat* h, hipStream_t stream) {
+  twell_status st = check_shape(sh);
+  if (!st) st = check_tensors(sh, {x, WgT});
+  if (!st && !aligned16(bg)) st = fail(TWELL_EINVAL, "bg must be 16-byte aligned");
+  if (!st) st = check_h(sh, h);
+  if (st) return st;
+  if (sh->T == 0) return TWELL_OK;
+  return hip_status(launch_gate_twell(sh->in_dt == TWELL_BF16 ? DT_BF16 : DT_F32, x, WgT, bg, sh->T, sh->d,
+                                      sh->F, view_of(h), stream), "gate GEMM");
+}
+
+twell_status twell_sparse_up(const twell_ffn_shape* sh, const void* x, const void* WuT, const twell_mat* h,
+                             float* aval, hipStream_t stream) {
+  twell_status st = check_shape(sh);
+  if (!st) st = check_tensors(sh, {x, WuT, aval});
+  if (!st) st = check_h(sh, h);
+  if (st) return st;
+  if (sh->T == 0) return TWELL_OK;
+  return hip_status(launch_sddmm_up(sh->in_dt == TWELL_BF16 ? DT_BF16 : DT_F32, x, WuT, sh->T, sh->d, sh->F,
+                                    view_of(h), aval, nullptr, stream), "sparse up-projection");
+}
+
+twell_status twell_sparse_down(const twell_ffn_shape* sh, const float* aval, const void* Wd,
+                               const twell_mat* pattern, void* y, hipStream_t stream) {
+  twell_status st = check_shape(sh);
+  if (!st) st = check_tensors(sh, {aval, Wd, y});
+  if (!st) st = check_h(sh, pattern);
+  if (st) return st;
+  if (sh->T == 0) return TWELL_OK;
+  return hip_status(launch_spmm_down(sh->in_dt == TWELL_BF16 ? DT_BF16 : DT_F32,
+                                     sh->out_dt == TWELL_BF16 ? DT_BF16 : DT_F32, aval, Wd, sh->T, sh->d, sh->F,
+                                     view_of(pattern), y, nullptr, stream), "sparse down-projection");
+}
+
+size_t twell_ffn_dense_fwd_workspace(const twell_ffn_shape* sh) {
+  if (!sh || check_shape(sh) != TWELL_OK) return 0;
+  return round_up((size_t)sh->T * sh->F * 2, 256);
+}
+
+twell_status twell_ffn_dense_fwd(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
+                                 const void* WuT, const void* Wd, void* y, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  twell_status st = check_shape(sh);
+  if (st) return st;
+  if (sh->in_dt != TWELL_BF16) return fail(TWELL_EUNSUPPORTED, "the dense baseline is bf16 only");
+  if (sh->T > 0 && (!x || !WgT || !WuT || !Wd || !y)) return fail(TWELL_EINVAL, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(WgT) || !aligned16(WuT) || !aligned16(Wd) || !aligned16(y) || !aligned16(bg))
+    return fail(TWELL_EINVAL, "tensors must be 16-byte aligned");
+  if (sh->F % 128 != 0) return fail(TWELL_EUNSUPPORTED, "the dense baseline needs F %% 128 == 0");
+  const size_t need = twell_ffn_dense_fwd_workspace(sh);
+  if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (sh->T == 0) return TWELL_OK;
+  return hip_status(launch_dense_fwd(x, WgT, bg, WuT, Wd, sh->T, sh->d, sh->F, ws,
+                                     sh->out_dt == TWELL_BF16 ? DT_BF16 : DT_F32, y, stream),
+                    "dense FFN");
+}
+
+const char* twell_status_string(twell_status st) {
+  switch (st) {
+    case TWELL_OK: return "ok";
+    case TWELL_EINVAL: return "invalid argument";
+    case TWELL_EUNSUPPORTED: return "unsupported by the GPU path";
+    case TWELL_EWORKSPACE: return "workspace too small";
+    case TWELL_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* twell_last_error(void) { return g_err; }
+
+}  // extern "C"

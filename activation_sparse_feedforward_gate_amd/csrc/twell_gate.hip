@@ -1,0 +1,270 @@
+// Gate GEMM with the TwELL pack in its epilogue, and the standalone
+// pack/unpack kernels.
+//
+// TwELL (tile-wise ELLPACK) follows the intellectnews.ru TwELL article,
+// section "Формат TwELL вместо классической sparse-упаковки", and gate.com/es
+// post 20977915, paragraph 3: the gate output is cut into tiles and each tile
+// is compacted where it is produced, at the end of the kernel that computes
+// it, with no further launch and no second pass over the dense matrix.  Here a
+// tile is 16 rows x 64 columns, the 64 columns being one wave64 ballot:
+//   mask  = ballot(h > 0) per row of the tile      (bit c = column c active)
+//   cnt   = popcount(mask)
+//   slot  = popcount(mask & bits below my column)  (ascending column order)
+//   width = max cnt over the 16 rows               (the tile's ELL width)
+// Values are stored [row tile][column tile][slot][row]; slots in
+// [cnt, width) hold (+0.0, index 0).
+#include "gemm_core.hpp"
+#include "internal.hpp"
+
+namespace twell {
+
+struct GateArgs {
+  const void* x;
+  const void* WgT;
+  const void* bg;
+  int T, d, F, NT;
+  uint8_t* cnt;
+  uint8_t* width;
+  float* val;
+  uint8_t* idx;
+  uint64_t* mask;
+};
+
+template <bool BF16IN>
+__device__ __forceinline__ float load_bias(const void* b, int n) {
+  if (b == nullptr) return 0.f;
+  if constexpr (BF16IN) return bf16_to_f32(((const uint16_t*)b)[n]);
+  else return ((const float*)b)[n];
+}
+
+// Tile order: groups of GM row blocks sweep all column blocks, so the
+// workgroups resident on one XCD share both x rows and gate weight rows in L2.
+__device__ __forceinline__ void tile_coords(int id, int nbm, int nbn, int& bm, int& bn) {
+  constexpr int GM = 8;
+  const int per_group = GM * nbn;
+  const int group = id / per_group;
+  const int first = group * GM;
+  const int gsize = min(nbm - first, GM);
+  const int r = id - group * per_group;
+  bm = first + r % gsize;
+  bn = r / gsize;
+}
+
+template <class Cfg, bool BF16IN>
+__global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
+  static_assert(Cfg::BN / Cfg::WN == 64 && Cfg::TN == 2, "one 64-column TwELL tile per wave");
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  const int nbm = (a.T + Cfg::BM - 1) / Cfg::BM;
+  const int nbn = a.F / Cfg::BN;
+  int bm, bn;
+  tile_coords(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, bm, bn);
+  const int m0 = bm * Cfg::BM, n0 = bn * Cfg::BN;
+
+  GemmTile<Cfg> g;
+  const Operand A{a.x, a.d, nullptr, a.T};
+  const Operand B{a.WgT, a.d, nullptr, a.F};
+  g.run(A, &B, m0, n0, a.d, lds);
+
+  // ---- epilogue: bias, ReLU, ballot compaction into TwELL
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wr = m0 + (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
+  const int wc = n0 + (wave % Cfg::WN) * 64;
+  const int j = wc >> 6;
+  const int hl = lane >> 5;
+  const int c0 = lane & 31, c1 = 32 + (lane & 31);
+  const float b0 = load_bias<BF16IN>(a.bg, wc + c0);
+  const float b1 = load_bias<BF16IN>(a.bg, wc + c1);
+#pragma unroll
+  for (int tm = 0; tm < Cfg::TM; ++tm) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int rt0 = wr + tm * 32 + half * 16;   // first row of this TwELL row tile
+      if (rt0 >= a.T) continue;                   // wave-uniform
+      uint64_t mrow[8];
+      int width = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int e = half * 8 + q;
+        const int rl = 8 * (q >> 2) + 4 * hl + (q & 3);
+        const bool rowok = rt0 + rl < a.T;
+        const float v0 = g.acc[0][tm][0][e] + b0;
+        const float v1 = g.acc[0][tm][1][e] + b1;
+        const uint64_t B0 = ballot(rowok && v0 > 0.f);
+        const uint64_t B1 = ballot(rowok && v1 > 0.f);
+        const uint64_t mlo = (B0 & 0xffffffffull) | (B1 << 32);
+        const uint64_t mhi = (B0 >> 32) | (B1 & 0xffffffff00000000ull);
+        width = max(width, max(popc64(mlo), popc64(mhi)));
+        mrow[q] = hl ? mhi : mlo;
+      }
+      const int64_t tix = (int64_t)(rt0 >> 4) * a.NT + j;
+      const int64_t tbase = tix * (64 * 16);
+      if (lane == 0) a.width[tix] = (uint8_t)width;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int e = half * 8 + q;
+        const int rl = 8 * (q >> 2) + 4 * hl + (q & 3);
+        const int row = rt0 + rl;
+        const uint64_t M = mrow[q];
+        const int cnt = popc64(M);
+        if (c0 == 0 && row < a.T) {
+          a.cnt[(int64_t)row * a.NT + j] = (uint8_t)cnt;
+          if (a.mask) a.mask[(int64_t)row * a.NT + j] = M;
+        }
+        {
+          const float v = g.acc[0][tm][0][e] + b0;
+          const int nb = popc64(M & below(c0));
+          const bool act = (M >> c0) & 1ull;
+          const int slot = act ? nb : cnt + (c0 - nb);
+          if (slot < width) {
+            a.val[tbase + slot * 16 + rl] = act ? v : 0.f;
+            a.idx[tbase + slot * 16 + rl] = act ? (uint8_t)c0 : (uint8_t)0;
+          }
+        }
+        {
+          const float v = g.acc[0][tm][1][e] + b1;
+          const int nb = popc64(M & below(c1));
+          const bool act = (M >> c1) & 1ull;
+          const int slot = act ? nb : cnt + (c1 - nb);
+          if (slot < width) {
+            a.val[tbase + slot * 16 + rl] = act ? v : 0.f;
+            a.idx[tbase + slot * 16 + rl] = act ? (uint8_t)c1 : (uint8_t)0;
+          }
+        }
+      }
+    }
+  }
+}
+
+using GateBigBf16 = GemmCfg<256, 256, 2, 4, OP_BF16_K, OP_BF16_K>;
+using GateSmallBf16 = GemmCfg<64, 64, 1, 1, OP_BF16_K, OP_BF16_K>;
+using GateBigF32 = GemmCfg<256, 256, 2, 4, OP_F32_K, OP_F32_K>;
+using GateSmallF32 = GemmCfg<64, 64, 1, 1, OP_F32_K, OP_F32_K>;
+
+template <class Cfg, bool BF16IN>
+static hipError_t launch_gate_cfg(const GateArgs& a, hipStream_t s) {
+  const int nbm = (a.T + Cfg::BM - 1) / Cfg::BM;
+  const int nbn = a.F / Cfg::BN;
+  const int grid = nbm * nbn;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((gate_twell_kernel<Cfg, BF16IN>), dim3(grid), dim3(Cfg::NTH), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_twell(int in_dt, const void* x, const void* WgT, const void* bg, int T,
+                             int d, int F, const TwellView& out, hipStream_t s) {
+  GateArgs a{x, WgT, bg, T, d, F, F / 64, out.cnt, out.width, (float*)out.val, out.idx, out.mask};
+  const bool big = T >= 512 && F % 256 == 0;
+  if (in_dt == DT_BF16)
+    return big ? launch_gate_cfg<GateBigBf16, true>(a, s) : launch_gate_cfg<GateSmallBf16, true>(a, s);
+  return big ? launch_gate_cfg<GateBigF32, false>(a, s) : launch_gate_cfg<GateSmallF32, false>(a, s);
+}
+
+// ------------------------------------------------------------------ standalone pack
+
+template <bool BF16>
+__device__ __forceinline__ float as_float(uint32_t bits) {
+  if constexpr (BF16) return __uint_as_float(bits << 16);
+  else return __uint_as_float(bits);
+}
+
+// One wave per (row tile, column tile); lane = column inside the tile.  The 16
+// row loads are issued before any is used so that each wave keeps 16 reads in
+// flight.
+template <bool BF16>
+__global__ __launch_bounds__(256) void pack_kernel(const void* G, int64_t ldg, int T, int F, int NT,
+                                                   int NR, uint8_t* cnt, uint8_t* width, void* val,
+                                                   uint8_t* idx, uint64_t* mask) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile >= (int64_t)NR * NT) return;
+  const int i = (int)(tile / NT), j = (int)(tile % NT);
+  const int col = j * 64 + lane;
+  uint32_t bits[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int t = i * 16 + r;
+    bits[r] = 0;
+    if (t < T) {
+      if constexpr (BF16) bits[r] = ((const uint16_t*)G)[(int64_t)t * ldg + col];
+      else bits[r] = ((const uint32_t*)G)[(int64_t)t * ldg + col];
+    }
+  }
+  uint64_t M[16];
+  int w = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    M[r] = ballot(as_float<BF16>(bits[r]) > 0.f);
+    w = max(w, popc64(M[r]));
+  }
+  if (lane == 0) width[tile] = (uint8_t)w;
+  const int64_t tbase = tile * (64 * 16);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int t = i * 16 + r;
+    const int c = popc64(M[r]);
+    if (lane == 0 && t < T) {
+      cnt[(int64_t)t * NT + j] = (uint8_t)c;
+      if (mask) mask[(int64_t)t * NT + j] = M[r];
+    }
+    const int nb = popc64(M[r] & below(lane));
+    const bool act = (M[r] >> lane) & 1ull;
+    const int slot = act ? nb : c + (lane - nb);
+    if (slot < w) {
+      if constexpr (BF16) ((uint16_t*)val)[tbase + slot * 16 + r] = act ? (uint16_t)bits[r] : (uint16_t)0;
+      else ((uint32_t*)val)[tbase + slot * 16 + r] = act ? bits[r] : 0u;
+      idx[tbase + slot * 16 + r] = act ? (uint8_t)lane : (uint8_t)0;
+    }
+  }
+}
+
+hipError_t launch_pack(const void* G, int gdt, int64_t ldg, const TwellView& o, hipStream_t s) {
+  const int64_t tiles = (int64_t)o.NR * o.NT;
+  if (tiles == 0) return hipSuccess;
+  const int grid = (int)((tiles + 3) / 4);
+  if (gdt == DT_BF16)
+    hipLaunchKernelGGL(pack_kernel<true>, dim3(grid), dim3(256), 0, s, G, ldg, o.T, o.F, o.NT, o.NR,
+                       o.cnt, o.width, o.val, o.idx, o.mask);
+  else
+    hipLaunchKernelGGL(pack_kernel<false>, dim3(grid), dim3(256), 0, s, G, ldg, o.T, o.F, o.NT, o.NR,
+                       o.cnt, o.width, o.val, o.idx, o.mask);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ unpack (test helper)
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void unpack_kernel(int T, int NT, const uint8_t* cnt, const void* val,
+                                                     const uint8_t* idx, void* H, int64_t ldh) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rowtile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (t, j) pair
+  if (rowtile >= (int64_t)T * NT) return;
+  const int t = (int)(rowtile / NT), j = (int)(rowtile % NT);
+  const int i = t >> 4, r = t & 15;
+  const int64_t tbase = ((int64_t)i * NT + j) * (64 * 16);
+  const int c = min((int)cnt[rowtile], 64);
+  uint32_t out = 0;
+  for (int s = 0; s < c; ++s) {
+    if (idx[tbase + s * 16 + r] == lane) {
+      if constexpr (BF16) out = ((const uint16_t*)val)[tbase + s * 16 + r];
+      else out = ((const uint32_t*)val)[tbase + s * 16 + r];
+    }
+  }
+  if constexpr (BF16) ((uint16_t*)H)[(int64_t)t * ldh + j * 64 + lane] = (uint16_t)out;
+  else ((uint32_t*)H)[(int64_t)t * ldh + j * 64 + lane] = out;
+}
+
+hipError_t launch_unpack(const TwellView& in, int vdt, void* H, int64_t ldh, hipStream_t s) {
+  const int64_t n = (int64_t)in.T * in.NT;
+  if (n == 0) return hipSuccess;
+  const int grid = (int)((n + 3) / 4);
+  if (vdt == DT_BF16)
+    hipLaunchKernelGGL(unpack_kernel<true>, dim3(grid), dim3(256), 0, s, in.T, in.NT, in.cnt, in.val,
+                       in.idx, H, ldh);
+  else
+    hipLaunchKernelGGL(unpack_kernel<false>, dim3(grid), dim3(256), 0, s, in.T, in.NT, in.cnt, in.val,
+                       in.idx, H, ldh);
+  return hipGetLastError();
+}
+
+}  // namespace twell

@@ -1,0 +1,196 @@
+/*
+ * libtwell: the ReLU-gated transformer FFN that skips exact-zero gate
+ * activations through the Tile-wise ELLPACK (TwELL) format, on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Sources, cited by page and section:
+ *   intellectnews.ru article on the Sakana AI + NVIDIA TwELL work
+ *   ("...twell-uskorenie-llm-do-20-procentov"), sections
+ *     "Формат TwELL вместо классической sparse-упаковки"   (TwELL format),
+ *     "Слитые CUDA-ядра для инференса и гибрид для обучения" (fused inference
+ *        kernel, hybrid sparse/dense format for training),
+ *     "Минимальные изменения в рецепте обучения"            (ReLU gate),
+ *     "Ограничения и открытые вопросы"                      (gated FFN);
+ *   gate.com/es post 20977915, paragraph 3 (per-tile packing inside the GPU's
+ *   compute units); gate.com/id post 20978418, paragraphs 4-5 (same).
+ *
+ * The layer computed everywhere below, with weights stored neuron-major
+ * (WgT, WuT and Wd are each [F][d] row-major, F = d_ff):
+ *     g = x . WgT^T + bg        h = ReLU(g)   (exact zeros where g <= 0)
+ *     u = x . WuT^T             a = h * u
+ *     y = a . Wd
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument is a DEVICE pointer, except the twell_mat and
+ *     twell_ffn_shape structs themselves, which live in host memory (their
+ *     array members are device pointers).
+ *   - Every call is asynchronous on the caller's HIP stream.  No call
+ *     synchronises the device, allocates or frees memory; the caller owns
+ *     every buffer, including the workspace.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Arguments are checked on the host before anything is launched: a NULL
+ *     pointer or an inconsistent shape returns TWELL_EINVAL, a shape or layout
+ *     the GPU path does not handle returns TWELL_EUNSUPPORTED, a workspace that
+ *     is too small returns TWELL_EWORKSPACE, and a failed launch returns
+ *     TWELL_EHIP.  twell_last_error() then gives a thread-local description.
+ *   - Device arrays must be 16-byte aligned.  Dense matrices are row-major.
+ *   - The GPU path needs d % 64 == 0 and F % 64 == 0 (64 <= F <= 65472); T may
+ *     be any value >= 0 (ragged last tiles are handled).
+ */
+#ifndef TWELL_H
+#define TWELL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TWELL_OK = 0,
+  TWELL_EINVAL = 1,
+  TWELL_EUNSUPPORTED = 2,
+  TWELL_EWORKSPACE = 3,
+  TWELL_EHIP = 4
+} twell_status;
+
+typedef enum { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype;
+
+/*
+ * A [T x F] matrix of ReLU outputs in TwELL form (intellectnews.ru TwELL
+ * article, section "Формат TwELL вместо классической sparse-упаковки"):
+ * the matrix is cut into R x C tiles (R = 16 rows, C = 64 columns on the GPU;
+ * NR = ceil(T/R) row tiles, NT = F/C column tiles) and inside each tile every
+ * row keeps only its entries > 0, compacted in ascending column order
+ * (ELLPACK per tile).
+ *   cnt   uint8  [T][NT]        number of kept entries of row t in tile j
+ *   width uint8  [NR][NT]       ELL width of tile (i, j): max cnt of its rows
+ *   val   vdtype [NR][NT][C][R] value of slot s of row r of tile (i, j)
+ *   idx   uint8  [NR][NT][C][R] its column inside the tile (0..C-1)
+ *   mask  uint64 [T][NT]        optional (may be NULL): bit c set iff column
+ *                               j*C + c of row t is kept; the same information
+ *                               as idx, in the form the kernels consume
+ * Slots s < cnt hold the row's entries; slots cnt <= s < width hold value
+ * +0.0 and index 0; slots >= width are left unwritten.  Row positions past T
+ * in the last row tile behave as empty rows.  The caller allocates every
+ * array (twell_mat_bytes gives the sizes).
+ */
+typedef struct {
+  int32_t T, F, R, C;
+  twell_dtype vdtype;
+  uint8_t *cnt;
+  uint8_t *width;
+  void *val;
+  uint8_t *idx;
+  uint64_t *mask;
+} twell_mat;
+
+/* Shape and dtypes of one FFN layer call. in_dt is the dtype of x, the three
+ * weight matrices, bg and dY; out_dt the dtype of y. */
+typedef struct {
+  int32_t T, d, F;
+  twell_dtype in_dt, out_dt;
+} twell_ffn_shape;
+
+/* Bytes of each TwELL array (parts: cnt, width, val, idx, mask) for a T x F
+ * matrix with R x C tiles and value dtype vdtype; returns their sum.  parts
+ * may be NULL.  Pure host arithmetic. */
+size_t twell_mat_bytes(int32_t T, int32_t F, int32_t R, int32_t C, twell_dtype vdtype, size_t parts[5]);
+
+/*
+ * twell_pack: G (device, [T][ldg] row-major, dtype gdtype, the first F
+ * columns used) -> out, the TwELL form of ReLU(G); entries > 0 are kept and
+ * their values are bit copies of G (out->vdtype must equal gdtype).  Shape is
+ * taken from out (T, F); R must be 16 and C 64.  out->mask may be NULL.
+ * One pass over G in HBM (intellectnews.ru TwELL article, TwELL section).
+ */
+twell_status twell_pack(const void *G, twell_dtype gdtype, int64_t ldg, twell_mat *out, hipStream_t stream);
+
+/* twell_unpack: dense H ([T][ldh], dtype in->vdtype) = the matrix in holds:
+ * kept entries at their columns, +0.0 elsewhere.  A test helper. */
+twell_status twell_unpack(const twell_mat *in, void *H, int64_t ldh, hipStream_t stream);
+
+/* Workspace bytes for twell_ffn_fwd with this shape (training != 0: the
+ * hybrid forward with a dense-row threshold). */
+size_t twell_ffn_fwd_workspace(const twell_ffn_shape *sh, int32_t training);
+
+/*
+ * twell_ffn_fwd: y = (ReLU(x.WgT^T + bg) * (x.WuT^T)) . Wd through TwELL
+ * (intellectnews.ru TwELL article, section "Слитые CUDA-ядра для инференса и
+ * гибрид для обучения"): the gate GEMM packs h into TwELL in its epilogue
+ * (no pass over a dense h), then the up-projection and the down-projection
+ * visit only the stored (token, neuron) pairs.
+ *   x    [T][d]   in_dt
+ *   WgT, WuT, Wd  [F][d] in_dt
+ *   bg   [F]      in_dt, may be NULL (no bias)
+ *   y    [T][d]   out_dt
+ *   saved_h       NULL, or a caller-allocated twell_mat (vdtype TWELL_F32,
+ *                 R=16, C=64, T and F of the shape, mask required) that
+ *                 receives h for the backward pass
+ *   dense_row_threshold   < 0: every row takes the sparse path (inference).
+ *                 >= 0: hybrid forward; rows whose nnz exceeds it take the
+ *                 dense branch (requires saved_h)
+ *   ws, ws_bytes  workspace of at least twell_ffn_fwd_workspace(sh, thr >= 0)
+ * Stored pairs are exactly the (t, n) with g > 0 in fp32; h, u and a are
+ * kept in fp32, accumulation is fp32.
+ */
+twell_status twell_ffn_fwd(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
+                           const void *WuT, const void *Wd, void *y, twell_mat *saved_h,
+                           int32_t dense_row_threshold, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The three stages of twell_ffn_fwd, callable one by one (twell_ffn_fwd is
+ * exactly these three calls in sequence):
+ *
+ * twell_gate_pack: gate GEMM g = x.WgT^T + bg with ReLU and the TwELL pack in
+ *   its epilogue (intellectnews.ru TwELL article, TwELL section: the format is
+ *   assembled at the end of the kernel that produces it).  h must be T x F,
+ *   vdtype TWELL_F32, R=16, C=64, mask required; every array of h is written
+ *   (slots >= width excepted).  sh->out_dt is ignored.
+ */
+twell_status twell_gate_pack(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
+                             twell_mat *h, hipStream_t stream);
+
+/*
+ * twell_sparse_up: a[t,n] = h[t,n] * (x_t . WuT[n]) for every (t, n) stored
+ *   in h, fp32, written at the same slot positions as h->val into aval
+ *   ([NR][NT][64][16] floats; aval may be h->val itself, which is then
+ *   overwritten).  Slots that hold no stored pair are not written.
+ */
+twell_status twell_sparse_up(const twell_ffn_shape *sh, const void *x, const void *WuT, const twell_mat *h,
+                             float *aval, hipStream_t stream);
+
+/*
+ * twell_sparse_down: y_t = sum over the pairs (t, n) stored in pattern of
+ *   a[t,n] * Wd[n] (a read from aval at pattern's slot positions), for every
+ *   row t; y is [T][d] in sh->out_dt.  fp32 accumulation; a enters the bf16
+ *   matrix cores as a hi + lo pair of bf16 values.
+ */
+twell_status twell_sparse_down(const twell_ffn_shape *sh, const float *aval, const void *Wd,
+                               const twell_mat *pattern, void *y, hipStream_t stream);
+
+/* Workspace bytes for twell_ffn_dense_fwd. */
+size_t twell_ffn_dense_fwd_workspace(const twell_ffn_shape *sh);
+
+/*
+ * twell_ffn_dense_fwd: the same layer computed densely (the library's own
+ * dense MFMA baseline, bf16 only): a fused gate/up GEMM writes
+ * act = bf16(ReLU(g) * u) for every (t, n), then y = act . Wd.
+ * Arguments as for twell_ffn_fwd.
+ */
+twell_status twell_ffn_dense_fwd(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
+                                 const void *WuT, const void *Wd, void *y, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* Static description of a status code. */
+const char *twell_status_string(twell_status st);
+/* Thread-local description of the last error returned on this thread. */
+const char *twell_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWELL_H */

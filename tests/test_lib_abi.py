@@ -1,0 +1,97 @@
+"""Host-side checks of libtwell that need no GPU: the library loads against
+the installed ROCm runtime, exports every function include/twell.h declares,
+and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import activation_sparse_feedforward_gate_amd as tw
+from activation_sparse_feedforward_gate_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_header_function():
+    L = tw.lib()
+    names = tw.header_functions()
+    assert {"twell_pack", "twell_ffn_fwd", "twell_ffn_dense_fwd", "twell_unpack"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libtwell.so does not export {n}"
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_header_is_plain_c():
+    """The public header compiles as C (no torch, no C++ types in signatures)."""
+    src = '#include "twell.h"\nint main(void){ twell_mat m; (void)m; return (int)TWELL_OK; }\n'
+    r = subprocess.run(["gcc", "-x", "c", "-std=c99", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", "-"],
+                       input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_mat_bytes():
+    total, parts = tw.twell_mat_bytes(33, 128, 16, 64, tw.TWELL_F32)
+    NR, NT = 3, 2
+    assert parts == [33 * NT, NR * NT, NR * NT * 64 * 16 * 4, NR * NT * 64 * 16, 33 * NT * 8]
+    assert total == sum(parts)
+    _, p16 = tw.twell_mat_bytes(33, 128, 16, 64, tw.TWELL_BF16)
+    assert p16[2] == NR * NT * 64 * 16 * 2
+
+
+def _call_fwd(shape, **kw):
+    L = tw.lib()
+    args = dict(x=16, WgT=32, bg=None, WuT=48, Wd=64, y=80, saved=None, thr=-1, ws=None, ws_bytes=0)
+    args.update(kw)
+    return L.twell_ffn_fwd(ctypes.byref(shape) if shape is not None else None, args["x"], args["WgT"], args["bg"],
+                           args["WuT"], args["Wd"], args["y"], args["saved"], args["thr"], args["ws"],
+                           args["ws_bytes"], None)
+
+
+def test_fwd_argument_errors_are_synchronous():
+    L = tw.lib()
+    sh = tw.ffn_shape(64, 128, 512, tw.TWELL_BF16, tw.TWELL_F32)
+    assert _call_fwd(None) == tw.TWELL_EINVAL
+    assert _call_fwd(sh, x=None) == tw.TWELL_EINVAL
+    assert _call_fwd(tw.ffn_shape(64, 100, 512, tw.TWELL_BF16, tw.TWELL_F32)) == tw.TWELL_EUNSUPPORTED
+    assert _call_fwd(tw.ffn_shape(64, 128, 500, tw.TWELL_BF16, tw.TWELL_F32)) == tw.TWELL_EUNSUPPORTED
+    assert _call_fwd(tw.ffn_shape(-1, 128, 512, tw.TWELL_BF16, tw.TWELL_F32)) == tw.TWELL_EINVAL
+    assert _call_fwd(tw.ffn_shape(64, 128, 512, 7, tw.TWELL_F32)) == tw.TWELL_EINVAL
+    assert _call_fwd(sh, x=16 + 2) == tw.TWELL_EINVAL         # misaligned
+    need = tw.twell_ffn_fwd_workspace(sh)
+    assert need > 0
+    assert _call_fwd(sh, ws=4096, ws_bytes=need - 1) == tw.TWELL_EWORKSPACE
+    assert b"workspace" in L.twell_last_error()
+    # empty batch: nothing to do, nothing launched
+    assert _call_fwd(tw.ffn_shape(0, 128, 512, tw.TWELL_BF16, tw.TWELL_F32), ws=4096,
+                     ws_bytes=tw.twell_ffn_fwd_workspace(tw.ffn_shape(0, 128, 512, tw.TWELL_BF16, tw.TWELL_F32))) \
+        == tw.TWELL_OK
+
+
+def test_pack_argument_errors():
+    L = tw.lib()
+    m = tw.c_twell_mat(32, 128, 16, 64, tw.TWELL_F32, 16, 16, 16, 16, None)
+    assert L.twell_pack(None, tw.TWELL_F32, 128, ctypes.byref(m), None) == tw.TWELL_EINVAL
+    assert L.twell_pack(64, tw.TWELL_BF16, 128, ctypes.byref(m), None) == tw.TWELL_EINVAL   # dtype mismatch
+    assert L.twell_pack(64, tw.TWELL_F32, 64, ctypes.byref(m), None) == tw.TWELL_EINVAL     # ldg < F
+    m8 = tw.c_twell_mat(32, 128, 8, 64, tw.TWELL_F32, 16, 16, 16, 16, None)
+    assert L.twell_pack(64, tw.TWELL_F32, 128, ctypes.byref(m8), None) == tw.TWELL_EUNSUPPORTED
+    m0 = tw.c_twell_mat(0, 128, 16, 64, tw.TWELL_F32, None, None, None, None, None)
+    assert L.twell_pack(None, tw.TWELL_F32, 128, ctypes.byref(m0), None) == tw.TWELL_OK
+    assert L.twell_pack(64, tw.TWELL_F32, 128, None, None) == tw.TWELL_EINVAL
+
+
+def test_dense_baseline_argument_errors():
+    L = tw.lib()
+    sh = tw.ffn_shape(64, 128, 512, tw.TWELL_F32, tw.TWELL_F32)
+    assert L.twell_ffn_dense_fwd(ctypes.byref(sh), 16, 16, None, 16, 16, 16, 16, 1 << 20, None) == tw.TWELL_EUNSUPPORTED
+    sh = tw.ffn_shape(64, 128, 512, tw.TWELL_BF16, tw.TWELL_F32)
+    assert L.twell_ffn_dense_fwd(ctypes.byref(sh), 16, 16, None, 16, 16, 16, 16, 1, None) == tw.TWELL_EWORKSPACE
+
+
+def test_status_strings():
+    for st in range(5):
+        assert tw.twell_status_string(st)
