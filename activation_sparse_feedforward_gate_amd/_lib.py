@@ -56,6 +56,10 @@ def lib() -> ctypes.CDLL:
         L.twell_ffn_fwd_workspace.argtypes = [P(c_twell_ffn_shape), i32]
         L.twell_ffn_fwd_workspace.restype = sz
         L.twell_ffn_fwd.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_mat), i32, vp, sz, vp]
+        L.twell_ffn_bwd_workspace.argtypes = [P(c_twell_ffn_shape), i32]
+        L.twell_ffn_bwd_workspace.restype = sz
+        L.twell_ffn_bwd_hybrid.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_mat), i32,
+                                           vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.twell_gate_pack.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, P(c_twell_mat), vp]
         L.twell_sparse_up.argtypes = [P(c_twell_ffn_shape), vp, vp, P(c_twell_mat), vp, vp]
         L.twell_sparse_down.argtypes = [P(c_twell_ffn_shape), vp, vp, P(c_twell_mat), vp, vp]
@@ -66,7 +70,8 @@ def lib() -> ctypes.CDLL:
         L.twell_status_string.restype = ctypes.c_char_p
         L.twell_last_error.argtypes = []
         L.twell_last_error.restype = ctypes.c_char_p
-        for name in ("twell_pack", "twell_unpack", "twell_ffn_fwd", "twell_ffn_dense_fwd", "twell_gate_pack",
+        for name in ("twell_pack", "twell_unpack", "twell_ffn_fwd", "twell_ffn_bwd_hybrid", "twell_ffn_dense_fwd",
+                     "twell_gate_pack",
                      "twell_sparse_up", "twell_sparse_down"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -181,6 +186,20 @@ def twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, saved_h: Optional[TwellMat], de
                                ctypes.byref(sh) if sh is not None else None, dense_row_threshold,
                                _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
                                _stream(stream)))
+
+
+def twell_ffn_bwd_workspace(shape: c_twell_ffn_shape, dense_row_threshold: int) -> int:
+    return int(lib().twell_ffn_bwd_workspace(ctypes.byref(shape), int(dense_row_threshold)))
+
+
+def twell_ffn_bwd_hybrid(shape, x, WgT, bg, WuT, Wd, dY, saved_h: TwellMat, dense_row_threshold: int,
+                         dX, dWgT, dWuT, dWd, dbg, n_dense_rows, ws, stream=None) -> None:
+    hm = saved_h.c()
+    _check(lib().twell_ffn_bwd_hybrid(ctypes.byref(shape), _ptr(x), _ptr(WgT), _ptr(bg), _ptr(WuT), _ptr(Wd),
+                                      _ptr(dY), ctypes.byref(hm), int(dense_row_threshold), _ptr(dX), _ptr(dWgT),
+                                      _ptr(dWuT), _ptr(dWd), _ptr(dbg), _ptr(n_dense_rows), _ptr(ws),
+                                      ws.numel() * ws.element_size() if ws is not None else 0,
+                                      _stream(stream)))
 
 
 def twell_gate_pack(shape, x, WgT, bg, h: TwellMat, stream=None) -> None:

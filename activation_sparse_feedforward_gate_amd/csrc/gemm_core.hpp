@@ -295,21 +295,26 @@ struct GemmTile {
   static constexpr int TM = Cfg::TM, TN = Cfg::TN, NB = Cfg::NB, NTH = Cfg::NTH;
   f32x16 acc[NB][TM][TN];
 
-  // Multiply the MxN block at (m0, n0) over K; LDS is Cfg::LDS_BYTES.
-  __device__ void run(const Operand& A, const Operand* B, int m0, int n0, int K, char* lds) {
+  // Multiply the MxN block at (m0, n0) over K; LDS is Cfg::LDS_BYTES.  With
+  // zero == false the products are added to the accumulators already held
+  // (a second operand pair summed into the same block).
+  __device__ void run(const Operand& A, const Operand* B, int m0, int n0, int K, char* lds,
+                      bool zero = true) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wr = (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
     const int wc = (wave % Cfg::WN) * (Cfg::BN / Cfg::WN);
+    if (zero) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+          for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) acc[b][i][j][e] = 0.f;
+            for (int e = 0; e < 16; ++e) acc[b][i][j][e] = 0.f;
+    }
 
     Loader<Cfg::A_KIND, Cfg::BM, NTH> la;
     Loader<Cfg::B_KIND, Cfg::BN, NTH> lb[NB];

@@ -42,6 +42,48 @@ hipError_t launch_spmm_down(int in_dt, int out_dt, const float* aval, const void
                             int d, int F, const TwellView& pat, void* y, const uint8_t* skip,
                             hipStream_t s);
 
+// Backward SDDMM on the pattern of h (rows with skip[t] != 0 untouched):
+//   u = x_t.WuT[n], da = dY_t.Wd[n];  a = h*u, dg = da*u, du = da*h
+// written at the TwELL slot positions of h into aval, dgval, duval.
+hipError_t launch_sddmm_bwd(int in_dt, const void* x, const void* dY, const void* WuT, const void* Wd, int T,
+                            int d, int F, const TwellView& h, float* aval, float* dgval, float* duval,
+                            const uint8_t* skip, hipStream_t s);
+
+// Backward SpMM: dX_t = sum over stored n of dg*WgT[n] + du*WuT[n] (fp32),
+// rows with skip[t] != 0 not written.
+hipError_t launch_spmm_dx(int in_dt, const float* dgval, const float* duval, const void* WgT, const void* WuT,
+                          int T, int d, int F, const TwellView& pat, float* dX, const uint8_t* skip,
+                          hipStream_t s);
+
+// Row classification of the hybrid format: flag[t] = (sum_j cnt[t][j] > tau);
+// list[0..n) = flagged rows ascending; *n_out = n (and *n_copy if non-null).
+hipError_t launch_classify(const TwellView& h, int tau, uint8_t* flag, int* list, int* n_out, int* n_copy,
+                           hipStream_t s);
+
+// Dense-branch forward on the listed rows: actbuf [T][F] (rows < n used)
+// receives ReLU(g)*u, then y[list[r]] = actbuf[r].Wd.
+hipError_t launch_dense_rows_fwd(int in_dt, const void* x, const void* WgT, const void* bg, const void* WuT,
+                                 const void* Wd, int T, int d, int F, const int* rows, const int* n_rows,
+                                 float* actbuf, int out_dt, void* y, hipStream_t s);
+
+// Dense-branch backward on the listed rows: buf3 [T][3F] receives [dG|dU|A];
+// dX[list[r]] written; dWgT, dWuT, dWd (and dbg if non-null) are WRITTEN with
+// the dense rows' contributions (zero when there are none).  dbg_part is
+// [ceil(T/64)][F] scratch.
+hipError_t launch_dense_rows_bwd(int in_dt, const void* x, const void* WgT, const void* bg, const void* WuT,
+                                 const void* Wd, const void* dY, int T, int d, int F, const int* rows,
+                                 const int* n_rows, float* buf3, float* dbg_part, float* dX, float* dWgT,
+                                 float* dWuT, float* dWd, float* dbg, hipStream_t s);
+
+// Sparse-branch weight gradients, ADDED to dWgT, dWuT, dWd (and dbg): a
+// column-major index of the stored pairs of rows with skip[t] == 0 is built
+// (part: [ceil(T/256)][F] ints, start: [F+1] ints, entries: one u32 per
+// pair), then per neuron the sums over its tokens in ascending order.
+hipError_t launch_sparse_wgrad(int in_dt, const void* x, const void* dY, int T, int d, int F,
+                               const TwellView& h, const uint8_t* skip, int* part, int* start,
+                               uint32_t* entries, const float* aval, const float* dgval, const float* duval,
+                               float* dWgT, float* dWuT, float* dWd, float* dbg, hipStream_t s);
+
 // Dense baseline: act = ReLU(x.WgT^T + bg) * (x.WuT^T) in bf16 (fused dual GEMM),
 // then y = act.Wd.  act is a [T][F] bf16 workspace.
 hipError_t launch_dense_fwd(const void* x, const void* WgT, const void* bg, const void* WuT,

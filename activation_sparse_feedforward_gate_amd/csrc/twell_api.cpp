@@ -87,23 +87,74 @@ TwellView view_of(const twell_mat* m) {
   return v;
 }
 
-// Workspace of the inference forward: one TwELL (fp32 values, with mask).
+// Workspace of the forward: one TwELL (fp32 values, with mask; with saved_h
+// only its value array is used, for a); training adds the row classification
+// and the dense rows' activation buffer.
 struct FwdWs {
   TwellView h;
+  uint8_t* flag;
+  int* list;
+  int* nD;
+  float* act;
 };
 
-size_t fwd_layout(const twell_ffn_shape* sh, void* ws, FwdWs* out) {
+size_t fwd_layout(const twell_ffn_shape* sh, bool training, void* ws, FwdWs* out) {
   size_t parts[5];
   mat_parts(sh->T, sh->F, GPU_R, GPU_C, TWELL_F32, parts);
   Carver c(ws);
-  TwellView v;
+  FwdWs w{};
+  TwellView& v = w.h;
   v.T = sh->T; v.F = sh->F; v.NT = sh->F / GPU_C; v.NR = (sh->T + GPU_R - 1) / GPU_R;
   v.cnt = (uint8_t*)c.take(parts[0]);
   v.width = (uint8_t*)c.take(parts[1]);
   v.val = c.take(parts[2]);
   v.idx = (uint8_t*)c.take(parts[3]);
   v.mask = (uint64_t*)c.take(parts[4]);
-  if (out) out->h = v;
+  if (training) {
+    w.flag = (uint8_t*)c.take((size_t)sh->T);
+    w.list = (int*)c.take((size_t)sh->T * 4);
+    w.nD = (int*)c.take(4);
+    w.act = (float*)c.take((size_t)sh->T * sh->F * 4);
+  }
+  if (out) *out = w;
+  return c.off;
+}
+
+// Workspace of the hybrid backward.
+struct BwdWs {
+  uint8_t* flag;
+  int* list;
+  int* nD;
+  float* buf3;       // [T][3F]
+  float* dbg_part;   // [ceil(T/64)][F]
+  float* aval;       // TwELL-shaped value arrays
+  float* dgval;
+  float* duval;
+  int* part;         // [ceil(T/256)][F]
+  int* start;        // [F+1]
+  uint32_t* entries; // one per stored pair of a sparse row
+};
+
+size_t bwd_layout(const twell_ffn_shape* sh, int32_t tau, void* ws, BwdWs* out) {
+  const int64_t T = sh->T, F = sh->F;
+  const int64_t NR = (T + GPU_R - 1) / GPU_R, NT = F / GPU_C;
+  const size_t slots = (size_t)(NR * NT * GPU_C * GPU_R);
+  // a sparse row holds at most min(F, tau) pairs
+  const int64_t per_row = tau < 0 ? 0 : (tau < F ? tau : F);
+  Carver c(ws);
+  BwdWs w{};
+  w.flag = (uint8_t*)c.take((size_t)T);
+  w.list = (int*)c.take((size_t)T * 4);
+  w.nD = (int*)c.take(4);
+  w.buf3 = (float*)c.take((size_t)(T * 3 * F) * 4);
+  w.dbg_part = (float*)c.take((size_t)(((T + 63) / 64) * F) * 4);
+  w.aval = (float*)c.take(slots * 4);
+  w.dgval = (float*)c.take(slots * 4);
+  w.duval = (float*)c.take(slots * 4);
+  w.part = (int*)c.take((size_t)(((T + 255) / 256) * F) * 4);
+  w.start = (int*)c.take((size_t)(F + 1) * 4);
+  w.entries = (uint32_t*)c.take((size_t)(T * per_row) * 4);
+  if (out) *out = w;
   return c.off;
 }
 
@@ -140,8 +191,7 @@ twell_status twell_unpack(const twell_mat* in, void* H, int64_t ldh, hipStream_t
 
 size_t twell_ffn_fwd_workspace(const twell_ffn_shape* sh, int32_t training) {
   if (!sh || check_shape(sh) != TWELL_OK) return 0;
-  (void)training;
-  return fwd_layout(sh, nullptr, nullptr);
+  return fwd_layout(sh, training != 0, nullptr, nullptr);
 }
 
 twell_status twell_ffn_fwd(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
@@ -158,14 +208,14 @@ twell_status twell_ffn_fwd(const twell_ffn_shape* sh, const void* x, const void*
     if (saved_h->T != sh->T || saved_h->F != sh->F || saved_h->vdtype != TWELL_F32)
       return fail(TWELL_EINVAL, "saved_h must be T x F with fp32 values");
   }
-  if (dense_row_threshold >= 0)
-    return fail(TWELL_EUNSUPPORTED, "the hybrid forward (dense_row_threshold >= 0) is not built yet");
-  const size_t need = fwd_layout(sh, nullptr, nullptr);
+  const bool training = dense_row_threshold >= 0;
+  if (training && !saved_h) return fail(TWELL_EINVAL, "the hybrid forward (dense_row_threshold >= 0) needs saved_h");
+  const size_t need = fwd_layout(sh, training, nullptr, nullptr);
   if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
   if (sh->T == 0) return TWELL_OK;
 
   FwdWs w;
-  fwd_layout(sh, ws, &w);
+  fwd_layout(sh, training, ws, &w);
   const int in_dt = sh->in_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
   const int out_dt = sh->out_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
   TwellView h = w.h;
@@ -176,10 +226,68 @@ twell_status twell_ffn_fwd(const twell_ffn_shape* sh, const void* x, const void*
   }
   hipError_t e = launch_gate_twell(in_dt, x, WgT, bg, sh->T, sh->d, sh->F, h, stream);
   if (e != hipSuccess) return hip_status(e, "gate GEMM");
-  e = launch_sddmm_up(in_dt, x, WuT, sh->T, sh->d, sh->F, h, aval, nullptr, stream);
+  const uint8_t* skip = nullptr;
+  if (training) {
+    e = launch_classify(h, dense_row_threshold, w.flag, w.list, w.nD, nullptr, stream);
+    if (e != hipSuccess) return hip_status(e, "row classification");
+    skip = w.flag;
+  }
+  e = launch_sddmm_up(in_dt, x, WuT, sh->T, sh->d, sh->F, h, aval, skip, stream);
   if (e != hipSuccess) return hip_status(e, "sparse up-projection");
-  e = launch_spmm_down(in_dt, out_dt, aval, Wd, sh->T, sh->d, sh->F, h, y, nullptr, stream);
-  return hip_status(e, "sparse down-projection");
+  e = launch_spmm_down(in_dt, out_dt, aval, Wd, sh->T, sh->d, sh->F, h, y, skip, stream);
+  if (e != hipSuccess) return hip_status(e, "sparse down-projection");
+  if (training) {
+    e = launch_dense_rows_fwd(in_dt, x, WgT, bg, WuT, Wd, sh->T, sh->d, sh->F, w.list, w.nD, w.act, out_dt, y,
+                              stream);
+    if (e != hipSuccess) return hip_status(e, "dense-row forward");
+  }
+  return TWELL_OK;
+}
+
+size_t twell_ffn_bwd_workspace(const twell_ffn_shape* sh, int32_t dense_row_threshold) {
+  if (!sh || check_shape(sh) != TWELL_OK) return 0;
+  return bwd_layout(sh, dense_row_threshold, nullptr, nullptr);
+}
+
+twell_status twell_ffn_bwd_hybrid(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
+                                  const void* WuT, const void* Wd, const void* dY, const twell_mat* saved_h,
+                                  int32_t dense_row_threshold, float* dX, float* dWgT, float* dWuT, float* dWd,
+                                  float* dbg, int32_t* n_dense_rows, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  twell_status st = check_shape(sh);
+  if (st) return st;
+  if (!WgT || !WuT || !Wd || !dWgT || !dWuT || !dWd) return fail(TWELL_EINVAL, "NULL weight or gradient argument");
+  if (sh->T > 0 && (!x || !dY || !dX)) return fail(TWELL_EINVAL, "NULL tensor argument");
+  for (const void* p : {x, WgT, bg, WuT, Wd, dY, (const void*)dX, (const void*)dWgT, (const void*)dWuT,
+                        (const void*)dWd, (const void*)dbg})
+    if (!aligned16(p)) return fail(TWELL_EINVAL, "tensors must be 16-byte aligned");
+  st = check_mat(saved_h, true);
+  if (st) return st;
+  if (saved_h->T != sh->T || saved_h->F != sh->F || saved_h->vdtype != TWELL_F32)
+    return fail(TWELL_EINVAL, "saved_h must be T x F with fp32 values");
+  const int64_t NR = (sh->T + GPU_R - 1) / GPU_R;
+  if (NR * (sh->F / GPU_C) * GPU_C * GPU_R >= ((int64_t)1 << 32))
+    return fail(TWELL_EUNSUPPORTED, "T x F too large for 32-bit TwELL slot offsets");
+  const size_t need = bwd_layout(sh, dense_row_threshold, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+
+  BwdWs w;
+  bwd_layout(sh, dense_row_threshold, ws, &w);
+  const int in_dt = sh->in_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
+  const TwellView h = view_of(saved_h);
+  const int T = sh->T, d = sh->d, F = sh->F;
+  hipError_t e = launch_classify(h, dense_row_threshold, w.flag, w.list, w.nD, n_dense_rows, stream);
+  if (e != hipSuccess) return hip_status(e, "row classification");
+  e = launch_dense_rows_bwd(in_dt, x, WgT, bg, WuT, Wd, dY, T, d, F, w.list, w.nD, w.buf3, w.dbg_part, dX, dWgT,
+                            dWuT, dWd, dbg, stream);
+  if (e != hipSuccess) return hip_status(e, "dense-row backward");
+  e = launch_sddmm_bwd(in_dt, x, dY, WuT, Wd, T, d, F, h, w.aval, w.dgval, w.duval, w.flag, stream);
+  if (e != hipSuccess) return hip_status(e, "sparse backward SDDMM");
+  e = launch_spmm_dx(in_dt, w.dgval, w.duval, WgT, WuT, T, d, F, h, dX, w.flag, stream);
+  if (e != hipSuccess) return hip_status(e, "sparse backward dX");
+  e = launch_sparse_wgrad(in_dt, x, dY, T, d, F, h, w.flag, w.part, w.start, w.entries, w.aval, w.dgval,
+                          w.duval, dWgT, dWuT, dWd, dbg, stream);
+  return hip_status(e, "sparse weight gradients");
 }
 
 static twell_status check_tensors(const twell_ffn_shape* sh, std::initializer_list<const void*> ptrs) {

@@ -29,12 +29,16 @@
 namespace twell {
 
 struct SparseArgs {
-  const void* x;          // [T][d] (up)
-  const void* W;          // WuT (up) or Wd (down), [F][d]
+  const void* x;          // [T][d] (up; backward: x)
+  const void* W;          // WuT (up) or Wd / WgT (down), [F][d]
+  const void* x2;         // backward up: dY [T][d]
+  const void* W2;         // backward up: Wd; backward down: WuT
   int T, d, F, NT, NR;
   const uint64_t* mask;   // [T][NT]
   const float* hval;      // up: h values in TwELL layout
-  float* aval;            // up: output; down: input
+  float* aval;            // up: output a; down: input values
+  float* dgval;           // backward up: output dg = da*u; backward down: input (with W)
+  float* duval;           // backward up: output du = da*h; backward down: input (with W2)
   const uint8_t* skip;    // [T] or null
   void* y;                // down output [T][d]
   int out_bf16;
@@ -65,7 +69,9 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane, int* total) {
 
 // ------------------------------------------------------------------ up (SDDMM)
 
-template <bool BF16IN>
+// BWD: also da = dY_t . Wd[n] on the same pattern, and the outputs become
+// a = h*u, dg = da*u, du = da*h (the backward pass's per-pair quantities).
+template <bool BF16IN, bool BWD>
 __global__ __launch_bounds__(256) void sddmm_up_kernel(SparseArgs a) {
   __shared__ uint64_t smask[SP_WPB][16][UP_MAXT];
   __shared__ uint16_t sunion[SP_WPB][UP_MAXT * 64];
@@ -95,29 +101,43 @@ __global__ __launch_bounds__(256) void sddmm_up_kernel(SparseArgs a) {
 
   constexpr int KS = BF16IN ? 32 : 16;           // k per MFMA step
   constexpr int ESZ = BF16IN ? 2 : 4;
-  const char* xrow = (const char*)a.x + ((int64_t)min(t0 + (lane & 15), a.T - 1) * a.d) * ESZ;
+  const int64_t xoff = ((int64_t)min(t0 + (lane & 15), a.T - 1) * a.d) * ESZ;
+  const char* xrow = (const char*)a.x + xoff;
+  const char* yrow = BWD ? (const char*)a.x2 + xoff : nullptr;
   const int koff = (lane >> 4) * (KS / 4);       // element offset of my fragment
   const int npad = (total + 15) & ~15;
   for (int base = 0; base < npad; base += 16 * UP_NBLK) {
     const int nb = min(UP_NBLK, (npad - base) >> 4);
-    const char* wrow[UP_NBLK];
+    int64_t wofs[UP_NBLK];
 #pragma unroll
     for (int b = 0; b < UP_NBLK; ++b) {
       const int q = base + b * 16 + (lane & 15);
       const int n = sunion[w][q < total ? q : 0];
-      wrow[b] = (const char*)a.W + ((int64_t)n * a.d) * ESZ;
+      wofs[b] = ((int64_t)n * a.d) * ESZ;
     }
-    f32x4 acc[UP_NBLK];
+    f32x4 acc[UP_NBLK], acc2[BWD ? UP_NBLK : 1];
 #pragma unroll
     for (int b = 0; b < UP_NBLK; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (BWD) {
+#pragma unroll
+      for (int b = 0; b < UP_NBLK; ++b) acc2[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     for (int k0 = 0; k0 < a.d; k0 += KS) {
-      const uint4 fa = *(const uint4*)(xrow + (int64_t)(k0 + koff) * ESZ);
+      const int64_t ko = (int64_t)(k0 + koff) * ESZ;
+      const uint4 fa = *(const uint4*)(xrow + ko);
+      uint4 fy;
+      if constexpr (BWD) fy = *(const uint4*)(yrow + ko);
 #pragma unroll
       for (int b = 0; b < UP_NBLK; ++b) {
         if (b < nb) {
-          const uint4 fb = *(const uint4*)(wrow[b] + (int64_t)(k0 + koff) * ESZ);
+          const uint4 fb = *(const uint4*)((const char*)a.W + wofs[b] + ko);
           if constexpr (BF16IN) acc[b] = mfma16(fa, fb, acc[b]);
           else acc[b] = mfma16_f32(fa, fb, acc[b]);
+          if constexpr (BWD) {
+            const uint4 fd = *(const uint4*)((const char*)a.W2 + wofs[b] + ko);
+            if constexpr (BF16IN) acc2[b] = mfma16(fy, fd, acc2[b]);
+            else acc2[b] = mfma16_f32(fy, fd, acc2[b]);
+          }
         }
       }
     }
@@ -134,7 +154,12 @@ __global__ __launch_bounds__(256) void sddmm_up_kernel(SparseArgs a) {
           if ((M >> c) & 1ull) {
             const int slot = popc64(M & below(c));
             const int64_t off = ((int64_t)grp * a.NT + j) * 1024 + slot * 16 + r;
-            a.aval[off] = a.hval[off] * acc[b][i];
+            const float h = a.hval[off];
+            a.aval[off] = h * acc[b][i];
+            if constexpr (BWD) {
+              a.dgval[off] = acc2[b][i] * acc[b][i];
+              a.duval[off] = acc2[b][i] * h;
+            }
           }
         }
       }
@@ -144,7 +169,9 @@ __global__ __launch_bounds__(256) void sddmm_up_kernel(SparseArgs a) {
 
 // ------------------------------------------------------------------ down (SpMM)
 
-template <bool BF16IN>
+// TWO: y_t = sum over stored n of dgval*W[n] + duval*W2[n] (the backward
+// pass's dX = dG.WgT + dU.WuT on the sparse rows); otherwise aval*W[n].
+template <bool BF16IN, bool TWO>
 __global__ __launch_bounds__(256) void spmm_down_kernel(SparseArgs a) {
   __shared__ uint64_t smask[SP_WPB][16][DN_TCH];
   __shared__ uint16_t sunion[SP_WPB][DN_TCH * 64];
@@ -182,12 +209,16 @@ __global__ __launch_bounds__(256) void spmm_down_kernel(SparseArgs a) {
     __syncthreads();
 
     for (int kc = 0; kc < total; kc += KC) {
-      uint32_t ahi[EPL], alo[EPL];
+      constexpr int NV = TWO ? 2 : 1;
+      const float* vsrc[2] = {TWO ? a.dgval : a.aval, a.duval};
+      uint32_t ahi[NV][EPL], alo[NV][EPL];
       int nid[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int q = kc + (lane >> 4) * EPL + e;
-        float av = 0.f;
+        float av[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) av[v] = 0.f;
         int n = 0;
         if (q < total) {
           n = sunion[w][q];
@@ -195,39 +226,54 @@ __global__ __launch_bounds__(256) void spmm_down_kernel(SparseArgs a) {
           const uint64_t M = smask[w][r_a][j - jc];
           if ((M >> c) & 1ull) {
             const int slot = popc64(M & below(c));
-            av = a.aval[((int64_t)grp * a.NT + j) * 1024 + slot * 16 + r_a];
+            const int64_t off = ((int64_t)grp * a.NT + j) * 1024 + slot * 16 + r_a;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) av[v] = vsrc[v][off];
           }
         }
         nid[e] = n;
-        if constexpr (BF16IN) split_bf16(av, ahi[e], alo[e]);
-        else ahi[e] = __float_as_uint(av);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          if constexpr (BF16IN) split_bf16(av[v], ahi[v][e], alo[v][e]);
+          else ahi[v][e] = __float_as_uint(av[v]);
+        }
       }
-      uint4 Ahi, Alo;
-      if constexpr (BF16IN) {
-        Ahi = make_uint4(ahi[0] | (ahi[1] << 16), ahi[2] | (ahi[3] << 16), ahi[4] | (ahi[5] << 16), ahi[6] | (ahi[7] << 16));
-        Alo = make_uint4(alo[0] | (alo[1] << 16), alo[2] | (alo[3] << 16), alo[4] | (alo[5] << 16), alo[6] | (alo[7] << 16));
-      } else {
-        Ahi = make_uint4(ahi[0], ahi[1], ahi[2], ahi[3]);
-        Alo = Ahi;
+      uint4 Ahi[NV], Alo[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        if constexpr (BF16IN) {
+          Ahi[v] = make_uint4(ahi[v][0] | (ahi[v][1] << 16), ahi[v][2] | (ahi[v][3] << 16),
+                              ahi[v][4] | (ahi[v][5] << 16), ahi[v][6] | (ahi[v][7] << 16));
+          Alo[v] = make_uint4(alo[v][0] | (alo[v][1] << 16), alo[v][2] | (alo[v][3] << 16),
+                              alo[v][4] | (alo[v][5] << 16), alo[v][6] | (alo[v][7] << 16));
+        } else {
+          Ahi[v] = make_uint4(ahi[v][0], ahi[v][1], ahi[v][2], ahi[v][3]);
+          Alo[v] = Ahi[v];
+        }
       }
 #pragma unroll
       for (int cb = 0; cb < DN_MAXCB; ++cb) {
         if (cb < ncb) {
           const int col = (cb0 + cb) * 16 + (lane & 15);
-          uint4 B;
-          if constexpr (BF16IN) {
-            const uint16_t* W = (const uint16_t*)a.W;
-            uint32_t v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = W[(int64_t)nid[e] * a.d + col];
-            B = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
-            acc[cb] = mfma16(Ahi, B, acc[cb]);
-            acc[cb] = mfma16(Alo, B, acc[cb]);
-          } else {
-            const uint32_t* W = (const uint32_t*)a.W;
-            B = make_uint4(W[(int64_t)nid[0] * a.d + col], W[(int64_t)nid[1] * a.d + col],
-                           W[(int64_t)nid[2] * a.d + col], W[(int64_t)nid[3] * a.d + col]);
-            acc[cb] = mfma16_f32(Ahi, B, acc[cb]);
+          for (int v = 0; v < NV; ++v) {
+            const void* Wv = v == 0 ? a.W : a.W2;
+            uint4 B;
+            if constexpr (BF16IN) {
+              const uint16_t* W = (const uint16_t*)Wv;
+              uint32_t bv[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) bv[e] = W[(int64_t)nid[e] * a.d + col];
+              B = make_uint4(bv[0] | (bv[1] << 16), bv[2] | (bv[3] << 16), bv[4] | (bv[5] << 16),
+                             bv[6] | (bv[7] << 16));
+              acc[cb] = mfma16(Ahi[v], B, acc[cb]);
+              acc[cb] = mfma16(Alo[v], B, acc[cb]);
+            } else {
+              const uint32_t* W = (const uint32_t*)Wv;
+              B = make_uint4(W[(int64_t)nid[0] * a.d + col], W[(int64_t)nid[1] * a.d + col],
+                             W[(int64_t)nid[2] * a.d + col], W[(int64_t)nid[3] * a.d + col]);
+              acc[cb] = mfma16_f32(Ahi[v], B, acc[cb]);
+            }
           }
         }
       }
@@ -266,8 +312,22 @@ hipError_t launch_sddmm_up(int in_dt, const void* x, const void* WuT, int T, int
   a.nslices = choose_slices(a.NT, UP_MAXT);
   if (a.NR == 0) return hipSuccess;
   const int grid = ((a.NR + SP_WPB - 1) / SP_WPB) * a.nslices;
-  if (in_dt == DT_BF16) hipLaunchKernelGGL(sddmm_up_kernel<true>, dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(sddmm_up_kernel<false>, dim3(grid), dim3(256), 0, s, a);
+  if (in_dt == DT_BF16) hipLaunchKernelGGL((sddmm_up_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((sddmm_up_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sddmm_bwd(int in_dt, const void* x, const void* dY, const void* WuT, const void* Wd, int T,
+                            int d, int F, const TwellView& h, float* aval, float* dgval, float* duval,
+                            const uint8_t* skip, hipStream_t s) {
+  SparseArgs a{};
+  a.x = x; a.x2 = dY; a.W = WuT; a.W2 = Wd; a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
+  a.mask = h.mask; a.hval = (const float*)h.val; a.aval = aval; a.dgval = dgval; a.duval = duval; a.skip = skip;
+  a.nslices = choose_slices(a.NT, UP_MAXT);
+  if (a.NR == 0) return hipSuccess;
+  const int grid = ((a.NR + SP_WPB - 1) / SP_WPB) * a.nslices;
+  if (in_dt == DT_BF16) hipLaunchKernelGGL((sddmm_up_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((sddmm_up_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -280,8 +340,23 @@ hipError_t launch_spmm_down(int in_dt, int out_dt, const float* aval, const void
   if (d / 16 < a.nslices) a.nslices = d / 16;
   if (a.NR == 0) return hipSuccess;
   const int grid = ((a.NR + SP_WPB - 1) / SP_WPB) * a.nslices;
-  if (in_dt == DT_BF16) hipLaunchKernelGGL(spmm_down_kernel<true>, dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(spmm_down_kernel<false>, dim3(grid), dim3(256), 0, s, a);
+  if (in_dt == DT_BF16) hipLaunchKernelGGL((spmm_down_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((spmm_down_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_spmm_dx(int in_dt, const float* dgval, const float* duval, const void* WgT, const void* WuT,
+                          int T, int d, int F, const TwellView& pat, float* dX, const uint8_t* skip,
+                          hipStream_t s) {
+  SparseArgs a{};
+  a.W = WgT; a.W2 = WuT; a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
+  a.mask = pat.mask; a.dgval = (float*)dgval; a.duval = (float*)duval; a.skip = skip; a.y = dX; a.out_bf16 = 0;
+  a.nslices = choose_slices(d / 16, DN_MAXCB);
+  if (d / 16 < a.nslices) a.nslices = d / 16;
+  if (a.NR == 0) return hipSuccess;
+  const int grid = ((a.NR + SP_WPB - 1) / SP_WPB) * a.nslices;
+  if (in_dt == DT_BF16) hipLaunchKernelGGL((spmm_down_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((spmm_down_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -113,7 +113,7 @@ twell_status twell_pack(const void *G, twell_dtype gdtype, int64_t ldg, twell_ma
 twell_status twell_unpack(const twell_mat *in, void *H, int64_t ldh, hipStream_t stream);
 
 /* Workspace bytes for twell_ffn_fwd with this shape (training != 0: the
- * hybrid forward with a dense-row threshold). */
+ * hybrid forward with a dense-row threshold).  0 for an invalid shape. */
 size_t twell_ffn_fwd_workspace(const twell_ffn_shape *sh, int32_t training);
 
 /*
@@ -131,7 +131,7 @@ size_t twell_ffn_fwd_workspace(const twell_ffn_shape *sh, int32_t training);
  *                 receives h for the backward pass
  *   dense_row_threshold   < 0: every row takes the sparse path (inference).
  *                 >= 0: hybrid forward; rows whose nnz exceeds it take the
- *                 dense branch (requires saved_h)
+ *                 dense branch, gathered-row MFMA GEMMs (requires saved_h)
  *   ws, ws_bytes  workspace of at least twell_ffn_fwd_workspace(sh, thr >= 0)
  * Stored pairs are exactly the (t, n) with g > 0 in fp32; h, u and a are
  * kept in fp32, accumulation is fp32.
@@ -139,6 +139,41 @@ size_t twell_ffn_fwd_workspace(const twell_ffn_shape *sh, int32_t training);
 twell_status twell_ffn_fwd(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
                            const void *WuT, const void *Wd, void *y, twell_mat *saved_h,
                            int32_t dense_row_threshold, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for twell_ffn_bwd_hybrid with this shape and threshold
+ * (the sparse branch's pair index is sized by min(F, threshold) pairs per
+ * row).  0 for an invalid shape. */
+size_t twell_ffn_bwd_workspace(const twell_ffn_shape *sh, int32_t dense_row_threshold);
+
+/*
+ * twell_ffn_bwd_hybrid: gradients of L = <y, dY> for the layer of
+ * twell_ffn_fwd, in the hybrid sparse/dense training format
+ * (intellectnews.ru TwELL article, section "Слитые CUDA-ядра для инференса и
+ * гибрид для обучения": well-sparse rows are handled in the compact sparse
+ * format, rows with many active values in a dense branch).
+ *   x, WgT, bg, WuT, Wd   as for twell_ffn_fwd (bg may be NULL)
+ *   dY       [T][d] in_dt, the gradient of the output
+ *   saved_h  the TwELL of h written by twell_ffn_fwd (fp32 values, mask
+ *            required); it fixes the pattern of the sparse rows
+ *   dense_row_threshold   rows whose non-zero count exceeds it take the dense
+ *            branch, the others the sparse branch (any value; < 0: all dense)
+ *   dX       [T][d] fp32;  dWgT, dWuT, dWd  [F][d] fp32;  dbg [F] fp32 or NULL
+ *            -- all overwritten
+ *   n_dense_rows  NULL or one device int32 that receives the number of rows
+ *            taken by the dense branch
+ *   ws, ws_bytes  workspace of at least twell_ffn_bwd_workspace(sh, thr)
+ * ReLU'(g) is 1 for g > 0 and 0 otherwise.  Sparse rows: per stored pair,
+ * u = x_t.WuT[n], da = dY_t.Wd[n], dg = da*u, du = da*h; dX_t = sum dg*WgT[n]
+ * + du*WuT[n]; dWd[n] += h*u*dY_t, dWgT[n] += dg*x_t, dWuT[n] += du*x_t,
+ * summed per neuron over its tokens in ascending order (deterministic).
+ * Dense rows: the same gradient from gathered-row GEMMs.  fp32 accumulation
+ * throughout; needs T*F < 2^32.
+ */
+twell_status twell_ffn_bwd_hybrid(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
+                                  const void *WuT, const void *Wd, const void *dY, const twell_mat *saved_h,
+                                  int32_t dense_row_threshold, float *dX, float *dWgT, float *dWuT, float *dWd,
+                                  float *dbg, int32_t *n_dense_rows, void *ws, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /*
  * The three stages of twell_ffn_fwd, callable one by one (twell_ffn_fwd is

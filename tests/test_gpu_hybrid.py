@@ -1,0 +1,173 @@
+"""GPU parity of the hybrid sparse/dense training path against the CPU oracle.
+
+twell_ffn_fwd with a dense-row threshold (hybrid forward) and
+twell_ffn_bwd_hybrid are compared with the float64 oracle run on the same
+rounded inputs: y, dX, dWgT, dWuT, dWd and dbg within relative Frobenius error
+1e-3 (bf16 inputs, fp32 accumulation) or 1e-5 (fp32 inputs), globally and on
+the sparse and dense row sets separately.  The number of rows the dense branch
+took must equal the count of rows of the GPU's own TwELL whose non-zero count
+exceeds the threshold (the classification is integer work on a pattern that
+is itself checked against the oracle's).  Full-size runs are checked on
+sampled tokens (dX, y) and sampled neurons (weight gradients): a token's dX
+depends on its own row only, a neuron's weight gradient on its own column of
+g, u and dA only.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from workloads import make_workload
+
+from gpu_util import log, mat_to_numpy, rel_fro, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-3, "f32": 1e-5}
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    assert _t.cuda.is_available(), "GPU tests need a GPU"
+    return _t
+
+
+@pytest.fixture(scope="module")
+def tw():
+    import activation_sparse_feedforward_gate_amd as _tw
+    _tw.lib()
+    return _tw
+
+
+def run_train(torch, tw, w, tau, with_dbg=True, bias=True):
+    """Hybrid forward then backward on the GPU; returns host arrays."""
+    dt = w.cfg.dtype
+    in_dt = tw.TWELL_BF16 if dt == "bf16" else tw.TWELL_F32
+    x, WgT, WuT, Wd, dY = (to_dev(a, dt) for a in (w.x, w.WgT, w.WuT, w.Wd, w.dY))
+    bg = to_dev(w.bg, dt) if bias else None
+    T, d, F = w.T, w.d, w.f
+    shape = tw.ffn_shape(T, d, F, in_dt, tw.TWELL_F32)
+    h = tw.alloc_twell_mat(T, F, tw.TWELL_F32)
+    y = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    wsf = torch.empty(max(1, tw.twell_ffn_fwd_workspace(shape, True)), dtype=torch.uint8, device="cuda")
+    tw.twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, h, tau, wsf)
+    dX = torch.full((T, d), float("nan"), dtype=torch.float32, device="cuda")
+    dW = [torch.full((F, d), float("nan"), dtype=torch.float32, device="cuda") for _ in range(3)]
+    dbg = torch.full((F,), float("nan"), dtype=torch.float32, device="cuda") if with_dbg else None
+    nD = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    wsb = torch.empty(max(1, tw.twell_ffn_bwd_workspace(shape, tau)), dtype=torch.uint8, device="cuda")
+    tw.twell_ffn_bwd_hybrid(shape, x, WgT, bg, WuT, Wd, dY, h, tau, dX, dW[0], dW[1], dW[2], dbg, nD, wsb)
+    torch.cuda.synchronize()
+    out = {"y": y.cpu().numpy(), "dX": dX.cpu().numpy(), "dWgT": dW[0].cpu().numpy(),
+           "dWuT": dW[1].cpu().numpy(), "dWd": dW[2].cpu().numpy(), "nD": int(nD.item()),
+           "h": mat_to_numpy(h)}
+    if with_dbg:
+        out["dbg"] = dbg.cpu().numpy()
+    return out
+
+
+def check_full(w, got, tau, bias=True):
+    tol = TOL[w.cfg.dtype]
+    bg = w.bg if bias else None
+    ref = O.ffn_dense_bwd(w.x, w.WgT, bg, w.WuT, w.Wd, w.dY)
+    dense = got["h"]["cnt"].sum(axis=1) > tau
+    assert got["nD"] == int(dense.sum()), (got["nD"], int(dense.sum()))
+    log(f"   dense rows {got['nD']} of {w.T}")
+    for k, r in (("y", ref["fwd"]["y"]), ("dX", ref["dX"])):
+        e = rel_fro(got[k], r)
+        log(f"   {k} rel-Frobenius {e:.3e}")
+        assert e <= tol, (k, e)
+        for name, sel in (("dense rows", dense), ("sparse rows", ~dense)):
+            if sel.any():
+                es = rel_fro(got[k][sel], r[sel])
+                assert es <= tol, (k, name, es)
+    for k in ("dWgT", "dWuT", "dWd") + (("dbg",) if "dbg" in got else ()):
+        e = rel_fro(got[k], ref[k])
+        log(f"   {k} rel-Frobenius {e:.3e}")
+        assert np.isfinite(got[k]).all(), k
+        assert e <= tol, (k, e)
+
+
+SMALL = [
+    ("hybrid", dict(T=520, d=256, f=1280)),
+    ("hybrid", dict(T=333, d=128, f=640)),
+    ("0.5b", dict(T=300, d=256, f=1024, grad=True)),
+    ("tiny_f32", dict(grad=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=["hybrid-520", "hybrid-333", "0.5b-300", "tiny_f32"])
+def test_hybrid_small(torch, tw, name, kw):
+    w = make_workload(name, **kw)
+    log(f"[hybrid] {name} T={w.T} d={w.d} f={w.f} tau={w.tau}")
+    got = run_train(torch, tw, w, w.tau)
+    check_full(w, got, w.tau)
+
+
+@pytest.mark.parametrize("tau_kind", ["all_dense", "all_sparse", "zero"])
+def test_hybrid_threshold_limits(torch, tw, tau_kind):
+    w = make_workload("hybrid", T=200, d=128, f=640)
+    tau = {"all_dense": -1, "all_sparse": w.f, "zero": 0}[tau_kind]
+    log(f"[hybrid] tau={tau}")
+    got = run_train(torch, tw, w, tau)
+    if tau_kind == "all_dense":
+        assert got["nD"] == w.T
+    if tau_kind == "all_sparse":
+        assert got["nD"] == 0
+    check_full(w, got, tau)
+
+
+def test_hybrid_no_bias_no_dbg(torch, tw):
+    """Without the gate bias about half the gate values are positive; a
+    threshold at half the width sends about half the rows to each branch."""
+    w = make_workload("hybrid", T=160, d=128, f=640)
+    log("[hybrid] no bias, no dbg")
+    got = run_train(torch, tw, w, 320, with_dbg=False, bias=False)
+    assert 0 < got["nD"] < w.T
+    check_full(w, got, 320, bias=False)
+
+
+@pytest.mark.parametrize("T", [1, 17, 0])
+def test_hybrid_ragged(torch, tw, T):
+    w = make_workload("hybrid", T=T, d=128, f=640)
+    log(f"[hybrid] ragged T={T}")
+    got = run_train(torch, tw, w, w.tau)
+    if T == 0:
+        for k in ("dWgT", "dWuT", "dWd", "dbg"):
+            assert not got[k].any(), k            # gradients are written even with no tokens
+        assert got["nD"] == 0
+        return
+    check_full(w, got, w.tau)
+
+
+def test_hybrid_deterministic(torch, tw):
+    w = make_workload("hybrid", T=400, d=256, f=1280)
+    log("[hybrid] determinism")
+    a = run_train(torch, tw, w, w.tau)
+    b = run_train(torch, tw, w, w.tau)
+    for k in ("y", "dX", "dWgT", "dWuT", "dWd", "dbg"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_hybrid_full_size_sampled(torch, tw):
+    """The hybrid training workload at full size: T=16384, d=2048, F=5632."""
+    w = make_workload("hybrid")
+    log(f"[hybrid] full size T={w.T} d={w.d} f={w.f} tau={w.tau}")
+    got = run_train(torch, tw, w, w.tau)
+    dense = got["h"]["cnt"].sum(axis=1) > w.tau
+    assert got["nD"] == int(dense.sum())
+    log(f"   dense rows {got['nD']} (drawn dense: {len(w.dense_rows)})")
+    rng = np.random.default_rng(7)
+    toks = np.unique(np.concatenate([rng.choice(w.T, 192, replace=False), w.dense_rows[:32],
+                                     np.arange(w.T - 16, w.T)]))
+    neur = np.sort(rng.choice(w.f, 48, replace=False))
+    ref = O.ffn_bwd_sampled(w.x, w.WgT, w.bg, w.WuT, w.Wd, w.dY, toks, neur)
+    tol = TOL["bf16"]
+    for k, g, r in (("y", got["y"][toks], ref["y_rows"]), ("dX", got["dX"][toks], ref["dX_rows"]),
+                    ("dWgT", got["dWgT"][neur], ref["dWgT_rows"]), ("dWuT", got["dWuT"][neur], ref["dWuT_rows"]),
+                    ("dWd", got["dWd"][neur], ref["dWd_rows"]), ("dbg", got["dbg"][neur], ref["dbg_rows"])):
+        e = rel_fro(g, r)
+        log(f"   {k} rel-Frobenius {e:.3e} (sampled)")
+        assert e <= tol, (k, e)
+    for k in ("dX", "dWgT", "dWuT", "dWd", "dbg"):
+        assert np.isfinite(got[k]).all(), k

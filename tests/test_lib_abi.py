@@ -92,6 +92,40 @@ def test_dense_baseline_argument_errors():
     assert L.twell_ffn_dense_fwd(ctypes.byref(sh), 16, 16, None, 16, 16, 16, 16, 1, None) == tw.TWELL_EWORKSPACE
 
 
+def test_bwd_argument_errors():
+    L = tw.lib()
+    sh = tw.ffn_shape(64, 128, 512, tw.TWELL_BF16, tw.TWELL_F32)
+    h = tw.c_twell_mat(64, 512, 16, 64, tw.TWELL_F32, 16, 16, 16, 16, 16)
+    need = tw.twell_ffn_bwd_workspace(sh, 51)
+    assert need > 0
+    assert tw.twell_ffn_bwd_workspace(sh, 51) < tw.twell_ffn_bwd_workspace(sh, 512)   # pair index sized by tau
+
+    def call(shape=sh, hm=h, x=16, dY=16, dX=16, dW=16, ws=4096, ws_bytes=need, tau=51):
+        return L.twell_ffn_bwd_hybrid(ctypes.byref(shape) if shape is not None else None, x, 16, None, 16, 16, dY,
+                                      ctypes.byref(hm) if hm is not None else None, tau, dX, dW, dW, dW, None,
+                                      None, ws, ws_bytes, None)
+    assert call(shape=None) == tw.TWELL_EINVAL
+    assert call(hm=None) == tw.TWELL_EINVAL
+    assert call(dY=None) == tw.TWELL_EINVAL
+    assert call(dW=None) == tw.TWELL_EINVAL
+    assert call(x=24) == tw.TWELL_EINVAL                                       # misaligned
+    assert call(ws_bytes=need - 1) == tw.TWELL_EWORKSPACE
+    hb = tw.c_twell_mat(64, 512, 16, 64, tw.TWELL_BF16, 16, 16, 16, 16, 16)
+    assert call(hm=hb) == tw.TWELL_EINVAL                                      # saved h must hold fp32
+    hn = tw.c_twell_mat(64, 512, 16, 64, tw.TWELL_F32, 16, 16, 16, 16, None)
+    assert call(hm=hn) == tw.TWELL_EINVAL                                      # mask required
+    h32 = tw.c_twell_mat(32, 512, 16, 64, tw.TWELL_F32, 16, 16, 16, 16, 16)
+    assert call(hm=h32) == tw.TWELL_EINVAL                                     # T mismatch
+    assert call(shape=tw.ffn_shape(64, 100, 512, tw.TWELL_BF16, tw.TWELL_F32)) == tw.TWELL_EUNSUPPORTED
+
+
+def test_hybrid_fwd_needs_saved_h():
+    sh = tw.ffn_shape(64, 128, 512, tw.TWELL_BF16, tw.TWELL_F32)
+    need = tw.twell_ffn_fwd_workspace(sh, True)
+    assert need > tw.twell_ffn_fwd_workspace(sh, False)
+    assert _call_fwd(sh, thr=5, ws=4096, ws_bytes=need) == tw.TWELL_EINVAL
+
+
 def test_status_strings():
     for st in range(5):
         assert tw.twell_status_string(st)

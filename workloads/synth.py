@@ -157,9 +157,11 @@ class Workload:
 
 def make_workload(name: str, seed: int = 0, T: Optional[int] = None,
                   d: Optional[int] = None, f: Optional[int] = None,
-                  decode: bool = False) -> Workload:
+                  decode: bool = False, grad: bool = False) -> Workload:
     """Draw the inputs of workload ``name``; T, d, f may be overridden (smaller
-    parity cases keep the same value distributions and activation structure)."""
+    parity cases keep the same value distributions and activation structure).
+    grad=True also draws an output gradient dY ~ N(0, 1) and a dense-row
+    threshold tau = floor(0.10 * f) for workloads that do not define them."""
     cfg = CONFIGS[name]
     d = cfg.d if d is None else d
     f = cfg.f if f is None else f
@@ -195,8 +197,8 @@ def make_workload(name: str, seed: int = 0, T: Optional[int] = None,
 
     dY = None
     tau = None
-    if cfg.tau_frac is not None:
+    if cfg.tau_frac is not None or grad:
         dY = _normal(seed, _ID_DY, (T, d), 1.0, dt)
-        tau = int(math.floor(cfg.tau_frac * f))
+        tau = int(math.floor((cfg.tau_frac if cfg.tau_frac is not None else 0.10) * f))
     return Workload(cfg=cfg, seed=seed, T=T, d=d, f=f, x=x, WgT=WgT, bg=bg, WuT=WuT,
                     Wd=Wd, p=p, dead=dead, dY=dY, tau=tau, dense_rows=dense_rows)
