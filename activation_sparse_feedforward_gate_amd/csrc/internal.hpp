@@ -84,6 +84,15 @@ hipError_t launch_sparse_wgrad(int in_dt, const void* x, const void* dY, int T, 
                                uint32_t* entries, const float* aval, const float* dgval, const float* duval,
                                float* dWgT, float* dWuT, float* dWd, float* dbg, hipStream_t s);
 
+// bf16 sparse kernels with workgroup-shared weight staging (dY == null:
+// forward up-projection; otherwise the backward's u/da products).
+hipError_t launch_up_bf16(const void* x, const void* dY, const void* WuT, const void* Wd, int T, int d, int F,
+                          const TwellView& h, float* aval, float* dgval, float* duval, const uint8_t* skip,
+                          hipStream_t s);
+// y = v0 . W (+ v1 . W2 when v1 != null) over the stored pairs of pat.
+hipError_t launch_down_bf16(const float* v0, const float* v1, const void* W, const void* W2, int T, int d, int F,
+                            const TwellView& pat, void* y, int out_dt, const uint8_t* skip, hipStream_t s);
+
 // Dense baseline: act = ReLU(x.WgT^T + bg) * (x.WuT^T) in bf16 (fused dual GEMM),
 // then y = act.Wd.  act is a [T][F] bf16 workspace.
 hipError_t launch_dense_fwd(const void* x, const void* WgT, const void* bg, const void* WuT,

@@ -1,4 +1,5 @@
-// Sparse up- and down-projections on the TwELL pattern of the gate.
+// Sparse up- and down-projections on the TwELL pattern of the gate (generic
+// kernels, used for fp32 inputs; bf16 inputs go to twell_sparse_bf16.hip).
 //
 // The intellectnews.ru TwELL article, section "Слитые CUDA-ядра для инференса
 // и гибрид для обучения", describes the inference FFN as a few fused steps
@@ -309,11 +310,11 @@ hipError_t launch_sddmm_up(int in_dt, const void* x, const void* WuT, int T, int
   SparseArgs a{};
   a.x = x; a.W = WuT; a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
   a.mask = h.mask; a.hval = (const float*)h.val; a.aval = aval; a.skip = skip;
+  if (in_dt == DT_BF16) return launch_up_bf16(x, nullptr, WuT, nullptr, T, d, F, h, aval, nullptr, nullptr, skip, s);
   a.nslices = choose_slices(a.NT, UP_MAXT);
   if (a.NR == 0) return hipSuccess;
   const int grid = ((a.NR + SP_WPB - 1) / SP_WPB) * a.nslices;
-  if (in_dt == DT_BF16) hipLaunchKernelGGL((sddmm_up_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((sddmm_up_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((sddmm_up_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -323,11 +324,11 @@ hipError_t launch_sddmm_bwd(int in_dt, const void* x, const void* dY, const void
   SparseArgs a{};
   a.x = x; a.x2 = dY; a.W = WuT; a.W2 = Wd; a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
   a.mask = h.mask; a.hval = (const float*)h.val; a.aval = aval; a.dgval = dgval; a.duval = duval; a.skip = skip;
+  if (in_dt == DT_BF16) return launch_up_bf16(x, dY, WuT, Wd, T, d, F, h, aval, dgval, duval, skip, s);
   a.nslices = choose_slices(a.NT, UP_MAXT);
   if (a.NR == 0) return hipSuccess;
   const int grid = ((a.NR + SP_WPB - 1) / SP_WPB) * a.nslices;
-  if (in_dt == DT_BF16) hipLaunchKernelGGL((sddmm_up_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((sddmm_up_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((sddmm_up_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -336,12 +337,12 @@ hipError_t launch_spmm_down(int in_dt, int out_dt, const float* aval, const void
   SparseArgs a{};
   a.W = Wd; a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
   a.mask = pat.mask; a.aval = (float*)aval; a.skip = skip; a.y = y; a.out_bf16 = out_dt == DT_BF16;
+  if (in_dt == DT_BF16) return launch_down_bf16(aval, nullptr, Wd, nullptr, T, d, F, pat, y, out_dt, skip, s);
   a.nslices = choose_slices(d / 16, DN_MAXCB);
   if (d / 16 < a.nslices) a.nslices = d / 16;
   if (a.NR == 0) return hipSuccess;
   const int grid = ((a.NR + SP_WPB - 1) / SP_WPB) * a.nslices;
-  if (in_dt == DT_BF16) hipLaunchKernelGGL((spmm_down_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((spmm_down_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((spmm_down_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -351,12 +352,12 @@ hipError_t launch_spmm_dx(int in_dt, const float* dgval, const float* duval, con
   SparseArgs a{};
   a.W = WgT; a.W2 = WuT; a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
   a.mask = pat.mask; a.dgval = (float*)dgval; a.duval = (float*)duval; a.skip = skip; a.y = dX; a.out_bf16 = 0;
+  if (in_dt == DT_BF16) return launch_down_bf16(dgval, duval, WgT, WuT, T, d, F, pat, dX, DT_F32, skip, s);
   a.nslices = choose_slices(d / 16, DN_MAXCB);
   if (d / 16 < a.nslices) a.nslices = d / 16;
   if (a.NR == 0) return hipSuccess;
   const int grid = ((a.NR + SP_WPB - 1) / SP_WPB) * a.nslices;
-  if (in_dt == DT_BF16) hipLaunchKernelGGL((spmm_down_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((spmm_down_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((spmm_down_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
