@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.twell_ffn_bwd_workspace.restype = sz
         L.twell_ffn_bwd_hybrid.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_mat), i32,
                                            vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.twell_ffn_fwd_ex.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_mat), i32, vp, sz, vp,
+                                       vp, i32]
         L.twell_gate_pack.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, P(c_twell_mat), vp]
         L.twell_sparse_up.argtypes = [P(c_twell_ffn_shape), vp, vp, P(c_twell_mat), vp, vp]
         L.twell_sparse_down.argtypes = [P(c_twell_ffn_shape), vp, vp, P(c_twell_mat), vp, vp]
@@ -70,7 +72,8 @@ def lib() -> ctypes.CDLL:
         L.twell_status_string.restype = ctypes.c_char_p
         L.twell_last_error.argtypes = []
         L.twell_last_error.restype = ctypes.c_char_p
-        for name in ("twell_pack", "twell_unpack", "twell_ffn_fwd", "twell_ffn_bwd_hybrid", "twell_ffn_dense_fwd",
+        for name in ("twell_pack", "twell_unpack", "twell_ffn_fwd", "twell_ffn_fwd_ex", "twell_ffn_bwd_hybrid",
+                     "twell_ffn_dense_fwd",
                      "twell_gate_pack",
                      "twell_sparse_up", "twell_sparse_down"):
             getattr(L, name).restype = ctypes.c_int
@@ -94,6 +97,11 @@ def _check(st: int):
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+def _stream_obj(stream):
+    import torch
+    return torch.cuda.current_stream() if stream is None else stream
 
 
 def _stream(stream) -> Optional[int]:
@@ -200,6 +208,21 @@ def twell_ffn_bwd_hybrid(shape, x, WgT, bg, WuT, Wd, dY, saved_h: TwellMat, dens
                                       _ptr(dWuT), _ptr(dWd), _ptr(dbg), _ptr(n_dense_rows), _ptr(ws),
                                       ws.numel() * ws.element_size() if ws is not None else 0,
                                       _stream(stream)))
+
+
+def twell_ffn_fwd_ex(shape, x, WgT, bg, WuT, Wd, y, saved_h: Optional[TwellMat], dense_row_threshold: int,
+                     ws, events, stream=None) -> None:
+    """twell_ffn_fwd recording the torch.cuda.Event objects in `events` at the
+    stage boundaries (see include/twell.h)."""
+    sh = saved_h.c() if saved_h is not None else None
+    for e in events:                 # torch creates the HIP event on its first record
+        if not e.cuda_event:
+            e.record(_stream_obj(stream))
+    arr = (ctypes.c_void_p * max(1, len(events)))(*[e.cuda_event for e in events])
+    _check(lib().twell_ffn_fwd_ex(ctypes.byref(shape), _ptr(x), _ptr(WgT), _ptr(bg), _ptr(WuT), _ptr(Wd), _ptr(y),
+                                  ctypes.byref(sh) if sh is not None else None, dense_row_threshold,
+                                  _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+                                  _stream(stream), arr, len(events)))
 
 
 def twell_gate_pack(shape, x, WgT, bg, h: TwellMat, stream=None) -> None:

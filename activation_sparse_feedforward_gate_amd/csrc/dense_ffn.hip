@@ -91,7 +91,7 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_down_kernel(DenseArgs a) {
 }
 
 using DenseGateUp = GemmCfg<128, 128, 2, 2, OP_BF16_K, OP_BF16_K, 2>;
-using DenseDownBig = GemmCfg<256, 128, 2, 2, OP_BF16_K, OP_BF16_T>;
+using DenseDownBig = GemmCfg<256, 256, 2, 4, OP_BF16_K, OP_BF16_T>;
 using DenseDownSmall = GemmCfg<128, 64, 2, 1, OP_BF16_K, OP_BF16_T>;
 
 template <class Cfg, class K>
@@ -108,7 +108,7 @@ hipError_t launch_dense_fwd(const void* x, const void* WgT, const void* bg, cons
   DenseArgs a{x, WgT, bg, WuT, Wd, T, d, F, (uint16_t*)act, y, out_dt == DT_BF16};
   hipError_t e = launch_grid<DenseGateUp>(dense_gateup_kernel<DenseGateUp>, T, F, a, s);
   if (e != hipSuccess) return e;
-  if (d % 128 == 0) return launch_grid<DenseDownBig>(dense_down_kernel<DenseDownBig>, T, d, a, s);
+  if (d % 256 == 0) return launch_grid<DenseDownBig>(dense_down_kernel<DenseDownBig>, T, d, a, s);
   return launch_grid<DenseDownSmall>(dense_down_kernel<DenseDownSmall>, T, d, a, s);
 }
 

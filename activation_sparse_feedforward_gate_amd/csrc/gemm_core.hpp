@@ -6,11 +6,15 @@
 // Operand kinds:
 //   OP_BF16_K  bf16, [rows][K] (K contiguous), optional row gather list
 //   OP_BF16_T  bf16, [K][rows] (rows contiguous), optional K gather list;
-//              transposed into LDS with 16-bit writes
+//              copied into LDS as [k][row] and read with transpose loads
 //   OP_F32S_K  fp32 [rows][K], split into bf16 hi and lo tiles
 //   OP_F32S_T  fp32 [K][rows], split into bf16 hi and lo tiles
 //   OP_F32_K   fp32 [rows][K] fed to fp32 MFMA (fp32 workloads)
 //   OP_F32_T   fp32 [K][rows] fed to fp32 MFMA
+//   OP_F16_K   fp16 [rows][K] fed to fp16 MFMA
+//   OP_BF16_T16 bf16 [K][rows], optional K gather list, converted to fp16 as
+//              it is transposed into LDS (exact for |v| >= 2^-17; smaller
+//              magnitudes keep fp16's subnormal resolution), fed to fp16 MFMA
 // A split operand costs two MFMAs (hi and lo) per fragment; B is always exact
 // in its type.  K-contiguous kinds need K % 64 == 0 (bf16) / 32 (fp32);
 // transposed kinds zero-fill past K and read whole row blocks, so the caller
@@ -20,7 +24,8 @@
 
 namespace twell {
 
-enum OpKind { OP_BF16_K = 0, OP_BF16_T = 1, OP_F32S_K = 2, OP_F32S_T = 3, OP_F32_K = 4, OP_F32_T = 5 };
+enum OpKind { OP_BF16_K = 0, OP_BF16_T = 1, OP_F32S_K = 2, OP_F32S_T = 3, OP_F32_K = 4, OP_F32_T = 5,
+              OP_F16_K = 6, OP_BF16_T16 = 7 };
 
 struct Operand {
   const void* ptr;
@@ -30,12 +35,14 @@ struct Operand {
 };
 
 template <int KIND> struct KindInfo;
-template <> struct KindInfo<OP_BF16_K> { static constexpr bool split = false, f32mma = false, trans = false; static constexpr int esz = 2; };
-template <> struct KindInfo<OP_BF16_T> { static constexpr bool split = false, f32mma = false, trans = true;  static constexpr int esz = 2; };
-template <> struct KindInfo<OP_F32S_K> { static constexpr bool split = true,  f32mma = false, trans = false; static constexpr int esz = 4; };
-template <> struct KindInfo<OP_F32S_T> { static constexpr bool split = true,  f32mma = false, trans = true;  static constexpr int esz = 4; };
-template <> struct KindInfo<OP_F32_K>  { static constexpr bool split = false, f32mma = true,  trans = false; static constexpr int esz = 4; };
-template <> struct KindInfo<OP_F32_T>  { static constexpr bool split = false, f32mma = true,  trans = true;  static constexpr int esz = 4; };
+template <> struct KindInfo<OP_BF16_K> { static constexpr bool split = false, f32mma = false, f16 = false, trans = false; static constexpr int esz = 2; };
+template <> struct KindInfo<OP_BF16_T> { static constexpr bool split = false, f32mma = false, f16 = false, trans = true;  static constexpr int esz = 2; };
+template <> struct KindInfo<OP_F32S_K> { static constexpr bool split = true,  f32mma = false, f16 = false, trans = false; static constexpr int esz = 4; };
+template <> struct KindInfo<OP_F32S_T> { static constexpr bool split = true,  f32mma = false, f16 = false, trans = true;  static constexpr int esz = 4; };
+template <> struct KindInfo<OP_F32_K>  { static constexpr bool split = false, f32mma = true,  f16 = false, trans = false; static constexpr int esz = 4; };
+template <> struct KindInfo<OP_F32_T>  { static constexpr bool split = false, f32mma = true,  f16 = false, trans = true;  static constexpr int esz = 4; };
+template <> struct KindInfo<OP_F16_K>  { static constexpr bool split = false, f32mma = false, f16 = true,  trans = false; static constexpr int esz = 2; };
+template <> struct KindInfo<OP_BF16_T16> { static constexpr bool split = false, f32mma = false, f16 = true, trans = true; static constexpr int esz = 2; };
 
 // K elements per LDS row (= per K tile).
 template <int KIND> constexpr int ktile() { return KindInfo<KIND>::f32mma ? 32 : 64; }
@@ -48,25 +55,30 @@ template <int KIND> constexpr int ktile() { return KindInfo<KIND>::f32mma ? 32 :
 template <int KIND, int ROWS, int NTH> struct Loader;
 
 // bf16 or fp32, K contiguous: 8 chunks of 16 bytes per row.
+// Row addresses are kept as 32-bit element offsets from the operand base (the
+// caller guarantees every matrix holds fewer than 2^32 elements), which keeps
+// the loader's register footprint at one VGPR per 16-byte chunk.
 template <int KIND, int ROWS, int NTH>
 struct LoaderK {
   static constexpr int ESZ = KindInfo<KIND>::esz;
   static constexpr int CH = ROWS * 8 / NTH;
   static_assert(CH * NTH == ROWS * 8, "tile rows must divide the thread count");
-  const char* rowp[CH];
+  const char* base;
+  uint32_t off[CH];
   uint4 r[CH];
   __device__ void init(const Operand& op, int row0, int tid) {
+    base = (const char*)op.ptr;
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
       int id = tid + q * NTH;
       int gr = min(row0 + (id >> 3), op.nrows - 1);
       if (op.gather) gr = op.gather[gr];
-      rowp[q] = (const char*)op.ptr + ((int64_t)gr * op.ld) * ESZ + (id & 7) * 16;
+      off[q] = (uint32_t)gr * (uint32_t)op.ld + (uint32_t)(id & 7) * (16 / ESZ);
     }
   }
   __device__ void load(int k0, int /*K*/) {
 #pragma unroll
-    for (int q = 0; q < CH; ++q) r[q] = *(const uint4*)(rowp[q] + (int64_t)k0 * ESZ);
+    for (int q = 0; q < CH; ++q) r[q] = *(const uint4*)(base + ((uint64_t)off[q] + (uint32_t)k0) * ESZ);
   }
   __device__ void store(char* lds, char* /*lds_lo*/, int tid) const {
 #pragma unroll
@@ -78,39 +90,45 @@ struct LoaderK {
 };
 template <int ROWS, int NTH> struct Loader<OP_BF16_K, ROWS, NTH> : LoaderK<OP_BF16_K, ROWS, NTH> {};
 template <int ROWS, int NTH> struct Loader<OP_F32_K, ROWS, NTH> : LoaderK<OP_F32_K, ROWS, NTH> {};
+template <int ROWS, int NTH> struct Loader<OP_F16_K, ROWS, NTH> : LoaderK<OP_F16_K, ROWS, NTH> {};
 
-// bf16, [K][rows]: a chunk is 8 consecutive rows at one k.  Within a wave,
-// lanes cover 8 k x 8 row-chunks so both the global read (128 contiguous
-// bytes per k) and the transposed LDS writes are conflict free.
-template <int ROWS, int NTH>
-struct Loader<OP_BF16_T, ROWS, NTH> {
+// 16-bit [K][rows] operands (used as B): each K tile is copied into LDS as it
+// is laid out in memory, [k][row] with a padded pitch of 2*ROWS + 32 bytes
+// (consecutive k rows 32 bytes apart modulo 128, so the four rows one
+// transpose read touches sit in different bank groups), with 16-byte stores,
+// and the MFMA fragments are read with the gfx950 transpose load
+// ds_read_b64_tr_b16 (lane i of a 16-lane group receives element i of four
+// consecutive k rows).  TO_F16 converts bf16 to fp16 on the way in.
+template <int ROWS, int NTH, bool TO_F16>
+struct LoaderTR {
   static_assert(ROWS % 64 == 0, "transposed operand block must be a multiple of 64 rows");
-  static constexpr int CH = 64 * ROWS / 8 / NTH;
-  static_assert(CH * NTH == 64 * ROWS / 8, "bad thread count");
+  static constexpr int PITCH = ROWS * 2 + 32;
+  static constexpr int CPR = ROWS / 8;             // 16-byte chunks per k row
+  static constexpr int CH = 64 * CPR / NTH;
+  static_assert(CH * NTH == 64 * CPR, "bad thread count");
   const uint16_t* base;
   int64_t ld;
   const int* gather;
   int row0;
   uint4 r[CH];
-  __device__ static void coords(int id, int& k, int& rc) {
-    const int rch = ROWS / 64;
-    int rest = id >> 6;
-    rc = (rest % rch) * 8 + ((id >> 3) & 7);
-    k = (rest / rch) * 8 + (id & 7);
-  }
   __device__ void init(const Operand& op, int row0_, int /*tid*/) {
     base = (const uint16_t*)op.ptr; ld = op.ld; gather = op.gather; row0 = row0_;
+  }
+  __device__ static uint32_t cvt2(uint32_t w) {
+    const _Float16 lo = (_Float16)bf16_lo(w), hi = (_Float16)bf16_hi(w);
+    return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
   }
   __device__ void load(int k0, int K) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
-      int k, rc;
-      coords(tid + q * NTH, k, rc);
+      const int id = tid + q * NTH;
+      const int k = id / CPR, cc = id - k * CPR;
       int gk = k0 + k;
       if (gk < K) {
         if (gather) gk = gather[gk];
-        r[q] = *(const uint4*)(base + (int64_t)gk * ld + row0 + rc * 8);
+        r[q] = *(const uint4*)(base + (int64_t)gk * ld + row0 + cc * 8);
+        if constexpr (TO_F16) r[q] = make_uint4(cvt2(r[q].x), cvt2(r[q].y), cvt2(r[q].z), cvt2(r[q].w));
       } else {
         r[q] = make_uint4(0, 0, 0, 0);
       }
@@ -119,37 +137,53 @@ struct Loader<OP_BF16_T, ROWS, NTH> {
   __device__ void store(char* lds, char* /*lds_lo*/, int tid) const {
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
-      int k, rc;
-      coords(tid + q * NTH, k, rc);
-      const uint32_t w[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint16_t v = (uint16_t)(w[i >> 1] >> ((i & 1) * 16));
-        *(uint16_t*)(lds + swz(rc * 8 + i, k >> 3) + ((k & 7) << 1)) = v;
-      }
+      const int id = tid + q * NTH;
+      const int k = id / CPR, cc = id - k * CPR;
+      *(uint4*)(lds + k * PITCH + cc * 16) = r[q];
     }
   }
 };
+template <int ROWS, int NTH> struct Loader<OP_BF16_T, ROWS, NTH> : LoaderTR<ROWS, NTH, false> {};
+template <int ROWS, int NTH> struct Loader<OP_BF16_T16, ROWS, NTH> : LoaderTR<ROWS, NTH, true> {};
+
+typedef short trv4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) trv4i16 lds_trv4i16;
+typedef __attribute__((address_space(3))) char lds_trchar;
+
+// B fragment of a 32x32x16 MFMA from a [k][col] tile: k = 16*kk + 8*(lane/32)
+// + 0..7, column col0 + lane%32.
+__device__ __forceinline__ uint4 tr_frag(const char* tile, int pitch, int kk, int col0, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int krow = 16 * kk + 8 * (g >> 1) + (i >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (i & 3);
+  lds_trchar* p = (lds_trchar*)tile + krow * pitch + col * 2;
+  const trv4i16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_trv4i16*)p);
+  const trv4i16 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_trv4i16*)(p + 4 * pitch));
+  const uint2 u0 = __builtin_bit_cast(uint2, v0), u1 = __builtin_bit_cast(uint2, v1);
+  return make_uint4(u0.x, u0.y, u1.x, u1.y);
+}
 
 // fp32 [rows][K] split into bf16 hi/lo tiles: 16 chunks of 4 floats per row.
 template <int ROWS, int NTH>
 struct Loader<OP_F32S_K, ROWS, NTH> {
   static constexpr int CH = ROWS * 16 / NTH;
   static_assert(CH * NTH == ROWS * 16, "bad thread count");
-  const char* rowp[CH];
+  const float* base;
+  uint32_t off[CH];
   uint4 r[CH];
   __device__ void init(const Operand& op, int row0, int tid) {
+    base = (const float*)op.ptr;
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
       int id = tid + q * NTH;
       int gr = min(row0 + (id >> 4), op.nrows - 1);
       if (op.gather) gr = op.gather[gr];
-      rowp[q] = (const char*)op.ptr + (int64_t)gr * op.ld * 4 + (id & 15) * 16;
+      off[q] = (uint32_t)gr * (uint32_t)op.ld + (uint32_t)(id & 15) * 4u;
     }
   }
   __device__ void load(int k0, int /*K*/) {
 #pragma unroll
-    for (int q = 0; q < CH; ++q) r[q] = *(const uint4*)(rowp[q] + (int64_t)k0 * 4);
+    for (int q = 0; q < CH; ++q) r[q] = *(const uint4*)(base + (uint64_t)off[q] + (uint32_t)k0);
   }
   __device__ void store(char* lds_hi, char* lds_lo, int tid) const {
 #pragma unroll
@@ -279,11 +313,15 @@ struct GemmCfg {
   static_assert(TM >= 1 && TN >= 1, "wave tile must hold whole 32x32 blocks");
   static constexpr bool ASPLIT = KindInfo<AKIND>::split;
   static constexpr bool F32MMA = KindInfo<AKIND>::f32mma;
+  static constexpr bool F16MMA = KindInfo<AKIND>::f16;
   static_assert(KindInfo<BKIND>::f32mma == F32MMA, "A and B must both be fp32 or both bf16");
+  static_assert(KindInfo<BKIND>::f16 == F16MMA, "A and B must both be fp16 or neither");
   static_assert(!KindInfo<BKIND>::split, "B operand is never split");
   static constexpr int KT = ktile<AKIND>();
+  static constexpr bool BTR = KindInfo<BKIND>::trans && KindInfo<BKIND>::esz == 2;   // B read by transpose loads
+  static constexpr int B_PITCH = BN * 2 + 32;
   static constexpr int A_BYTES = BM * 128;
-  static constexpr int B_BYTES = BN * 128;
+  static constexpr int B_BYTES = BTR ? 64 * B_PITCH : BN * 128;
   static constexpr int STAGE = A_BYTES * (ASPLIT ? 2 : 1) + B_BYTES * NB;
   static constexpr int LDS_BYTES = 2 * STAGE;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -361,8 +399,10 @@ struct GemmTile {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            fb[b][j] = *(const uint4*)(b_ptr(cur, b) + swz(wc + j * 32 + (lane & 31), ch));
+          for (int j = 0; j < TN; ++j) {
+            if constexpr (Cfg::BTR) fb[b][j] = tr_frag(b_ptr(cur, b), Cfg::B_PITCH, kk, wc + j * 32, lane);
+            else fb[b][j] = *(const uint4*)(b_ptr(cur, b) + swz(wc + j * 32 + (lane & 31), ch));
+          }
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -371,6 +411,8 @@ struct GemmTile {
             for (int j = 0; j < TN; ++j) {
               if constexpr (Cfg::F32MMA) {
                 acc[b][i][j] = mfma32_f32(fa[i], fb[b][j], acc[b][i][j]);
+              } else if constexpr (Cfg::F16MMA) {
+                acc[b][i][j] = mfma32_f16(fa[i], fb[b][j], acc[b][i][j]);
               } else {
                 acc[b][i][j] = mfma32(fa[i], fb[b][j], acc[b][i][j]);
                 if constexpr (Cfg::ASPLIT) acc[b][i][j] = mfma32(fal[i], fb[b][j], acc[b][i][j]);

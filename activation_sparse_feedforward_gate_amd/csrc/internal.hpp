@@ -86,12 +86,25 @@ hipError_t launch_sparse_wgrad(int in_dt, const void* x, const void* dY, int T, 
 
 // bf16 sparse kernels with workgroup-shared weight staging (dY == null:
 // forward up-projection; otherwise the backward's u/da products).
+// gate: null, or a device flag; the kernels do nothing unless it is non-zero.
 hipError_t launch_up_bf16(const void* x, const void* dY, const void* WuT, const void* Wd, int T, int d, int F,
                           const TwellView& h, float* aval, float* dgval, float* duval, const uint8_t* skip,
-                          hipStream_t s);
+                          hipStream_t s, const int* gate = nullptr);
 // y = v0 . W (+ v1 . W2 when v1 != null) over the stored pairs of pat.
 hipError_t launch_down_bf16(const float* v0, const float* v1, const void* W, const void* W2, int T, int d, int F,
-                            const TwellView& pat, void* y, int out_dt, const uint8_t* skip, hipStream_t s);
+                            const TwellView& pat, void* y, int out_dt, const uint8_t* skip, hipStream_t s,
+                            const int* gate = nullptr);
+
+// Forward up/down over each 256-token row block's union of active neurons
+// (bf16 inputs): union lists, up GEMM writing a as fp16 over the union, down
+// GEMM into y (rows with skip[t] != 0 untouched).  ws holds
+// union_ws_bytes(T, F).  *flag_out receives the device flag that is set when
+// an a value overflows fp16; the caller then runs the pattern kernels gated on
+// it (they recompute and overwrite y).
+size_t union_ws_bytes(int T, int F);
+hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int T, int d, int F,
+                            const TwellView& h, const uint8_t* skip, void* ws, void* y, int out_dt,
+                            int** flag_out, hipStream_t s);
 
 // Dense baseline: act = ReLU(x.WgT^T + bg) * (x.WuT^T) in bf16 (fused dual GEMM),
 // then y = act.Wd.  act is a [T][F] bf16 workspace.

@@ -96,6 +96,7 @@ struct FwdWs {
   int* list;
   int* nD;
   float* act;
+  void* uni;         // union-GEMM workspace (bf16 inputs)
 };
 
 size_t fwd_layout(const twell_ffn_shape* sh, bool training, void* ws, FwdWs* out) {
@@ -116,6 +117,7 @@ size_t fwd_layout(const twell_ffn_shape* sh, bool training, void* ws, FwdWs* out
     w.nD = (int*)c.take(4);
     w.act = (float*)c.take((size_t)sh->T * sh->F * 4);
   }
+  if (sh->in_dt == TWELL_BF16) w.uni = c.take(union_ws_bytes(sh->T, sh->F));
   if (out) *out = w;
   return c.off;
 }
@@ -194,9 +196,10 @@ size_t twell_ffn_fwd_workspace(const twell_ffn_shape* sh, int32_t training) {
   return fwd_layout(sh, training != 0, nullptr, nullptr);
 }
 
-twell_status twell_ffn_fwd(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
-                           const void* WuT, const void* Wd, void* y, twell_mat* saved_h,
-                           int32_t dense_row_threshold, void* ws, size_t ws_bytes, hipStream_t stream) {
+twell_status twell_ffn_fwd_ex(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
+                              const void* WuT, const void* Wd, void* y, twell_mat* saved_h,
+                              int32_t dense_row_threshold, void* ws, size_t ws_bytes, hipStream_t stream,
+                              hipEvent_t* stage_events, int32_t n_events) {
   twell_status st = check_shape(sh);
   if (st) return st;
   if (sh->T > 0 && (!x || !WgT || !WuT || !Wd || !y)) return fail(TWELL_EINVAL, "NULL tensor argument");
@@ -208,6 +211,10 @@ twell_status twell_ffn_fwd(const twell_ffn_shape* sh, const void* x, const void*
     if (saved_h->T != sh->T || saved_h->F != sh->F || saved_h->vdtype != TWELL_F32)
       return fail(TWELL_EINVAL, "saved_h must be T x F with fp32 values");
   }
+  if (n_events < 0 || (n_events > 0 && !stage_events)) return fail(TWELL_EINVAL, "bad stage event array");
+  if ((int64_t)sh->T * sh->d >= ((int64_t)1 << 32) || (int64_t)sh->F * sh->d >= ((int64_t)1 << 32) ||
+      (int64_t)sh->T * sh->F >= ((int64_t)1 << 32))
+    return fail(TWELL_EUNSUPPORTED, "matrices must hold fewer than 2^32 elements");
   const bool training = dense_row_threshold >= 0;
   if (training && !saved_h) return fail(TWELL_EINVAL, "the hybrid forward (dense_row_threshold >= 0) needs saved_h");
   const size_t need = fwd_layout(sh, training, nullptr, nullptr);
@@ -224,6 +231,11 @@ twell_status twell_ffn_fwd(const twell_ffn_shape* sh, const void* x, const void*
     h = view_of(saved_h);                    // h is kept for the backward pass
     aval = (float*)w.h.val;
   }
+  int ev = 0;
+  auto mark = [&]() {
+    if (ev < n_events) (void)hipEventRecord(stage_events[ev++], stream);
+  };
+  mark();                                                             // 0: start
   hipError_t e = launch_gate_twell(in_dt, x, WgT, bg, sh->T, sh->d, sh->F, h, stream);
   if (e != hipSuccess) return hip_status(e, "gate GEMM");
   const uint8_t* skip = nullptr;
@@ -232,16 +244,38 @@ twell_status twell_ffn_fwd(const twell_ffn_shape* sh, const void* x, const void*
     if (e != hipSuccess) return hip_status(e, "row classification");
     skip = w.flag;
   }
-  e = launch_sddmm_up(in_dt, x, WuT, sh->T, sh->d, sh->F, h, aval, skip, stream);
-  if (e != hipSuccess) return hip_status(e, "sparse up-projection");
-  e = launch_spmm_down(in_dt, out_dt, aval, Wd, sh->T, sh->d, sh->F, h, y, skip, stream);
-  if (e != hipSuccess) return hip_status(e, "sparse down-projection");
+  mark();                                                             // 1: gate GEMM + pack done
+  if (in_dt == DT_BF16) {
+    int* ovf = nullptr;
+    e = launch_union_fwd(x, WuT, Wd, sh->T, sh->d, sh->F, h, skip, w.uni, y, out_dt, &ovf, stream);
+    if (e != hipSuccess) return hip_status(e, "union up/down GEMMs");
+    mark();                                                           // 2: up/down done
+    // fp16 overflow fallback (does nothing unless the flag is set)
+    e = launch_up_bf16(x, nullptr, WuT, nullptr, sh->T, sh->d, sh->F, h, aval, nullptr, nullptr, skip, stream, ovf);
+    if (e == hipSuccess)
+      e = launch_down_bf16(aval, nullptr, Wd, nullptr, sh->T, sh->d, sh->F, h, y, out_dt, skip, stream, ovf);
+    if (e != hipSuccess) return hip_status(e, "overflow fallback");
+  } else {
+    e = launch_sddmm_up(in_dt, x, WuT, sh->T, sh->d, sh->F, h, aval, skip, stream);
+    if (e != hipSuccess) return hip_status(e, "sparse up-projection");
+    e = launch_spmm_down(in_dt, out_dt, aval, Wd, sh->T, sh->d, sh->F, h, y, skip, stream);
+    if (e != hipSuccess) return hip_status(e, "sparse down-projection");
+    mark();
+  }
+  mark();                                                             // 3: sparse phases done
   if (training) {
     e = launch_dense_rows_fwd(in_dt, x, WgT, bg, WuT, Wd, sh->T, sh->d, sh->F, w.list, w.nD, w.act, out_dt, y,
                               stream);
     if (e != hipSuccess) return hip_status(e, "dense-row forward");
   }
+  mark();                                                             // 4: end
   return TWELL_OK;
+}
+
+twell_status twell_ffn_fwd(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
+                           const void* WuT, const void* Wd, void* y, twell_mat* saved_h,
+                           int32_t dense_row_threshold, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return twell_ffn_fwd_ex(sh, x, WgT, bg, WuT, Wd, y, saved_h, dense_row_threshold, ws, ws_bytes, stream, nullptr, 0);
 }
 
 size_t twell_ffn_bwd_workspace(const twell_ffn_shape* sh, int32_t dense_row_threshold) {

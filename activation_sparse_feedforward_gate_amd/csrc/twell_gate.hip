@@ -52,7 +52,7 @@ __device__ __forceinline__ void tile_coords(int id, int nbm, int nbn, int& bm, i
 
 template <class Cfg, bool BF16IN>
 __global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
-  static_assert(Cfg::BN / Cfg::WN == 64 && Cfg::TN == 2, "one 64-column TwELL tile per wave");
+  static_assert((Cfg::BN / Cfg::WN) % 64 == 0 && Cfg::TN % 2 == 0, "whole 64-column TwELL tiles per wave");
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
   const int nbm = (a.T + Cfg::BM - 1) / Cfg::BM;
   const int nbn = a.F / Cfg::BN;
@@ -65,78 +65,100 @@ __global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
   const Operand B{a.WgT, a.d, nullptr, a.F};
   g.run(A, &B, m0, n0, a.d, lds);
 
-  // ---- epilogue: bias, ReLU, ballot compaction into TwELL
+  // ---- epilogue: bias, ReLU, ballot compaction into TwELL.  Accumulator
+  // blocks 2*tc and 2*tc+1 of a wave hold the 64 columns of one TwELL tile;
+  // register e of a 32x32 block holds row 8*(e/4) + 4*(lane/32) + e%4, column
+  // lane%32.  For each 16-row tile: (1) every lane drops its biased values into
+  // a dense 16x64 LDS tile and two ballots per register give the 64-bit masks
+  // of two rows; (2) the width*16 output slots [slot][row] are produced one
+  // per lane: slot s of row r is the s-th set bit of r's mask (found by a
+  // branch-free binary search on popcounts), or padding (+0.0, index 0) past
+  // the row's count; (3) coalesced stores of the values, indices, row counts
+  // and masks.  The mainloop's LDS is free once it returns.
+  constexpr int STG = 16 * 64 * 4 + 16 * 8;                 // dense tile + row masks, per wave
+  static_assert(Cfg::LDS_BYTES >= Cfg::NTH / 64 * STG, "epilogue staging");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wr = m0 + (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
-  const int wc = n0 + (wave % Cfg::WN) * 64;
-  const int j = wc >> 6;
   const int hl = lane >> 5;
-  const int c0 = lane & 31, c1 = 32 + (lane & 31);
-  const float b0 = load_bias<BF16IN>(a.bg, wc + c0);
-  const float b1 = load_bias<BF16IN>(a.bg, wc + c1);
+  const int cl = lane & 31;
+  float* sd = (float*)(lds + wave * STG);                   // [16 rows][64 cols]
+  uint64_t* sm = (uint64_t*)(lds + wave * STG + 16 * 64 * 4);
 #pragma unroll
-  for (int tm = 0; tm < Cfg::TM; ++tm) {
+  for (int tc = 0; tc < Cfg::TN / 2; ++tc) {
+    const int wc = n0 + (wave % Cfg::WN) * (Cfg::BN / Cfg::WN) + tc * 64;
+    const int j = wc >> 6;
+    const float b0 = load_bias<BF16IN>(a.bg, wc + cl);
+    const float b1 = load_bias<BF16IN>(a.bg, wc + 32 + cl);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int rt0 = wr + tm * 32 + half * 16;   // first row of this TwELL row tile
-      if (rt0 >= a.T) continue;                   // wave-uniform
-      uint64_t mrow[8];
-      int width = 0;
+    for (int tm = 0; tm < Cfg::TM; ++tm) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int e = half * 8 + q;
-        const int rl = 8 * (q >> 2) + 4 * hl + (q & 3);
-        const bool rowok = rt0 + rl < a.T;
-        const float v0 = g.acc[0][tm][0][e] + b0;
-        const float v1 = g.acc[0][tm][1][e] + b1;
-        const uint64_t B0 = ballot(rowok && v0 > 0.f);
-        const uint64_t B1 = ballot(rowok && v1 > 0.f);
-        const uint64_t mlo = (B0 & 0xffffffffull) | (B1 << 32);
-        const uint64_t mhi = (B0 >> 32) | (B1 & 0xffffffff00000000ull);
-        width = max(width, max(popc64(mlo), popc64(mhi)));
-        mrow[q] = hl ? mhi : mlo;
-      }
-      const int64_t tix = (int64_t)(rt0 >> 4) * a.NT + j;
-      const int64_t tbase = tix * (64 * 16);
-      if (lane == 0) a.width[tix] = (uint8_t)width;
+      for (int half = 0; half < 2; ++half) {
+        const int rt0 = wr + tm * 32 + half * 16;   // first row of this TwELL row tile
+        if (rt0 >= a.T) continue;                   // wave-uniform
+        int width = 0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int e = half * 8 + q;
-        const int rl = 8 * (q >> 2) + 4 * hl + (q & 3);
-        const int row = rt0 + rl;
-        const uint64_t M = mrow[q];
-        const int cnt = popc64(M);
-        if (c0 == 0 && row < a.T) {
-          a.cnt[(int64_t)row * a.NT + j] = (uint8_t)cnt;
-          if (a.mask) a.mask[(int64_t)row * a.NT + j] = M;
-        }
-        {
-          const float v = g.acc[0][tm][0][e] + b0;
-          const int nb = popc64(M & below(c0));
-          const bool act = (M >> c0) & 1ull;
-          const int slot = act ? nb : cnt + (c0 - nb);
-          if (slot < width) {
-            a.val[tbase + slot * 16 + rl] = act ? v : 0.f;
-            a.idx[tbase + slot * 16 + rl] = act ? (uint8_t)c0 : (uint8_t)0;
+        for (int q = 0; q < 8; ++q) {
+          const int e = half * 8 + q;
+          const int rl = 8 * (q >> 2) + 4 * hl + (q & 3);
+          const bool rowok = rt0 + rl < a.T;
+          const float v0 = g.acc[0][tm][2 * tc][e] + b0;
+          const float v1 = g.acc[0][tm][2 * tc + 1][e] + b1;
+          const uint64_t B0 = __builtin_amdgcn_ballot_w64(rowok && v0 > 0.f);
+          const uint64_t B1 = __builtin_amdgcn_ballot_w64(rowok && v1 > 0.f);
+          sd[rl * 64 + cl] = v0;
+          sd[rl * 64 + 32 + cl] = v1;
+          const uint64_t mA = (B0 & 0xffffffffull) | (B1 << 32);               // row 8*(q/4) + q%4
+          const uint64_t mB = (B0 >> 32) | (B1 & 0xffffffff00000000ull);        // that row + 4
+          width = max(width, max(popc64(mA), popc64(mB)));
+          if (lane == 0) {
+            const int r0 = 8 * (q >> 2) + (q & 3);
+            sm[r0] = mA;
+            sm[r0 + 4] = mB;
           }
         }
-        {
-          const float v = g.acc[0][tm][1][e] + b1;
-          const int nb = popc64(M & below(c1));
-          const bool act = (M >> c1) & 1ull;
-          const int slot = act ? nb : cnt + (c1 - nb);
-          if (slot < width) {
-            a.val[tbase + slot * 16 + rl] = act ? v : 0.f;
-            a.idx[tbase + slot * 16 + rl] = act ? (uint8_t)c1 : (uint8_t)0;
+        __builtin_amdgcn_wave_barrier();
+        const int64_t tix = (int64_t)(rt0 >> 4) * a.NT + j;
+        const int64_t tbase = tix * (64 * 16);
+        for (int i = lane; i < width * 16; i += 64) {
+          const int sl = i >> 4, r = i & 15;
+          uint64_t m = sm[r];
+          float v = 0.f;
+          int c = 0;
+          if (sl < popc64(m)) {
+            // position of the sl-th set bit of m
+            int k = sl;
+#pragma unroll
+            for (int w = 32; w >= 1; w >>= 1) {
+              const uint64_t lowmask = (w == 64) ? ~0ull : ((1ull << w) - 1ull);
+              const int pc = popc64(m & lowmask);
+              const bool up = k >= pc;
+              k = up ? k - pc : k;
+              c = up ? c + w : c;
+              m = up ? (m >> w) : m;
+            }
+            v = sd[r * 64 + c];
           }
+          a.val[tbase + i] = v;
+          a.idx[tbase + i] = (uint8_t)c;
         }
+        if (lane < 16 && rt0 + lane < a.T) {
+          const uint64_t M = sm[lane];
+          a.cnt[(int64_t)(rt0 + lane) * a.NT + j] = (uint8_t)popc64(M);
+          if (a.mask) a.mask[(int64_t)(rt0 + lane) * a.NT + j] = M;
+        }
+        if (lane == 0) a.width[tix] = (uint8_t)width;
+        __builtin_amdgcn_wave_barrier();
       }
     }
   }
 }
 
-using GateBigBf16 = GemmCfg<256, 256, 2, 4, OP_BF16_K, OP_BF16_K>;
+#ifndef TWELL_GATE_WM
+#define TWELL_GATE_WM 2
+#define TWELL_GATE_WN 4
+#endif
+using GateBigBf16 = GemmCfg<256, 256, TWELL_GATE_WM, TWELL_GATE_WN, OP_BF16_K, OP_BF16_K>;
 using GateSmallBf16 = GemmCfg<64, 64, 1, 1, OP_BF16_K, OP_BF16_K>;
 using GateBigF32 = GemmCfg<256, 256, 2, 4, OP_F32_K, OP_F32_K>;
 using GateSmallF32 = GemmCfg<64, 64, 1, 1, OP_F32_K, OP_F32_K>;

@@ -68,6 +68,7 @@ struct SpArgs {
   int out_bf16;
   int S;                // slices
   int ngroups;          // ceil(NR / GW)
+  const int* gate;      // null, or a device flag: the kernel runs only if it is non-zero
 };
 
 // Workgroup -> (token group g, slice s).  With S a multiple of 8, slice s runs
@@ -299,6 +300,7 @@ template <int NP>
 __global__ __launch_bounds__(256) void up_bf16_kernel(SpArgs a) {
   __shared__ UnionLds L;
   __shared__ __attribute__((aligned(16))) char sw[NP][UP_CAP * 128];
+  if (a.gate && *a.gate == 0) return;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int g, s;
@@ -334,6 +336,7 @@ template <int NV, int NCB>
 __global__ __launch_bounds__(256) void down_bf16_kernel(SpArgs a) {
   __shared__ UnionLds L;
   __shared__ __attribute__((aligned(16))) char sb[NV][DN_KC * DN_PITCH_MAX];
+  if (a.gate && *a.gate == 0) return;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int g, s;
@@ -491,12 +494,13 @@ int pick_slices(int units, int max_units, double bytes_per_unit, int ngroups) {
 
 hipError_t launch_up_bf16(const void* x, const void* dY, const void* WuT, const void* Wd, int T, int d, int F,
                           const TwellView& h, float* aval, float* dgval, float* duval, const uint8_t* skip,
-                          hipStream_t s) {
+                          hipStream_t s, const int* gate) {
   if ((int64_t)F * d >= ((int64_t)1 << 32)) return hipErrorInvalidValue;   // 32-bit weight offsets
   SpArgs a{};
   a.x = (const uint16_t*)x; a.x2 = (const uint16_t*)dY; a.W = (const uint16_t*)WuT; a.W2 = (const uint16_t*)Wd;
   a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
   a.mask = h.mask; a.skip = skip; a.hval = (const float*)h.val; a.v0 = aval; a.v1 = dgval; a.v2 = duval;
+  a.gate = gate;
   if (a.NR == 0) return hipSuccess;
   a.ngroups = (a.NR + GW - 1) / GW;
   const int NP = dY ? 2 : 1;
@@ -522,11 +526,13 @@ static void launch_down_ncb(int ncb, dim3 grid, const SpArgs& a, hipStream_t s) 
 }
 
 hipError_t launch_down_bf16(const float* v0, const float* v1, const void* W, const void* W2, int T, int d, int F,
-                            const TwellView& pat, void* y, int out_dt, const uint8_t* skip, hipStream_t s) {
+                            const TwellView& pat, void* y, int out_dt, const uint8_t* skip, hipStream_t s,
+                            const int* gate) {
   SpArgs a{};
   a.W = (const uint16_t*)W; a.W2 = (const uint16_t*)W2;
   a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
   a.mask = pat.mask; a.skip = skip; a.v0 = (float*)v0; a.v1 = (float*)v1; a.y = y; a.out_bf16 = out_dt == DT_BF16;
+  a.gate = gate;
   if (a.NR == 0) return hipSuccess;
   a.ngroups = (a.NR + GW - 1) / GW;
   const int NV = v1 ? 2 : 1;

@@ -133,8 +133,12 @@ size_t twell_ffn_fwd_workspace(const twell_ffn_shape *sh, int32_t training);
  *                 >= 0: hybrid forward; rows whose nnz exceeds it take the
  *                 dense branch, gathered-row MFMA GEMMs (requires saved_h)
  *   ws, ws_bytes  workspace of at least twell_ffn_fwd_workspace(sh, thr >= 0)
- * Stored pairs are exactly the (t, n) with g > 0 in fp32; h, u and a are
- * kept in fp32, accumulation is fp32.
+ * Stored pairs are exactly the (t, n) with g > 0 in fp32; accumulation is
+ * fp32.  bf16 inputs: the up- and down-projections run as MFMA GEMMs over each
+ * 256-token block's union of active neurons, with a = h*u passed between them
+ * in fp16 (if any |a| exceeds the fp16 range the layer is recomputed with a in
+ * fp32 automatically); fp32 inputs keep h, u and a in fp32 throughout.
+ * Matrices must hold fewer than 2^32 elements each.
  */
 twell_status twell_ffn_fwd(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
                            const void *WuT, const void *Wd, void *y, twell_mat *saved_h,
@@ -174,6 +178,18 @@ twell_status twell_ffn_bwd_hybrid(const twell_ffn_shape *sh, const void *x, cons
                                   int32_t dense_row_threshold, float *dX, float *dWgT, float *dWuT, float *dWd,
                                   float *dbg, int32_t *n_dense_rows, void *ws, size_t ws_bytes,
                                   hipStream_t stream);
+
+/*
+ * twell_ffn_fwd_ex: twell_ffn_fwd that also records up to n_events caller-
+ * created HIP events on the stream at its stage boundaries, for timing:
+ *   [0] start  [1] gate GEMM + pack done  [2] up/down GEMMs done
+ *   [3] sparse phases done (incl. the fp16-overflow fallback)  [4] end
+ * Arguments otherwise as for twell_ffn_fwd.
+ */
+twell_status twell_ffn_fwd_ex(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
+                              const void *WuT, const void *Wd, void *y, twell_mat *saved_h,
+                              int32_t dense_row_threshold, void *ws, size_t ws_bytes, hipStream_t stream,
+                              hipEvent_t *stage_events, int32_t n_events);
 
 /*
  * The three stages of twell_ffn_fwd, callable one by one (twell_ffn_fwd is
