@@ -257,6 +257,29 @@ def test_fwd_everything_fires(torch, tw):
     check_fwd(w, y, m)
 
 
+def test_fwd_fp16_overflow_falls_back(torch, tw):
+    """a = h*u beyond the fp16 range (inputs scaled up) takes the fallback
+    path that keeps a in fp32; y must still match the oracle."""
+    w = make_workload("0.5b", T=300, d=256, f=1024)
+    w.x[:] = round_bf16(w.x * np.float32(80.0))
+    w.bg[:] = round_bf16(w.bg * np.float32(80.0))
+    log("[fwd] fp16 overflow fallback")
+    ref = O.ffn_fwd_rows(w.x, w.WgT, w.bg, w.WuT, w.Wd, np.arange(w.T))
+    assert np.abs(ref["a"]).max() > 65504.0          # the case really overflows fp16
+    y, m = run_fwd(torch, tw, w)
+    check_fwd(w, y, m)
+
+
+@pytest.mark.parametrize("name,kw", [("0.5b", dict(T=513, d=320, f=640)), ("2b", dict(T=257, d=192, f=1344))],
+                         ids=["d320-f640", "d192-f1344"])
+def test_fwd_odd_multiples(torch, tw, name, kw):
+    """d and F multiples of 64 but not of 128/256 (other tile paths)."""
+    w = make_workload(name, **kw)
+    log(f"[fwd] {name} T={w.T} d={w.d} f={w.f}")
+    y, m = run_fwd(torch, tw, w)
+    check_fwd(w, y, m)
+
+
 FULL = ["0.5b", "1.5b", "2b"]
 
 
