@@ -35,24 +35,26 @@ __device__ __forceinline__ void tile_order(int id, int nbm, int nbn, int& bm, in
 
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTH) void dense_gateup_kernel(DenseArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
   const int nbm = (a.T + Cfg::BM - 1) / Cfg::BM, nbn = a.F / Cfg::BN;
   int bm, bn;
   tile_order(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, bm, bn);
   const int m0 = bm * Cfg::BM, n0 = bn * Cfg::BN;
-  GemmTile<Cfg> g;
+  typedef DmaTile<Cfg> Tile;
+  Tile g;
   const Operand A{a.x, a.d, nullptr, a.T};
   const Operand B[2] = {{a.WgT, a.d, nullptr, a.F}, {a.WuT, a.d, nullptr, a.F}};
-  g.run(A, B, m0, n0, a.d, lds);
+  g.run(A, B, m0, n0, a.d, st0, st1);
 #pragma unroll
   for (int j = 0; j < Cfg::TN; ++j) {
-    const int col = n0 + GemmTile<Cfg>::col_of(j);
+    const int col = n0 + Tile::col_of(j);
     const float b = a.bg ? bf16_to_f32(((const uint16_t*)a.bg)[col]) : 0.f;
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = m0 + GemmTile<Cfg>::row_of(i, e);
+        const int row = m0 + Tile::row_of(i, e);
         if (row < a.T) {
           const float gv = g.acc[0][i][j][e] + b;
           const float h = gv > 0.f ? gv : 0.f;
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_down_kernel(DenseArgs a) {
   }
 }
 
-using DenseGateUp = GemmCfg<128, 128, 2, 2, OP_BF16_K, OP_BF16_K, 2>;
+using DenseGateUp = DmaCfg<256, 128, 4, 2, 2>;
 using DenseDownBig = GemmCfg<256, 256, 2, 4, OP_BF16_K, OP_BF16_T>;
 using DenseDownSmall = GemmCfg<128, 64, 2, 1, OP_BF16_K, OP_BF16_T>;
 

@@ -325,6 +325,7 @@ struct GemmCfg {
   static constexpr int STAGE = A_BYTES * (ASPLIT ? 2 : 1) + B_BYTES * NB;
   static constexpr int LDS_BYTES = 2 * STAGE;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static constexpr int EPI_BYTES = LDS_BYTES;
   static constexpr int A_KIND = AKIND, B_KIND = BKIND;
 };
 
@@ -437,6 +438,172 @@ struct GemmTile {
     const int wave = threadIdx.x >> 6;
     return (wave % Cfg::WN) * (Cfg::BN / Cfg::WN) + j * 32 + (threadIdx.x & 31);
   }
+};
+
+
+// ------------------------------------------------------------------ direct-to-LDS mainloop
+//
+// For 16-bit K-major operands (bf16, or fp16 with F16) the K tiles move from
+// global memory straight into LDS with global_load_lds_dwordx4: no staging
+// registers and no LDS store instructions in the wave's stream, so the loads
+// of tile k+1 run entirely under the MFMAs of tile k.  One instruction fills
+// 1 KB of LDS (lane l writes bytes 16l..16l+15 of it), which is 8 consecutive
+// 128-byte tile rows; the XOR swizzle is applied on the global side: the lane
+// that lands on physical chunk p of row r fetches logical chunk
+// p ^ (r & 7) ^ ((r >> 3) & 7) (the swizzle is its own inverse), so the
+// fragment reads see the same swizzled layout as swz().  The two stage buffers
+// are separate LDS arrays owned by the kernel: the compiler can then tell that
+// a fragment read of one stage never overlaps the loads in flight into the
+// other, and it waits for those loads only where the loop says so (a vmcnt
+// wait before the barrier that hands the next stage over).
+template <int BM_, int BN_, int WM_, int WN_, int NB_ = 1, bool F16_ = false>
+struct DmaCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NB = NB_;
+  static constexpr bool F16MMA = F16_;
+  static constexpr int NW = WM * WN, NTH = NW * WAVE;
+  static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  static_assert(TM >= 1 && TN >= 1, "wave tile must hold whole 32x32 blocks");
+  static constexpr int KT = 64;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int STAGE = A_BYTES + NB * B_BYTES;
+  static constexpr int LDS_BYTES = 2 * STAGE;
+  static constexpr int EPI_BYTES = STAGE;                         // contiguous LDS free after run()
+  static constexpr int LA = BM / (8 * NW), LB = BN / (8 * NW);   // 1 KB loads per wave per operand
+  static_assert(LA * 8 * NW == BM && LB * 8 * NW == BN, "block rows must split into whole 1 KB loads per wave");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <class Cfg>
+struct DmaTile {
+  static constexpr int TM = Cfg::TM, TN = Cfg::TN, NB = Cfg::NB, NW = Cfg::NW;
+  f32x16 acc[NB][TM][TN];
+
+  // Multiply the block at (m0, n0) over K (a multiple of 64); st0 and st1 are
+  // the kernel's two stage arrays of Cfg::STAGE bytes each.  Both are free
+  // again when run() returns.
+  __device__ void run(const Operand& A, const Operand* B, int m0, int n0, int K, char* st0, char* st1) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
+    const int wc = (wave % Cfg::WN) * (Cfg::BN / Cfg::WN);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[b][i][j][e] = 0.f;
+
+    // per-lane byte offsets (below 2^32: each operand is under 4 GB) of the
+    // rows this lane fills; the K-tile base is wave-uniform, so each load is
+    // one scalar base plus one 32-bit lane offset
+    const int rsub = lane >> 3, p = lane & 7;
+    uint32_t offa[Cfg::LA], offb[NB][Cfg::LB];
+#pragma unroll
+    for (int q = 0; q < Cfg::LA; ++q) {
+      const int r = (q * NW + wave) * 8 + rsub;
+      int gr = min(m0 + r, A.nrows - 1);
+      if (A.gather) gr = A.gather[gr];
+      offa[q] = ((uint32_t)gr * (uint32_t)A.ld + (uint32_t)(((p ^ r ^ (r >> 3)) & 7) * 8)) * 2u;
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int q = 0; q < Cfg::LB; ++q) {
+        const int r = (q * NW + wave) * 8 + rsub;
+        int gr = min(n0 + r, B[b].nrows - 1);
+        if (B[b].gather) gr = B[b].gather[gr];
+        offb[b][q] = ((uint32_t)gr * (uint32_t)B[b].ld + (uint32_t)(((p ^ r ^ (r >> 3)) & 7) * 8)) * 2u;
+      }
+    const char* pa = (const char*)A.ptr;
+    const char* pb[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) pb[b] = (const char*)B[b].ptr;
+
+    auto issue = [&](int kt, char* st) {
+      const char* ka = pa + (size_t)kt * 128;
+#pragma unroll
+      for (int q = 0; q < Cfg::LA; ++q)
+        __builtin_amdgcn_global_load_lds((const void*)(ka + offa[q]), (lds_void*)(st + (q * NW + wave) * 1024), 16, 0, 0);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const char* kb = pb[b] + (size_t)kt * 128;
+#pragma unroll
+        for (int q = 0; q < Cfg::LB; ++q)
+          __builtin_amdgcn_global_load_lds((const void*)(kb + offb[b][q]),
+                                           (lds_void*)(st + Cfg::A_BYTES + b * Cfg::B_BYTES + (q * NW + wave) * 1024),
+                                           16, 0, 0);
+      }
+    };
+    auto compute = [&](const char* st) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ch = 2 * kk + (lane >> 5);
+        uint4 fa[TM], fb[NB][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[i] = *(const uint4*)(st + swz(wr + i * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            fb[b][j] = *(const uint4*)(st + Cfg::A_BYTES + b * Cfg::B_BYTES + swz(wc + j * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              if constexpr (Cfg::F16MMA) acc[b][i][j] = mfma32_f16(fa[i], fb[b][j], acc[b][i][j]);
+              else acc[b][i][j] = mfma32(fa[i], fb[b][j], acc[b][i][j]);
+            }
+      }
+    };
+    // Hand-over of a stage: this wave's loads are complete (vmcnt(0), the
+    // other counters left alone), then the workgroup barrier.  The empty asm
+    // statements keep the compiler from moving LDS accesses across it.
+    auto stage_barrier = [] {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+
+    // tile kt: wait for it, start loading tile kt+1 into the other stage, compute
+    const int nk = K / 64;
+    auto step = [&](int kt, const char* cur, char* nxt) {
+      stage_barrier();
+      if (kt + 1 < nk) issue(kt + 1, nxt);
+      compute(cur);
+    };
+    if (nk > 0) issue(0, st0);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, st0, st1);
+      step(kt + 1, st1, st0);
+    }
+    if (kt < nk) step(kt, st0, st1);
+    __syncthreads();
+  }
+
+  __device__ static int row_of(int i, int e) {
+    const int wave = threadIdx.x >> 6;
+    return (wave / Cfg::WN) * (Cfg::BM / Cfg::WM) + i * 32 + mfma32_row(threadIdx.x & 63, e);
+  }
+  __device__ static int col_of(int j) {
+    const int wave = threadIdx.x >> 6;
+    return (wave % Cfg::WN) * (Cfg::BN / Cfg::WN) + j * 32 + (threadIdx.x & 31);
+  }
+};
+
+// Mainloop type of a configuration.
+template <class Cfg> struct TileFor { typedef GemmTile<Cfg> type; static constexpr bool dma = false; };
+template <int BM, int BN, int WM, int WN, int NB, bool F16>
+struct TileFor<DmaCfg<BM, BN, WM, WN, NB, F16>> {
+  typedef DmaTile<DmaCfg<BM, BN, WM, WN, NB, F16>> type;
+  static constexpr bool dma = true;
 };
 
 }  // namespace twell

@@ -53,17 +53,26 @@ __device__ __forceinline__ void tile_coords(int id, int nbm, int nbn, int& bm, i
 template <class Cfg, bool BF16IN>
 __global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
   static_assert((Cfg::BN / Cfg::WN) % 64 == 0 && Cfg::TN % 2 == 0, "whole 64-column TwELL tiles per wave");
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
   const int nbm = (a.T + Cfg::BM - 1) / Cfg::BM;
   const int nbn = a.F / Cfg::BN;
   int bm, bn;
   tile_coords(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, bm, bn);
   const int m0 = bm * Cfg::BM, n0 = bn * Cfg::BN;
 
-  GemmTile<Cfg> g;
+  typename TileFor<Cfg>::type g;
   const Operand A{a.x, a.d, nullptr, a.T};
   const Operand B{a.WgT, a.d, nullptr, a.F};
-  g.run(A, &B, m0, n0, a.d, lds);
+  char* lds;
+  if constexpr (TileFor<Cfg>::dma) {
+    __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
+    __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
+    g.run(A, &B, m0, n0, a.d, st0, st1);
+    lds = st0;
+  } else {
+    __shared__ __attribute__((aligned(16))) char buf[Cfg::LDS_BYTES];
+    g.run(A, &B, m0, n0, a.d, buf);
+    lds = buf;
+  }
 
   // ---- epilogue: bias, ReLU, ballot compaction into TwELL.  Accumulator
   // blocks 2*tc and 2*tc+1 of a wave hold the 64 columns of one TwELL tile;
@@ -76,7 +85,7 @@ __global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
   // the row's count; (3) coalesced stores of the values, indices, row counts
   // and masks.  The mainloop's LDS is free once it returns.
   constexpr int STG = 16 * 64 * 4 + 16 * 8;                 // dense tile + row masks, per wave
-  static_assert(Cfg::LDS_BYTES >= Cfg::NTH / 64 * STG, "epilogue staging");
+  static_assert(Cfg::EPI_BYTES >= Cfg::NTH / 64 * STG, "epilogue staging");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wr = m0 + (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
@@ -154,11 +163,7 @@ __global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
   }
 }
 
-#ifndef TWELL_GATE_WM
-#define TWELL_GATE_WM 2
-#define TWELL_GATE_WN 4
-#endif
-using GateBigBf16 = GemmCfg<256, 256, TWELL_GATE_WM, TWELL_GATE_WN, OP_BF16_K, OP_BF16_K>;
+using GateBigBf16 = DmaCfg<256, 256, 4, 2>;
 using GateSmallBf16 = GemmCfg<64, 64, 1, 1, OP_BF16_K, OP_BF16_K>;
 using GateBigF32 = GemmCfg<256, 256, 2, 4, OP_F32_K, OP_F32_K>;
 using GateSmallF32 = GemmCfg<64, 64, 1, 1, OP_F32_K, OP_F32_K>;

@@ -110,7 +110,8 @@ __global__ __launch_bounds__(256) void union_list_kernel(UnionArgs a, const uint
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   static_assert(Cfg::BM == UB, "one row block per M tile");
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
   const int npt = (a.F + Cfg::BN - 1) / Cfg::BN;
   const int nblk = (a.T + UB - 1) / UB;
   int b, pt;
@@ -133,10 +134,11 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   const int m0 = b * UB;
   const int* ul = a.ulist + (int64_t)b * a.F;
 
-  GemmTile<Cfg> g;
+  typedef DmaTile<Cfg> Tile;
+  Tile g;
   const Operand A{a.x, a.d, nullptr, a.T};
   const Operand B{a.WuT, a.d, ul, nb};
-  g.run(A, &B, m0, p0, a.d, lds);
+  g.run(A, &B, m0, p0, a.d, st0, st1);
 
   // epilogue: a = h * u on stored pairs, else 0, stored as fp16 into
   // adense[t][p] (32 consecutive positions per half-wave store).  The masks of
@@ -145,12 +147,14 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   // once it returns), so the per-element lookups stay on chip; tiles beyond
   // the staging budget fall back to global reads.  Positions in
   // [n_b, roundup64(n_b)) are written as zeros (the down GEMM reads whole
-  // 64-position K tiles).
+  // 64-position K tiles).  The masks take the first stage buffer, the h
+  // blocks and their offsets the second.
   constexpr int SMAX = 32;                     // column tiles whose masks are staged
-  constexpr int HBUDGET = (Cfg::LDS_BYTES - UB * SMAX * 8 - 16 * SMAX * 4 - 64) / 4;   // floats of h
-  uint64_t* sm = (uint64_t*)lds;                                    // [UB][S]
-  int* hoff = (int*)(lds + UB * SMAX * 8);                          // [16 row tiles][S]
-  float* hb = (float*)(lds + UB * SMAX * 8 + 16 * SMAX * 4 + 64);   // h blocks
+  static_assert(UB * SMAX * 8 <= Cfg::STAGE, "mask staging");
+  constexpr int HBUDGET = (Cfg::STAGE - 16 * SMAX * 4 - 64) / 4;     // floats of h
+  uint64_t* sm = (uint64_t*)st0;                                    // [UB][S]
+  int* hoff = (int*)st1;                                            // [16 row tiles][S]
+  float* hb = (float*)(st1 + 16 * SMAX * 4 + 64);                   // h blocks
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int pl = min(p0 + Cfg::BN, nb) - 1;
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   bool over = false;
 #pragma unroll
   for (int j = 0; j < Cfg::TN; ++j) {
-    const int p = p0 + GemmTile<Cfg>::col_of(j);
+    const int p = p0 + Tile::col_of(j);
     const int n = p < nb ? ul[p] : -1;
     const int tj = n >> 6, c = n & 63, sj = tj - tjf;
     const bool wr = p < ((nb + 63) & ~63);
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
     for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int r = GemmTile<Cfg>::row_of(i, e);
+        const int r = Tile::row_of(i, e);
         const int t = m0 + r;
         float v = 0.f;
         if (n >= 0) {
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(Cfg::NTH) void down_union_kernel(UnionArgs a) {
   }
 }
 
-using UpUnionCfg = GemmCfg<256, 256, 2, 4, OP_BF16_K, OP_BF16_K>;
+using UpUnionCfg = DmaCfg<256, 256, 4, 2>;
 using DownUnionCfg = GemmCfg<256, 256, 2, 4, OP_F16_K, OP_BF16_T16>;
 using DownUnionCfg128 = GemmCfg<256, 128, 2, 2, OP_F16_K, OP_BF16_T16>;
 using DownUnionCfg64 = GemmCfg<256, 64, 4, 1, OP_F16_K, OP_BF16_T16>;
