@@ -27,7 +27,11 @@ namespace twell {
 
 namespace {
 
-constexpr int UB = 256;   // tokens per row block
+#ifndef TWELL_UNION_ROWS
+#define TWELL_UNION_ROWS 256
+#endif
+constexpr int UB = TWELL_UNION_ROWS;   // tokens per row block
+constexpr int RT = UB / 16;            // TwELL row tiles per row block
 
 struct UnionArgs {
   const void* x;
@@ -151,29 +155,38 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   // blocks and their offsets the second.
   constexpr int SMAX = 32;                     // column tiles whose masks are staged
   static_assert(UB * SMAX * 8 <= Cfg::STAGE, "mask staging");
-  constexpr int HBUDGET = (Cfg::STAGE - 16 * SMAX * 4 - 64) / 4;     // floats of h
+  constexpr int HBUDGET = (Cfg::STAGE - RT * SMAX * 4 - 64) / 4;     // floats of h
   uint64_t* sm = (uint64_t*)st0;                                    // [UB][S]
-  int* hoff = (int*)st1;                                            // [16 row tiles][S]
-  float* hb = (float*)(st1 + 16 * SMAX * 4 + 64);                   // h blocks
+  int* hoff = (int*)st1;                                            // [RT row tiles][S]
+  float* hb = (float*)(st1 + RT * SMAX * 4 + 64);                   // h blocks
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int pl = min(p0 + Cfg::BN, nb) - 1;
   const int tjf = ul[p0] >> 6, tjl = ul[pl] >> 6;
   const int S = min(tjl - tjf + 1, SMAX);
-  for (int q = tid; q < UB * S; q += Cfg::NTH) {
-    const int r = q / S, sj = q - r * S;
-    const int t = m0 + r;
-    sm[q] = live(a, t) ? a.mask[(int64_t)t * a.NT + tjf + sj] : 0ull;
+  // mask staging: four independent loads in flight per thread
+  for (int q0 = tid; q0 < UB * S; q0 += 4 * Cfg::NTH) {
+    uint64_t mv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = q0 + u * Cfg::NTH;
+      const int r = q / S, sj = q - r * S;
+      const int t = m0 + r;
+      mv[u] = (q < UB * S && live(a, t)) ? a.mask[(int64_t)t * a.NT + tjf + sj] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (q0 + u * Cfg::NTH < UB * S) sm[q0 + u * Cfg::NTH] = mv[u];
   }
-  __shared__ int hmeta[2];                          // [0] staged pairs, [1] staged floats
+  __shared__ int hmeta[1];                          // staged (row tile, column tile) pairs
   if (tid < 64) {
     // h block starts: prefix over (row tile, column tile) of width*16 floats;
     // the pairs that fit the budget form a prefix of that order
-    int run = 0;
-    for (int q0 = 0; q0 < 16 * S; q0 += 64) {
+    int run = 0, nv = 0;
+    for (int q0 = 0; q0 < RT * S; q0 += 64) {
       const int q = q0 + lane;
       int wdt = 0;
-      if (q < 16 * S) {
+      if (q < RT * S) {
         const int i = q / S, sj = q - i * S;
         const int rt = (m0 >> 4) + i;
         wdt = rt * 16 < a.T ? a.hwidth[(int64_t)rt * a.NT + tjf + sj] : 0;
@@ -185,37 +198,50 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
         if (lane >= o) incl += u;
       }
       const int start = run + incl - wdt * 16;
-      if (q < 16 * S) hoff[q] = (start + wdt * 16 <= HBUDGET) ? start : -1;
+      const bool fits = q < RT * S && start + wdt * 16 <= HBUDGET;
+      if (q < RT * S) hoff[q] = fits ? start : -1;
+      nv += popc64(__builtin_amdgcn_ballot_w64(fits));
       run += __shfl(incl, 63);
     }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int nv = 0;
-    while (nv < 16 * S && hoff[nv] >= 0) ++nv;
-    int tot = 0;
-    if (nv > 0) {
-      const int q = nv - 1, i = q / S, sj = q - i * S;
-      const int rt = (m0 >> 4) + i;
-      tot = hoff[q] + (rt * 16 < a.T ? a.hwidth[(int64_t)rt * a.NT + tjf + sj] * 16 : 0);
-    }
-    hmeta[0] = nv;
-    hmeta[1] = tot;
+    if (lane == 0) hmeta[0] = nv;
   }
   __syncthreads();
   {
-    // flattened copy of the staged h blocks: float e belongs to the last pair
-    // whose start is <= e (binary search over the starts)
-    const int nv = hmeta[0], tot = hmeta[1];
-    for (int e = tid; e < tot; e += Cfg::NTH) {
-      int lo = 0, hi = nv - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (hoff[mid] <= e) lo = mid; else hi = mid - 1;
+    // copy of the staged h blocks: a 16-lane group per (row tile, column
+    // tile) block, 16-byte pieces (a block is width*16 contiguous floats)
+    const int nv = hmeta[0];
+    const int grp = tid >> 4, gl = tid & 15;
+    constexpr int NG = Cfg::NTH / 16;
+    for (int q0 = grp; q0 < nv; q0 += 2 * NG) {
+      float4 v[2][2];
+      int dst[2][2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int q = q0 + u * NG;
+        int w = 0;
+        const float4* src = nullptr;
+        if (q < nv) {
+          const int i = q / S, sj = q - i * S;
+          const int rt = (m0 >> 4) + i;
+          if (rt * 16 < a.T) {                    // row tiles past T hold nothing
+            w = a.hwidth[(int64_t)rt * a.NT + tjf + sj];
+            src = (const float4*)(a.hval + ((int64_t)rt * a.NT + tjf + sj) * 1024);
+          }
+        }
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const int c = gl + 16 * c2;
+          dst[u][c2] = c < w * 4 ? hoff[q] / 4 + c : -1;
+          v[u][c2] = c < w * 4 ? src[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        // widths above 8 (rare): the rest of the block directly
+        for (int c = gl + 32; c < w * 4; c += 16) ((float4*)hb)[hoff[q] / 4 + c] = src[c];
       }
-      const int i = lo / S, sj = lo - i * S;
-      const int rt = (m0 >> 4) + i;
-      hb[e] = a.hval[((int64_t)rt * a.NT + tjf + sj) * 1024 + (e - hoff[lo])];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+          if (dst[u][c2] >= 0) ((float4*)hb)[dst[u][c2]] = v[u][c2];
     }
   }
   __syncthreads();
@@ -282,10 +308,22 @@ __global__ __launch_bounds__(Cfg::NTH) void down_union_kernel(UnionArgs a) {
   }
 }
 
+#if TWELL_UNION_ROWS == 256
 using UpUnionCfg = DmaCfg<256, 256, 4, 2>;
 using DownUnionCfg = GemmCfg<256, 256, 2, 4, OP_F16_K, OP_BF16_T16>;
 using DownUnionCfg128 = GemmCfg<256, 128, 2, 2, OP_F16_K, OP_BF16_T16>;
 using DownUnionCfg64 = GemmCfg<256, 64, 4, 1, OP_F16_K, OP_BF16_T16>;
+#elif TWELL_UNION_ROWS == 128
+using UpUnionCfg = DmaCfg<128, 256, 2, 4>;
+using DownUnionCfg = GemmCfg<128, 256, 2, 4, OP_F16_K, OP_BF16_T16>;
+using DownUnionCfg128 = GemmCfg<128, 128, 2, 2, OP_F16_K, OP_BF16_T16>;
+using DownUnionCfg64 = GemmCfg<128, 64, 2, 1, OP_F16_K, OP_BF16_T16>;
+#else
+using UpUnionCfg = DmaCfg<64, 256, 1, 4>;
+using DownUnionCfg = GemmCfg<64, 256, 1, 4, OP_F16_K, OP_BF16_T16>;
+using DownUnionCfg128 = GemmCfg<64, 128, 1, 2, OP_F16_K, OP_BF16_T16>;
+using DownUnionCfg64 = GemmCfg<64, 64, 1, 1, OP_F16_K, OP_BF16_T16>;
+#endif
 
 size_t union_ws_bytes(int T, int F) {
   const size_t nblk = (size_t)(T + UB - 1) / UB;
