@@ -41,10 +41,12 @@ struct UnionArgs {
   const uint64_t* mask;   // [T][NT]
   const uint8_t* skip;    // [T] or null
   const float* hval;      // TwELL values of h
+  const uint8_t* hidx;    // TwELL column indices of h
   const uint8_t* hwidth;  // TwELL widths of h
   int* ulist;             // [NBLK][F]
   int* ucount;            // [NBLK]
-  _Float16* adense;       // [T][F]
+  _Float16* adense;       // [T][F], then spare slots
+  uint32_t spare;         // element index of a spare slot (T*F)
   int* flag;              // fp16 overflow flag
   void* y;
   int out_bf16;
@@ -145,135 +147,113 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   g.run(A, &B, m0, p0, a.d, st0, st1);
 
   // epilogue: a = h * u on stored pairs, else 0, stored as fp16 into
-  // adense[t][p] (32 consecutive positions per half-wave store).  The masks of
-  // the tile's 256 rows and the TwELL value blocks of h over the column tiles
-  // its positions span are first staged in LDS (the mainloop's LDS is free
-  // once it returns), so the per-element lookups stay on chip; tiles beyond
-  // the staging budget fall back to global reads.  Positions in
+  // adense[t][p] (32 consecutive positions per half-wave store).  Positions in
   // [n_b, roundup64(n_b)) are written as zeros (the down GEMM reads whole
-  // 64-position K tiles).  The masks take the first stage buffer, the h
-  // blocks and their offsets the second.
-  constexpr int SMAX = 32;                     // column tiles whose masks are staged
-  static_assert(UB * SMAX * 8 <= Cfg::STAGE, "mask staging");
-  constexpr int HBUDGET = (Cfg::STAGE - RT * SMAX * 4 - 64) / 4;     // floats of h
-  uint64_t* sm = (uint64_t*)st0;                                    // [UB][S]
-  int* hoff = (int*)st1;                                            // [RT row tiles][S]
-  float* hb = (float*)(st1 + RT * SMAX * 4 + 64);                   // h blocks
+  // 64-position K tiles).  h is brought to the accumulator layout through
+  // LDS, 128 rows per pass: the two stage buffers are zeroed, every stored
+  // TwELL pair of those rows whose neuron falls in this tile's positions is
+  // written at (position, row) (position found through posmap, the inverse of
+  // the union list over the tile's neuron span), and the four waves owning
+  // the rows read their h values back with 16-byte loads.  A buffer holds 64
+  // rows as [position][row] (256 bytes per position, 16-byte pieces XOR-
+  // swizzled by position so 8 consecutive positions hit 8 bank groups).
+  static_assert(Cfg::BM == 256 && Cfg::BN == 256 && Cfg::WM == 4 && Cfg::WN == 2, "epilogue layout");
+  static_assert(Cfg::STAGE >= 256 * 64 * 4, "h buffers");
+  constexpr int POSCAP = 12288;
+  __shared__ int16_t posmap[POSCAP];
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane = tid & 63, wave = tid >> 6;
   const int pl = min(p0 + Cfg::BN, nb) - 1;
-  const int tjf = ul[p0] >> 6, tjl = ul[pl] >> 6;
-  const int S = min(tjl - tjf + 1, SMAX);
-  // mask staging: four independent loads in flight per thread
-  for (int q0 = tid; q0 < UB * S; q0 += 4 * Cfg::NTH) {
-    uint64_t mv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = q0 + u * Cfg::NTH;
-      const int r = q / S, sj = q - r * S;
-      const int t = m0 + r;
-      mv[u] = (q < UB * S && live(a, t)) ? a.mask[(int64_t)t * a.NT + tjf + sj] : 0ull;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (q0 + u * Cfg::NTH < UB * S) sm[q0 + u * Cfg::NTH] = mv[u];
-  }
-  __shared__ int hmeta[1];                          // staged (row tile, column tile) pairs
-  if (tid < 64) {
-    // h block starts: prefix over (row tile, column tile) of width*16 floats;
-    // the pairs that fit the budget form a prefix of that order
-    int run = 0, nv = 0;
-    for (int q0 = 0; q0 < RT * S; q0 += 64) {
-      const int q = q0 + lane;
-      int wdt = 0;
-      if (q < RT * S) {
-        const int i = q / S, sj = q - i * S;
-        const int rt = (m0 >> 4) + i;
-        wdt = rt * 16 < a.T ? a.hwidth[(int64_t)rt * a.NT + tjf + sj] : 0;
-      }
-      int incl = wdt * 16;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(incl, o);
-        if (lane >= o) incl += u;
-      }
-      const int start = run + incl - wdt * 16;
-      const bool fits = q < RT * S && start + wdt * 16 <= HBUDGET;
-      if (q < RT * S) hoff[q] = fits ? start : -1;
-      nv += popc64(__builtin_amdgcn_ballot_w64(fits));
-      run += __shfl(incl, 63);
-    }
-    if (lane == 0) hmeta[0] = nv;
-  }
-  __syncthreads();
-  {
-    // copy of the staged h blocks: a 16-lane group per (row tile, column
-    // tile) block, 16-byte pieces (a block is width*16 contiguous floats)
-    const int nv = hmeta[0];
-    const int grp = tid >> 4, gl = tid & 15;
-    constexpr int NG = Cfg::NTH / 16;
-    for (int q0 = grp; q0 < nv; q0 += 2 * NG) {
-      float4 v[2][2];
-      int dst[2][2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int q = q0 + u * NG;
-        int w = 0;
-        const float4* src = nullptr;
-        if (q < nv) {
-          const int i = q / S, sj = q - i * S;
-          const int rt = (m0 >> 4) + i;
-          if (rt * 16 < a.T) {                    // row tiles past T hold nothing
-            w = a.hwidth[(int64_t)rt * a.NT + tjf + sj];
-            src = (const float4*)(a.hval + ((int64_t)rt * a.NT + tjf + sj) * 1024);
-          }
-        }
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const int c = gl + 16 * c2;
-          dst[u][c2] = c < w * 4 ? hoff[q] / 4 + c : -1;
-          v[u][c2] = c < w * 4 ? src[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        // widths above 8 (rare): the rest of the block directly
-        for (int c = gl + 32; c < w * 4; c += 16) ((float4*)hb)[hoff[q] / 4 + c] = src[c];
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
-          if (dst[u][c2] >= 0) ((float4*)hb)[dst[u][c2]] = v[u][c2];
-    }
-  }
-  __syncthreads();
+  const int nlo = ul[p0], nhi = ul[pl];
+  const bool use_map = nhi - nlo < POSCAP;
+  if (use_map)
+    for (int p = p0 + tid; p <= pl; p += Cfg::NTH) posmap[ul[p] - nlo] = (int16_t)(p - p0);
+  const int tjf = nlo >> 6, S = (nhi >> 6) - tjf + 1;
+  const int hl = lane >> 5;
+  uint32_t vbits = 0;               // largest |a| bit pattern (NaN patterns sort above every number)
+  auto hslot = [](int p, int r64) { return p * 256 + (((r64 >> 2) ^ (p & 7)) << 4) + ((r64 & 3) << 2); };
 
-  bool over = false;
+  // pass: zero the h buffers, scatter the pairs of rows [128 pass, +128)
+  auto prep = [&](int pass) {
 #pragma unroll
-  for (int j = 0; j < Cfg::TN; ++j) {
-    const int p = p0 + Tile::col_of(j);
-    const int n = p < nb ? ul[p] : -1;
-    const int tj = n >> 6, c = n & 63, sj = tj - tjf;
-    const bool wr = p < ((nb + 63) & ~63);
+    for (int o = 0; o < Cfg::STAGE / (16 * Cfg::NTH); ++o) {
+      ((float4*)st0)[o * Cfg::NTH + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+      ((float4*)st1)[o * Cfg::NTH + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+    // scatter: a 16-lane group per (row tile, column tile) block; lane piece c
+    // holds slot c/4, rows 4*(c%4)..+3 of the block
+    for (int q = tid >> 4; q < 8 * S; q += Cfg::NTH / 16) {
+      const int i = q / S, sj = q - i * S;
+      const int rt = (m0 >> 4) + pass * 8 + i;
+      if (rt * 16 >= a.T) continue;
+      const int tj = tjf + sj;
+      const int64_t blk = (int64_t)rt * a.NT + tj;
+      const int w = a.hwidth[blk];
+      char* hbuf = (i >> 2) ? st1 : st0;
+      for (int c = tid & 15; c < w * 4; c += 16) {
+        const float4 v4 = ((const float4*)(a.hval + blk * 1024))[c];
+        const uint32_t i4 = ((const uint32_t*)(a.hidx + blk * 1024))[c];
+        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
-    for (int i = 0; i < Cfg::TM; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = Tile::row_of(i, e);
-        const int t = m0 + r;
-        float v = 0.f;
-        if (n >= 0) {
-          const uint64_t M = sj < S ? sm[r * S + sj] : (live(a, t) ? a.mask[(int64_t)t * a.NT + tj] : 0ull);
-          if ((M >> c) & 1ull) {
-            const int slot = popc64(M & below(c));
-            const int o = sj < S ? hoff[(r >> 4) * S + sj] : -1;
-            const float h = o >= 0 ? hb[o + slot * 16 + (r & 15)]
-                                   : a.hval[((int64_t)(t >> 4) * a.NT + tj) * 1024 + slot * 16 + (t & 15)];
-            v = h * g.acc[0][i][j][e];
-            over |= !(fabsf(v) <= 65504.f);
+        for (int k = 0; k < 4; ++k) {
+          const int rl = 4 * (c & 3) + k;                 // row in the tile
+          const int n = tj * 64 + (int)((i4 >> (8 * k)) & 255u);
+          if (vv[k] > 0.f && n >= nlo && n <= nhi && live(a, rt * 16 + rl)) {
+            int pr;
+            if (use_map) {
+              pr = posmap[n - nlo];
+            } else {
+              int lo = p0, hi = pl;                       // n is in the union: find its position
+              while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (ul[mid] < n) lo = mid + 1; else hi = mid;
+              }
+              pr = lo - p0;
+            }
+            *(float*)(hbuf + hslot(pr, (i & 3) * 16 + rl)) = vv[k];
           }
         }
-        if (wr && t < a.T) a.adense[(int64_t)t * a.F + p] = (_Float16)v;
       }
-  }
+    }
+    __syncthreads();
+  };
+  // the four waves owning the pass's rows apply h to their accumulators
+  auto mul = [&]() {
+    const char* hbuf = ((wave >> 1) & 1) ? st1 : st0;
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j) {
+      const int pr = Tile::col_of(j);
+      const int p = p0 + pr;
+      const bool wr = p < ((nb + 63) & ~63);
+#pragma unroll
+      for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const float4 h4 = *(const float4*)(hbuf + hslot(pr, i * 32 + 8 * qq + 4 * hl));
+          const float hv[4] = {h4.x, h4.y, h4.z, h4.w};
+          const int t0 = m0 + Tile::row_of(i, 4 * qq);
+          // element offsets stay below 2^32 (the matrix holds fewer elements);
+          // elements that are not written go to the spare slot past the
+          // matrix, so the stores need no branches
+          const uint32_t o0 = (uint32_t)t0 * (uint32_t)a.F + (uint32_t)p;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float v = hv[k] != 0.f ? hv[k] * g.acc[0][i][j][4 * qq + k] : 0.f;
+            vbits = max(vbits, __float_as_uint(v) & 0x7fffffffu);
+            const uint32_t keep = 0u - (uint32_t)(wr && t0 + k < a.T);
+            const uint32_t o = ((o0 + (uint32_t)k * (uint32_t)a.F) & keep) | (a.spare & ~keep);
+            a.adense[o] = (_Float16)v;
+          }
+        }
+    }
+  };
+  prep(0);
+  if (wave < 4) mul();
+  __syncthreads();
+  prep(1);
+  if (wave >= 4) mul();
+  const bool over = vbits > 0x477fe000u;   // above 65504, the largest finite fp16
   if (__builtin_amdgcn_ballot_w64(over) != 0ull && lane == 0) atomicOr(a.flag, 1);
 }
 
@@ -328,7 +308,7 @@ using DownUnionCfg64 = GemmCfg<64, 64, 1, 1, OP_F16_K, OP_BF16_T16>;
 size_t union_ws_bytes(int T, int F) {
   const size_t nblk = (size_t)(T + UB - 1) / UB;
   const size_t nslab = (size_t)(T + 63) / 64;
-  return nblk * F * 4 + nblk * 4 + (size_t)T * F * 2 + nslab * (F / 64) * 8 + 256 * 4;
+  return nblk * F * 4 + nblk * 4 + (size_t)T * F * 2 + 256 + nslab * (F / 64) * 8 + 256 * 4;
 }
 
 hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int T, int d, int F,
@@ -339,11 +319,12 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
   char* w = (char*)ws;
   UnionArgs a{};
   a.x = x; a.WuT = WuT; a.Wd = Wd; a.T = T; a.d = d; a.F = F; a.NT = F / 64;
-  a.mask = h.mask; a.skip = skip; a.hval = (const float*)h.val; a.hwidth = h.width;
+  a.mask = h.mask; a.skip = skip; a.hval = (const float*)h.val; a.hidx = h.idx; a.hwidth = h.width;
   a.ulist = (int*)w;
   a.ucount = (int*)(w + (size_t)nblk * F * 4);
   a.adense = (_Float16*)(w + (((size_t)nblk * F * 4 + (size_t)nblk * 4 + 255) & ~(size_t)255));
-  a.flag = (int*)((char*)a.adense + (((size_t)T * F * 2 + 255) & ~(size_t)255));
+  a.spare = (uint32_t)((size_t)T * F);
+  a.flag = (int*)((char*)a.adense + (((size_t)T * F * 2 + 256 + 255) & ~(size_t)255));
   uint64_t* U = (uint64_t*)((char*)a.flag + 256);
   a.y = y; a.out_bf16 = out_dt == DT_BF16;
   if (flag_out) *flag_out = a.flag;
