@@ -66,23 +66,30 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_gateup_kernel(DenseArgs a) {
 
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTH) void dense_down_kernel(DenseArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
   const int nbm = (a.T + Cfg::BM - 1) / Cfg::BM, nbn = a.d / Cfg::BN;
   int bm, bn;
   tile_order(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, bm, bn);
   const int m0 = bm * Cfg::BM, n0 = bn * Cfg::BN;
-  GemmTile<Cfg> g;
+  typedef typename TileFor<Cfg>::type Tile;
+  Tile g;
   const Operand A{a.act, a.F, nullptr, a.T};
   const Operand B{a.Wd, a.d, nullptr, a.d};
-  g.run(A, &B, m0, n0, a.F, lds);
+  if constexpr (TileFor<Cfg>::dma) {
+    __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
+    __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
+    g.run(A, &B, m0, n0, a.F, st0, st1);
+  } else {
+    __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+    g.run(A, &B, m0, n0, a.F, lds);
+  }
 #pragma unroll
   for (int j = 0; j < Cfg::TN; ++j) {
-    const int col = n0 + GemmTile<Cfg>::col_of(j);
+    const int col = n0 + Tile::col_of(j);
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = m0 + GemmTile<Cfg>::row_of(i, e);
+        const int row = m0 + Tile::row_of(i, e);
         if (row < a.T) {
           const float v = g.acc[0][i][j][e];
           if (a.out_bf16) ((uint16_t*)a.y)[(int64_t)row * a.d + col] = (uint16_t)f32_to_bf16_bits(v);
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_down_kernel(DenseArgs a) {
 }
 
 using DenseGateUp = DmaCfg<256, 128, 4, 2, 2>;
-using DenseDownBig = GemmCfg<256, 256, 2, 4, OP_BF16_K, OP_BF16_T>;
+using DenseDownBig = DmaCfg<256, 256, 4, 2, 1, false, true>;
 using DenseDownSmall = GemmCfg<128, 64, 2, 1, OP_BF16_K, OP_BF16_T>;
 
 template <class Cfg, class K>

@@ -456,10 +456,19 @@ struct GemmTile {
 // a fragment read of one stage never overlaps the loads in flight into the
 // other, and it waits for those loads only where the loop says so (a vmcnt
 // wait before the barrier that hands the next stage over).
-template <int BM_, int BN_, int WM_, int WN_, int NB_ = 1, bool F16_ = false>
+// With Cfg::BT the B operand is [K][N] (N contiguous, K optionally gathered
+// through B.gather): its tile is stored as it lies in memory, 64 k-rows of
+// 2*BN bytes whose 16-byte pieces are XOR-swizzled by 2*(k & 3), and read
+// with the gfx950 transpose load (the four k-rows one 16-lane group touches
+// then sit in different bank groups).  K need not be a multiple of 64 there:
+// the gathered k index is clamped to K-1, so the rows read past K are real
+// rows, and the caller's A must hold zeros in those K columns.
+template <int BM_, int BN_, int WM_, int WN_, int NB_ = 1, bool F16_ = false, bool BT_ = false>
 struct DmaCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NB = NB_;
   static constexpr bool F16MMA = F16_;
+  static constexpr bool BT = BT_;                  // B given as [K][N] (see DmaTile)
+  static_assert(!BT || NB == 1, "a transposed B operand comes alone");
   static constexpr int NW = WM * WN, NTH = NW * WAVE;
   static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   static_assert(TM >= 1 && TN >= 1, "wave tile must hold whole 32x32 blocks");
@@ -480,9 +489,9 @@ struct DmaTile {
   static constexpr int TM = Cfg::TM, TN = Cfg::TN, NB = Cfg::NB, NW = Cfg::NW;
   f32x16 acc[NB][TM][TN];
 
-  // Multiply the block at (m0, n0) over K (a multiple of 64); st0 and st1 are
-  // the kernel's two stage arrays of Cfg::STAGE bytes each.  Both are free
-  // again when run() returns.
+  // Multiply the block at (m0, n0) over K (a multiple of 64 unless B is
+  // transposed); st0 and st1 are the kernel's two stage arrays of Cfg::STAGE
+  // bytes each.  Both are free again when run() returns.
   __device__ void run(const Operand& A, const Operand* B, int m0, int n0, int K, char* st0, char* st1) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -509,35 +518,106 @@ struct DmaTile {
       if (A.gather) gr = A.gather[gr];
       offa[q] = ((uint32_t)gr * (uint32_t)A.ld + (uint32_t)(((p ^ r ^ (r >> 3)) & 7) * 8)) * 2u;
     }
+    constexpr int BROWB = Cfg::BN * 2, KPI = 1024 / BROWB;   // transposed B: bytes per k-row, k-rows per load
+    const int* bgat = Cfg::BT ? B[0].gather : nullptr;
+    const int nk = (K + 63) / 64;
+    auto bt_krow = [&](int q) { return (q * NW + wave) * KPI + (16 * lane) / BROWB; };
+    // gathered k rows of the next tile to issue: one load carries KPI k-rows,
+    // so each wave needs KPI * LB indices per tile, all wave-uniform; they are
+    // read with scalar loads (constant address space) into SGPRs, which keeps
+    // them out of the vector memory counter the stage hand-over waits on
+    typedef __attribute__((address_space(4))) const int cint;
+    cint* cgat = (cint*)bgat;
+    uint32_t gsc[Cfg::LB][KPI];
+    auto bt_fetch = [&](int kt) {
+#pragma unroll
+      for (int q = 0; q < Cfg::LB; ++q)
+#pragma unroll
+        for (int j = 0; j < KPI; ++j) gsc[q][j] = (uint32_t)cgat[min(kt * 64 + (q * NW + wave) * KPI + j, K - 1)];
+    };
+    auto gidx = [&](int q) {
+      const int kl = (16 * lane) / BROWB;
+      uint32_t v = gsc[q][0];
+#pragma unroll
+      for (int j = 1; j < KPI; ++j) v = kl == j ? gsc[q][j] : v;
+      return v;
+    };
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int q = 0; q < Cfg::LB; ++q) {
-        const int r = (q * NW + wave) * 8 + rsub;
-        int gr = min(n0 + r, B[b].nrows - 1);
-        if (B[b].gather) gr = B[b].gather[gr];
-        offb[b][q] = ((uint32_t)gr * (uint32_t)B[b].ld + (uint32_t)(((p ^ r ^ (r >> 3)) & 7) * 8)) * 2u;
+        if constexpr (Cfg::BT) {
+          const int kr = bt_krow(q), pc = ((16 * lane) % BROWB) / 16;
+          const uint32_t col = (uint32_t)(n0 * 2 + ((pc ^ (2 * (kr & 3))) << 4));
+          offb[b][q] = bgat ? col : (uint32_t)kr * (uint32_t)B[0].ld * 2u + col;
+        } else {
+          const int r = (q * NW + wave) * 8 + rsub;
+          int gr = min(n0 + r, B[b].nrows - 1);
+          if (B[b].gather) gr = B[b].gather[gr];
+          offb[b][q] = ((uint32_t)gr * (uint32_t)B[b].ld + (uint32_t)(((p ^ r ^ (r >> 3)) & 7) * 8)) * 2u;
+        }
       }
-    const char* pa = (const char*)A.ptr;
-    const char* pb[NB];
+    if (Cfg::BT && bgat && nk > 0) bt_fetch(0);
+    // buffer resources (base, byte range) of the operands: the loads are
+    // buffer_load ... lds with a per-lane offset that stays fixed over the K
+    // loop and a wave-uniform per-tile offset, so no address arithmetic is
+    // repeated per tile (the range also bounds every access)
+    // (a gathered operand's rows are not bounded by nrows: its range is open)
+    auto rsrc = [](const Operand& op, int64_t rows) {
+      const int64_t bytes = op.gather ? 0xffffffffLL : rows * op.ld * 2;
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(op.ptr), (short)0,
+                                               (int)(uint32_t)(bytes < 0xffffffffLL ? bytes : 0xffffffffLL), 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t ra = rsrc(A, A.nrows);
+    __amdgpu_buffer_rsrc_t rb[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) pb[b] = (const char*)B[b].ptr;
+    for (int b = 0; b < NB; ++b) rb[b] = rsrc(B[b], Cfg::BT ? (int64_t)K : (int64_t)B[b].nrows);
+    uint32_t bvo[Cfg::LB];            // gathered B: this tile's lane offsets, kept live through compute()
 
     auto issue = [&](int kt, char* st) {
-      const char* ka = pa + (size_t)kt * 128;
 #pragma unroll
       for (int q = 0; q < Cfg::LA; ++q)
-        __builtin_amdgcn_global_load_lds((const void*)(ka + offa[q]), (lds_void*)(st + (q * NW + wave) * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (q * NW + wave) * 1024), 16, offa[q],
+                                                 (uint32_t)kt * 128u, 0, 0);
+      if constexpr (Cfg::BT) {
+        if (bgat) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const char* kb = pb[b] + (size_t)kt * 128;
+          for (int q = 0; q < Cfg::LB; ++q) {
+            bvo[q] = gidx(q) * (uint32_t)B[0].ld * 2u + offb[0][q];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[0], (lds_void*)(st + Cfg::A_BYTES + (q * NW + wave) * 1024),
+                                                     16, bvo[q], 0u, 0, 0);
+          }
+          if (kt + 1 < nk) bt_fetch(kt + 1);
+        } else {
 #pragma unroll
-        for (int q = 0; q < Cfg::LB; ++q)
-          __builtin_amdgcn_global_load_lds((const void*)(kb + offb[b][q]),
-                                           (lds_void*)(st + Cfg::A_BYTES + b * Cfg::B_BYTES + (q * NW + wave) * 1024),
-                                           16, 0, 0);
+          for (int q = 0; q < Cfg::LB; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[0], (lds_void*)(st + Cfg::A_BYTES + (q * NW + wave) * 1024),
+                                                     16, offb[0][q], (uint32_t)kt * 64u * (uint32_t)B[0].ld * 2u, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int q = 0; q < Cfg::LB; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[b],
+                                                     (lds_void*)(st + Cfg::A_BYTES + b * Cfg::B_BYTES + (q * NW + wave) * 1024),
+                                                     16, offb[b][q], (uint32_t)kt * 128u, 0, 0);
       }
     };
+    // transposed B: this lane's byte offset inside the tile for column block
+    // j (the k-tile and half offsets are added as constants).  It is passed
+    // through an empty asm so that the optimizer keeps each read's address a
+    // short chain from the LDS array (long chains lose the alias information
+    // that lets the reads run under the loads in flight into the other stage).
+    int btl[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int g = lane >> 4, i = lane & 15;
+      const int krow = 8 * (g >> 1) + (i >> 2);
+      const int col = wc + j * 32 + 16 * (g & 1) + 4 * (i & 3);
+      btl[j] = krow * BROWB + (((col >> 3) ^ (2 * (krow & 3))) << 4) + (col & 7) * 2;
+      if constexpr (Cfg::BT) asm volatile("" : "+v"(btl[j]));
+    }
     auto compute = [&](const char* st) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -548,8 +628,17 @@ struct DmaTile {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            fb[b][j] = *(const uint4*)(st + Cfg::A_BYTES + b * Cfg::B_BYTES + swz(wc + j * 32 + (lane & 31), ch));
+          for (int j = 0; j < TN; ++j) {
+            if constexpr (Cfg::BT) {
+              lds_trchar* q0 = (lds_trchar*)st + btl[j] + (Cfg::A_BYTES + 16 * kk * BROWB);
+              const trv4i16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_trv4i16*)q0);
+              const trv4i16 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_trv4i16*)(q0 + 4 * BROWB));
+              const uint2 u0 = __builtin_bit_cast(uint2, v0), u1 = __builtin_bit_cast(uint2, v1);
+              fb[b][j] = make_uint4(u0.x, u0.y, u1.x, u1.y);
+            } else {
+              fb[b][j] = *(const uint4*)(st + Cfg::A_BYTES + b * Cfg::B_BYTES + swz(wc + j * 32 + (lane & 31), ch));
+            }
+          }
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -572,11 +661,18 @@ struct DmaTile {
     };
 
     // tile kt: wait for it, start loading tile kt+1 into the other stage, compute
-    const int nk = K / 64;
     auto step = [&](int kt, const char* cur, char* nxt) {
       stage_barrier();
       if (kt + 1 < nk) issue(kt + 1, nxt);
       compute(cur);
+      if constexpr (Cfg::BT) {
+        // the loads just issued may still read their offset registers: keep
+        // them from being reused by the fragment reads above
+        if (bgat) {
+#pragma unroll
+          for (int q = 0; q < Cfg::LB; ++q) asm volatile("" ::"v"(bvo[q]));
+        }
+      }
     };
     if (nk > 0) issue(0, st0);
     int kt = 0;
@@ -600,9 +696,9 @@ struct DmaTile {
 
 // Mainloop type of a configuration.
 template <class Cfg> struct TileFor { typedef GemmTile<Cfg> type; static constexpr bool dma = false; };
-template <int BM, int BN, int WM, int WN, int NB, bool F16>
-struct TileFor<DmaCfg<BM, BN, WM, WN, NB, F16>> {
-  typedef DmaTile<DmaCfg<BM, BN, WM, WN, NB, F16>> type;
+template <int BM, int BN, int WM, int WN, int NB, bool F16, bool BT>
+struct TileFor<DmaCfg<BM, BN, WM, WN, NB, F16, BT>> {
+  typedef DmaTile<DmaCfg<BM, BN, WM, WN, NB, F16, BT>> type;
   static constexpr bool dma = true;
 };
 

@@ -98,10 +98,10 @@ hipError_t launch_down_bf16(const float* v0, const float* v1, const void* W, con
 // Forward up/down over each 256-token row block's union of active neurons
 // (bf16 inputs): union lists, up GEMM writing a as fp16 over the union, down
 // GEMM into y (rows with skip[t] != 0 untouched).  ws holds
-// union_ws_bytes(T, F).  *flag_out receives the device flag that is set when
+// union_ws_bytes(T, d, F).  *flag_out receives the device flag that is set when
 // an a value overflows fp16; the caller then runs the pattern kernels gated on
 // it (they recompute and overwrite y).
-size_t union_ws_bytes(int T, int F);
+size_t union_ws_bytes(int T, int d, int F);
 hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int T, int d, int F,
                             const TwellView& h, const uint8_t* skip, void* ws, void* y, int out_dt,
                             int** flag_out, hipStream_t s);

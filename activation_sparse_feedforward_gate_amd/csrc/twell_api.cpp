@@ -117,7 +117,7 @@ size_t fwd_layout(const twell_ffn_shape* sh, bool training, void* ws, FwdWs* out
     w.nD = (int*)c.take(4);
     w.act = (float*)c.take((size_t)sh->T * sh->F * 4);
   }
-  if (sh->in_dt == TWELL_BF16) w.uni = c.take(union_ws_bytes(sh->T, sh->F));
+  if (sh->in_dt == TWELL_BF16) w.uni = c.take(union_ws_bytes(sh->T, sh->d, sh->F));
   if (out) *out = w;
   return c.off;
 }

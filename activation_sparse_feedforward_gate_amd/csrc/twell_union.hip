@@ -27,16 +27,14 @@ namespace twell {
 
 namespace {
 
-#ifndef TWELL_UNION_ROWS
-#define TWELL_UNION_ROWS 256
-#endif
-constexpr int UB = TWELL_UNION_ROWS;   // tokens per row block
+constexpr int UB = 256;               // tokens per row block
 constexpr int RT = UB / 16;            // TwELL row tiles per row block
 
 struct UnionArgs {
   const void* x;
   const void* WuT;
   const void* Wd;
+  const _Float16* Wd16;   // fp16 copy of Wd for the down GEMM
   int T, d, F, NT;
   const uint64_t* mask;   // [T][NT]
   const uint8_t* skip;    // [T] or null
@@ -257,28 +255,54 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   if (__builtin_amdgcn_ballot_w64(over) != 0ull && lane == 0) atomicOr(a.flag, 1);
 }
 
-// Down-projection over the union: y rows of the block, one 256-column tile.
+// fp16 copy of Wd for the down GEMM (exact for every bf16 value inside the
+// fp16 range); a value beyond that range raises the flag, and the layer then
+// takes the fp32 path.
+__global__ __launch_bounds__(256) void wd_to_f16_kernel(const uint16_t* Wd, _Float16* W16, int64_t n8, int* flag) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  bool over = false;
+  if (i < n8) {
+    const uint4 w = ((const uint4*)Wd)[i];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float lo = bf16_lo(ws[k]), hi = bf16_hi(ws[k]);
+      over |= !(fabsf(lo) <= 65504.f) || !(fabsf(hi) <= 65504.f);
+      o[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+    }
+    ((uint4*)W16)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (__builtin_amdgcn_ballot_w64(over) != 0ull && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
+}
+
+// Down-projection over the union: y rows of the block, one column tile.  K
+// runs over the block's n_b positions; A = adense holds zeros in the
+// positions past n_b of the last K tile.
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTH) void down_union_kernel(UnionArgs a) {
   static_assert(Cfg::BM == UB, "one row block per M tile");
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
   if (*a.flag) return;                              // fp16 overflow: the fallback path writes y
   const int nct = a.d / Cfg::BN;
   const int b = blockIdx.x / nct, ct = blockIdx.x - b * nct;
   const int nb = a.ucount[b];
   const int m0 = b * UB, n0 = ct * Cfg::BN;
-  GemmTile<Cfg> g;
+  typedef DmaTile<Cfg> Tile;
+  Tile g;
   const Operand A{a.adense, a.F, nullptr, a.T};
-  const Operand B{a.Wd, a.d, a.ulist + (int64_t)b * a.F, a.F};
-  g.run(A, &B, m0, n0, nb, lds);
+  const Operand B{a.Wd16, a.d, a.ulist + (int64_t)b * a.F, a.F};
+  g.run(A, &B, m0, n0, nb, st0, st1);
 #pragma unroll
   for (int j = 0; j < Cfg::TN; ++j) {
-    const int col = n0 + GemmTile<Cfg>::col_of(j);
+    const int col = n0 + Tile::col_of(j);
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int t = m0 + GemmTile<Cfg>::row_of(i, e);
+        const int t = m0 + Tile::row_of(i, e);
         if (live(a, t)) {
           const float v = g.acc[0][i][j][e];
           if (a.out_bf16) ((uint16_t*)a.y)[(int64_t)t * a.d + col] = (uint16_t)f32_to_bf16_bits(v);
@@ -288,27 +312,15 @@ __global__ __launch_bounds__(Cfg::NTH) void down_union_kernel(UnionArgs a) {
   }
 }
 
-#if TWELL_UNION_ROWS == 256
 using UpUnionCfg = DmaCfg<256, 256, 4, 2>;
-using DownUnionCfg = GemmCfg<256, 256, 2, 4, OP_F16_K, OP_BF16_T16>;
-using DownUnionCfg128 = GemmCfg<256, 128, 2, 2, OP_F16_K, OP_BF16_T16>;
-using DownUnionCfg64 = GemmCfg<256, 64, 4, 1, OP_F16_K, OP_BF16_T16>;
-#elif TWELL_UNION_ROWS == 128
-using UpUnionCfg = DmaCfg<128, 256, 2, 4>;
-using DownUnionCfg = GemmCfg<128, 256, 2, 4, OP_F16_K, OP_BF16_T16>;
-using DownUnionCfg128 = GemmCfg<128, 128, 2, 2, OP_F16_K, OP_BF16_T16>;
-using DownUnionCfg64 = GemmCfg<128, 64, 2, 1, OP_F16_K, OP_BF16_T16>;
-#else
-using UpUnionCfg = DmaCfg<64, 256, 1, 4>;
-using DownUnionCfg = GemmCfg<64, 256, 1, 4, OP_F16_K, OP_BF16_T16>;
-using DownUnionCfg128 = GemmCfg<64, 128, 1, 2, OP_F16_K, OP_BF16_T16>;
-using DownUnionCfg64 = GemmCfg<64, 64, 1, 1, OP_F16_K, OP_BF16_T16>;
-#endif
+using DownUnionCfg = DmaCfg<256, 256, 4, 2, 1, true, true>;
+using DownUnionCfg128 = DmaCfg<256, 128, 4, 2, 1, true, true>;
+using DownUnionCfg64 = DmaCfg<256, 64, 4, 1, 1, true, true>;
 
-size_t union_ws_bytes(int T, int F) {
+size_t union_ws_bytes(int T, int d, int F) {
   const size_t nblk = (size_t)(T + UB - 1) / UB;
   const size_t nslab = (size_t)(T + 63) / 64;
-  return nblk * F * 4 + nblk * 4 + (size_t)T * F * 2 + 256 + nslab * (F / 64) * 8 + 256 * 4;
+  return nblk * F * 4 + nblk * 4 + (size_t)T * F * 2 + 256 + nslab * (F / 64) * 8 + (size_t)F * d * 2 + 256 * 5;
 }
 
 hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int T, int d, int F,
@@ -326,10 +338,16 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
   a.spare = (uint32_t)((size_t)T * F);
   a.flag = (int*)((char*)a.adense + (((size_t)T * F * 2 + 256 + 255) & ~(size_t)255));
   uint64_t* U = (uint64_t*)((char*)a.flag + 256);
+  a.Wd16 = (const _Float16*)((char*)U + (((size_t)((T + 63) / 64) * a.NT * 8 + 255) & ~(size_t)255));
   a.y = y; a.out_bf16 = out_dt == DT_BF16;
   if (flag_out) *flag_out = a.flag;
   hipLaunchKernelGGL(union_or_kernel, dim3((T + 63) / 64, (a.NT + 63) / 64), dim3(256), 0, s, a, U);
   hipLaunchKernelGGL(union_list_kernel, dim3(nblk), dim3(256), 0, s, a, (const uint64_t*)U);
+  {
+    const int64_t n8 = (int64_t)F * d / 8;
+    hipLaunchKernelGGL(wd_to_f16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, (const uint16_t*)Wd,
+                       (_Float16*)a.Wd16, n8, a.flag);
+  }
   const int npt = (F + UpUnionCfg::BN - 1) / UpUnionCfg::BN;
   const int nbx_max = (nblk + 7) / 8;
   hipLaunchKernelGGL((up_union_kernel<UpUnionCfg>), dim3(8 * nbx_max * npt), dim3(UpUnionCfg::NTH), 0, s, a);
