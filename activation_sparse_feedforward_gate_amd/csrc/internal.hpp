@@ -102,9 +102,12 @@ hipError_t launch_down_bf16(const float* v0, const float* v1, const void* W, con
 // an a value overflows fp16; the caller then runs the pattern kernels gated on
 // it (they recompute and overwrite y).
 size_t union_ws_bytes(int T, int d, int F);
+// ev_lists / ev_up (nullable) are recorded after the union lists and the fp16
+// copy of Wd, and after the up-projection.
 hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int T, int d, int F,
                             const TwellView& h, const uint8_t* skip, void* ws, void* y, int out_dt,
-                            int** flag_out, hipStream_t s);
+                            int** flag_out, hipStream_t s, hipEvent_t ev_lists = nullptr,
+                            hipEvent_t ev_up = nullptr);
 
 // Dense baseline: act = ReLU(x.WgT^T + bg) * (x.WuT^T) in bf16 (fused dual GEMM),
 // then y = act.Wd.  act is a [T][F] bf16 workspace.

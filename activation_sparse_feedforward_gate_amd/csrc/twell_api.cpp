@@ -231,11 +231,11 @@ twell_status twell_ffn_fwd_ex(const twell_ffn_shape* sh, const void* x, const vo
     h = view_of(saved_h);                    // h is kept for the backward pass
     aval = (float*)w.h.val;
   }
-  int ev = 0;
-  auto mark = [&]() {
-    if (ev < n_events) (void)hipEventRecord(stage_events[ev++], stream);
+  auto evt = [&](int i) -> hipEvent_t { return i < n_events ? stage_events[i] : nullptr; };
+  auto mark = [&](int i) {
+    if (i < n_events) (void)hipEventRecord(stage_events[i], stream);
   };
-  mark();                                                             // 0: start
+  mark(0);                                                            // start
   hipError_t e = launch_gate_twell(in_dt, x, WgT, bg, sh->T, sh->d, sh->F, h, stream);
   if (e != hipSuccess) return hip_status(e, "gate GEMM");
   const uint8_t* skip = nullptr;
@@ -244,31 +244,33 @@ twell_status twell_ffn_fwd_ex(const twell_ffn_shape* sh, const void* x, const vo
     if (e != hipSuccess) return hip_status(e, "row classification");
     skip = w.flag;
   }
-  mark();                                                             // 1: gate GEMM + pack done
+  mark(1);                                                            // gate GEMM + pack done
   if (in_dt == DT_BF16) {
     int* ovf = nullptr;
-    e = launch_union_fwd(x, WuT, Wd, sh->T, sh->d, sh->F, h, skip, w.uni, y, out_dt, &ovf, stream);
+    e = launch_union_fwd(x, WuT, Wd, sh->T, sh->d, sh->F, h, skip, w.uni, y, out_dt, &ovf, stream, evt(2), evt(3));
     if (e != hipSuccess) return hip_status(e, "union up/down GEMMs");
-    mark();                                                           // 2: up/down done
+    mark(4);                                                          // down-projection done
     // fp16 overflow fallback (does nothing unless the flag is set)
     e = launch_up_bf16(x, nullptr, WuT, nullptr, sh->T, sh->d, sh->F, h, aval, nullptr, nullptr, skip, stream, ovf);
     if (e == hipSuccess)
       e = launch_down_bf16(aval, nullptr, Wd, nullptr, sh->T, sh->d, sh->F, h, y, out_dt, skip, stream, ovf);
     if (e != hipSuccess) return hip_status(e, "overflow fallback");
   } else {
+    mark(2);
     e = launch_sddmm_up(in_dt, x, WuT, sh->T, sh->d, sh->F, h, aval, skip, stream);
     if (e != hipSuccess) return hip_status(e, "sparse up-projection");
+    mark(3);
     e = launch_spmm_down(in_dt, out_dt, aval, Wd, sh->T, sh->d, sh->F, h, y, skip, stream);
     if (e != hipSuccess) return hip_status(e, "sparse down-projection");
-    mark();
+    mark(4);
   }
-  mark();                                                             // 3: sparse phases done
+  mark(5);                                                            // sparse phases done
   if (training) {
     e = launch_dense_rows_fwd(in_dt, x, WgT, bg, WuT, Wd, sh->T, sh->d, sh->F, w.list, w.nD, w.act, out_dt, y,
                               stream);
     if (e != hipSuccess) return hip_status(e, "dense-row forward");
   }
-  mark();                                                             // 4: end
+  mark(6);                                                            // end
   return TWELL_OK;
 }
 

@@ -325,8 +325,12 @@ size_t union_ws_bytes(int T, int d, int F) {
 
 hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int T, int d, int F,
                             const TwellView& h, const uint8_t* skip, void* ws, void* y, int out_dt,
-                            int** flag_out, hipStream_t s) {
-  if (T == 0) return hipSuccess;
+                            int** flag_out, hipStream_t s, hipEvent_t ev_lists, hipEvent_t ev_up) {
+  if (T == 0) {
+    if (ev_lists) (void)hipEventRecord(ev_lists, s);
+    if (ev_up) (void)hipEventRecord(ev_up, s);
+    return hipSuccess;
+  }
   const int nblk = (T + UB - 1) / UB;
   char* w = (char*)ws;
   UnionArgs a{};
@@ -348,9 +352,11 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
     hipLaunchKernelGGL(wd_to_f16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, (const uint16_t*)Wd,
                        (_Float16*)a.Wd16, n8, a.flag);
   }
+  if (ev_lists) (void)hipEventRecord(ev_lists, s);
   const int npt = (F + UpUnionCfg::BN - 1) / UpUnionCfg::BN;
   const int nbx_max = (nblk + 7) / 8;
   hipLaunchKernelGGL((up_union_kernel<UpUnionCfg>), dim3(8 * nbx_max * npt), dim3(UpUnionCfg::NTH), 0, s, a);
+  if (ev_up) (void)hipEventRecord(ev_up, s);
   if (d % 256 == 0)
     hipLaunchKernelGGL((down_union_kernel<DownUnionCfg>), dim3(nblk * (d / 256)), dim3(DownUnionCfg::NTH), 0, s, a);
   else if (d % 128 == 0)

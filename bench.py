@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates the PMC byte counters)")
     return ap.parse_args()
 
 
@@ -73,12 +75,60 @@ def cpu_baseline(w, budget_s: float, training: bool) -> dict:
             "sample": f"first {done} of {w.T} token rows, float64 numpy {what}, {dt:.1f} s"}
 
 
+# kernels whose HBM traffic is recorded in profiles/hbm_traffic.json, with the
+# source files that define each (a recorded figure is dropped once they change)
+TRAFFIC_SOURCES = {
+    "gate_gemm_twell_pack": ["twell_gate.hip", "gemm_core.hpp", "common.hpp"],
+    "up_projection": ["twell_union.hip", "gemm_core.hpp", "common.hpp"],
+    "down_projection": ["twell_union.hip", "gemm_core.hpp", "common.hpp"],
+}
+
+
+def source_digest(files) -> str:
+    import hashlib
+    hsh = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "activation_sparse_feedforward_gate_amd", "csrc", f), "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()[:16]
+
+
+def load_traffic(config: str) -> dict:
+    """HBM bytes per launch from the recorded PMC runs (FETCH_SIZE + WRITE_SIZE,
+    scaled by the copy-kernel calibration), for kernels unchanged since then."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return {}
+    rec = json.load(open(path))
+    out = {}
+    for k, files in TRAFFIC_SOURCES.items():
+        r = rec.get("kernels", {}).get(config, {}).get(k)
+        if r and r.get("source_digest") == source_digest(files):
+            out[k] = r["bytes_per_launch"]
+    return out
+
+
+def copy_calibration(steps: int) -> int:
+    """A plain device copy of a known size, for scaling the PMC byte counters."""
+    import torch
+    n = 1 << 28                                         # 256 Mi floats = 1 GiB read + 1 GiB written
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": steps}))
+    return 0
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only (the library has no multi-GPU path); "
                                    "use --gpus 1", "n_gpus": args.gpus}))
         return 2
+    if args.copy_calibration:
+        return copy_calibration(max(1, args.steps))
     import numpy as np
     import torch
 
@@ -119,14 +169,14 @@ def main() -> int:
         if evs is None:
             tw.twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, h, tau, wsf, stream)
         else:
-            tw.twell_ffn_fwd_ex(shape, x, WgT, bg, WuT, Wd, y, h, tau, wsf, evs[:5], stream)
+            tw.twell_ffn_fwd_ex(shape, x, WgT, bg, WuT, Wd, y, h, tau, wsf, evs[:7], stream)
         if training:
             if evs is not None:
-                evs[5].record(stream)
+                evs[7].record(stream)
             tw.twell_ffn_bwd_hybrid(shape, x, WgT, bg, WuT, Wd, dY, h, tau, dX, dW[0], dW[1], dW[2], dbg, nD, wsb,
                                     stream)
             if evs is not None:
-                evs[6].record(stream)
+                evs[8].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -141,17 +191,18 @@ def main() -> int:
     ms_step = t0.elapsed_time(t1) / args.steps
 
     # per-stage durations from events recorded between the kernel launches
-    nst = 7 if training else 5
+    nst = 9 if training else 7
     recs = [[ev() for _ in range(nst)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
         step(recs[k])
     torch.cuda.synchronize()
     st = np.array([[r[i].elapsed_time(r[i + 1]) for i in range(nst - 1)] for r in recs]).mean(axis=0)
-    stages = {"gate_gemm_twell_pack": st[0], "up_down_union_gemms": st[1], "overflow_fallback_check": st[2]}
+    stages = {"gate_gemm_twell_pack": st[0], "union_lists_wd_fp16": st[1], "up_projection": st[2],
+              "down_projection": st[3], "overflow_fallback_check": st[4]}
     if training:
-        stages["dense_rows_fwd"] = st[3]
-        stages["hybrid_bwd"] = st[5]
+        stages["dense_rows_fwd"] = st[5]
+        stages["hybrid_bwd"] = st[7]
     nnz = int(h.cnt.to(torch.int64).sum().item())
 
     out = {
@@ -165,24 +216,47 @@ def main() -> int:
         "stages_ms": {k: float(v) for k, v in stages.items()},
     }
 
-    # roofline of each forward stage (algorithmic work per launch / its duration)
+    # roofline of each forward kernel: algorithmic work per launch / its duration
+    bf = cfg.dtype == "bf16"
+    mma_peak = PEAK["bf16_mfma_tflops"] if bf else PEAK["fp32_vector_tflops"]
     gate_flops = 2.0 * T * d * f                       # 2 d F per token
-    sparse_flops = 2.0 * 2.0 * nnz * d                 # up + down: 2 d per stored pair each
+    pair_flops = 2.0 * nnz * d                         # 2 d per stored (token, neuron) pair, each projection
     lines = {
-        "gate_gemm_twell_pack": {"bound": "mfma", "achieved": gate_flops / (st[0] * 1e-3) / 1e12,
-                                 "peak": PEAK["bf16_mfma_tflops"], "unit": "TFLOP/s", "work": gate_flops},
-        "up_down_union_gemms": {"bound": "mfma", "achieved": sparse_flops / (st[1] * 1e-3) / 1e12,
-                                "peak": PEAK["bf16_mfma_tflops"], "unit": "TFLOP/s", "work": sparse_flops},
+        "gate_gemm_twell_pack": {"bound": "mfma", "work": gate_flops, "ms": st[0]},
+        "up_projection": {"bound": "mfma", "work": pair_flops, "ms": st[2]},
+        "down_projection": {"bound": "mfma", "work": pair_flops, "ms": st[3]},
     }
-    for v in lines.values():
+    traffic = load_traffic(args.config)
+    for k, v in lines.items():
+        v["achieved"] = v["work"] / (v["ms"] * 1e-3) / 1e12
+        v["peak"] = mma_peak
+        v["unit"] = "TFLOP/s"
         v["frac"] = v["achieved"] / v["peak"]
-        v["traffic"] = None
-    dom = max(lines, key=lambda k: out["stages_ms"][k])
-    roof = dict(lines[dom])
+        v["traffic"] = traffic.get(k)
+    if bf and h.mask is not None:
+        # MFMA work the union GEMMs execute (all union positions of every
+        # 256-token row block, in whole tiles), beside the useful work above
+        m = h.mask.cpu().numpy().view(np.uint64)
+        nb = np.zeros(0, dtype=np.int64)
+        if T:
+            pad = (-T) % 256
+            mm = np.concatenate([m, np.zeros((pad, m.shape[1]), np.uint64)]) if pad else m
+            u = np.bitwise_or.reduce(mm.reshape(-1, 256, m.shape[1]), axis=1)
+            nb = np.unpackbits(u.view(np.uint8), axis=1).sum(axis=1).astype(np.int64)
+        up_exec = 2.0 * float((-(-nb // 256) * 256).sum()) * 256 * d
+        dn_exec = 2.0 * float((-(-nb // 64) * 64).sum()) * 256 * d
+        for k, w_exec in (("up_projection", up_exec), ("down_projection", dn_exec)):
+            lines[k]["executed_work"] = w_exec
+            lines[k]["executed_tflops"] = w_exec / (lines[k]["ms"] * 1e-3) / 1e12
+        out["config"]["mean_union_fraction"] = float(nb.mean() / f) if len(nb) else 0.0
+    dom = max(lines, key=lambda k: lines[k]["ms"])
+    roof = {k2: lines[dom][k2] for k2 in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roof["kernel"] = dom
-    roof.pop("work")
+    roof["launch_ms"] = float(lines[dom]["ms"])
+    roof["work_per_launch"] = lines[dom]["work"]
     out["roofline"] = roof
-    out["stage_roofline"] = lines
+    out["stage_roofline"] = {k: {k2: (float(v2) if isinstance(v2, (np.floating, float)) else v2)
+                                 for k2, v2 in v.items()} for k, v in lines.items()}
 
     if not args.no_dense and cfg.dtype == "bf16" and not training:
         dws = torch.empty(tw.twell_ffn_dense_fwd_workspace(shape), dtype=torch.uint8, device=dev)

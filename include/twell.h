@@ -182,9 +182,15 @@ twell_status twell_ffn_bwd_hybrid(const twell_ffn_shape *sh, const void *x, cons
 /*
  * twell_ffn_fwd_ex: twell_ffn_fwd that also records up to n_events caller-
  * created HIP events on the stream at its stage boundaries, for timing:
- *   [0] start  [1] gate GEMM + pack done  [2] up/down GEMMs done
- *   [3] sparse phases done (incl. the fp16-overflow fallback)  [4] end
- * Arguments otherwise as for twell_ffn_fwd.
+ *   [0] start
+ *   [1] gate GEMM + TwELL pack done (and the row classification, training)
+ *   [2] row-block neuron unions and the fp16 copy of Wd done (bf16 inputs;
+ *       for fp32 inputs recorded right after [1])
+ *   [3] up-projection done   [4] down-projection done
+ *   [5] sparse phases done (incl. the fp16-overflow fallback)
+ *   [6] end (after the dense-row forward, training)
+ * Arguments otherwise as for twell_ffn_fwd; events past n_events are not
+ * recorded.
  */
 twell_status twell_ffn_fwd_ex(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
                               const void *WuT, const void *Wd, void *y, twell_mat *saved_h,
