@@ -100,7 +100,7 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_down_kernel(DenseArgs a) {
 }
 
 using DenseGateUp = DmaCfg<256, 128, 4, 2, 2>;
-using DenseDownBig = DmaCfg<256, 256, 4, 2, 1, false, true>;
+using DenseDownBig = DmaCfg<256, 256, 2, 4, 1, false, true>;
 using DenseDownSmall = GemmCfg<128, 64, 2, 1, OP_BF16_K, OP_BF16_T>;
 
 template <class Cfg, class K>

@@ -463,11 +463,14 @@ struct GemmTile {
 // then sit in different bank groups).  K need not be a multiple of 64 there:
 // the gathered k index is clamped to K-1, so the rows read past K are real
 // rows, and the caller's A must hold zeros in those K columns.
-template <int BM_, int BN_, int WM_, int WN_, int NB_ = 1, bool F16_ = false, bool BT_ = false>
+// With Cfg::AT the A operand is [K][M] in the same way (never gathered, K a
+// multiple of 64), its fragments read with the same transpose load.
+template <int BM_, int BN_, int WM_, int WN_, int NB_ = 1, bool F16_ = false, bool BT_ = false, bool AT_ = false>
 struct DmaCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NB = NB_;
   static constexpr bool F16MMA = F16_;
   static constexpr bool BT = BT_;                  // B given as [K][N] (see DmaTile)
+  static constexpr bool AT = AT_;                  // A given as [K][M], never gathered
   static_assert(!BT || NB == 1, "a transposed B operand comes alone");
   static constexpr int NW = WM * WN, NTH = NW * WAVE;
   static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
@@ -492,31 +495,40 @@ struct DmaTile {
   // Multiply the block at (m0, n0) over K (a multiple of 64 unless B is
   // transposed); st0 and st1 are the kernel's two stage arrays of Cfg::STAGE
   // bytes each.  Both are free again when run() returns.
-  __device__ void run(const Operand& A, const Operand* B, int m0, int n0, int K, char* st0, char* st1) {
+  __device__ void run(const Operand& A, const Operand* B, int m0, int n0, int K, char* st0, char* st1,
+                      bool zero = true) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
     const int wc = (wave % Cfg::WN) * (Cfg::BN / Cfg::WN);
+    if (zero) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+          for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) acc[b][i][j][e] = 0.f;
+            for (int e = 0; e < 16; ++e) acc[b][i][j][e] = 0.f;
+    }
 
     // per-lane byte offsets (below 2^32: each operand is under 4 GB) of the
     // rows this lane fills; the K-tile base is wave-uniform, so each load is
     // one scalar base plus one 32-bit lane offset
     const int rsub = lane >> 3, p = lane & 7;
     uint32_t offa[Cfg::LA], offb[NB][Cfg::LB];
+    constexpr int AROWB = Cfg::BM * 2, KPIA = 1024 / AROWB;  // transposed A: bytes per k-row, k-rows per load
 #pragma unroll
     for (int q = 0; q < Cfg::LA; ++q) {
-      const int r = (q * NW + wave) * 8 + rsub;
-      int gr = min(m0 + r, A.nrows - 1);
-      if (A.gather) gr = A.gather[gr];
-      offa[q] = ((uint32_t)gr * (uint32_t)A.ld + (uint32_t)(((p ^ r ^ (r >> 3)) & 7) * 8)) * 2u;
+      if constexpr (Cfg::AT) {
+        const int kr = (q * NW + wave) * KPIA + (16 * lane) / AROWB, pc = ((16 * lane) % AROWB) / 16;
+        offa[q] = (uint32_t)kr * (uint32_t)A.ld * 2u + (uint32_t)(m0 * 2 + ((pc ^ (2 * (kr & 3))) << 4));
+      } else {
+        const int r = (q * NW + wave) * 8 + rsub;
+        int gr = min(m0 + r, A.nrows - 1);
+        if (A.gather) gr = A.gather[gr];
+        offa[q] = ((uint32_t)gr * (uint32_t)A.ld + (uint32_t)(((p ^ r ^ (r >> 3)) & 7) * 8)) * 2u;
+      }
     }
     constexpr int BROWB = Cfg::BN * 2, KPI = 1024 / BROWB;   // transposed B: bytes per k-row, k-rows per load
     const int* bgat = Cfg::BT ? B[0].gather : nullptr;
@@ -568,17 +580,17 @@ struct DmaTile {
       return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(op.ptr), (short)0,
                                                (int)(uint32_t)(bytes < 0xffffffffLL ? bytes : 0xffffffffLL), 0x00020000);
     };
-    const __amdgpu_buffer_rsrc_t ra = rsrc(A, A.nrows);
+    const __amdgpu_buffer_rsrc_t ra = rsrc(A, Cfg::AT ? (int64_t)K : (int64_t)A.nrows);
     __amdgpu_buffer_rsrc_t rb[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) rb[b] = rsrc(B[b], Cfg::BT ? (int64_t)K : (int64_t)B[b].nrows);
     uint32_t bvo[Cfg::LB];            // gathered B: this tile's lane offsets, kept live through compute()
 
     auto issue = [&](int kt, char* st) {
+      const uint32_t ka = Cfg::AT ? (uint32_t)kt * 64u * (uint32_t)A.ld * 2u : (uint32_t)kt * 128u;
 #pragma unroll
       for (int q = 0; q < Cfg::LA; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (q * NW + wave) * 1024), 16, offa[q],
-                                                 (uint32_t)kt * 128u, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (q * NW + wave) * 1024), 16, offa[q], ka, 0, 0);
       if constexpr (Cfg::BT) {
         if (bgat) {
 #pragma unroll
@@ -618,13 +630,32 @@ struct DmaTile {
       btl[j] = krow * BROWB + (((col >> 3) ^ (2 * (krow & 3))) << 4) + (col & 7) * 2;
       if constexpr (Cfg::BT) asm volatile("" : "+v"(btl[j]));
     }
+    int atl[TM];                      // the same for a transposed A, row block i
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int g = lane >> 4, ii = lane & 15;
+      const int krow = 8 * (g >> 1) + (ii >> 2);
+      const int row = wr + i * 32 + 16 * (g & 1) + 4 * (ii & 3);
+      atl[i] = krow * AROWB + (((row >> 3) ^ (2 * (krow & 3))) << 4) + (row & 7) * 2;
+      if constexpr (Cfg::AT) asm volatile("" : "+v"(atl[i]));
+    }
     auto compute = [&](const char* st) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int ch = 2 * kk + (lane >> 5);
         uint4 fa[TM], fb[NB][TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[i] = *(const uint4*)(st + swz(wr + i * 32 + (lane & 31), ch));
+        for (int i = 0; i < TM; ++i) {
+          if constexpr (Cfg::AT) {
+            lds_trchar* q0 = (lds_trchar*)st + atl[i] + 16 * kk * AROWB;
+            const trv4i16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_trv4i16*)q0);
+            const trv4i16 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_trv4i16*)(q0 + 4 * AROWB));
+            const uint2 u0 = __builtin_bit_cast(uint2, v0), u1 = __builtin_bit_cast(uint2, v1);
+            fa[i] = make_uint4(u0.x, u0.y, u1.x, u1.y);
+          } else {
+            fa[i] = *(const uint4*)(st + swz(wr + i * 32 + (lane & 31), ch));
+          }
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -648,6 +679,13 @@ struct DmaTile {
               if constexpr (Cfg::F16MMA) acc[b][i][j] = mfma32_f16(fa[i], fb[b][j], acc[b][i][j]);
               else acc[b][i][j] = mfma32(fa[i], fb[b][j], acc[b][i][j]);
             }
+        // scheduling hint: alternate one MFMA and one LDS read, so the reads
+        // of the next step issue under this step's MFMAs
+#pragma unroll
+        for (int q = 0; q < NB * TM * TN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
     };
     // Hand-over of a stage: this wave's loads are complete (vmcnt(0), the
@@ -696,9 +734,9 @@ struct DmaTile {
 
 // Mainloop type of a configuration.
 template <class Cfg> struct TileFor { typedef GemmTile<Cfg> type; static constexpr bool dma = false; };
-template <int BM, int BN, int WM, int WN, int NB, bool F16, bool BT>
-struct TileFor<DmaCfg<BM, BN, WM, WN, NB, F16, BT>> {
-  typedef DmaTile<DmaCfg<BM, BN, WM, WN, NB, F16, BT>> type;
+template <int BM, int BN, int WM, int WN, int NB, bool F16, bool BT, bool AT>
+struct TileFor<DmaCfg<BM, BN, WM, WN, NB, F16, BT, AT>> {
+  typedef DmaTile<DmaCfg<BM, BN, WM, WN, NB, F16, BT, AT>> type;
   static constexpr bool dma = true;
 };
 

@@ -163,7 +163,7 @@ __global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
   }
 }
 
-using GateBigBf16 = DmaCfg<256, 256, 4, 2>;
+using GateBigBf16 = DmaCfg<256, 256, 2, 4>;
 using GateSmallBf16 = GemmCfg<64, 64, 1, 1, OP_BF16_K, OP_BF16_K>;
 using GateBigF32 = GemmCfg<256, 256, 2, 4, OP_F32_K, OP_F32_K>;
 using GateSmallF32 = GemmCfg<64, 64, 1, 1, OP_F32_K, OP_F32_K>;

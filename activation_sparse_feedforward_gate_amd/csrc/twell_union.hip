@@ -155,7 +155,7 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   // the rows read their h values back with 16-byte loads.  A buffer holds 64
   // rows as [position][row] (256 bytes per position, 16-byte pieces XOR-
   // swizzled by position so 8 consecutive positions hit 8 bank groups).
-  static_assert(Cfg::BM == 256 && Cfg::BN == 256 && Cfg::WM == 4 && Cfg::WN == 2, "epilogue layout");
+  static_assert(Cfg::BM == 256 && Cfg::BN == 256 && Cfg::NW == 8 && Cfg::BM / Cfg::WM >= 64, "epilogue layout");
   static_assert(Cfg::STAGE >= 256 * 64 * 4, "h buffers");
   constexpr int POSCAP = 12288;
   __shared__ int16_t posmap[POSCAP];
@@ -217,8 +217,11 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
     __syncthreads();
   };
   // the four waves owning the pass's rows apply h to their accumulators
+  // rows of this wave inside its pass start at rbase (the pass is 128 rows:
+  // rows 0-63 in st0, 64-127 in st1)
+  const int wrow = (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
+  const int wpass = wrow >> 7, rbase = wrow & 127;
   auto mul = [&]() {
-    const char* hbuf = ((wave >> 1) & 1) ? st1 : st0;
 #pragma unroll
     for (int j = 0; j < Cfg::TN; ++j) {
       const int pr = Tile::col_of(j);
@@ -228,7 +231,9 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
       for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-          const float4 h4 = *(const float4*)(hbuf + hslot(pr, i * 32 + 8 * qq + 4 * hl));
+          const int r0 = rbase + i * 32;
+          const char* hbuf = (r0 >> 6) ? st1 : st0;
+          const float4 h4 = *(const float4*)(hbuf + hslot(pr, (r0 & 63) + 8 * qq + 4 * hl));
           const float hv[4] = {h4.x, h4.y, h4.z, h4.w};
           const int t0 = m0 + Tile::row_of(i, 4 * qq);
           // element offsets stay below 2^32 (the matrix holds fewer elements);
@@ -247,10 +252,10 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
     }
   };
   prep(0);
-  if (wave < 4) mul();
+  if (wpass == 0) mul();
   __syncthreads();
   prep(1);
-  if (wave >= 4) mul();
+  if (wpass == 1) mul();
   const bool over = vbits > 0x477fe000u;   // above 65504, the largest finite fp16
   if (__builtin_amdgcn_ballot_w64(over) != 0ull && lane == 0) atomicOr(a.flag, 1);
 }
@@ -312,8 +317,8 @@ __global__ __launch_bounds__(Cfg::NTH) void down_union_kernel(UnionArgs a) {
   }
 }
 
-using UpUnionCfg = DmaCfg<256, 256, 4, 2>;
-using DownUnionCfg = DmaCfg<256, 256, 4, 2, 1, true, true>;
+using UpUnionCfg = DmaCfg<256, 256, 2, 4>;
+using DownUnionCfg = DmaCfg<256, 256, 2, 4, 1, true, true>;
 using DownUnionCfg128 = DmaCfg<256, 128, 4, 2, 1, true, true>;
 using DownUnionCfg64 = DmaCfg<256, 64, 4, 1, 1, true, true>;
 
