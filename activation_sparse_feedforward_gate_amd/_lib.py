@@ -68,12 +68,16 @@ def lib() -> ctypes.CDLL:
         L.twell_ffn_dense_fwd_workspace.argtypes = [P(c_twell_ffn_shape)]
         L.twell_ffn_dense_fwd_workspace.restype = sz
         L.twell_ffn_dense_fwd.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.twell_ffn_dense_bwd_workspace.argtypes = [P(c_twell_ffn_shape)]
+        L.twell_ffn_dense_bwd_workspace.restype = sz
+        L.twell_ffn_dense_bwd.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          sz, vp]
         L.twell_status_string.argtypes = [ctypes.c_int]
         L.twell_status_string.restype = ctypes.c_char_p
         L.twell_last_error.argtypes = []
         L.twell_last_error.restype = ctypes.c_char_p
         for name in ("twell_pack", "twell_unpack", "twell_ffn_fwd", "twell_ffn_fwd_ex", "twell_ffn_bwd_hybrid",
-                     "twell_ffn_dense_fwd",
+                     "twell_ffn_dense_fwd", "twell_ffn_dense_bwd",
                      "twell_gate_pack",
                      "twell_sparse_up", "twell_sparse_down"):
             getattr(L, name).restype = ctypes.c_int
@@ -250,6 +254,17 @@ def twell_ffn_dense_fwd_workspace(shape: c_twell_ffn_shape) -> int:
 def twell_ffn_dense_fwd(shape, x, WgT, bg, WuT, Wd, y, ws, stream=None) -> None:
     _check(lib().twell_ffn_dense_fwd(ctypes.byref(shape), _ptr(x), _ptr(WgT), _ptr(bg), _ptr(WuT), _ptr(Wd),
                                      _ptr(y), _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+                                     _stream(stream)))
+
+
+def twell_ffn_dense_bwd_workspace(shape: c_twell_ffn_shape) -> int:
+    return int(lib().twell_ffn_dense_bwd_workspace(ctypes.byref(shape)))
+
+
+def twell_ffn_dense_bwd(shape, x, WgT, bg, WuT, Wd, dY, y, dX, dWgT, dWuT, dWd, dbg, ws, stream=None) -> None:
+    _check(lib().twell_ffn_dense_bwd(ctypes.byref(shape), _ptr(x), _ptr(WgT), _ptr(bg), _ptr(WuT), _ptr(Wd),
+                                     _ptr(dY), _ptr(y), _ptr(dX), _ptr(dWgT), _ptr(dWuT), _ptr(dWd), _ptr(dbg),
+                                     _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
                                      _stream(stream)))
 
 

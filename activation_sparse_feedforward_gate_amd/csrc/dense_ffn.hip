@@ -111,14 +111,20 @@ static hipError_t launch_grid(K kernel, int M, int N, const DenseArgs& a, hipStr
   return hipGetLastError();
 }
 
+hipError_t launch_dense_down(const void* act, const void* Wd, int T, int d, int F, int out_dt, void* y,
+                             hipStream_t s) {
+  DenseArgs a{nullptr, nullptr, nullptr, nullptr, Wd, T, d, F, (uint16_t*)act, y, out_dt == DT_BF16};
+  if (d % 256 == 0) return launch_grid<DenseDownBig>(dense_down_kernel<DenseDownBig>, T, d, a, s);
+  return launch_grid<DenseDownSmall>(dense_down_kernel<DenseDownSmall>, T, d, a, s);
+}
+
 hipError_t launch_dense_fwd(const void* x, const void* WgT, const void* bg, const void* WuT,
                             const void* Wd, int T, int d, int F, void* act, int out_dt, void* y,
                             hipStream_t s) {
   DenseArgs a{x, WgT, bg, WuT, Wd, T, d, F, (uint16_t*)act, y, out_dt == DT_BF16};
   hipError_t e = launch_grid<DenseGateUp>(dense_gateup_kernel<DenseGateUp>, T, F, a, s);
   if (e != hipSuccess) return e;
-  if (d % 256 == 0) return launch_grid<DenseDownBig>(dense_down_kernel<DenseDownBig>, T, d, a, s);
-  return launch_grid<DenseDownSmall>(dense_down_kernel<DenseDownSmall>, T, d, a, s);
+  return launch_dense_down(act, Wd, T, d, F, out_dt, y, s);
 }
 
 }  // namespace twell

@@ -114,5 +114,18 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
 hipError_t launch_dense_fwd(const void* x, const void* WgT, const void* bg, const void* WuT,
                             const void* Wd, int T, int d, int F, void* act, int out_dt, void* y,
                             hipStream_t s);
+// y = act.Wd for a bf16 act [T][F].
+hipError_t launch_dense_down(const void* act, const void* Wd, int T, int d, int F, int out_dt, void* y,
+                             hipStream_t s);
+
+// Dense training step (forward + backward, bf16 intermediates): writes y and
+// the fp32 gradients; dbg may be null.  Needs T % 64 == 0, d % 256 == 0,
+// F % 256 == 0; workspace dense_train_ws_bytes(T, d, F).
+size_t dense_train_ws_bytes(int T, int d, int F);
+// p[0..n) = 0 with a kernel (no memset node, so the call can be graph-captured).
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+hipError_t launch_dense_train(const void* x, const void* WgT, const void* bg, const void* WuT, const void* Wd,
+                              const void* dY, int T, int d, int F, void* ws, int out_dt, void* y, float* dX,
+                              float* dWgT, float* dWuT, float* dWd, float* dbg, hipStream_t s);
 
 }  // namespace twell

@@ -400,6 +400,44 @@ twell_status twell_ffn_dense_fwd(const twell_ffn_shape* sh, const void* x, const
                     "dense FFN");
 }
 
+size_t twell_ffn_dense_bwd_workspace(const twell_ffn_shape* sh) {
+  if (!sh || check_shape(sh) != TWELL_OK) return 0;
+  return dense_train_ws_bytes(sh->T, sh->d, sh->F);
+}
+
+twell_status twell_ffn_dense_bwd(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
+                                 const void* WuT, const void* Wd, const void* dY, void* y, float* dX, float* dWgT,
+                                 float* dWuT, float* dWd, float* dbg, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  twell_status st = check_shape(sh);
+  if (st) return st;
+  if (sh->in_dt != TWELL_BF16) return fail(TWELL_EUNSUPPORTED, "the dense training baseline is bf16 only");
+  if (!WgT || !WuT || !Wd || !dWgT || !dWuT || !dWd) return fail(TWELL_EINVAL, "NULL weight or gradient argument");
+  if (sh->T > 0 && (!x || !dY || !y || !dX)) return fail(TWELL_EINVAL, "NULL tensor argument");
+  for (const void* p : {x, WgT, bg, WuT, Wd, dY, (const void*)y, (const void*)dX, (const void*)dWgT,
+                        (const void*)dWuT, (const void*)dWd, (const void*)dbg})
+    if (!aligned16(p)) return fail(TWELL_EINVAL, "tensors must be 16-byte aligned");
+  if (sh->T % 64 != 0 || sh->d % 256 != 0 || sh->F % 256 != 0)
+    return fail(TWELL_EUNSUPPORTED, "the dense training baseline needs T %% 64 == 0, d %% 256 == 0, F %% 256 == 0");
+  if ((int64_t)sh->T * sh->F * 2 >= ((int64_t)1 << 32) || (int64_t)sh->T * sh->d * 2 >= ((int64_t)1 << 32))
+    return fail(TWELL_EUNSUPPORTED, "[T][F] and [T][d] bf16 matrices must be under 4 GB");
+  const size_t need = dense_train_ws_bytes(sh->T, sh->d, sh->F);
+  if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (sh->T == 0) {
+    // no tokens: the weight gradients are zero
+    const int64_t n = (int64_t)sh->F * sh->d;
+    hipError_t e = launch_zero_f32(dWgT, n, stream);
+    if (e == hipSuccess) e = launch_zero_f32(dWuT, n, stream);
+    if (e == hipSuccess) e = launch_zero_f32(dWd, n, stream);
+    if (e == hipSuccess) e = launch_zero_f32(dbg, sh->F, stream);
+    return hip_status(e, "dense training baseline");
+  }
+  return hip_status(launch_dense_train(x, WgT, bg, WuT, Wd, dY, sh->T, sh->d, sh->F, ws,
+                                       sh->out_dt == TWELL_BF16 ? DT_BF16 : DT_F32, y, dX, dWgT, dWuT, dWd, dbg,
+                                       stream),
+                    "dense training baseline");
+}
+
 const char* twell_status_string(twell_status st) {
   switch (st) {
     case TWELL_OK: return "ok";

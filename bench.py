@@ -258,6 +258,31 @@ def main() -> int:
     out["stage_roofline"] = {k: {k2: (float(v2) if isinstance(v2, (np.floating, float)) else v2)
                                  for k2, v2 in v.items()} for k, v in lines.items()}
 
+    if not args.no_dense and cfg.dtype == "bf16" and training:
+        # own dense training step (forward + backward, bf16 intermediates)
+        dws = torch.empty(tw.twell_ffn_dense_bwd_workspace(shape), dtype=torch.uint8, device=dev)
+        yd, dXd = torch.empty_like(y), torch.empty_like(dX)
+        dWd_ = [torch.empty_like(t) for t in dW]
+        dbgd = torch.empty_like(dbg)
+
+        def dense_step():
+            tw.twell_ffn_dense_bwd(shape, x, WgT, bg, WuT, Wd, dY, yd, dXd, dWd_[0], dWd_[1], dWd_[2], dbgd, dws,
+                                   stream)
+        for _ in range(args.warmup):
+            dense_step()
+        torch.cuda.synchronize()
+        a0, a1 = ev(), ev()
+        a0.record(stream)
+        for _ in range(args.steps):
+            dense_step()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        dms = a0.elapsed_time(a1) / args.steps
+        out["dense_baseline"] = {"tokens_per_s": T / (dms * 1e-3), "ms_per_step": dms,
+                                 "tflops": 18.0 * T * d * f / (dms * 1e-3) / 1e12,
+                                 "what": "dense forward + backward, bf16 intermediates"}
+        out["speedup_vs_dense"] = dms / ms_step
+
     if not args.no_dense and cfg.dtype == "bf16" and not training:
         dws = torch.empty(tw.twell_ffn_dense_fwd_workspace(shape), dtype=torch.uint8, device=dev)
         yd = torch.empty_like(y)

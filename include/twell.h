@@ -241,6 +241,33 @@ twell_status twell_ffn_dense_fwd(const twell_ffn_shape *sh, const void *x, const
                                  const void *WuT, const void *Wd, void *y, void *ws, size_t ws_bytes,
                                  hipStream_t stream);
 
+/* Workspace bytes for twell_ffn_dense_bwd. */
+size_t twell_ffn_dense_bwd_workspace(const twell_ffn_shape *sh);
+
+/*
+ * twell_ffn_dense_bwd: the library's own dense training step of the same
+ * layer, the denominator for the hybrid training path ([IN] "Слитые
+ * CUDA-ядра для инференса и гибрид для обучения" describes the hybrid; this
+ * is its plain dense counterpart).  Runs the dense forward, keeping
+ * h = ReLU(g), u and a = h*u as bf16 [T][F] in the workspace, writes y, then
+ * the backward: dA = dY.Wd^T, dG = dA*u*[g > 0], dU = dA*h (bf16),
+ * dX = dG.WgT + dU.WuT, dWgT = dG^T.x, dWuT = dU^T.x, dWd = a^T.dY,
+ * dbg = column sums of dG.  bf16 inputs only; fp32 accumulation; the bf16
+ * intermediates make it the fastest dense variant, not an fp32-accurate one.
+ *   x, dY     [T][d] bf16;  WgT, WuT, Wd [F][d] bf16;  bg [F] bf16 or NULL
+ *   y         [T][d] in sh->out_dt (overwritten)
+ *   dX        [T][d] fp32;  dWgT, dWuT, dWd [F][d] fp32;  dbg [F] fp32 or NULL
+ *             (all overwritten; with T == 0 the weight gradients are zeros)
+ *   ws        twell_ffn_dense_bwd_workspace(sh) bytes
+ * Errors: EINVAL for NULL or misaligned arguments, EUNSUPPORTED unless
+ * T % 64 == 0, d % 256 == 0 and F % 256 == 0 (or for fp32 inputs),
+ * EWORKSPACE, EHIP.
+ */
+twell_status twell_ffn_dense_bwd(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
+                                 const void *WuT, const void *Wd, const void *dY, void *y, float *dX, float *dWgT,
+                                 float *dWuT, float *dWd, float *dbg, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
 /* Static description of a status code. */
 const char *twell_status_string(twell_status st);
 /* Thread-local description of the last error returned on this thread. */

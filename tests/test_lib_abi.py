@@ -92,6 +92,26 @@ def test_dense_baseline_argument_errors():
     assert L.twell_ffn_dense_fwd(ctypes.byref(sh), 16, 16, None, 16, 16, 16, 16, 1, None) == tw.TWELL_EWORKSPACE
 
 
+def test_dense_train_baseline_argument_errors():
+    L = tw.lib()
+    args = [16] * 13 + [1 << 30, None]      # x WgT bg WuT Wd dY y dX dWgT dWuT dWd dbg ws, ws_bytes, stream
+    sh = tw.ffn_shape(64, 256, 512, tw.TWELL_F32, tw.TWELL_F32)
+    assert L.twell_ffn_dense_bwd(ctypes.byref(sh), *args) == tw.TWELL_EUNSUPPORTED        # fp32 inputs
+    sh = tw.ffn_shape(64, 128, 512, tw.TWELL_BF16, tw.TWELL_F32)
+    assert L.twell_ffn_dense_bwd(ctypes.byref(sh), *args) == tw.TWELL_EUNSUPPORTED        # d % 256
+    sh = tw.ffn_shape(100, 256, 512, tw.TWELL_BF16, tw.TWELL_F32)
+    assert L.twell_ffn_dense_bwd(ctypes.byref(sh), *args) == tw.TWELL_EUNSUPPORTED        # T % 64
+    sh = tw.ffn_shape(64, 256, 512, tw.TWELL_BF16, tw.TWELL_F32)
+    need = tw.twell_ffn_dense_bwd_workspace(sh)
+    assert need >= 5 * 64 * 512 * 2
+    small = [16] * 13 + [need - 1, None]
+    assert L.twell_ffn_dense_bwd(ctypes.byref(sh), *small) == tw.TWELL_EWORKSPACE
+    bad = [16] * 8 + [None] + [16] * 4 + [need, None]                 # dWgT missing
+    assert L.twell_ffn_dense_bwd(ctypes.byref(sh), *bad) == tw.TWELL_EINVAL
+    unaligned = [16] * 6 + [24] + [16] * 6 + [need, None]             # y misaligned
+    assert L.twell_ffn_dense_bwd(ctypes.byref(sh), *unaligned) == tw.TWELL_EINVAL
+
+
 def test_bwd_argument_errors():
     L = tw.lib()
     sh = tw.ffn_shape(64, 128, 512, tw.TWELL_BF16, tw.TWELL_F32)
