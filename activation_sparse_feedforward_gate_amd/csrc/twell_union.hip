@@ -142,6 +142,49 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   Tile g;
   const Operand A{a.x, a.d, nullptr, a.T};
   const Operand B{a.WuT, a.d, ul, nb};
+
+  // epilogue set-up, issued before the mainloop so that its global reads
+  // (the position map, and the first TwELL pieces of each pass) complete
+  // under the MFMAs: see the epilogue below
+  static_assert(Cfg::BM == 256 && Cfg::BN == 256 && Cfg::NW == 8 && Cfg::BM / Cfg::WM >= 64, "epilogue layout");
+  static_assert(Cfg::STAGE >= 256 * 64 * 4, "h buffers");
+  constexpr int POSCAP = 12288;
+  __shared__ int16_t posmap[POSCAP];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int pl = min(p0 + Cfg::BN, nb) - 1;
+  const int nlo = ul[p0], nhi = ul[pl];
+  const bool use_map = nhi - nlo < POSCAP;
+  if (use_map)
+    for (int p = p0 + tid; p <= pl; p += Cfg::NTH) posmap[ul[p] - nlo] = (int16_t)(p - p0);
+  const int tjf = nlo >> 6, S = (nhi >> 6) - tjf + 1;
+  constexpr int NG = Cfg::NTH / 16;        // 16-lane groups
+  const int grp = tid >> 4, gl = tid & 15;
+  // first piece (slots 0-3) of the group's first two blocks of each pass;
+  // the whole 4 KB block is allocated, so the reads need no width check
+  struct Piece { int w; float4 v; uint32_t i; };
+  Piece pre[2][2];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int q = grp + it * NG;
+      Piece& pc = pre[pass][it];
+      pc.w = 0;
+      pc.v = make_float4(0.f, 0.f, 0.f, 0.f);
+      pc.i = 0;
+      if (q < 8 * S) {
+        const int i = q / S, sj = q - i * S;
+        const int rt = (m0 >> 4) + pass * 8 + i;
+        if (rt * 16 < a.T) {
+          const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
+          pc.w = a.hwidth[blk];
+          pc.v = ((const float4*)(a.hval + blk * 1024))[gl];
+          pc.i = ((const uint32_t*)(a.hidx + blk * 1024))[gl];
+        }
+      }
+    }
+
   g.run(A, &B, m0, p0, a.d, st0, st1);
 
   // epilogue: a = h * u on stored pairs, else 0, stored as fp16 into
@@ -155,18 +198,6 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   // the rows read their h values back with 16-byte loads.  A buffer holds 64
   // rows as [position][row] (256 bytes per position, 16-byte pieces XOR-
   // swizzled by position so 8 consecutive positions hit 8 bank groups).
-  static_assert(Cfg::BM == 256 && Cfg::BN == 256 && Cfg::NW == 8 && Cfg::BM / Cfg::WM >= 64, "epilogue layout");
-  static_assert(Cfg::STAGE >= 256 * 64 * 4, "h buffers");
-  constexpr int POSCAP = 12288;
-  __shared__ int16_t posmap[POSCAP];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int pl = min(p0 + Cfg::BN, nb) - 1;
-  const int nlo = ul[p0], nhi = ul[pl];
-  const bool use_map = nhi - nlo < POSCAP;
-  if (use_map)
-    for (int p = p0 + tid; p <= pl; p += Cfg::NTH) posmap[ul[p] - nlo] = (int16_t)(p - p0);
-  const int tjf = nlo >> 6, S = (nhi >> 6) - tjf + 1;
   const int hl = lane >> 5;
   uint32_t vbits = 0;               // largest |a| bit pattern (NaN patterns sort above every number)
   auto hslot = [](int p, int r64) { return p * 256 + (((r64 >> 2) ^ (p & 7)) << 4) + ((r64 & 3) << 2); };
@@ -181,38 +212,51 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
     __syncthreads();
     // scatter: a 16-lane group per (row tile, column tile) block; lane piece c
     // holds slot c/4, rows 4*(c%4)..+3 of the block
-    for (int q = tid >> 4; q < 8 * S; q += Cfg::NTH / 16) {
+    auto scatter = [&](int i, int tj, int rt, int c, const float4& v4, uint32_t i4) {
+      char* hbuf = (i >> 2) ? st1 : st0;
+      const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int rl = 4 * (c & 3) + k;                   // row in the tile
+        const int n = tj * 64 + (int)((i4 >> (8 * k)) & 255u);
+        if (vv[k] > 0.f && n >= nlo && n <= nhi && live(a, rt * 16 + rl)) {
+          int pr;
+          if (use_map) {
+            pr = posmap[n - nlo];
+          } else {
+            int lo = p0, hi = pl;                         // n is in the union: find its position
+            while (lo < hi) {
+              const int mid = (lo + hi) >> 1;
+              if (ul[mid] < n) lo = mid + 1; else hi = mid;
+            }
+            pr = lo - p0;
+          }
+          *(float*)(hbuf + hslot(pr, (i & 3) * 16 + rl)) = vv[k];
+        }
+      }
+    };
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int q = grp + it * NG;
+      if (q >= 8 * S) break;
+      const int i = q / S, sj = q - i * S;
+      const int rt = (m0 >> 4) + pass * 8 + i;
+      const Piece& pc = pre[pass][it];
+      if (gl < pc.w * 4) scatter(i, tjf + sj, rt, gl, pc.v, pc.i);
+      const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
+      for (int c = gl + 16; c < pc.w * 4; c += 16)
+        scatter(i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
+                ((const uint32_t*)(a.hidx + blk * 1024))[c]);
+    }
+    for (int q = grp + 2 * NG; q < 8 * S; q += NG) {
       const int i = q / S, sj = q - i * S;
       const int rt = (m0 >> 4) + pass * 8 + i;
       if (rt * 16 >= a.T) continue;
-      const int tj = tjf + sj;
-      const int64_t blk = (int64_t)rt * a.NT + tj;
+      const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
       const int w = a.hwidth[blk];
-      char* hbuf = (i >> 2) ? st1 : st0;
-      for (int c = tid & 15; c < w * 4; c += 16) {
-        const float4 v4 = ((const float4*)(a.hval + blk * 1024))[c];
-        const uint32_t i4 = ((const uint32_t*)(a.hidx + blk * 1024))[c];
-        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int rl = 4 * (c & 3) + k;                 // row in the tile
-          const int n = tj * 64 + (int)((i4 >> (8 * k)) & 255u);
-          if (vv[k] > 0.f && n >= nlo && n <= nhi && live(a, rt * 16 + rl)) {
-            int pr;
-            if (use_map) {
-              pr = posmap[n - nlo];
-            } else {
-              int lo = p0, hi = pl;                       // n is in the union: find its position
-              while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (ul[mid] < n) lo = mid + 1; else hi = mid;
-              }
-              pr = lo - p0;
-            }
-            *(float*)(hbuf + hslot(pr, (i & 3) * 16 + rl)) = vv[k];
-          }
-        }
-      }
+      for (int c = gl; c < w * 4; c += 16)
+        scatter(i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
+                ((const uint32_t*)(a.hidx + blk * 1024))[c]);
     }
     __syncthreads();
   };
