@@ -102,6 +102,22 @@ hipError_t launch_down_bf16(const float* v0, const float* v1, const void* W, con
 // an a value overflows fp16; the caller then runs the pattern kernels gated on
 // it (they recompute and overwrite y).
 size_t union_ws_bytes(int T, int d, int F);
+// The union lists alone (for the few-token path), in the same workspace:
+// pointers to the list and count of row block 0, and the two list kernels.
+void union_lists_only(int T, int F, const TwellView& h, void* ws, int** ulist, int** ucount);
+hipError_t launch_union_lists(int T, int F, const TwellView& h, void* ws, hipStream_t s);
+
+// Forward for few tokens (T <= DECODE_T_MAX, bf16, inference): split-K GEMMs
+// over one-wave workgroups with fixed-order partial sums.  h receives the
+// TwELL of ReLU(g); uni_ws is the union workspace (union_ws_bytes), ws
+// decode_ws_bytes(T, d, F) bytes.  Events (nullable) after the gate + pack,
+// after the union lists, after the up-projection.
+constexpr int DECODE_T_MAX = 256;
+size_t decode_ws_bytes(int T, int d, int F);
+hipError_t launch_decode_fwd(const void* x, const void* WgT, const void* bg, const void* WuT, const void* Wd, int T,
+                             int d, int F, const TwellView& h, void* ws, void* uni_ws, void* y, int out_dt,
+                             hipStream_t s, hipEvent_t ev_gate, hipEvent_t ev_lists, hipEvent_t ev_up);
+
 // ev_lists / ev_up (nullable) are recorded after the union lists and the fp16
 // copy of Wd, and after the up-projection.
 hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int T, int d, int F,

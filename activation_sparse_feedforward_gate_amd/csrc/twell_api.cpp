@@ -97,7 +97,12 @@ struct FwdWs {
   int* nD;
   float* act;
   void* uni;         // union-GEMM workspace (bf16 inputs)
+  void* dec;         // few-token path workspace (bf16 inference, T <= DECODE_T_MAX)
 };
+
+bool few_token_path(const twell_ffn_shape* sh, bool training) {
+  return sh->in_dt == TWELL_BF16 && !training && sh->T > 0 && sh->T <= DECODE_T_MAX;
+}
 
 size_t fwd_layout(const twell_ffn_shape* sh, bool training, void* ws, FwdWs* out) {
   size_t parts[5];
@@ -118,6 +123,9 @@ size_t fwd_layout(const twell_ffn_shape* sh, bool training, void* ws, FwdWs* out
     w.act = (float*)c.take((size_t)sh->T * sh->F * 4);
   }
   if (sh->in_dt == TWELL_BF16) w.uni = c.take(union_ws_bytes(sh->T, sh->d, sh->F));
+  // reserved whatever the mode, so that a workspace sized for training also
+  // serves an inference call of the same shape
+  if (few_token_path(sh, false)) w.dec = c.take(decode_ws_bytes(sh->T, sh->d, sh->F));
   if (out) *out = w;
   return c.off;
 }
@@ -236,6 +244,15 @@ twell_status twell_ffn_fwd_ex(const twell_ffn_shape* sh, const void* x, const vo
     if (i < n_events) (void)hipEventRecord(stage_events[i], stream);
   };
   mark(0);                                                            // start
+  if (few_token_path(sh, training)) {
+    hipError_t e = launch_decode_fwd(x, WgT, bg, WuT, Wd, sh->T, sh->d, sh->F, h, w.dec, w.uni, y, out_dt, stream,
+                                     evt(1), evt(2), evt(3));
+    if (e != hipSuccess) return hip_status(e, "few-token forward");
+    mark(4);
+    mark(5);
+    mark(6);
+    return TWELL_OK;
+  }
   hipError_t e = launch_gate_twell(in_dt, x, WgT, bg, sh->T, sh->d, sh->F, h, stream);
   if (e != hipSuccess) return hip_status(e, "gate GEMM");
   const uint8_t* skip = nullptr;

@@ -372,14 +372,11 @@ size_t union_ws_bytes(int T, int d, int F) {
   return nblk * F * 4 + nblk * 4 + (size_t)T * F * 2 + 256 + nslab * (F / 64) * 8 + (size_t)F * d * 2 + 256 * 5;
 }
 
-hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int T, int d, int F,
-                            const TwellView& h, const uint8_t* skip, void* ws, void* y, int out_dt,
-                            int** flag_out, hipStream_t s, hipEvent_t ev_lists, hipEvent_t ev_up) {
-  if (T == 0) {
-    if (ev_lists) (void)hipEventRecord(ev_lists, s);
-    if (ev_up) (void)hipEventRecord(ev_up, s);
-    return hipSuccess;
-  }
+namespace {
+
+// Pointers into the union workspace (layout of union_ws_bytes).
+UnionArgs union_setup(const void* x, const void* WuT, const void* Wd, int T, int d, int F, const TwellView& h,
+                      const uint8_t* skip, void* ws, void* y, int out_dt, uint64_t** U) {
   const int nblk = (T + UB - 1) / UB;
   char* w = (char*)ws;
   UnionArgs a{};
@@ -390,12 +387,48 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
   a.adense = (_Float16*)(w + (((size_t)nblk * F * 4 + (size_t)nblk * 4 + 255) & ~(size_t)255));
   a.spare = (uint32_t)((size_t)T * F);
   a.flag = (int*)((char*)a.adense + (((size_t)T * F * 2 + 256 + 255) & ~(size_t)255));
-  uint64_t* U = (uint64_t*)((char*)a.flag + 256);
-  a.Wd16 = (const _Float16*)((char*)U + (((size_t)((T + 63) / 64) * a.NT * 8 + 255) & ~(size_t)255));
+  *U = (uint64_t*)((char*)a.flag + 256);
+  a.Wd16 = (const _Float16*)((char*)*U + (((size_t)((T + 63) / 64) * a.NT * 8 + 255) & ~(size_t)255));
   a.y = y; a.out_bf16 = out_dt == DT_BF16;
+  return a;
+}
+
+void union_lists_launch(const UnionArgs& a, const uint64_t* U, hipStream_t s) {
+  const int nblk = (a.T + UB - 1) / UB;
+  hipLaunchKernelGGL(union_or_kernel, dim3((a.T + 63) / 64, (a.NT + 63) / 64), dim3(256), 0, s, a, (uint64_t*)U);
+  hipLaunchKernelGGL(union_list_kernel, dim3(nblk), dim3(256), 0, s, a, U);
+}
+
+}  // namespace
+
+void union_lists_only(int T, int F, const TwellView& h, void* ws, int** ulist, int** ucount) {
+  uint64_t* U;
+  const UnionArgs a = union_setup(nullptr, nullptr, nullptr, T, 0, F, h, nullptr, ws, nullptr, DT_F32, &U);
+  *ulist = a.ulist;
+  *ucount = a.ucount;
+}
+
+hipError_t launch_union_lists(int T, int F, const TwellView& h, void* ws, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  uint64_t* U;
+  const UnionArgs a = union_setup(nullptr, nullptr, nullptr, T, 0, F, h, nullptr, ws, nullptr, DT_F32, &U);
+  union_lists_launch(a, U, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int T, int d, int F,
+                            const TwellView& h, const uint8_t* skip, void* ws, void* y, int out_dt,
+                            int** flag_out, hipStream_t s, hipEvent_t ev_lists, hipEvent_t ev_up) {
+  if (T == 0) {
+    if (ev_lists) (void)hipEventRecord(ev_lists, s);
+    if (ev_up) (void)hipEventRecord(ev_up, s);
+    return hipSuccess;
+  }
+  const int nblk = (T + UB - 1) / UB;
+  uint64_t* U;
+  const UnionArgs a = union_setup(x, WuT, Wd, T, d, F, h, skip, ws, y, out_dt, &U);
   if (flag_out) *flag_out = a.flag;
-  hipLaunchKernelGGL(union_or_kernel, dim3((T + 63) / 64, (a.NT + 63) / 64), dim3(256), 0, s, a, U);
-  hipLaunchKernelGGL(union_list_kernel, dim3(nblk), dim3(256), 0, s, a, (const uint64_t*)U);
+  union_lists_launch(a, U, s);
   {
     const int64_t n8 = (int64_t)F * d / 8;
     hipLaunchKernelGGL(wd_to_f16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, (const uint16_t*)Wd,

@@ -222,6 +222,18 @@ def test_fwd_decode_small(torch, tw):
     check_fwd(w, y, m)
 
 
+@pytest.mark.parametrize("T", [129, 256])
+def test_fwd_few_token_path(torch, tw, T):
+    """Batches of at most 256 bf16 tokens take the split-K path; its partial
+    sums are reduced in a fixed order, so repeated runs give the same bits."""
+    w = make_workload("2b", T=T, d=384, f=1536)
+    log(f"[fwd] few-token path T={T}")
+    y, m = run_fwd(torch, tw, w)
+    check_fwd(w, y, m)
+    y2, _ = run_fwd(torch, tw, w)
+    np.testing.assert_array_equal(y2, y)
+
+
 @pytest.mark.parametrize("T", [1, 17, 31, 16])
 def test_fwd_ragged_tiny(torch, tw, T):
     w = make_workload("0.5b", T=T, d=128, f=256)
