@@ -82,6 +82,9 @@ TRAFFIC_SOURCES = {
     "up_projection": ["twell_union.hip", "gemm_core.hpp", "common.hpp"],
     "down_projection": ["twell_union.hip", "gemm_core.hpp", "common.hpp"],
 }
+# the few-token (decode) path runs its own kernels
+TRAFFIC_SOURCES_DECODE = {k: ["twell_decode.hip", "twell_union.hip", "gemm_core.hpp", "common.hpp"]
+                          for k in TRAFFIC_SOURCES}
 
 
 def source_digest(files) -> str:
@@ -101,7 +104,8 @@ def load_traffic(config: str) -> dict:
         return {}
     rec = json.load(open(path))
     out = {}
-    for k, files in TRAFFIC_SOURCES.items():
+    sources = TRAFFIC_SOURCES_DECODE if config.endswith("_decode") else TRAFFIC_SOURCES
+    for k, files in sources.items():
         r = rec.get("kernels", {}).get(config, {}).get(k)
         if r and r.get("source_digest") == source_digest(files):
             out[k] = r["bytes_per_launch"]
@@ -226,14 +230,31 @@ def main() -> int:
         "up_projection": {"bound": "mfma", "work": pair_flops, "ms": st[2]},
         "down_projection": {"bound": "mfma", "work": pair_flops, "ms": st[3]},
     }
-    traffic = load_traffic(args.config)
+    few_tokens = bf and not training and 0 < T <= 256
+    if few_tokens:
+        # a few tokens make every phase a pass over weights: HBM-bound, with
+        # algorithmic bytes Wg whole (+x), the union's Wu rows (+x), the
+        # union's Wd rows (+y written)
+        m = h.mask.cpu().numpy().view(np.uint64)
+        n_union = int(np.unpackbits(np.bitwise_or.reduce(m, axis=0).view(np.uint8)).sum())
+        esz_y = 4
+        lines["gate_gemm_twell_pack"].update(bound="hbm", work=2.0 * f * d + 2.0 * T * d)
+        lines["up_projection"].update(bound="hbm", work=2.0 * n_union * d + 2.0 * T * d)
+        lines["down_projection"].update(bound="hbm", work=2.0 * n_union * d + esz_y * T * d)
+        out["config"]["union_neurons"] = n_union
+    traffic = load_traffic(args.config + ("_decode" if args.decode else ""))
     for k, v in lines.items():
-        v["achieved"] = v["work"] / (v["ms"] * 1e-3) / 1e12
-        v["peak"] = mma_peak
-        v["unit"] = "TFLOP/s"
+        if v["bound"] == "hbm":
+            v["achieved"] = v["work"] / (v["ms"] * 1e-3) / 1e9
+            v["peak"] = PEAK["hbm_gbs"]
+            v["unit"] = "GB/s"
+        else:
+            v["achieved"] = v["work"] / (v["ms"] * 1e-3) / 1e12
+            v["peak"] = mma_peak
+            v["unit"] = "TFLOP/s"
         v["frac"] = v["achieved"] / v["peak"]
         v["traffic"] = traffic.get(k)
-    if bf and h.mask is not None:
+    if bf and h.mask is not None and not few_tokens:
         # MFMA work the union GEMMs execute (all union positions of every
         # 256-token row block, in whole tiles), beside the useful work above
         m = h.mask.cpu().numpy().view(np.uint64)
