@@ -104,8 +104,10 @@ hipError_t launch_down_bf16(const float* v0, const float* v1, const void* W, con
 size_t union_ws_bytes(int T, int d, int F);
 // The union lists alone (for the few-token path), in the same workspace:
 // pointers to the list and count of row block 0, and the two list kernels.
-void union_lists_only(int T, int F, const TwellView& h, void* ws, int** ulist, int** ucount);
-hipError_t launch_union_lists(int T, int F, const TwellView& h, void* ws, hipStream_t s);
+// slabs: the 64-row slab unions u64 [ceil(T/64)][F/64] the list kernel reads;
+// with slabs_ready the caller has filled them and only the list kernel runs.
+void union_lists_only(int T, int F, const TwellView& h, void* ws, int** ulist, int** ucount, uint64_t** slabs);
+hipError_t launch_union_lists(int T, int F, const TwellView& h, void* ws, hipStream_t s, bool slabs_ready = false);
 
 // Forward for few tokens (T <= DECODE_T_MAX, bf16, inference): split-K GEMMs
 // over one-wave workgroups with fixed-order partial sums.  h receives the

@@ -10,7 +10,8 @@
 // reduce the partials:
 //   1 gate partials   Pg[s] = x . WgT[:, Ks]^T
 //   2 pack            g = sum_s Pg[s] + b, TwELL pack of ReLU(g) (fp32 values)
-//   3 union list      (the prefill kernels, one row block)
+//   3 union list      (the prefill list kernel, one row block; the pack has
+//                     already OR-ed each 64-row slab's masks)
 //   4 up partials     Pu[s] = x . WuT[ulist][:, Ks]^T
 //   5 a               a = h * sum_s Pu[s] at the stored pairs, else 0, split
 //                     into bf16 hi + lo (exact to about 2^-17 relative)
@@ -37,6 +38,7 @@ struct DecArgs {
   int T, d, F, NT;
   const int* ulist;     // the row block's union list (block 0)
   const int* ucount;
+  uint64_t* slabs;      // 64-row slab unions [ceil(T/64)][NT], filled by the pack
   float* pg;            // [KS_GATE][T][F]
   float* pu;            // [KS_UP][T][F]
   uint16_t* ahi;        // [T][F]
@@ -84,6 +86,7 @@ template <bool UP>
 __device__ __forceinline__ void dec_splitk(const DecArgs& a, char* st0, char* st1) {
   constexpr int KS = UP ? KS_UP : KS_GATE;
   const int s = blockIdx.y, n0 = blockIdx.x * 64, m0 = blockIdx.z * 64;
+  if (!UP && s == 0 && threadIdx.x == 0) a.slabs[(int64_t)blockIdx.z * a.NT + blockIdx.x] = 0;   // cleared for the pack
   const int ncols = UP ? *a.ucount : a.F;
   if (n0 >= ncols) return;
   int k0, kn;
@@ -143,7 +146,13 @@ __global__ __launch_bounds__(256) void dec_pack_kernel(DecArgs a) {
     M[r] = ballot(t < a.T && g > 0.f);
     w = max(w, popc64(M[r]));
   }
-  if (lane == 0) a.width[tile] = (uint8_t)w;
+  if (lane == 0) {
+    a.width[tile] = (uint8_t)w;
+    uint64_t u = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) u |= M[r];
+    if (u) atomicOr((unsigned long long*)&a.slabs[(int64_t)(i >> 2) * a.NT + j], (unsigned long long)u);
+  }
   const int64_t tbase = tile * (64 * 16);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -260,14 +269,15 @@ hipError_t launch_decode_fwd(const void* x, const void* WgT, const void* bg, con
   a.cnt = h.cnt; a.width = h.width; a.hval = (float*)h.val; a.hidx = h.idx; a.hmask = h.mask;
   int* ulist = nullptr;
   int* ucount = nullptr;
-  union_lists_only(T, F, h, uni_ws, &ulist, &ucount);
-  a.ulist = ulist; a.ucount = ucount;
+  uint64_t* slabs = nullptr;
+  union_lists_only(T, F, h, uni_ws, &ulist, &ucount, &slabs);
+  a.ulist = ulist; a.ucount = ucount; a.slabs = slabs;
   const int mt = (T + 63) / 64;
   hipLaunchKernelGGL(dec_gate_kernel, dim3(F / 64, KS_GATE, mt), dim3(SplitCfg::NTH), 0, s, a);
   const int NR = (T + 15) / 16;
   hipLaunchKernelGGL(dec_pack_kernel, dim3((unsigned)(((int64_t)NR * a.NT + 3) / 4)), dim3(256), 0, s, a);
   if (ev_gate) (void)hipEventRecord(ev_gate, s);
-  hipError_t e = launch_union_lists(T, F, h, uni_ws, s);
+  hipError_t e = launch_union_lists(T, F, h, uni_ws, s, true);
   if (e != hipSuccess) return e;
   if (ev_lists) (void)hipEventRecord(ev_lists, s);
   hipLaunchKernelGGL(dec_up_kernel, dim3(F / 64, KS_UP, mt), dim3(SplitCfg::NTH), 0, s, a);

@@ -401,18 +401,24 @@ void union_lists_launch(const UnionArgs& a, const uint64_t* U, hipStream_t s) {
 
 }  // namespace
 
-void union_lists_only(int T, int F, const TwellView& h, void* ws, int** ulist, int** ucount) {
+void union_lists_only(int T, int F, const TwellView& h, void* ws, int** ulist, int** ucount, uint64_t** slabs) {
   uint64_t* U;
   const UnionArgs a = union_setup(nullptr, nullptr, nullptr, T, 0, F, h, nullptr, ws, nullptr, DT_F32, &U);
   *ulist = a.ulist;
   *ucount = a.ucount;
+  *slabs = U;
 }
 
-hipError_t launch_union_lists(int T, int F, const TwellView& h, void* ws, hipStream_t s) {
+hipError_t launch_union_lists(int T, int F, const TwellView& h, void* ws, hipStream_t s, bool slabs_ready) {
   if (T == 0) return hipSuccess;
   uint64_t* U;
   const UnionArgs a = union_setup(nullptr, nullptr, nullptr, T, 0, F, h, nullptr, ws, nullptr, DT_F32, &U);
-  union_lists_launch(a, U, s);
+  if (slabs_ready) {
+    const int nblk = (T + UB - 1) / UB;
+    hipLaunchKernelGGL(union_list_kernel, dim3(nblk), dim3(256), 0, s, a, (const uint64_t*)U);
+  } else {
+    union_lists_launch(a, U, s);
+  }
   return hipGetLastError();
 }
 
