@@ -458,9 +458,12 @@ struct GemmTile {
 // wait before the barrier that hands the next stage over).
 // With Cfg::BT the B operand is [K][N] (N contiguous, K optionally gathered
 // through B.gather): its tile is stored as it lies in memory, 64 k-rows of
-// 2*BN bytes whose 16-byte pieces are XOR-swizzled by 2*(k & 3), and read
-// with the gfx950 transpose load (the four k-rows one 16-lane group touches
-// then sit in different bank groups).  K need not be a multiple of 64 there:
+// 2*BN bytes whose 16-byte pieces are XOR-swizzled by tr_swz(k), and read
+// with the gfx950 transpose load.  A 16-lane group of a transpose read takes
+// 32 contiguous bytes of four consecutive k-rows and the next group the 32
+// bytes after them; XOR-ing the piece index by 4*(k & 3) puts the 16 pieces
+// one half-wave touches in 16 different bank groups (rows of at least 16
+// pieces; narrower tiles use 2*(k & 3), distinct within each 16-lane group).  K need not be a multiple of 64 there:
 // the gathered k index is clamped to K-1, so the rows read past K are real
 // rows, and the caller's A must hold zeros in those K columns.
 // With Cfg::AT the A operand is [K][M] in the same way (never gathered, K a
@@ -486,6 +489,10 @@ struct DmaCfg {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// XOR applied to the 16-byte piece index of k-row k of a transposed tile
+// whose rows hold `pieces` pieces.
+__device__ __forceinline__ int tr_swz(int k, int pieces) { return (pieces >= 16 ? 4 : 2) * (k & 3); }
 
 template <class Cfg>
 struct DmaTile {
@@ -522,7 +529,7 @@ struct DmaTile {
     for (int q = 0; q < Cfg::LA; ++q) {
       if constexpr (Cfg::AT) {
         const int kr = (q * NW + wave) * KPIA + (16 * lane) / AROWB, pc = ((16 * lane) % AROWB) / 16;
-        offa[q] = (uint32_t)kr * (uint32_t)A.ld * 2u + (uint32_t)(m0 * 2 + ((pc ^ (2 * (kr & 3))) << 4));
+        offa[q] = (uint32_t)kr * (uint32_t)A.ld * 2u + (uint32_t)(m0 * 2 + ((pc ^ tr_swz(kr, AROWB / 16)) << 4));
       } else {
         const int r = (q * NW + wave) * 8 + rsub;
         int gr = min(m0 + r, A.nrows - 1);
@@ -560,7 +567,7 @@ struct DmaTile {
       for (int q = 0; q < Cfg::LB; ++q) {
         if constexpr (Cfg::BT) {
           const int kr = bt_krow(q), pc = ((16 * lane) % BROWB) / 16;
-          const uint32_t col = (uint32_t)(n0 * 2 + ((pc ^ (2 * (kr & 3))) << 4));
+          const uint32_t col = (uint32_t)(n0 * 2 + ((pc ^ tr_swz(kr, BROWB / 16)) << 4));
           offb[b][q] = bgat ? col : (uint32_t)kr * (uint32_t)B[0].ld * 2u + col;
         } else {
           const int r = (q * NW + wave) * 8 + rsub;
@@ -627,7 +634,7 @@ struct DmaTile {
       const int g = lane >> 4, i = lane & 15;
       const int krow = 8 * (g >> 1) + (i >> 2);
       const int col = wc + j * 32 + 16 * (g & 1) + 4 * (i & 3);
-      btl[j] = krow * BROWB + (((col >> 3) ^ (2 * (krow & 3))) << 4) + (col & 7) * 2;
+      btl[j] = krow * BROWB + (((col >> 3) ^ tr_swz(krow, BROWB / 16)) << 4) + (col & 7) * 2;
       if constexpr (Cfg::BT) asm volatile("" : "+v"(btl[j]));
     }
     int atl[TM];                      // the same for a transposed A, row block i
@@ -636,7 +643,7 @@ struct DmaTile {
       const int g = lane >> 4, ii = lane & 15;
       const int krow = 8 * (g >> 1) + (ii >> 2);
       const int row = wr + i * 32 + 16 * (g & 1) + 4 * (ii & 3);
-      atl[i] = krow * AROWB + (((row >> 3) ^ (2 * (krow & 3))) << 4) + (row & 7) * 2;
+      atl[i] = krow * AROWB + (((row >> 3) ^ tr_swz(krow, AROWB / 16)) << 4) + (row & 7) * 2;
       if constexpr (Cfg::AT) asm volatile("" : "+v"(atl[i]));
     }
     auto compute = [&](const char* st) {
