@@ -144,10 +144,10 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   const Operand B{a.WuT, a.d, ul, nb};
 
   // epilogue set-up, issued before the mainloop so that its global reads
-  // (the position map, and the first TwELL pieces of each pass) complete
-  // under the MFMAs: see the epilogue below
-  static_assert(Cfg::BM == 256 && Cfg::BN == 256 && Cfg::NW == 8 && Cfg::BM / Cfg::WM >= 64, "epilogue layout");
-  static_assert(Cfg::STAGE >= 256 * 64 * 4, "h buffers");
+  // (the position map, and the first TwELL pieces) complete under the MFMAs:
+  // see the epilogue below
+  static_assert(Cfg::BM == 256 && Cfg::BN == 256 && Cfg::NW == 8, "epilogue layout");
+  static_assert(Cfg::STAGE >= 128 * 512, "h tile: 128 positions x 256 rows of fp16 per stage buffer");
   constexpr int POSCAP = 12288;
   __shared__ int16_t posmap[POSCAP];
   const int tid = threadIdx.x;
@@ -159,147 +159,137 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
     for (int p = p0 + tid; p <= pl; p += Cfg::NTH) posmap[ul[p] - nlo] = (int16_t)(p - p0);
   const int tjf = nlo >> 6, S = (nhi >> 6) - tjf + 1;
   constexpr int NG = Cfg::NTH / 16;        // 16-lane groups
+  constexpr int NPRE = 4;                  // blocks per group fetched ahead
   const int grp = tid >> 4, gl = tid & 15;
-  // first piece (slots 0-3) of the group's first two blocks of each pass;
-  // the whole 4 KB block is allocated, so the reads need no width check
+  // first piece (slots 0-3) of the group's first NPRE (row tile, column tile)
+  // blocks; the whole 4 KB block is allocated, so the reads need no width check
   struct Piece { int w; float4 v; uint32_t i; };
-  Piece pre[2][2];
+  Piece pre[NPRE];
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass)
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int q = grp + it * NG;
-      Piece& pc = pre[pass][it];
-      pc.w = 0;
-      pc.v = make_float4(0.f, 0.f, 0.f, 0.f);
-      pc.i = 0;
-      if (q < 8 * S) {
-        const int i = q / S, sj = q - i * S;
-        const int rt = (m0 >> 4) + pass * 8 + i;
-        if (rt * 16 < a.T) {
-          const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
-          pc.w = a.hwidth[blk];
-          pc.v = ((const float4*)(a.hval + blk * 1024))[gl];
-          pc.i = ((const uint32_t*)(a.hidx + blk * 1024))[gl];
-        }
+  for (int it = 0; it < NPRE; ++it) {
+    const int q = grp + it * NG;
+    Piece& pc = pre[it];
+    pc.w = 0;
+    pc.v = make_float4(0.f, 0.f, 0.f, 0.f);
+    pc.i = 0;
+    if (q < 16 * S) {
+      const int i = q / S, sj = q - i * S;
+      const int rt = (m0 >> 4) + i;
+      if (rt * 16 < a.T) {
+        const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
+        pc.w = a.hwidth[blk];
+        pc.v = ((const float4*)(a.hval + blk * 1024))[gl];
+        pc.i = ((const uint32_t*)(a.hidx + blk * 1024))[gl];
       }
     }
+  }
 
   g.run(A, &B, m0, p0, a.d, st0, st1);
 
   // epilogue: a = h * u on stored pairs, else 0, stored as fp16 into
   // adense[t][p] (32 consecutive positions per half-wave store).  Positions in
   // [n_b, roundup64(n_b)) are written as zeros (the down GEMM reads whole
-  // 64-position K tiles).  h is brought to the accumulator layout through
-  // LDS, 128 rows per pass: the two stage buffers are zeroed, every stored
-  // TwELL pair of those rows whose neuron falls in this tile's positions is
-  // written at (position, row) (position found through posmap, the inverse of
-  // the union list over the tile's neuron span), and the four waves owning
-  // the rows read their h values back with 16-byte loads.  A buffer holds 64
-  // rows as [position][row] (256 bytes per position, 16-byte pieces XOR-
-  // swizzled by position so 8 consecutive positions hit 8 bank groups).
+  // 64-position K tiles).  h is brought to the accumulator layout through an
+  // LDS tile of fp16 (positions 0-127 in st0, 128-255 in st1; 512 bytes of
+  // rows per position, 8-byte pieces of 4 rows XOR-swizzled by position so a
+  // half-wave's 32 consecutive positions hit distinct banks): the tile is
+  // zeroed, every stored TwELL pair of the block whose neuron falls in this
+  // tile's positions is written at (position, row) (position from posmap,
+  // the inverse of the union list over the tile's neuron span), and every
+  // wave reads its h values back 4 rows at a time.  h in fp16 adds one
+  // rounding (2^-11 relative) before a is itself rounded to fp16.
   const int hl = lane >> 5;
   uint32_t vbits = 0;               // largest |a| bit pattern (NaN patterns sort above every number)
-  auto hslot = [](int p, int r64) { return p * 256 + (((r64 >> 2) ^ (p & 7)) << 4) + ((r64 & 3) << 2); };
-
-  // pass: zero the h buffers, scatter the pairs of rows [128 pass, +128)
-  auto prep = [&](int pass) {
+  auto hoff = [](int pr, int r) {
+    const int pb = pr & 127;
+    return pb * 512 + (((r >> 2) ^ (pb & 31)) << 3) + ((r & 3) << 1);
+  };
 #pragma unroll
-    for (int o = 0; o < Cfg::STAGE / (16 * Cfg::NTH); ++o) {
-      ((float4*)st0)[o * Cfg::NTH + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
-      ((float4*)st1)[o * Cfg::NTH + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    __syncthreads();
-    // scatter: a 16-lane group per (row tile, column tile) block; lane piece c
-    // holds slot c/4, rows 4*(c%4)..+3 of the block
-    auto scatter = [&](int i, int tj, int rt, int c, const float4& v4, uint32_t i4) {
-      char* hbuf = (i >> 2) ? st1 : st0;
-      const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+  for (int o = 0; o < Cfg::STAGE / (16 * Cfg::NTH); ++o) {
+    ((float4*)st0)[o * Cfg::NTH + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+    ((float4*)st1)[o * Cfg::NTH + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+  // scatter: a 16-lane group per (row tile, column tile) block; lane piece c
+  // holds slot c/4, rows 4*(c%4)..+3 of the block
+  auto scatter = [&](int i, int tj, int rt, int c, const float4& v4, uint32_t i4) {
+    const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int rl = 4 * (c & 3) + k;                   // row in the tile
-        const int n = tj * 64 + (int)((i4 >> (8 * k)) & 255u);
-        if (vv[k] > 0.f && n >= nlo && n <= nhi && live(a, rt * 16 + rl)) {
-          int pr;
-          if (use_map) {
-            pr = posmap[n - nlo];
-          } else {
-            int lo = p0, hi = pl;                         // n is in the union: find its position
-            while (lo < hi) {
-              const int mid = (lo + hi) >> 1;
-              if (ul[mid] < n) lo = mid + 1; else hi = mid;
-            }
-            pr = lo - p0;
+    for (int k = 0; k < 4; ++k) {
+      const int rl = 4 * (c & 3) + k;                     // row in the tile
+      const int n = tj * 64 + (int)((i4 >> (8 * k)) & 255u);
+      if (vv[k] > 0.f && n >= nlo && n <= nhi && live(a, rt * 16 + rl)) {
+        int pr;
+        if (use_map) {
+          pr = posmap[n - nlo];
+        } else {
+          int lo = p0, hi = pl;                           // n is in the union: find its position
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (ul[mid] < n) lo = mid + 1; else hi = mid;
           }
-          *(float*)(hbuf + hslot(pr, (i & 3) * 16 + rl)) = vv[k];
+          pr = lo - p0;
+        }
+        char* hbuf = (pr >> 7) ? st1 : st0;
+        *(_Float16*)(hbuf + hoff(pr, i * 16 + rl)) = (_Float16)vv[k];
+      }
+    }
+  };
+#pragma unroll
+  for (int it = 0; it < NPRE; ++it) {
+    const int q = grp + it * NG;
+    if (q >= 16 * S) break;
+    const int i = q / S, sj = q - i * S;
+    const int rt = (m0 >> 4) + i;
+    const Piece& pc = pre[it];
+    if (gl < pc.w * 4) scatter(i, tjf + sj, rt, gl, pc.v, pc.i);
+    const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
+    for (int c = gl + 16; c < pc.w * 4; c += 16)
+      scatter(i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
+              ((const uint32_t*)(a.hidx + blk * 1024))[c]);
+  }
+  for (int q = grp + NPRE * NG; q < 16 * S; q += NG) {
+    const int i = q / S, sj = q - i * S;
+    const int rt = (m0 >> 4) + i;
+    if (rt * 16 >= a.T) continue;
+    const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
+    const int w = a.hwidth[blk];
+    for (int c = gl; c < w * 4; c += 16)
+      scatter(i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
+              ((const uint32_t*)(a.hidx + blk * 1024))[c]);
+  }
+  __syncthreads();
+  const int wrow = (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
+#pragma unroll
+  for (int j = 0; j < Cfg::TN; ++j) {
+    const int pr = Tile::col_of(j);
+    const int p = p0 + pr;
+    const bool wr = p < ((nb + 63) & ~63);
+    const char* hbuf = (pr >> 7) ? st1 : st0;
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const uint2 h2 = *(const uint2*)(hbuf + hoff(pr, wrow + i * 32 + 8 * qq + 4 * hl));
+        const float hv[4] = {(float)__builtin_bit_cast(_Float16, (uint16_t)(h2.x & 0xffffu)),
+                             (float)__builtin_bit_cast(_Float16, (uint16_t)(h2.x >> 16)),
+                             (float)__builtin_bit_cast(_Float16, (uint16_t)(h2.y & 0xffffu)),
+                             (float)__builtin_bit_cast(_Float16, (uint16_t)(h2.y >> 16))};
+        const int t0 = m0 + Tile::row_of(i, 4 * qq);
+        // element offsets stay below 2^32 (the matrix holds fewer elements);
+        // elements that are not written go to the spare slot past the
+        // matrix, so the stores need no branches
+        const uint32_t o0 = (uint32_t)t0 * (uint32_t)a.F + (uint32_t)p;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float v = hv[k] != 0.f ? hv[k] * g.acc[0][i][j][4 * qq + k] : 0.f;
+          vbits = max(vbits, __float_as_uint(v) & 0x7fffffffu);
+          const uint32_t keep = 0u - (uint32_t)(wr && t0 + k < a.T);
+          const uint32_t o = ((o0 + (uint32_t)k * (uint32_t)a.F) & keep) | (a.spare & ~keep);
+          a.adense[o] = (_Float16)v;
         }
       }
-    };
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int q = grp + it * NG;
-      if (q >= 8 * S) break;
-      const int i = q / S, sj = q - i * S;
-      const int rt = (m0 >> 4) + pass * 8 + i;
-      const Piece& pc = pre[pass][it];
-      if (gl < pc.w * 4) scatter(i, tjf + sj, rt, gl, pc.v, pc.i);
-      const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
-      for (int c = gl + 16; c < pc.w * 4; c += 16)
-        scatter(i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
-                ((const uint32_t*)(a.hidx + blk * 1024))[c]);
-    }
-    for (int q = grp + 2 * NG; q < 8 * S; q += NG) {
-      const int i = q / S, sj = q - i * S;
-      const int rt = (m0 >> 4) + pass * 8 + i;
-      if (rt * 16 >= a.T) continue;
-      const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
-      const int w = a.hwidth[blk];
-      for (int c = gl; c < w * 4; c += 16)
-        scatter(i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
-                ((const uint32_t*)(a.hidx + blk * 1024))[c]);
-    }
-    __syncthreads();
-  };
-  // the four waves owning the pass's rows apply h to their accumulators
-  // rows of this wave inside its pass start at rbase (the pass is 128 rows:
-  // rows 0-63 in st0, 64-127 in st1)
-  const int wrow = (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
-  const int wpass = wrow >> 7, rbase = wrow & 127;
-  auto mul = [&]() {
-#pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j) {
-      const int pr = Tile::col_of(j);
-      const int p = p0 + pr;
-      const bool wr = p < ((nb + 63) & ~63);
-#pragma unroll
-      for (int i = 0; i < Cfg::TM; ++i)
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int r0 = rbase + i * 32;
-          const char* hbuf = (r0 >> 6) ? st1 : st0;
-          const float4 h4 = *(const float4*)(hbuf + hslot(pr, (r0 & 63) + 8 * qq + 4 * hl));
-          const float hv[4] = {h4.x, h4.y, h4.z, h4.w};
-          const int t0 = m0 + Tile::row_of(i, 4 * qq);
-          // element offsets stay below 2^32 (the matrix holds fewer elements);
-          // elements that are not written go to the spare slot past the
-          // matrix, so the stores need no branches
-          const uint32_t o0 = (uint32_t)t0 * (uint32_t)a.F + (uint32_t)p;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float v = hv[k] != 0.f ? hv[k] * g.acc[0][i][j][4 * qq + k] : 0.f;
-            vbits = max(vbits, __float_as_uint(v) & 0x7fffffffu);
-            const uint32_t keep = 0u - (uint32_t)(wr && t0 + k < a.T);
-            const uint32_t o = ((o0 + (uint32_t)k * (uint32_t)a.F) & keep) | (a.spare & ~keep);
-            a.adense[o] = (_Float16)v;
-          }
-        }
-    }
-  };
-  prep(0);
-  if (wpass == 0) mul();
-  __syncthreads();
-  prep(1);
-  if (wpass == 1) mul();
+  }
   const bool over = vbits > 0x477fe000u;   // above 65504, the largest finite fp16
   if (__builtin_amdgcn_ballot_w64(over) != 0ull && lane == 0) atomicOr(a.flag, 1);
 }
