@@ -276,17 +276,31 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
                              (float)__builtin_bit_cast(_Float16, (uint16_t)(h2.y & 0xffffu)),
                              (float)__builtin_bit_cast(_Float16, (uint16_t)(h2.y >> 16))};
         const int t0 = m0 + Tile::row_of(i, 4 * qq);
-        // element offsets stay below 2^32 (the matrix holds fewer elements);
-        // elements that are not written go to the spare slot past the
-        // matrix, so the stores need no branches
-        const uint32_t o0 = (uint32_t)t0 * (uint32_t)a.F + (uint32_t)p;
+        float v[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float v = hv[k] != 0.f ? hv[k] * g.acc[0][i][j][4 * qq + k] : 0.f;
-          vbits = max(vbits, __float_as_uint(v) & 0x7fffffffu);
-          const uint32_t keep = 0u - (uint32_t)(wr && t0 + k < a.T);
-          const uint32_t o = ((o0 + (uint32_t)k * (uint32_t)a.F) & keep) | (a.spare & ~keep);
-          a.adense[o] = (_Float16)v;
+          v[k] = hv[k] != 0.f ? hv[k] * g.acc[0][i][j][4 * qq + k] : 0.f;
+          vbits = max(vbits, __float_as_uint(v[k]) & 0x7fffffffu);
+        }
+        // stores of position pairs: lanes l and l^1 hold positions p and
+        // p^1 of the same rows; for rows k and k+1 the even lane stores
+        // (its k, the odd lane's k) at p, the odd lane (the even lane's k+1,
+        // its k+1) at p-1: one 4-byte store per two elements.  Element
+        // offsets stay below 2^32 (the matrix holds fewer elements); pairs
+        // that are not written go to the spare slot past the matrix, so the
+        // stores need no branches.
+        const bool odd = lane & 1;
+#pragma unroll
+        for (int k = 0; k < 4; k += 2) {
+          const float send = odd ? v[k] : v[k + 1];
+          const float recv = __shfl_xor(send, 1);
+          const int kr = odd ? k + 1 : k;                   // row this lane stores
+          const _Float16 lo = (_Float16)(odd ? recv : v[k]), hi = (_Float16)(odd ? v[k + 1] : recv);
+          const uint32_t pair = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          const uint32_t keep = 0u - (uint32_t)(wr && t0 + kr < a.T);
+          const uint32_t o = (((uint32_t)(t0 + kr) * (uint32_t)a.F + (uint32_t)(p & ~1)) & keep) | (a.spare & ~keep);
+          *(uint32_t*)(a.adense + o) = pair;
         }
       }
   }
