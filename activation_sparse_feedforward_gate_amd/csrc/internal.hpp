@@ -109,8 +109,8 @@ size_t union_ws_bytes(int T, int d, int F);
 void union_lists_only(int T, int F, const TwellView& h, void* ws, int** ulist, int** ucount, uint64_t** slabs);
 hipError_t launch_union_lists(int T, int F, const TwellView& h, void* ws, hipStream_t s, bool slabs_ready = false);
 
-// Forward for few tokens (T <= DECODE_T_MAX, bf16, inference): split-K GEMMs
-// over one-wave workgroups with fixed-order partial sums.  h receives the
+// Forward for few tokens (T <= DECODE_T_MAX, bf16, inference): GEMMs split
+// along K over many workgroups with fixed-order partial sums.  h receives the
 // TwELL of ReLU(g); uni_ws is the union workspace (union_ws_bytes), ws
 // decode_ws_bytes(T, d, F) bytes.  Events (nullable) after the gate + pack,
 // after the union lists, after the up-projection.
@@ -132,6 +132,13 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
 hipError_t launch_dense_fwd(const void* x, const void* WgT, const void* bg, const void* WuT,
                             const void* Wd, int T, int d, int F, void* act, int out_dt, void* y,
                             hipStream_t s);
+// Dense baseline for few tokens (T <= DECODE_T_MAX), from the same split-K
+// blocks as the few-token TwELL forward: gate and up partials in one GEMM,
+// act = bf16(ReLU(g + b) * u), the split-K down-projection.
+// ws: dense_few_ws_bytes(T, d, F).
+size_t dense_few_ws_bytes(int T, int d, int F);
+hipError_t launch_dense_few_fwd(const void* x, const void* WgT, const void* bg, const void* WuT, const void* Wd,
+                                int T, int d, int F, void* ws, int out_dt, void* y, hipStream_t s);
 // y = act.Wd for a bf16 act [T][F].
 hipError_t launch_dense_down(const void* act, const void* Wd, int T, int d, int F, int out_dt, void* y,
                              hipStream_t s);

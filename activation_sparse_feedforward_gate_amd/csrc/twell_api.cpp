@@ -394,8 +394,12 @@ twell_status twell_sparse_down(const twell_ffn_shape* sh, const float* aval, con
                                      view_of(pattern), y, nullptr, stream), "sparse down-projection");
 }
 
+// The dense baseline takes the few-token kernels where the TwELL forward does.
+bool dense_few_tokens(const twell_ffn_shape* sh) { return sh->T > 0 && sh->T <= DECODE_T_MAX; }
+
 size_t twell_ffn_dense_fwd_workspace(const twell_ffn_shape* sh) {
   if (!sh || check_shape(sh) != TWELL_OK) return 0;
+  if (dense_few_tokens(sh)) return dense_few_ws_bytes(sh->T, sh->d, sh->F);
   return round_up((size_t)sh->T * sh->F * 2, 256);
 }
 
@@ -412,6 +416,10 @@ twell_status twell_ffn_dense_fwd(const twell_ffn_shape* sh, const void* x, const
   const size_t need = twell_ffn_dense_fwd_workspace(sh);
   if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
   if (sh->T == 0) return TWELL_OK;
+  if (dense_few_tokens(sh))
+    return hip_status(launch_dense_few_fwd(x, WgT, bg, WuT, Wd, sh->T, sh->d, sh->F, ws,
+                                           sh->out_dt == TWELL_BF16 ? DT_BF16 : DT_F32, y, stream),
+                      "dense few-token FFN");
   return hip_status(launch_dense_fwd(x, WgT, bg, WuT, Wd, sh->T, sh->d, sh->F, ws,
                                      sh->out_dt == TWELL_BF16 ? DT_BF16 : DT_F32, y, stream),
                     "dense FFN");

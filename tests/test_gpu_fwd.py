@@ -224,14 +224,33 @@ def test_fwd_decode_small(torch, tw):
 
 @pytest.mark.parametrize("T", [129, 256])
 def test_fwd_few_token_path(torch, tw, T):
-    """Batches of at most 256 bf16 tokens take the split-K path; its partial
-    sums are reduced in a fixed order, so repeated runs give the same bits."""
+    """Batches of at most 256 bf16 tokens take the few-token kernels; their
+    partial sums are added in a fixed order, so repeated runs give the same
+    bits."""
     w = make_workload("2b", T=T, d=384, f=1536)
     log(f"[fwd] few-token path T={T}")
     y, m = run_fwd(torch, tw, w)
     check_fwd(w, y, m)
     y2, _ = run_fwd(torch, tw, w)
     np.testing.assert_array_equal(y2, y)
+
+
+@pytest.mark.parametrize("T", [48, 64])
+def test_fwd_few_token_tiles(torch, tw, T):
+    """One 64-token chunk with three and with four 16-token MFMA tiles."""
+    w = make_workload("2b", T=T, d=384, f=1536)
+    log(f"[fwd] few-token tiles T={T}")
+    y, m = run_fwd(torch, tw, w)
+    check_fwd(w, y, m)
+
+
+def test_fwd_few_token_wide_f(torch, tw):
+    """F = 20480: the few-token down-projection splits K over more workgroups
+    than its least split, each holding at most 64 K steps of the list."""
+    w = make_workload("2b", T=40, d=128, f=20480)
+    log(f"[fwd] few-token wide F T={w.T} f={w.f}")
+    y, m = run_fwd(torch, tw, w)
+    check_fwd(w, y, m)
 
 
 @pytest.mark.parametrize("T", [1, 17, 31, 16])
@@ -345,5 +364,28 @@ def test_dense_baseline_full_size_sampled(torch, tw, name):
     rows = np.random.default_rng(3).choice(w.T, size=512, replace=False)
     ref = O.ffn_fwd_rows(w.x, w.WgT, w.bg, w.WuT, w.Wd, rows)["y"]
     err = rel_fro(y[rows], ref)
+    log(f"   dense y rel error {err:.3e}")
+    assert err <= 5e-3
+
+
+@pytest.mark.parametrize("T", [1, 17, 64, 200])
+def test_dense_baseline_few_tokens(torch, tw, T):
+    """Batches of at most 256 tokens take the dense few-token kernels."""
+    w = make_workload("2b", T=T, d=384, f=1536)
+    log(f"[dense] few tokens T={T}")
+    y = run_dense(torch, tw, w)
+    ref = O.ffn_dense_fwd(w.x, w.WgT, w.bg, w.WuT, w.Wd)["y"]
+    err = rel_fro(y, ref)
+    log(f"   dense y rel error {err:.3e}")
+    assert err <= 5e-3
+    np.testing.assert_array_equal(run_dense(torch, tw, w), y)   # fixed-order partial sums
+
+
+def test_dense_baseline_full_size_decode(torch, tw):
+    w = make_workload("2b", decode=True)
+    log(f"[dense] full size decode T={w.T}")
+    y = run_dense(torch, tw, w)
+    ref = O.ffn_dense_fwd(w.x, w.WgT, w.bg, w.WuT, w.Wd)["y"]
+    err = rel_fro(y, ref)
     log(f"   dense y rel error {err:.3e}")
     assert err <= 5e-3
