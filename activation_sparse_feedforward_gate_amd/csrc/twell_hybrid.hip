@@ -338,38 +338,57 @@ hipError_t launch_dense_rows_bwd(int in_dt, const void* x, const void* WgT, cons
 
 constexpr int CSC_CHUNK = 256;   // tokens per count/fill chunk
 
-// part[c][n] = number of sparse rows t in chunk c with (t, n) stored.
+// part[c][n] = number of sparse rows t in chunk c with (t, n) stored.  The
+// loop takes 16 tokens at a time so their loads are in flight together.
 __global__ __launch_bounds__(64) void csc_count_kernel(const uint64_t* mask, const uint8_t* skip, int T,
                                                        int NT, int F, int* part) {
   const int lane = threadIdx.x;
   const int j = blockIdx.x, c = blockIdx.y;
   const int t0 = c * CSC_CHUNK, t1 = min(T, t0 + CSC_CHUNK);
   int k = 0;
-  for (int t = t0; t < t1; ++t) {
-    if (skip && skip[t]) continue;
-    k += (int)((mask[(int64_t)t * NT + j] >> lane) & 1ull);
+  for (int tb = t0; tb < t1; tb += 16) {
+    uint64_t m[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int t = tb + q;
+      m[q] = (t < t1 && !(skip && skip[t])) ? mask[(int64_t)t * NT + j] : 0ull;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) k += (int)((m[q] >> lane) & 1ull);
   }
   part[(int64_t)c * F + j * 64 + lane] = k;
 }
 
-// Single workgroup: start[n] = sum of the totals of neurons < n (start[F] =
-// total); part[c][n] becomes the position of chunk c's first entry of n.
-__global__ __launch_bounds__(1024) void csc_scan_kernel(int* part, int nchunk, int F, int* start) {
+// Per neuron n (one thread each): part[c][n] becomes the exclusive prefix of
+// the chunk counts over c, and start[n] the neuron's total.  Eight chunks'
+// loads are in flight at a time.
+__global__ __launch_bounds__(256) void csc_chunk_scan_kernel(int* part, int nchunk, int F, int* start) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= F) return;
+  int run = 0;
+  for (int c0 = 0; c0 < nchunk; c0 += 8) {
+    int v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = c0 + q < nchunk ? part[(int64_t)(c0 + q) * F + n] : 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (c0 + q < nchunk) {
+        part[(int64_t)(c0 + q) * F + n] = run;
+        run += v[q];
+      }
+  }
+  start[n] = run;
+}
+
+// Single workgroup: start[n] = sum of the totals of neurons < n, start[F] =
+// the grand total.
+__global__ __launch_bounds__(1024) void csc_total_scan_kernel(int F, int* start) {
   __shared__ int wsum[1024];
   const int tid = threadIdx.x;
   const int per = (F + 1023) / 1024;
   const int n0 = min(F, tid * per), n1 = min(F, n0 + per);
   int mine = 0;
-  for (int n = n0; n < n1; ++n) {
-    int run = 0;
-    for (int c = 0; c < nchunk; ++c) {
-      const int v = part[(int64_t)c * F + n];
-      part[(int64_t)c * F + n] = run;
-      run += v;
-    }
-    start[n] = run;            // total for now
-    mine += run;
-  }
+  for (int n = n0; n < n1; ++n) mine += start[n];
   wsum[tid] = mine;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
@@ -382,27 +401,35 @@ __global__ __launch_bounds__(1024) void csc_scan_kernel(int* part, int nchunk, i
   for (int n = n0; n < n1; ++n) {
     const int tot = start[n];
     start[n] = base;
-    for (int c = 0; c < nchunk; ++c) part[(int64_t)c * F + n] += base;
     base += tot;
   }
   if (tid == 1023) start[F] = wsum[1023];
 }
 
 // entries[pos] = flat TwELL slot offset of each stored pair of a sparse row,
-// grouped by neuron, tokens ascending within a neuron.
+// grouped by neuron, tokens ascending within a neuron; the neuron's block
+// starts at start[n], chunk c's part at part[c][n] within it.
 __global__ __launch_bounds__(64) void csc_fill_kernel(const uint64_t* mask, const uint8_t* skip, int T, int NT,
-                                                      int F, const int* part, uint32_t* entries) {
+                                                      int F, const int* part, const int* start, uint32_t* entries) {
   const int lane = threadIdx.x;
   const int j = blockIdx.x, c = blockIdx.y;
   const int t0 = c * CSC_CHUNK, t1 = min(T, t0 + CSC_CHUNK);
-  int pos = part[(int64_t)c * F + j * 64 + lane];
+  int pos = start[j * 64 + lane] + part[(int64_t)c * F + j * 64 + lane];
   const uint64_t lower = below(lane);
-  for (int t = t0; t < t1; ++t) {
-    if (skip && skip[t]) continue;
-    const uint64_t m = mask[(int64_t)t * NT + j];
-    if ((m >> lane) & 1ull) {
-      const uint32_t slot = (uint32_t)popc64(m & lower);
-      entries[pos++] = ((uint32_t)((t >> 4) * NT + j) * 64u + slot) * 16u + (uint32_t)(t & 15);
+  for (int tb = t0; tb < t1; tb += 16) {
+    uint64_t m[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int t = tb + q;
+      m[q] = (t < t1 && !(skip && skip[t])) ? mask[(int64_t)t * NT + j] : 0ull;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if ((m[q] >> lane) & 1ull) {
+        const int t = tb + q;
+        const uint32_t slot = (uint32_t)popc64(m[q] & lower);
+        entries[pos++] = ((uint32_t)((t >> 4) * NT + j) * 64u + slot) * 16u + (uint32_t)(t & 15);
+      }
     }
   }
 }
@@ -486,9 +513,11 @@ hipError_t launch_sparse_wgrad(int in_dt, const void* x, const void* dY, int T, 
   if (nchunk > 0) {
     hipLaunchKernelGGL(csc_count_kernel, dim3(NT, nchunk), dim3(64), 0, s, h.mask, skip, T, NT, F, part);
   }
-  hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(1024), 0, s, part, nchunk, F, start);
+  hipLaunchKernelGGL(csc_chunk_scan_kernel, dim3((F + 255) / 256), dim3(256), 0, s, part, nchunk, F, start);
+  hipLaunchKernelGGL(csc_total_scan_kernel, dim3(1), dim3(1024), 0, s, F, start);
   if (nchunk > 0) {
-    hipLaunchKernelGGL(csc_fill_kernel, dim3(NT, nchunk), dim3(64), 0, s, h.mask, skip, T, NT, F, part, entries);
+    hipLaunchKernelGGL(csc_fill_kernel, dim3(NT, nchunk), dim3(64), 0, s, h.mask, skip, T, NT, F, part, start,
+                       entries);
   }
   WgradArgs a{x, dY, T, d, F, NT, start, entries, aval, dgval, duval, dWgT, dWuT, dWd, dbg};
   if (in_dt == DT_BF16) hipLaunchKernelGGL(wgrad_sparse_kernel<true>, dim3(F), dim3(256), 0, s, a);
