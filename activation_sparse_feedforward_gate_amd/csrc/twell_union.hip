@@ -5,7 +5,7 @@
 // (intellectnews.ru TwELL article, section "Формат TwELL вместо классической
 // sparse-упаковки"), the up- and down-projections only need the neurons that
 // fire (section "Слитые CUDA-ядра для инференса и гибрид для обучения").  For
-// a block of 256 tokens the set of neurons that fire in ANY of them (the
+// a block of 128 tokens the set of neurons that fire in ANY of them (the
 // union, in ascending neuron order) is taken as the N dimension of the
 // up-projection and the K dimension of the down-projection:
 //
@@ -27,7 +27,11 @@ namespace twell {
 
 namespace {
 
-constexpr int UB = 256;               // tokens per row block
+// Tokens per row block.  Smaller blocks give smaller unions (less executed
+// work) but smaller GEMM tiles: 128 rows measured faster than 256 overall on
+// the 1.5B and 2B shapes (union fractions 42% / 26% against 58% / 38%, tile
+// throughput about 10% lower).
+constexpr int UB = 128;
 constexpr int RT = UB / 16;            // TwELL row tiles per row block
 
 struct UnionArgs {
@@ -43,6 +47,7 @@ struct UnionArgs {
   const uint8_t* hwidth;  // TwELL widths of h
   int* ulist;             // [NBLK][F]
   int* ucount;            // [NBLK]
+  int lrows;              // rows per list block: UB, or every row (one list) for the few-token path
   _Float16* adense;       // [T][F], then spare slots
   uint32_t spare;         // element index of a spare slot (T*F)
   int* flag;              // fp16 overflow flag
@@ -88,7 +93,7 @@ __global__ __launch_bounds__(256) void union_list_kernel(UnionArgs a, const uint
     const int j = j0 + tid;
     uint64_t u = 0;
     if (j < a.NT) {
-      const int s0 = b * (UB / 64), s1 = min((a.T + 63) / 64, s0 + UB / 64);
+      const int s0 = b * (a.lrows / 64), s1 = min((a.T + 63) / 64, s0 + a.lrows / 64);
       for (int sl = s0; sl < s1; ++sl) u |= U[(int64_t)sl * a.NT + j];
     }
     const int c = popc64(u);
@@ -146,8 +151,8 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   // epilogue set-up, issued before the mainloop so that its global reads
   // (the position map, and the first TwELL pieces) complete under the MFMAs:
   // see the epilogue below
-  static_assert(Cfg::BM == 256 && Cfg::BN == 256 && Cfg::NW == 8, "epilogue layout");
-  static_assert(Cfg::STAGE >= 128 * 512, "h tile: 128 positions x 256 rows of fp16 per stage buffer");
+  static_assert(Cfg::BN == 256 && Cfg::NW == 8 && Cfg::BM % 128 == 0 && Cfg::BM <= 256, "epilogue layout");
+  static_assert(Cfg::STAGE >= 128 * 2 * Cfg::BM, "h tile: 128 positions x BM rows of fp16 per stage buffer");
   constexpr int POSCAP = 12288;
   __shared__ int16_t posmap[POSCAP];
   const int tid = threadIdx.x;
@@ -163,6 +168,7 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   const int grp = tid >> 4, gl = tid & 15;
   // first piece (slots 0-3) of the group's first NPRE (row tile, column tile)
   // blocks; the whole 4 KB block is allocated, so the reads need no width check
+  constexpr int NRT = Cfg::BM / 16;        // TwELL row tiles of the block
   struct Piece { int w; float4 v; uint32_t i; };
   Piece pre[NPRE];
 #pragma unroll
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
     pc.w = 0;
     pc.v = make_float4(0.f, 0.f, 0.f, 0.f);
     pc.i = 0;
-    if (q < 16 * S) {
+    if (q < NRT * S) {
       const int i = q / S, sj = q - i * S;
       const int rt = (m0 >> 4) + i;
       if (rt * 16 < a.T) {
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   // adense[t][p] (32 consecutive positions per half-wave store).  Positions in
   // [n_b, roundup64(n_b)) are written as zeros (the down GEMM reads whole
   // 64-position K tiles).  h is brought to the accumulator layout through an
-  // LDS tile of fp16 (positions 0-127 in st0, 128-255 in st1; 512 bytes of
+  // LDS tile of fp16 (positions 0-127 in st0, 128-255 in st1; 2*BM bytes of
   // rows per position, 8-byte pieces of 4 rows XOR-swizzled by position so a
   // half-wave's 32 consecutive positions hit distinct banks): the tile is
   // zeroed, every stored TwELL pair of the block whose neuron falls in this
@@ -202,10 +208,10 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   uint32_t vbits = 0;               // largest |a| bit pattern (NaN patterns sort above every number)
   auto hoff = [](int pr, int r) {
     const int pb = pr & 127;
-    return pb * 512 + (((r >> 2) ^ (pb & 31)) << 3) + ((r & 3) << 1);
+    return pb * (2 * Cfg::BM) + (((r >> 2) ^ (pb & 31)) << 3) + ((r & 3) << 1);
   };
 #pragma unroll
-  for (int o = 0; o < Cfg::STAGE / (16 * Cfg::NTH); ++o) {
+  for (int o = 0; o < 128 * 2 * Cfg::BM / (16 * Cfg::NTH); ++o) {
     ((float4*)st0)[o * Cfg::NTH + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
     ((float4*)st1)[o * Cfg::NTH + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
 #pragma unroll
   for (int it = 0; it < NPRE; ++it) {
     const int q = grp + it * NG;
-    if (q >= 16 * S) break;
+    if (q >= NRT * S) break;
     const int i = q / S, sj = q - i * S;
     const int rt = (m0 >> 4) + i;
     const Piece& pc = pre[it];
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
       scatter(i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
               ((const uint32_t*)(a.hidx + blk * 1024))[c]);
   }
-  for (int q = grp + NPRE * NG; q < 16 * S; q += NG) {
+  for (int q = grp + NPRE * NG; q < NRT * S; q += NG) {
     const int i = q / S, sj = q - i * S;
     const int rt = (m0 >> 4) + i;
     if (rt * 16 >= a.T) continue;
@@ -365,10 +371,10 @@ __global__ __launch_bounds__(Cfg::NTH) void down_union_kernel(UnionArgs a) {
   }
 }
 
-using UpUnionCfg = DmaCfg<256, 256, 2, 4>;
-using DownUnionCfg = DmaCfg<256, 256, 2, 4, 1, true, true>;
-using DownUnionCfg128 = DmaCfg<256, 128, 4, 2, 1, true, true>;
-using DownUnionCfg64 = DmaCfg<256, 64, 4, 1, 1, true, true>;
+using UpUnionCfg = DmaCfg<UB, 256, 2, 4>;
+using DownUnionCfg = DmaCfg<UB, 256, 2, 4, 1, true, true>;
+using DownUnionCfg128 = DmaCfg<UB, 128, 4, 2, 1, true, true>;
+using DownUnionCfg64 = DmaCfg<UB, 64, 4, 2, 1, true, true>;
 
 size_t union_ws_bytes(int T, int d, int F) {
   const size_t nblk = (size_t)(T + UB - 1) / UB;
@@ -394,6 +400,7 @@ UnionArgs union_setup(const void* x, const void* WuT, const void* Wd, int T, int
   *U = (uint64_t*)((char*)a.flag + 256);
   a.Wd16 = (const _Float16*)((char*)*U + (((size_t)((T + 63) / 64) * a.NT * 8 + 255) & ~(size_t)255));
   a.y = y; a.out_bf16 = out_dt == DT_BF16;
+  a.lrows = UB;
   return a;
 }
 
@@ -416,10 +423,11 @@ void union_lists_only(int T, int F, const TwellView& h, void* ws, int** ulist, i
 hipError_t launch_union_lists(int T, int F, const TwellView& h, void* ws, hipStream_t s, bool slabs_ready) {
   if (T == 0) return hipSuccess;
   uint64_t* U;
-  const UnionArgs a = union_setup(nullptr, nullptr, nullptr, T, 0, F, h, nullptr, ws, nullptr, DT_F32, &U);
+  UnionArgs a = union_setup(nullptr, nullptr, nullptr, T, 0, F, h, nullptr, ws, nullptr, DT_F32, &U);
   if (slabs_ready) {
-    const int nblk = (T + UB - 1) / UB;
-    hipLaunchKernelGGL(union_list_kernel, dim3(nblk), dim3(256), 0, s, a, (const uint64_t*)U);
+    // the few-token path: one list over every row (T <= DECODE_T_MAX)
+    a.lrows = (T + 63) & ~63;
+    hipLaunchKernelGGL(union_list_kernel, dim3(1), dim3(256), 0, s, a, (const uint64_t*)U);
   } else {
     union_lists_launch(a, U, s);
   }

@@ -75,6 +75,9 @@ def cpu_baseline(w, budget_s: float, training: bool) -> dict:
             "sample": f"first {done} of {w.T} token rows, float64 numpy {what}, {dt:.1f} s"}
 
 
+# tokens per row block of the union up/down GEMMs (the library's row blocks)
+UNION_BLOCK = 128
+
 # kernels whose HBM traffic is recorded in profiles/hbm_traffic.json, with the
 # source files that define each (a recorded figure is dropped once they change)
 TRAFFIC_SOURCES = {
@@ -256,16 +259,17 @@ def main() -> int:
         v["traffic"] = traffic.get(k)
     if bf and h.mask is not None and not few_tokens:
         # MFMA work the union GEMMs execute (all union positions of every
-        # 256-token row block, in whole tiles), beside the useful work above
+        # UNION_BLOCK-token row block, in whole tiles), beside the useful work above
         m = h.mask.cpu().numpy().view(np.uint64)
         nb = np.zeros(0, dtype=np.int64)
+        ub = UNION_BLOCK
         if T:
-            pad = (-T) % 256
+            pad = (-T) % ub
             mm = np.concatenate([m, np.zeros((pad, m.shape[1]), np.uint64)]) if pad else m
-            u = np.bitwise_or.reduce(mm.reshape(-1, 256, m.shape[1]), axis=1)
+            u = np.bitwise_or.reduce(mm.reshape(-1, ub, m.shape[1]), axis=1)
             nb = np.unpackbits(u.view(np.uint8), axis=1).sum(axis=1).astype(np.int64)
-        up_exec = 2.0 * float((-(-nb // 256) * 256).sum()) * 256 * d
-        dn_exec = 2.0 * float((-(-nb // 64) * 64).sum()) * 256 * d
+        up_exec = 2.0 * float((-(-nb // 256) * 256).sum()) * ub * d
+        dn_exec = 2.0 * float((-(-nb // 64) * 64).sum()) * ub * d
         for k, w_exec in (("up_projection", up_exec), ("down_projection", dn_exec)):
             lines[k]["executed_work"] = w_exec
             lines[k]["executed_tflops"] = w_exec / (lines[k]["ms"] * 1e-3) / 1e12
