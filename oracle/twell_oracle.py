@@ -44,7 +44,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "relu", "ffn_dense_fwd", "ffn_dense_fwd_loops", "ffn_dense_bwd",
+    "relu", "ffn_dense_fwd", "ffn_dense_fwd_loops", "ffn_dense_bwd", "l1_coefficient",
     "TwellMat", "twell_pack", "twell_pack_loops", "twell_unpack", "twell_entries",
     "ffn_sparse_fwd", "ffn_sparse_fwd_loops", "classify_rows",
     "hybrid_fwd_bwd", "hybrid_fwd_bwd_loops", "ffn_fwd_rows", "ffn_bwd_sampled",
@@ -113,16 +113,29 @@ def ffn_dense_fwd_loops(x, WgT, bg, WuT, Wd) -> np.ndarray:
     return y
 
 
-def ffn_dense_bwd(x, WgT, bg, WuT, Wd, dY) -> dict:
-    """Gradient of L = <y, dY> for the dense gated FFN (float64).
+def l1_coefficient(lam: float, T: int, per_token_mean: bool) -> float:
+    """Coefficient c of the activation penalty's gradient, dL1/dg = c * 1[g > 0].
 
-    ReLU'(g) is taken as 1[g > 0] (0 at g = 0).  Returns dX, dWgT, dWuT, dWd,
-    dbg and the forward dict under "fwd".
+    [IN] section "Минимальные изменения в рецепте обучения" adds a small L1
+    penalty on the activations (weight about 2e-5) to the training loss but
+    does not say how it is normalised.  Readings: L1 = lam * sum_{t,n} h[t,n]
+    (sum), or lam / T times that sum (mean over tokens).  h >= 0, so |h| = h
+    and its derivative is 1[g > 0].
+    """
+    return float(lam) / T if (per_token_mean and T > 0) else float(lam)
+
+
+def ffn_dense_bwd(x, WgT, bg, WuT, Wd, dY, l1: float = 0.0) -> dict:
+    """Gradient of L = <y, dY> + l1 * sum(h) for the dense gated FFN (float64).
+
+    ReLU'(g) is taken as 1[g > 0] (0 at g = 0); l1 is the coefficient c of
+    l1_coefficient.  Returns dX, dWgT, dWuT, dWd, dbg and the forward dict
+    under "fwd".
     """
     fw = ffn_dense_fwd(x, WgT, bg, WuT, Wd)
     x, WgT, WuT, Wd, dY = _f64(x), _f64(WgT), _f64(WuT), _f64(Wd), _f64(dY)
     dA = dY @ Wd.T
-    dG = np.where(fw["g"] > 0, dA * fw["u"], 0.0)
+    dG = np.where(fw["g"] > 0, dA * fw["u"] + l1, 0.0)
     dU = dA * fw["h"]
     return {
         "dX": dG @ WgT + dU @ WuT,
@@ -333,12 +346,12 @@ def classify_rows(cnt: np.ndarray, tau: int) -> np.ndarray:
 
 
 def hybrid_fwd_bwd(x, WgT, bg, WuT, Wd, dY, tau: int, R: int = 16, C: int = 64,
-                   chunk_rows: int = 256) -> dict:
+                   chunk_rows: int = 256, l1: float = 0.0) -> dict:
     """Hybrid forward + backward (float64).
 
     Dense rows run the plain definition on the gathered rows; sparse rows run
     per active pair: u = x_t.WuT[n], a = h*u, y_t += a*Wd[n], da = dY_t.Wd[n],
-    dg = da*u (g > 0 on every stored pair), du = da*h, dX_t += dg*WgT[n] +
+    dg = da*u + l1 (g > 0 on every stored pair), du = da*h, dX_t += dg*WgT[n] +
     du*WuT[n], dWd[n] += a*dY_t, dWgT[n] += dg*x_t, dWuT[n] += du*x_t,
     dbg[n] += dg.  Weight gradients are the sum of both branches.
     """
@@ -366,7 +379,7 @@ def hybrid_fwd_bwd(x, WgT, bg, WuT, Wd, dY, tau: int, R: int = 16, C: int = 64,
         aD = hD * uD
         y[D] = aD @ Wd
         dAD = dY[D] @ Wd.T
-        dGD = np.where(gD > 0, dAD * uD, 0.0)
+        dGD = np.where(gD > 0, dAD * uD + l1, 0.0)
         dUD = dAD * hD
         dX[D] = dGD @ WgT + dUD @ WuT
         dWd += aD.T @ dY[D]
@@ -384,7 +397,7 @@ def hybrid_fwd_bwd(x, WgT, bg, WuT, Wd, dY, tau: int, R: int = 16, C: int = 64,
             u = np.einsum("pk,pk->p", x[t], WuT[n])
             a = h * u
             da = np.einsum("pk,pk->p", dY[t], Wd[n])
-            dg = da * u
+            dg = da * u + l1
             du = da * h
             np.add.at(y, t, a[:, None] * Wd[n])
             np.add.at(dX, t, dg[:, None] * WgT[n] + du[:, None] * WuT[n])
@@ -398,7 +411,7 @@ def hybrid_fwd_bwd(x, WgT, bg, WuT, Wd, dY, tau: int, R: int = 16, C: int = 64,
 
 
 def hybrid_fwd_bwd_loops(x, WgT, bg, WuT, Wd, dY, tau: int, R: int = 16,
-                         C: int = 64) -> dict:
+                         C: int = 64, l1: float = 0.0) -> dict:
     """Hybrid forward + backward with scalar loops (tiny inputs)."""
     x, WgT, WuT, Wd, dY = _f64(x), _f64(WgT), _f64(WuT), _f64(Wd), _f64(dY)
     T, d = x.shape
@@ -425,7 +438,7 @@ def hybrid_fwd_bwd_loops(x, WgT, bg, WuT, Wd, dY, tau: int, R: int = 16,
             u = sum(x[t, k] * WuT[n, k] for k in range(d))
             a = h * u
             da = sum(dY[t, c] * Wd[n, c] for c in range(d))
-            dg = da * u if gv > 0 else 0.0
+            dg = da * u + l1 if gv > 0 else 0.0
             du = da * h
             for c in range(d):
                 out["y"][t, c] += a * Wd[n, c]
@@ -450,7 +463,7 @@ def ffn_fwd_rows(x, WgT, bg, WuT, Wd, rows) -> dict:
     return ffn_dense_fwd(np.asarray(x)[rows], WgT, bg, WuT, Wd)
 
 
-def ffn_bwd_sampled(x, WgT, bg, WuT, Wd, dY, token_rows, neuron_rows) -> dict:
+def ffn_bwd_sampled(x, WgT, bg, WuT, Wd, dY, token_rows, neuron_rows, l1: float = 0.0) -> dict:
     """dX on the listed tokens and dWgT/dWuT/dWd/dbg on the listed neurons.
 
     dX_t needs only token t; the weight gradient of neuron n needs only column n
@@ -465,7 +478,7 @@ def ffn_bwd_sampled(x, WgT, bg, WuT, Wd, dY, token_rows, neuron_rows) -> dict:
     gt = x[tr] @ WgT.T + b[None, :]
     ut = x[tr] @ WuT.T
     dAt = dY[tr] @ Wd.T
-    dGt = np.where(gt > 0, dAt * ut, 0.0)
+    dGt = np.where(gt > 0, dAt * ut + l1, 0.0)
     dUt = dAt * relu(gt)
     dX_rows = dGt @ WgT + dUt @ WuT
     y_rows = (relu(gt) * ut) @ Wd
@@ -474,7 +487,7 @@ def ffn_bwd_sampled(x, WgT, bg, WuT, Wd, dY, token_rows, neuron_rows) -> dict:
     un = x @ WuT[nr].T
     hn = relu(gn)
     dAn = dY @ Wd[nr].T
-    dGn = np.where(gn > 0, dAn * un, 0.0)
+    dGn = np.where(gn > 0, dAn * un + l1, 0.0)
     dUn = dAn * hn
     return {
         "y_rows": y_rows, "dX_rows": dX_rows,

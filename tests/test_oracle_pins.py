@@ -345,3 +345,83 @@ def test_relu_exact_positive_zero():
     h = O.relu(g)
     np.testing.assert_array_equal(h.view(np.uint64),
                                   np.array([0.0, 0.0, 0.0, 0.0, 2.5, 0.0, np.inf]).view(np.uint64))
+
+
+# ------------------------------------------------------------------ L1 activation penalty
+
+@pytest.mark.parametrize("seed", [20, 21])
+def test_l1_backward_central_differences(seed):
+    """With the penalty c * sum(h) added to L, every gradient matches central
+    differences of the penalised loss (h computed here from its definition)."""
+    x, WgT, b, WuT, Wd, dY = _fd_inputs(seed)
+    c = 0.37
+
+    def L(x_, WgT_, b_, WuT_, Wd_):
+        g = x_ @ WgT_.T + b_[None, :]
+        pen = c * np.maximum(g, 0.0).sum()
+        return float((O.ffn_dense_fwd(x_, WgT_, b_, WuT_, Wd_)["y"] * dY).sum()) + pen
+
+    bw = O.ffn_dense_bwd(x, WgT, b, WuT, Wd, dY, l1=c)
+    args = [x, WgT, b, WuT, Wd]
+    eps = 1e-6
+    for ai, name in enumerate(["dX", "dWgT", "dbg", "dWuT", "dWd"]):
+        num = np.zeros_like(args[ai])
+        it = np.nditer(args[ai], flags=["multi_index"])
+        for _ in it:
+            mi = it.multi_index
+            p = [a.copy() for a in args]
+            q = [a.copy() for a in args]
+            p[ai][mi] += eps
+            q[ai][mi] -= eps
+            num[mi] = (L(*p) - L(*q)) / (2 * eps)
+        err = np.abs(num - bw[name]).max() / max(1.0, np.abs(num).max())
+        assert err < 1e-7, (name, err)
+
+
+def test_l1_alone_closed_form():
+    """With dY = 0 only the penalty remains: dG is c on the active pairs, so
+    dX = c * (active-count-weighted rows of WgT), dWgT[n] = c * sum of the x rows
+    that activate n, dbg[n] = c * (tokens activating n), dWuT = dWd = 0."""
+    rng = np.random.default_rng(22)
+    T, d, f = 9, 5, 13
+    x = rng.standard_normal((T, d))
+    WgT, WuT, Wd = (rng.standard_normal((f, d)) for _ in range(3))
+    b = rng.standard_normal(f)
+    c = 1.5
+    bw = O.ffn_dense_bwd(x, WgT, b, WuT, Wd, np.zeros((T, d)), l1=c)
+    active = [[n for n in range(f) if float(np.dot(x[t], WgT[n]) + b[n]) > 0] for t in range(T)]
+    for t in range(T):
+        want = sum((c * WgT[n] for n in active[t]), np.zeros(d))
+        np.testing.assert_allclose(bw["dX"][t], want, rtol=1e-12, atol=1e-12)
+    for n in range(f):
+        toks = [t for t in range(T) if n in active[t]]
+        np.testing.assert_allclose(bw["dWgT"][n], sum((c * x[t] for t in toks), np.zeros(d)), rtol=1e-12, atol=1e-12)
+        assert bw["dbg"][n] == pytest.approx(c * len(toks), rel=1e-12)
+    assert not bw["dWuT"].any() and not bw["dWd"].any()
+
+
+def test_l1_hybrid_branch_agreement_and_loops():
+    rng = np.random.default_rng(23)
+    T, d, f = 40, 16, 130
+    x = rng.standard_normal((T, d))
+    x[::7] *= 4.0
+    WgT, WuT, Wd = (rng.standard_normal((f, d)) / 4 for _ in range(3))
+    b = rng.standard_normal(f) - 1.0
+    dY = rng.standard_normal((T, d))
+    c = O.l1_coefficient(0.8, T, per_token_mean=True)
+    assert c == pytest.approx(0.8 / T)
+    assert O.l1_coefficient(0.8, T, per_token_mean=False) == 0.8
+    ref = O.ffn_dense_bwd(x, WgT, b, WuT, Wd, dY, l1=c)
+    nnz = (x @ WgT.T + b > 0).sum(axis=1)
+    for tau in (-1, f, int(np.median(nnz))):
+        hy = O.hybrid_fwd_bwd(x, WgT, b, WuT, Wd, dY, tau, R=16, C=64, l1=c)
+        for k in ("dX", "dWgT", "dWuT", "dWd", "dbg"):
+            np.testing.assert_allclose(hy[k], ref[k], rtol=1e-12, atol=1e-12, err_msg=f"{tau} {k}")
+    a = O.hybrid_fwd_bwd(x[:6, :4], WgT[:10, :4], b[:10], WuT[:10, :4], Wd[:10, :4], dY[:6, :4], 4, R=2, C=4, l1=0.3)
+    l = O.hybrid_fwd_bwd_loops(x[:6, :4], WgT[:10, :4], b[:10], WuT[:10, :4], Wd[:10, :4], dY[:6, :4], 4, R=2, C=4,
+                               l1=0.3)
+    for k in ("dX", "dWgT", "dWuT", "dWd", "dbg"):
+        np.testing.assert_allclose(a[k], l[k], rtol=1e-12, atol=1e-12)
+    s = O.ffn_bwd_sampled(x, WgT, b, WuT, Wd, dY, np.array([0, 39]), np.array([5, 129]), l1=c)
+    np.testing.assert_allclose(s["dX_rows"], ref["dX"][[0, 39]], rtol=1e-12)
+    np.testing.assert_allclose(s["dbg_rows"], ref["dbg"][[5, 129]], rtol=1e-12)
