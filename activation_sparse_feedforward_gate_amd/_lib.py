@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.twell_ffn_bwd_workspace.restype = sz
         L.twell_ffn_bwd_hybrid.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_mat), i32,
                                            vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.twell_ffn_bwd_hybrid_l1.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_mat), i32,
+                                              ctypes.c_float, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.twell_ffn_fwd_ex.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_mat), i32, vp, sz, vp,
                                        vp, i32]
         L.twell_gate_pack.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, P(c_twell_mat), vp]
@@ -77,6 +79,7 @@ def lib() -> ctypes.CDLL:
         L.twell_last_error.argtypes = []
         L.twell_last_error.restype = ctypes.c_char_p
         for name in ("twell_pack", "twell_unpack", "twell_ffn_fwd", "twell_ffn_fwd_ex", "twell_ffn_bwd_hybrid",
+                     "twell_ffn_bwd_hybrid_l1",
                      "twell_ffn_dense_fwd", "twell_ffn_dense_bwd",
                      "twell_gate_pack",
                      "twell_sparse_up", "twell_sparse_down"):
@@ -212,6 +215,18 @@ def twell_ffn_bwd_hybrid(shape, x, WgT, bg, WuT, Wd, dY, saved_h: TwellMat, dens
                                       _ptr(dWuT), _ptr(dWd), _ptr(dbg), _ptr(n_dense_rows), _ptr(ws),
                                       ws.numel() * ws.element_size() if ws is not None else 0,
                                       _stream(stream)))
+
+
+def twell_ffn_bwd_hybrid_l1(shape, x, WgT, bg, WuT, Wd, dY, saved_h: TwellMat, dense_row_threshold: int,
+                            l1_lambda: float, l1_per_token_mean: bool, dX, dWgT, dWuT, dWd, dbg, n_dense_rows, ws,
+                            stream=None) -> None:
+    hm = saved_h.c()
+    _check(lib().twell_ffn_bwd_hybrid_l1(ctypes.byref(shape), _ptr(x), _ptr(WgT), _ptr(bg), _ptr(WuT), _ptr(Wd),
+                                         _ptr(dY), ctypes.byref(hm), int(dense_row_threshold), float(l1_lambda),
+                                         int(bool(l1_per_token_mean)), _ptr(dX), _ptr(dWgT), _ptr(dWuT), _ptr(dWd),
+                                         _ptr(dbg), _ptr(n_dense_rows), _ptr(ws),
+                                         ws.numel() * ws.element_size() if ws is not None else 0,
+                                         _stream(stream)))
 
 
 def twell_ffn_fwd_ex(shape, x, WgT, bg, WuT, Wd, y, saved_h: Optional[TwellMat], dense_row_threshold: int,

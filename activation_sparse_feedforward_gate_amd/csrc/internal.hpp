@@ -43,11 +43,12 @@ hipError_t launch_spmm_down(int in_dt, int out_dt, const float* aval, const void
                             hipStream_t s);
 
 // Backward SDDMM on the pattern of h (rows with skip[t] != 0 untouched):
-//   u = x_t.WuT[n], da = dY_t.Wd[n];  a = h*u, dg = da*u, du = da*h
-// written at the TwELL slot positions of h into aval, dgval, duval.
+//   u = x_t.WuT[n], da = dY_t.Wd[n];  a = h*u, dg = da*u + l1, du = da*h
+// written at the TwELL slot positions of h into aval, dgval, duval (l1: the
+// activation penalty's gradient coefficient, added on every stored pair).
 hipError_t launch_sddmm_bwd(int in_dt, const void* x, const void* dY, const void* WuT, const void* Wd, int T,
                             int d, int F, const TwellView& h, float* aval, float* dgval, float* duval,
-                            const uint8_t* skip, hipStream_t s);
+                            const uint8_t* skip, hipStream_t s, float l1 = 0.f);
 
 // Backward SpMM: dX_t = sum over stored n of dg*WgT[n] + du*WuT[n] (fp32),
 // rows with skip[t] != 0 not written.
@@ -73,7 +74,7 @@ hipError_t launch_dense_rows_fwd(int in_dt, const void* x, const void* WgT, cons
 hipError_t launch_dense_rows_bwd(int in_dt, const void* x, const void* WgT, const void* bg, const void* WuT,
                                  const void* Wd, const void* dY, int T, int d, int F, const int* rows,
                                  const int* n_rows, float* buf3, float* dbg_part, float* dX, float* dWgT,
-                                 float* dWuT, float* dWd, float* dbg, hipStream_t s);
+                                 float* dWuT, float* dWd, float* dbg, hipStream_t s, float l1 = 0.f);
 
 // Sparse-branch weight gradients, ADDED to dWgT, dWuT, dWd (and dbg): a
 // column-major index of the stored pairs of rows with skip[t] == 0 is built
@@ -89,7 +90,7 @@ hipError_t launch_sparse_wgrad(int in_dt, const void* x, const void* dY, int T, 
 // gate: null, or a device flag; the kernels do nothing unless it is non-zero.
 hipError_t launch_up_bf16(const void* x, const void* dY, const void* WuT, const void* Wd, int T, int d, int F,
                           const TwellView& h, float* aval, float* dgval, float* duval, const uint8_t* skip,
-                          hipStream_t s, const int* gate = nullptr);
+                          hipStream_t s, const int* gate = nullptr, float l1 = 0.f);
 // y = v0 . W (+ v1 . W2 when v1 != null) over the stored pairs of pat.
 hipError_t launch_down_bf16(const float* v0, const float* v1, const void* W, const void* W2, int T, int d, int F,
                             const TwellView& pat, void* y, int out_dt, const uint8_t* skip, hipStream_t s,

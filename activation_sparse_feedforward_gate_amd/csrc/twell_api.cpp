@@ -307,7 +307,20 @@ twell_status twell_ffn_bwd_hybrid(const twell_ffn_shape* sh, const void* x, cons
                                   int32_t dense_row_threshold, float* dX, float* dWgT, float* dWuT, float* dWd,
                                   float* dbg, int32_t* n_dense_rows, void* ws, size_t ws_bytes,
                                   hipStream_t stream) {
+  return twell_ffn_bwd_hybrid_l1(sh, x, WgT, bg, WuT, Wd, dY, saved_h, dense_row_threshold, 0.f, 0, dX, dWgT, dWuT,
+                                 dWd, dbg, n_dense_rows, ws, ws_bytes, stream);
+}
+
+twell_status twell_ffn_bwd_hybrid_l1(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
+                                     const void* WuT, const void* Wd, const void* dY, const twell_mat* saved_h,
+                                     int32_t dense_row_threshold, float l1_lambda, int32_t l1_per_token_mean,
+                                     float* dX, float* dWgT, float* dWuT, float* dWd, float* dbg,
+                                     int32_t* n_dense_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
   twell_status st = check_shape(sh);
+  if (!(l1_lambda >= 0.f) || l1_lambda > 3.0e38f)
+    return fail(TWELL_EINVAL, "l1_lambda must be finite and >= 0 (got %g)", (double)l1_lambda);
+  if (l1_per_token_mean != 0 && l1_per_token_mean != 1)
+    return fail(TWELL_EINVAL, "l1_per_token_mean must be 0 or 1");
   if (st) return st;
   if (!WgT || !WuT || !Wd || !dWgT || !dWuT || !dWd) return fail(TWELL_EINVAL, "NULL weight or gradient argument");
   if (sh->T > 0 && (!x || !dY || !dX)) return fail(TWELL_EINVAL, "NULL tensor argument");
@@ -329,12 +342,15 @@ twell_status twell_ffn_bwd_hybrid(const twell_ffn_shape* sh, const void* x, cons
   const int in_dt = sh->in_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
   const TwellView h = view_of(saved_h);
   const int T = sh->T, d = sh->d, F = sh->F;
+  // gradient coefficient of the penalty: lambda for a sum over the
+  // activations, lambda / T for a mean over tokens
+  const float l1 = (l1_per_token_mean && T > 0) ? l1_lambda / (float)T : l1_lambda;
   hipError_t e = launch_classify(h, dense_row_threshold, w.flag, w.list, w.nD, n_dense_rows, stream);
   if (e != hipSuccess) return hip_status(e, "row classification");
   e = launch_dense_rows_bwd(in_dt, x, WgT, bg, WuT, Wd, dY, T, d, F, w.list, w.nD, w.buf3, w.dbg_part, dX, dWgT,
-                            dWuT, dWd, dbg, stream);
+                            dWuT, dWd, dbg, stream, l1);
   if (e != hipSuccess) return hip_status(e, "dense-row backward");
-  e = launch_sddmm_bwd(in_dt, x, dY, WuT, Wd, T, d, F, h, w.aval, w.dgval, w.duval, w.flag, stream);
+  e = launch_sddmm_bwd(in_dt, x, dY, WuT, Wd, T, d, F, h, w.aval, w.dgval, w.duval, w.flag, stream, l1);
   if (e != hipSuccess) return hip_status(e, "sparse backward SDDMM");
   e = launch_spmm_dx(in_dt, w.dgval, w.duval, WgT, WuT, T, d, F, h, dX, w.flag, stream);
   if (e != hipSuccess) return hip_status(e, "sparse backward dX");

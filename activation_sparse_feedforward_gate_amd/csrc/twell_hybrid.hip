@@ -10,7 +10,8 @@
 //
 // Dense rows D (gathered, n_D of them, order of increasing token index):
 //   forward :  g = x_D.WgT^T + b, u = x_D.WuT^T, A = ReLU(g)*u,  y_D = A.Wd
-//   backward:  dA = dY_D.Wd^T, dG = dA*u*1[g>0], dU = dA*ReLU(g)
+//   backward:  dA = dY_D.Wd^T, dG = (dA*u + l1)*1[g>0], dU = dA*ReLU(g)
+//              (l1: gradient coefficient of an L1 penalty on h, else 0)
 //              dX_D = dG.WgT + dU.WuT
 //              dWgT = dG^T.x_D, dWuT = dU^T.x_D, dWd = A^T.dY_D, dbg = sum dG
 // The fp32 intermediates (A, dG, dU) enter the bf16 matrix cores as a hi + lo
@@ -96,6 +97,7 @@ struct DenseRowsArgs {
   float* dWd;
   float* dbg_part;    // [ceil(T/64)][F]
   float* dbg;
+  float l1;           // backward: added to dG where g > 0 (activation penalty)
 };
 
 template <bool BF16IN>
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(Cfg2::NTH) void dense_rows_act_kernel(DenseRowsArgs
           float* row = a.buf + (int64_t)r * ldb;
           if constexpr (BWD) {
             const float da = gd.acc[0][i][j][e];
-            row[col] = gv > 0.f ? da * u : 0.f;
+            row[col] = gv > 0.f ? da * u + a.l1 : 0.f;
             row[a.F + col] = da * h;
             row[2 * a.F + col] = h * u;
           } else {
@@ -326,8 +328,9 @@ hipError_t launch_dense_rows_fwd(int in_dt, const void* x, const void* WgT, cons
 hipError_t launch_dense_rows_bwd(int in_dt, const void* x, const void* WgT, const void* bg, const void* WuT,
                                  const void* Wd, const void* dY, int T, int d, int F, const int* rows,
                                  const int* n_rows, float* buf3, float* dbg_part, float* dX, float* dWgT,
-                                 float* dWuT, float* dWd, float* dbg, hipStream_t s) {
+                                 float* dWuT, float* dWd, float* dbg, hipStream_t s, float l1) {
   DenseRowsArgs a{};
+  a.l1 = l1;
   a.x = x; a.WgT = WgT; a.bg = bg; a.WuT = WuT; a.Wd = Wd; a.dY = dY; a.T = T; a.d = d; a.F = F;
   a.rows = rows; a.n_rows = n_rows; a.buf = buf3; a.dX = dX; a.dWgT = dWgT; a.dWuT = dWuT; a.dWd = dWd;
   a.dbg_part = dbg_part; a.dbg = dbg;

@@ -44,6 +44,7 @@ struct SparseArgs {
   void* y;                // down output [T][d]
   int out_bf16;
   int nslices;
+  float l1;               // backward up: added to dg on every stored pair (activation penalty)
 };
 
 constexpr int SP_WPB = 4;        // waves (token groups) per workgroup
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(256) void sddmm_up_kernel(SparseArgs a) {
             const float h = a.hval[off];
             a.aval[off] = h * acc[b][i];
             if constexpr (BWD) {
-              a.dgval[off] = acc2[b][i] * acc[b][i];
+              a.dgval[off] = acc2[b][i] * acc[b][i] + a.l1;
               a.duval[off] = acc2[b][i] * h;
             }
           }
@@ -320,11 +321,12 @@ hipError_t launch_sddmm_up(int in_dt, const void* x, const void* WuT, int T, int
 
 hipError_t launch_sddmm_bwd(int in_dt, const void* x, const void* dY, const void* WuT, const void* Wd, int T,
                             int d, int F, const TwellView& h, float* aval, float* dgval, float* duval,
-                            const uint8_t* skip, hipStream_t s) {
+                            const uint8_t* skip, hipStream_t s, float l1) {
   SparseArgs a{};
+  a.l1 = l1;
   a.x = x; a.x2 = dY; a.W = WuT; a.W2 = Wd; a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
   a.mask = h.mask; a.hval = (const float*)h.val; a.aval = aval; a.dgval = dgval; a.duval = duval; a.skip = skip;
-  if (in_dt == DT_BF16) return launch_up_bf16(x, dY, WuT, Wd, T, d, F, h, aval, dgval, duval, skip, s);
+  if (in_dt == DT_BF16) return launch_up_bf16(x, dY, WuT, Wd, T, d, F, h, aval, dgval, duval, skip, s, nullptr, l1);
   a.nslices = choose_slices(a.NT, UP_MAXT);
   if (a.NR == 0) return hipSuccess;
   const int grid = ((a.NR + SP_WPB - 1) / SP_WPB) * a.nslices;

@@ -69,6 +69,7 @@ struct SpArgs {
   int S;                // slices
   int ngroups;          // ceil(NR / GW)
   const int* gate;      // null, or a device flag: the kernel runs only if it is non-zero
+  float l1;             // up backward: added to dg on every stored pair (activation penalty)
 };
 
 // Workgroup -> (token group g, slice s).  With S a multiple of 8, slice s runs
@@ -287,7 +288,7 @@ __device__ __forceinline__ void up_pass(const SpArgs& a, const UnionLds& L, char
           a.v0[off] = h * u;
           if constexpr (NP == 2) {
             const float da = acc2[b][i];
-            a.v1[off] = da * u;
+            a.v1[off] = da * u + a.l1;
             a.v2[off] = da * h;
           }
         }
@@ -494,13 +495,14 @@ int pick_slices(int units, int max_units, double bytes_per_unit, int ngroups) {
 
 hipError_t launch_up_bf16(const void* x, const void* dY, const void* WuT, const void* Wd, int T, int d, int F,
                           const TwellView& h, float* aval, float* dgval, float* duval, const uint8_t* skip,
-                          hipStream_t s, const int* gate) {
+                          hipStream_t s, const int* gate, float l1) {
   if ((int64_t)F * d >= ((int64_t)1 << 32)) return hipErrorInvalidValue;   // 32-bit weight offsets
   SpArgs a{};
   a.x = (const uint16_t*)x; a.x2 = (const uint16_t*)dY; a.W = (const uint16_t*)WuT; a.W2 = (const uint16_t*)Wd;
   a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
   a.mask = h.mask; a.skip = skip; a.hval = (const float*)h.val; a.v0 = aval; a.v1 = dgval; a.v2 = duval;
   a.gate = gate;
+  a.l1 = l1;
   if (a.NR == 0) return hipSuccess;
   a.ngroups = (a.NR + GW - 1) / GW;
   const int NP = dY ? 2 : 1;

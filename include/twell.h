@@ -135,7 +135,7 @@ size_t twell_ffn_fwd_workspace(const twell_ffn_shape *sh, int32_t training);
  *   ws, ws_bytes  workspace of at least twell_ffn_fwd_workspace(sh, thr >= 0)
  * Stored pairs are exactly the (t, n) with g > 0 in fp32; accumulation is
  * fp32.  bf16 inputs: the up- and down-projections run as MFMA GEMMs over each
- * 256-token block's union of active neurons, with a = h*u passed between them
+ * 128-token block's union of active neurons, with a = h*u passed between them
  * in fp16 (if any |a| exceeds the fp16 range the layer is recomputed with a in
  * fp32 automatically); fp32 inputs keep h, u and a in fp32 throughout.
  * Matrices must hold fewer than 2^32 elements each.
@@ -178,6 +178,26 @@ twell_status twell_ffn_bwd_hybrid(const twell_ffn_shape *sh, const void *x, cons
                                   int32_t dense_row_threshold, float *dX, float *dWgT, float *dWuT, float *dWd,
                                   float *dbg, int32_t *n_dense_rows, void *ws, size_t ws_bytes,
                                   hipStream_t stream);
+
+/*
+ * twell_ffn_bwd_hybrid_l1: twell_ffn_bwd_hybrid for the loss with the
+ * activation penalty of the training recipe (intellectnews.ru TwELL article,
+ * section "Минимальные изменения в рецепте обучения": a small L1 term on the
+ * FFN activations, weight about 2e-5):
+ *   L = <y, dY> + lambda * sum_{t,n} h[t,n]          (l1_per_token_mean = 0)
+ *   L = <y, dY> + lambda / T * sum_{t,n} h[t,n]      (l1_per_token_mean = 1)
+ * The pages do not fix the normalisation; both are offered.  h >= 0, so the
+ * term adds c * 1[g > 0] to dG (c = lambda or lambda / T) on both branches,
+ * and through dG to dX, dWgT and dbg; dWuT and dWd are unchanged.
+ * lambda = 0 gives exactly twell_ffn_bwd_hybrid.  Other arguments, outputs
+ * and errors as for twell_ffn_bwd_hybrid; EINVAL also for a negative or
+ * non-finite lambda or a mean flag other than 0 or 1.
+ */
+twell_status twell_ffn_bwd_hybrid_l1(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
+                                     const void *WuT, const void *Wd, const void *dY, const twell_mat *saved_h,
+                                     int32_t dense_row_threshold, float l1_lambda, int32_t l1_per_token_mean,
+                                     float *dX, float *dWgT, float *dWuT, float *dWd, float *dbg,
+                                     int32_t *n_dense_rows, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * twell_ffn_fwd_ex: twell_ffn_fwd that also records up to n_events caller-

@@ -39,8 +39,10 @@ def tw():
     return _tw
 
 
-def run_train(torch, tw, w, tau, with_dbg=True, bias=True):
-    """Hybrid forward then backward on the GPU; returns host arrays."""
+def run_train(torch, tw, w, tau, with_dbg=True, bias=True, l1=None):
+    """Hybrid forward then backward on the GPU; returns host arrays.  l1:
+    None, or (lambda, per_token_mean) for the backward with the activation
+    penalty."""
     dt = w.cfg.dtype
     in_dt = tw.TWELL_BF16 if dt == "bf16" else tw.TWELL_F32
     x, WgT, WuT, Wd, dY = (to_dev(a, dt) for a in (w.x, w.WgT, w.WuT, w.Wd, w.dY))
@@ -56,7 +58,11 @@ def run_train(torch, tw, w, tau, with_dbg=True, bias=True):
     dbg = torch.full((F,), float("nan"), dtype=torch.float32, device="cuda") if with_dbg else None
     nD = torch.full((1,), -1, dtype=torch.int32, device="cuda")
     wsb = torch.empty(max(1, tw.twell_ffn_bwd_workspace(shape, tau)), dtype=torch.uint8, device="cuda")
-    tw.twell_ffn_bwd_hybrid(shape, x, WgT, bg, WuT, Wd, dY, h, tau, dX, dW[0], dW[1], dW[2], dbg, nD, wsb)
+    if l1 is None:
+        tw.twell_ffn_bwd_hybrid(shape, x, WgT, bg, WuT, Wd, dY, h, tau, dX, dW[0], dW[1], dW[2], dbg, nD, wsb)
+    else:
+        tw.twell_ffn_bwd_hybrid_l1(shape, x, WgT, bg, WuT, Wd, dY, h, tau, l1[0], l1[1], dX, dW[0], dW[1], dW[2],
+                                   dbg, nD, wsb)
     torch.cuda.synchronize()
     out = {"y": y.cpu().numpy(), "dX": dX.cpu().numpy(), "dWgT": dW[0].cpu().numpy(),
            "dWuT": dW[1].cpu().numpy(), "dWd": dW[2].cpu().numpy(), "nD": int(nD.item()),
@@ -66,10 +72,10 @@ def run_train(torch, tw, w, tau, with_dbg=True, bias=True):
     return out
 
 
-def check_full(w, got, tau, bias=True):
+def check_full(w, got, tau, bias=True, l1c=0.0):
     tol = TOL[w.cfg.dtype]
     bg = w.bg if bias else None
-    ref = O.ffn_dense_bwd(w.x, w.WgT, bg, w.WuT, w.Wd, w.dY)
+    ref = O.ffn_dense_bwd(w.x, w.WgT, bg, w.WuT, w.Wd, w.dY, l1=l1c)
     dense = got["h"]["cnt"].sum(axis=1) > tau
     assert got["nD"] == int(dense.sum()), (got["nD"], int(dense.sum()))
     log(f"   dense rows {got['nD']} of {w.T}")
@@ -171,3 +177,26 @@ def test_hybrid_full_size_sampled(torch, tw):
         assert e <= tol, (k, e)
     for k in ("dX", "dWgT", "dWuT", "dWd", "dbg"):
         assert np.isfinite(got[k]).all(), k
+
+
+@pytest.mark.parametrize("name,kw,mean", [("hybrid", dict(T=520, d=256, f=1280), False),
+                                          ("hybrid", dict(T=520, d=256, f=1280), True),
+                                          ("tiny_f32", dict(grad=True), False)],
+                         ids=["hybrid-sum", "hybrid-mean", "tiny_f32-sum"])
+def test_hybrid_l1_penalty(torch, tw, name, kw, mean):
+    """Backward with the L1 activation penalty on both branches.  The
+    coefficient is large enough that leaving the term out would fail the
+    tolerance many times over."""
+    w = make_workload(name, **kw)
+    c = 0.05
+    lam = c * w.T if mean else c
+    assert O.l1_coefficient(lam, w.T, mean) == pytest.approx(c)
+    log(f"[hybrid] L1 {'mean' if mean else 'sum'} lambda={lam} {name} T={w.T} tau={w.tau}")
+    ref0 = O.ffn_dense_bwd(w.x, w.WgT, w.bg, w.WuT, w.Wd, w.dY)
+    ref1 = O.ffn_dense_bwd(w.x, w.WgT, w.bg, w.WuT, w.Wd, w.dY, l1=O.l1_coefficient(lam, w.T, mean))
+    for k in ("dX", "dWgT", "dbg"):
+        assert rel_fro(ref0[k], ref1[k]) > 20 * TOL[w.cfg.dtype], k          # the term is visible
+    got = run_train(torch, tw, w, w.tau, l1=(lam, mean))
+    check_full(w, got, w.tau, l1c=O.l1_coefficient(lam, w.T, mean))
+    if name == "hybrid":
+        assert 0 < got["nD"] < w.T                                             # both branches ran

@@ -139,6 +139,24 @@ def test_bwd_argument_errors():
     assert call(shape=tw.ffn_shape(64, 100, 512, tw.TWELL_BF16, tw.TWELL_F32)) == tw.TWELL_EUNSUPPORTED
 
 
+def test_bwd_l1_argument_errors():
+    """The penalty's coefficient and normalisation flag are checked before any
+    launch (so these calls need no GPU)."""
+    L = tw.lib()
+    sh = tw.ffn_shape(64, 128, 512, tw.TWELL_BF16, tw.TWELL_F32)
+    h = tw.c_twell_mat(64, 512, 16, 64, tw.TWELL_F32, 16, 16, 16, 16, 16)
+    need = tw.twell_ffn_bwd_workspace(sh, 51)
+
+    def call(lam, mean):
+        return L.twell_ffn_bwd_hybrid_l1(ctypes.byref(sh), 16, 16, None, 16, 16, 16, ctypes.byref(h), 51,
+                                         ctypes.c_float(lam), mean, 16, 16, 16, 16, None, None, 4096, need, None)
+    assert call(-1e-5, 0) == tw.TWELL_EINVAL
+    assert call(float("nan"), 0) == tw.TWELL_EINVAL
+    assert call(float("inf"), 1) == tw.TWELL_EINVAL
+    assert call(2e-5, 2) == tw.TWELL_EINVAL
+    assert b"l1" in L.twell_last_error()
+
+
 def test_hybrid_fwd_needs_saved_h():
     sh = tw.ffn_shape(64, 128, 512, tw.TWELL_BF16, tw.TWELL_F32)
     need = tw.twell_ffn_fwd_workspace(sh, True)
