@@ -8,6 +8,15 @@ namespace twell {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
 
+// Compute units of the current device (persistent grids are sized by it).
+inline int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    return 256;
+  return n;
+}
+
 // Device view of a TwELL matrix (all pointers device memory).
 struct TwellView {
   int T, F, NT, NR;

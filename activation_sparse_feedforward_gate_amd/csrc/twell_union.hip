@@ -20,6 +20,8 @@
 // zeros.  a is fp16 for the down GEMM (relative rounding 2^-11, within the
 // 1e-3 output budget); if any |a| exceeds the fp16 range a device flag makes
 // the down GEMM stand down and the TwELL-pattern kernels recompute the layer.
+#include <algorithm>
+
 #include "gemm_core.hpp"
 #include "internal.hpp"
 
@@ -114,29 +116,13 @@ __global__ __launch_bounds__(256) void union_list_kernel(UnionArgs a, const uint
   if (tid == 0) a.ucount[b] = base;
 }
 
-// Up-projection over the union.  Workgroups of one row block are consecutive
-// so they share the block's x rows in L2.
+constexpr int POSCAP = 12288;         // neuron span of a position tile covered by the LDS position map
+
+// Up-projection over the union, one (row block b, position tile pt) tile.
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
+__device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt, char* st0, char* st1,
+                                              int16_t* posmap) {
   static_assert(Cfg::BM == UB, "one row block per M tile");
-  __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
-  const int npt = (a.F + Cfg::BN - 1) / Cfg::BN;
-  const int nblk = (a.T + UB - 1) / UB;
-  int b, pt;
-  {
-    // XCD-aware order: workgroup ids go round-robin over the 8 XCDs; XCD x
-    // takes the row blocks b = x (mod 8) and sweeps them position tile by
-    // position tile, so the WuT rows of neighbouring blocks' unions (largely
-    // the same neurons) are reused from that XCD's L2.
-    const int id = blockIdx.x;
-    const int x = id & 7, k = id >> 3;
-    const int nbx = (nblk - x + 7) / 8;                // row blocks on this XCD
-    if (nbx == 0) return;
-    pt = k / nbx;
-    b = x + 8 * (k - pt * nbx);
-    if (pt >= npt) return;
-  }
   const int nb = a.ucount[b];
   const int p0 = pt * Cfg::BN;
   if (p0 >= nb) return;
@@ -153,8 +139,6 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   // see the epilogue below
   static_assert(Cfg::BN == 256 && Cfg::NW == 8 && Cfg::BM % 128 == 0 && Cfg::BM <= 256, "epilogue layout");
   static_assert(Cfg::STAGE >= 128 * 2 * Cfg::BM, "h tile: 128 positions x BM rows of fp16 per stage buffer");
-  constexpr int POSCAP = 12288;
-  __shared__ int16_t posmap[POSCAP];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int pl = min(p0 + Cfg::BN, nb) - 1;
@@ -314,6 +298,31 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   if (__builtin_amdgcn_ballot_w64(over) != 0ull && lane == 0) atomicOr(a.flag, 1);
 }
 
+// Persistent workgroups (one per CU: the LDS holds one) walk the tiles, so a
+// tile's output stores drain while the next tile's first loads are in
+// flight.  XCD-aware order: workgroup ids go round-robin over the 8 XCDs; the
+// workgroups of XCD x take the row blocks b = x (mod 8) and sweep them
+// position tile by position tile, so the WuT rows of neighbouring blocks'
+// unions (largely the same neurons) are reused from that XCD's L2 (measured
+// faster than keeping each block's x rows in L2 instead).
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
+  __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
+  __shared__ int16_t posmap[POSCAP];
+  const int npt = (a.F + Cfg::BN - 1) / Cfg::BN;
+  const int nblk = (a.T + UB - 1) / UB;
+  const int x = blockIdx.x & 7;
+  const int nbx = (nblk - x + 7) / 8;                  // row blocks on this XCD
+  const int ntile = nbx * npt;
+  for (int k = blockIdx.x >> 3; k < ntile; k += gridDim.x >> 3) {
+    const int pt = k / nbx;
+    const int b = x + 8 * (k - pt * nbx);
+    up_union_tile<Cfg>(a, b, pt, st0, st1, posmap);
+    __syncthreads();                                   // stage buffers and position map free again
+  }
+}
+
 // fp16 copy of Wd for the down GEMM (exact for every bf16 value inside the
 // fp16 range); a value beyond that range raises the flag, and the layer then
 // takes the fp32 path.
@@ -340,13 +349,8 @@ __global__ __launch_bounds__(256) void wd_to_f16_kernel(const uint16_t* Wd, _Flo
 // runs over the block's n_b positions; A = adense holds zeros in the
 // positions past n_b of the last K tile.
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::NTH) void down_union_kernel(UnionArgs a) {
+__device__ __forceinline__ void down_union_tile(const UnionArgs& a, int b, int ct, char* st0, char* st1) {
   static_assert(Cfg::BM == UB, "one row block per M tile");
-  __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
-  if (*a.flag) return;                              // fp16 overflow: the fallback path writes y
-  const int nct = a.d / Cfg::BN;
-  const int b = blockIdx.x / nct, ct = blockIdx.x - b * nct;
   const int nb = a.ucount[b];
   const int m0 = b * UB, n0 = ct * Cfg::BN;
   typedef DmaTile<Cfg> Tile;
@@ -368,6 +372,26 @@ __global__ __launch_bounds__(Cfg::NTH) void down_union_kernel(UnionArgs a) {
           else ((float*)a.y)[(int64_t)t * a.d + col] = v;
         }
       }
+  }
+}
+
+// Persistent workgroups walk the (row block, column tile) tiles; the
+// workgroups of XCD x take the row blocks b = x (mod 8), all column tiles of
+// a block together, so the block's adense rows are reused from that XCD's L2.
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTH) void down_union_kernel(UnionArgs a) {
+  __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
+  if (*a.flag) return;                              // fp16 overflow: the fallback path writes y
+  const int nct = a.d / Cfg::BN;
+  const int nblk = (a.T + UB - 1) / UB;
+  const int x = blockIdx.x & 7;
+  const int nbx = (nblk - x + 7) / 8;
+  const int ntile = nbx * nct;
+  for (int k = blockIdx.x >> 3; k < ntile; k += gridDim.x >> 3) {
+    const int bi = k / nct;
+    down_union_tile<Cfg>(a, x + 8 * bi, k - bi * nct, st0, st1);
+    __syncthreads();
   }
 }
 
@@ -455,15 +479,21 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
   if (ev_lists) (void)hipEventRecord(ev_lists, s);
   const int npt = (F + UpUnionCfg::BN - 1) / UpUnionCfg::BN;
   const int nbx_max = (nblk + 7) / 8;
-  hipLaunchKernelGGL((up_union_kernel<UpUnionCfg>), dim3(8 * nbx_max * npt), dim3(UpUnionCfg::NTH), 0, s, a);
+  // persistent grids: one workgroup per CU (multiples of 8, one row of XCDs),
+  // never more than the tiles of the busiest XCD need
+  const int cus = device_cus();
+  auto grid_for = [&](int tiles_per_xcd) { return (unsigned)(8 * std::max(1, std::min(cus / 8, tiles_per_xcd))); };
+  hipLaunchKernelGGL((up_union_kernel<UpUnionCfg>), dim3(grid_for(nbx_max * npt)), dim3(UpUnionCfg::NTH), 0, s, a);
   if (ev_up) (void)hipEventRecord(ev_up, s);
   if (d % 256 == 0)
-    hipLaunchKernelGGL((down_union_kernel<DownUnionCfg>), dim3(nblk * (d / 256)), dim3(DownUnionCfg::NTH), 0, s, a);
+    hipLaunchKernelGGL((down_union_kernel<DownUnionCfg>), dim3(grid_for(nbx_max * (d / 256))), dim3(DownUnionCfg::NTH),
+                       0, s, a);
   else if (d % 128 == 0)
-    hipLaunchKernelGGL((down_union_kernel<DownUnionCfg128>), dim3(nblk * (d / 128)), dim3(DownUnionCfg128::NTH), 0, s,
-                       a);
+    hipLaunchKernelGGL((down_union_kernel<DownUnionCfg128>), dim3(grid_for(nbx_max * (d / 128))),
+                       dim3(DownUnionCfg128::NTH), 0, s, a);
   else
-    hipLaunchKernelGGL((down_union_kernel<DownUnionCfg64>), dim3(nblk * (d / 64)), dim3(DownUnionCfg64::NTH), 0, s, a);
+    hipLaunchKernelGGL((down_union_kernel<DownUnionCfg64>), dim3(grid_for(nbx_max * (d / 64))),
+                       dim3(DownUnionCfg64::NTH), 0, s, a);
   return hipGetLastError();
 }
 
