@@ -48,6 +48,7 @@ __all__ = [
     "TwellMat", "twell_pack", "twell_pack_loops", "twell_unpack", "twell_entries",
     "ffn_sparse_fwd", "ffn_sparse_fwd_loops", "classify_rows",
     "hybrid_fwd_bwd", "hybrid_fwd_bwd_loops", "ffn_fwd_rows", "ffn_bwd_sampled",
+    "relu_ffn_dense_fwd", "relu_ffn_sparse_fwd",
 ]
 
 
@@ -496,3 +497,41 @@ def ffn_bwd_sampled(x, WgT, bg, WuT, Wd, dY, token_rows, neuron_rows, l1: float 
         "dWuT_rows": dUn.T @ x,
         "dbg_rows": dGn.sum(axis=0),
     }
+
+
+# --------------------------------------------------------------------------
+# Non-gated ReLU FFN
+# --------------------------------------------------------------------------
+
+def relu_ffn_dense_fwd(x, W1T, b1, W2) -> dict:
+    """Non-gated ReLU FFN in float64: y = ReLU(x.W1 + b1) . W2.
+
+    [IN] section "Ограничения и открытые вопросы": the method targets gated
+    FFNs; a plain ReLU FFN has the same exact zeros in ReLU(x.W1 + b1) but no
+    up-projection to skip, so less to gain.  W1T and W2 are [f, d]
+    (neuron-major, as for the gated layer).  Returns g, h and y.
+    """
+    x, W1T, W2 = _f64(x), _f64(W1T), _f64(W2)
+    f = W1T.shape[0]
+    b = np.zeros(f) if b1 is None else _f64(b1)
+    g = x @ W1T.T + b[None, :]
+    h = relu(g)
+    return {"g": g, "h": h, "y": h @ W2}
+
+
+def relu_ffn_sparse_fwd(x, W1T, b1, W2, R: int = 16, C: int = 64) -> dict:
+    """The same layer through TwELL: pack ReLU(g), then y_t = sum over the
+    stored (t, n) of h * W2[n], neurons ascending per token."""
+    x, W1T, W2 = _f64(x), _f64(W1T), _f64(W2)
+    T, d = x.shape
+    f = W1T.shape[0]
+    b = np.zeros(f) if b1 is None else _f64(b1)
+    g = x @ W1T.T + b[None, :]
+    m = twell_pack(g, R, C)
+    t, n, h = twell_entries(m)
+    y = np.zeros((T, W2.shape[1]))
+    for tt in np.unique(t):
+        sel = t == tt
+        order = np.argsort(n[sel], kind="stable")
+        y[tt] = (h[sel][order][:, None] * W2[n[sel][order]]).sum(axis=0)
+    return {"y": y, "twell": m}

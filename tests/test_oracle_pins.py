@@ -425,3 +425,39 @@ def test_l1_hybrid_branch_agreement_and_loops():
     s = O.ffn_bwd_sampled(x, WgT, b, WuT, Wd, dY, np.array([0, 39]), np.array([5, 129]), l1=c)
     np.testing.assert_allclose(s["dX_rows"], ref["dX"][[0, 39]], rtol=1e-12)
     np.testing.assert_allclose(s["dbg_rows"], ref["dbg"][[5, 129]], rtol=1e-12)
+
+
+# ------------------------------------------------------------------ non-gated ReLU FFN
+
+def test_relu_ffn_is_gated_ffn_with_unit_up_projection():
+    """A gated FFN whose up-projection is 1 for every token (a constant input
+    column and an up weight that reads only it) is the non-gated ReLU FFN."""
+    rng = np.random.default_rng(30)
+    T, d, f = 37, 12, 150
+    x = rng.standard_normal((T, d))
+    W1T, W2 = rng.standard_normal((f, d)), rng.standard_normal((f, d))
+    b1 = rng.standard_normal(f) - 0.5
+    xa = np.concatenate([x, np.ones((T, 1))], axis=1)
+    W1a = np.concatenate([W1T, np.zeros((f, 1))], axis=1)
+    WuA = np.concatenate([np.zeros((f, d)), np.ones((f, 1))], axis=1)
+    W2a = W2                                                     # the output has d columns either way
+    gated = O.ffn_dense_fwd(xa, W1a, b1, WuA, W2a)
+    plain = O.relu_ffn_dense_fwd(x, W1T, b1, W2)
+    np.testing.assert_allclose(gated["u"], 1.0, rtol=0, atol=0)
+    np.testing.assert_allclose(plain["y"], gated["y"], rtol=1e-12, atol=1e-12)
+    sparse = O.relu_ffn_sparse_fwd(x, W1T, b1, W2)
+    np.testing.assert_allclose(sparse["y"], gated["y"], rtol=1e-12, atol=1e-12)
+
+
+def test_relu_ffn_bias_only_closed_form():
+    """With W1 = 0 the hidden layer is ReLU(b1) for every token, so every
+    output row is sum_n max(b1[n], 0) * W2[n]."""
+    rng = np.random.default_rng(31)
+    T, d, f = 5, 7, 70
+    W2 = rng.standard_normal((f, d))
+    b1 = rng.standard_normal(f)
+    want = sum(max(b1[n], 0.0) * W2[n] for n in range(f))
+    for fn in (O.relu_ffn_dense_fwd, O.relu_ffn_sparse_fwd):
+        y = fn(rng.standard_normal((T, d)), np.zeros((f, d)), b1, W2)["y"]
+        for t in range(T):
+            np.testing.assert_allclose(y[t], want, rtol=1e-12, atol=1e-12)
