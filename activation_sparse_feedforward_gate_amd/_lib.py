@@ -70,6 +70,12 @@ def lib() -> ctypes.CDLL:
         L.twell_ffn_dense_fwd_workspace.argtypes = [P(c_twell_ffn_shape)]
         L.twell_ffn_dense_fwd_workspace.restype = sz
         L.twell_ffn_dense_fwd.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.twell_relu_ffn_fwd_workspace.argtypes = [P(c_twell_ffn_shape)]
+        L.twell_relu_ffn_fwd_workspace.restype = sz
+        L.twell_relu_ffn_fwd.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, P(c_twell_mat), vp, sz, vp]
+        L.twell_relu_ffn_dense_fwd_workspace.argtypes = [P(c_twell_ffn_shape)]
+        L.twell_relu_ffn_dense_fwd_workspace.restype = sz
+        L.twell_relu_ffn_dense_fwd.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, sz, vp]
         L.twell_ffn_dense_bwd_workspace.argtypes = [P(c_twell_ffn_shape)]
         L.twell_ffn_dense_bwd_workspace.restype = sz
         L.twell_ffn_dense_bwd.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -79,7 +85,7 @@ def lib() -> ctypes.CDLL:
         L.twell_last_error.argtypes = []
         L.twell_last_error.restype = ctypes.c_char_p
         for name in ("twell_pack", "twell_unpack", "twell_ffn_fwd", "twell_ffn_fwd_ex", "twell_ffn_bwd_hybrid",
-                     "twell_ffn_bwd_hybrid_l1",
+                     "twell_ffn_bwd_hybrid_l1", "twell_relu_ffn_fwd", "twell_relu_ffn_dense_fwd",
                      "twell_ffn_dense_fwd", "twell_ffn_dense_bwd",
                      "twell_gate_pack",
                      "twell_sparse_up", "twell_sparse_down"):
@@ -215,6 +221,27 @@ def twell_ffn_bwd_hybrid(shape, x, WgT, bg, WuT, Wd, dY, saved_h: TwellMat, dens
                                       _ptr(dWuT), _ptr(dWd), _ptr(dbg), _ptr(n_dense_rows), _ptr(ws),
                                       ws.numel() * ws.element_size() if ws is not None else 0,
                                       _stream(stream)))
+
+
+def twell_relu_ffn_fwd_workspace(shape) -> int:
+    return int(lib().twell_relu_ffn_fwd_workspace(ctypes.byref(shape)))
+
+
+def twell_relu_ffn_fwd(shape, x, W1T, b1, W2, y, saved_h: Optional[TwellMat], ws, stream=None) -> None:
+    hm = saved_h.c() if saved_h is not None else None
+    _check(lib().twell_relu_ffn_fwd(ctypes.byref(shape), _ptr(x), _ptr(W1T), _ptr(b1), _ptr(W2), _ptr(y),
+                                    ctypes.byref(hm) if hm is not None else None, _ptr(ws),
+                                    ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def twell_relu_ffn_dense_fwd_workspace(shape) -> int:
+    return int(lib().twell_relu_ffn_dense_fwd_workspace(ctypes.byref(shape)))
+
+
+def twell_relu_ffn_dense_fwd(shape, x, W1T, b1, W2, y, ws, stream=None) -> None:
+    _check(lib().twell_relu_ffn_dense_fwd(ctypes.byref(shape), _ptr(x), _ptr(W1T), _ptr(b1), _ptr(W2), _ptr(y),
+                                          _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+                                          _stream(stream)))
 
 
 def twell_ffn_bwd_hybrid_l1(shape, x, WgT, bg, WuT, Wd, dY, saved_h: TwellMat, dense_row_threshold: int,

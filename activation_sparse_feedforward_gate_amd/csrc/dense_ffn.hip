@@ -64,6 +64,37 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_gateup_kernel(DenseArgs a) {
   }
 }
 
+// Non-gated layer: act = bf16(ReLU(x.W1T^T + b1)) (W1T passed as WgT).
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTH) void dense_relu_act_kernel(DenseArgs a) {
+  __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
+  const int nbm = (a.T + Cfg::BM - 1) / Cfg::BM, nbn = a.F / Cfg::BN;
+  int bm, bn;
+  tile_order(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, bm, bn);
+  const int m0 = bm * Cfg::BM, n0 = bn * Cfg::BN;
+  typedef DmaTile<Cfg> Tile;
+  Tile g;
+  const Operand A{a.x, a.d, nullptr, a.T};
+  const Operand B{a.WgT, a.d, nullptr, a.F};
+  g.run(A, &B, m0, n0, a.d, st0, st1);
+#pragma unroll
+  for (int j = 0; j < Cfg::TN; ++j) {
+    const int col = n0 + Tile::col_of(j);
+    const float b = a.bg ? bf16_to_f32(((const uint16_t*)a.bg)[col]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + Tile::row_of(i, e);
+        if (row < a.T) {
+          const float gv = g.acc[0][i][j][e] + b;
+          a.act[(int64_t)row * a.F + col] = (uint16_t)f32_to_bf16_bits(gv > 0.f ? gv : 0.f);
+        }
+      }
+  }
+}
+
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTH) void dense_down_kernel(DenseArgs a) {
   const int nbm = (a.T + Cfg::BM - 1) / Cfg::BM, nbn = a.d / Cfg::BN;
@@ -100,6 +131,7 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_down_kernel(DenseArgs a) {
 }
 
 using DenseGateUp = DmaCfg<256, 128, 4, 2, 2>;
+using DenseReluAct = DmaCfg<256, 128, 4, 2>;
 using DenseDownBig = DmaCfg<256, 256, 2, 4, 1, false, true>;
 using DenseDownSmall = GemmCfg<128, 64, 2, 1, OP_BF16_K, OP_BF16_T>;
 
@@ -116,6 +148,14 @@ hipError_t launch_dense_down(const void* act, const void* Wd, int T, int d, int 
   DenseArgs a{nullptr, nullptr, nullptr, nullptr, Wd, T, d, F, (uint16_t*)act, y, out_dt == DT_BF16};
   if (d % 256 == 0) return launch_grid<DenseDownBig>(dense_down_kernel<DenseDownBig>, T, d, a, s);
   return launch_grid<DenseDownSmall>(dense_down_kernel<DenseDownSmall>, T, d, a, s);
+}
+
+hipError_t launch_dense_relu_fwd(const void* x, const void* W1T, const void* b1, const void* W2, int T, int d, int F,
+                                 void* act, int out_dt, void* y, hipStream_t s) {
+  DenseArgs a{x, W1T, b1, nullptr, W2, T, d, F, (uint16_t*)act, y, out_dt == DT_BF16};
+  hipError_t e = launch_grid<DenseReluAct>(dense_relu_act_kernel<DenseReluAct>, T, F, a, s);
+  if (e != hipSuccess) return e;
+  return launch_dense_down(act, W2, T, d, F, out_dt, y, s);
 }
 
 hipError_t launch_dense_fwd(const void* x, const void* WgT, const void* bg, const void* WuT,

@@ -131,11 +131,17 @@ hipError_t launch_decode_fwd(const void* x, const void* WgT, const void* bg, con
                              hipStream_t s, hipEvent_t ev_gate, hipEvent_t ev_lists, hipEvent_t ev_up);
 
 // ev_lists / ev_up (nullable) are recorded after the union lists and the fp16
-// copy of Wd, and after the up-projection.
+// copy of Wd, and after the up-projection.  WuT == null: the non-gated ReLU FFN
+// (a = h, no up GEMM; x is not read).
 hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int T, int d, int F,
                             const TwellView& h, const uint8_t* skip, void* ws, void* y, int out_dt,
                             int** flag_out, hipStream_t s, hipEvent_t ev_lists = nullptr,
                             hipEvent_t ev_up = nullptr);
+
+// Dense non-gated ReLU FFN baseline: act = bf16(ReLU(x.W1T^T + b1)), then
+// y = act.W2.  act is a [T][F] bf16 workspace; needs F % 128 == 0.
+hipError_t launch_dense_relu_fwd(const void* x, const void* W1T, const void* b1, const void* W2, int T, int d, int F,
+                                 void* act, int out_dt, void* y, hipStream_t s);
 
 // Dense baseline: act = ReLU(x.WgT^T + bg) * (x.WuT^T) in bf16 (fused dual GEMM),
 // then y = act.Wd.  act is a [T][F] bf16 workspace.

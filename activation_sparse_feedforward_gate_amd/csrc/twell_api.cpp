@@ -410,6 +410,97 @@ twell_status twell_sparse_down(const twell_ffn_shape* sh, const float* aval, con
                                      view_of(pattern), y, nullptr, stream), "sparse down-projection");
 }
 
+// ------------------------------------------------------------------ non-gated ReLU FFN
+
+// Workspace of the non-gated forward: the TwELL of h (when the caller keeps
+// none) and, for bf16 inputs, the union workspace.
+static size_t relu_layout(const twell_ffn_shape* sh, void* ws, FwdWs* out) {
+  size_t parts[5];
+  mat_parts(sh->T, sh->F, GPU_R, GPU_C, TWELL_F32, parts);
+  Carver c(ws);
+  FwdWs w{};
+  TwellView& v = w.h;
+  v.T = sh->T; v.F = sh->F; v.NT = sh->F / GPU_C; v.NR = (sh->T + GPU_R - 1) / GPU_R;
+  v.cnt = (uint8_t*)c.take(parts[0]);
+  v.width = (uint8_t*)c.take(parts[1]);
+  v.val = c.take(parts[2]);
+  v.idx = (uint8_t*)c.take(parts[3]);
+  v.mask = (uint64_t*)c.take(parts[4]);
+  if (sh->in_dt == TWELL_BF16) w.uni = c.take(union_ws_bytes(sh->T, sh->d, sh->F));
+  if (out) *out = w;
+  return c.off;
+}
+
+size_t twell_relu_ffn_fwd_workspace(const twell_ffn_shape* sh) {
+  if (!sh || check_shape(sh) != TWELL_OK) return 0;
+  return relu_layout(sh, nullptr, nullptr);
+}
+
+twell_status twell_relu_ffn_fwd(const twell_ffn_shape* sh, const void* x, const void* W1T, const void* b1,
+                                const void* W2, void* y, twell_mat* saved_h, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  twell_status st = check_shape(sh);
+  if (st) return st;
+  if (sh->T > 0 && (!x || !W1T || !W2 || !y)) return fail(TWELL_EINVAL, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(W1T) || !aligned16(W2) || !aligned16(y) || !aligned16(b1))
+    return fail(TWELL_EINVAL, "tensors must be 16-byte aligned");
+  if (saved_h) {
+    st = check_mat(saved_h, true);
+    if (st) return st;
+    if (saved_h->T != sh->T || saved_h->F != sh->F || saved_h->vdtype != TWELL_F32)
+      return fail(TWELL_EINVAL, "saved_h must be T x F with fp32 values");
+  }
+  if ((int64_t)sh->T * sh->d >= ((int64_t)1 << 32) || (int64_t)sh->F * sh->d >= ((int64_t)1 << 32) ||
+      (int64_t)sh->T * sh->F >= ((int64_t)1 << 32))
+    return fail(TWELL_EUNSUPPORTED, "matrices must hold fewer than 2^32 elements");
+  const size_t need = relu_layout(sh, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (sh->T == 0) return TWELL_OK;
+  FwdWs w;
+  relu_layout(sh, ws, &w);
+  const int in_dt = sh->in_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
+  const int out_dt = sh->out_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
+  const TwellView h = saved_h ? view_of(saved_h) : w.h;
+  hipError_t e = launch_gate_twell(in_dt, x, W1T, b1, sh->T, sh->d, sh->F, h, stream);
+  if (e != hipSuccess) return hip_status(e, "gate GEMM");
+  if (in_dt == DT_BF16) {
+    int* ovf = nullptr;
+    e = launch_union_fwd(x, nullptr, W2, sh->T, sh->d, sh->F, h, nullptr, w.uni, y, out_dt, &ovf, stream, nullptr,
+                         nullptr);
+    if (e != hipSuccess) return hip_status(e, "union down GEMM");
+    // h beyond the fp16 range: the per-pair kernel with fp32 h (does nothing unless the flag is set)
+    e = launch_down_bf16((const float*)h.val, nullptr, W2, nullptr, sh->T, sh->d, sh->F, h, y, out_dt, nullptr,
+                         stream, ovf);
+    if (e != hipSuccess) return hip_status(e, "overflow fallback");
+  } else {
+    e = launch_spmm_down(in_dt, out_dt, (const float*)h.val, W2, sh->T, sh->d, sh->F, h, y, nullptr, stream);
+    if (e != hipSuccess) return hip_status(e, "sparse down-projection");
+  }
+  return TWELL_OK;
+}
+
+size_t twell_relu_ffn_dense_fwd_workspace(const twell_ffn_shape* sh) {
+  if (!sh || check_shape(sh) != TWELL_OK) return 0;
+  return round_up((size_t)sh->T * sh->F * 2, 256);
+}
+
+twell_status twell_relu_ffn_dense_fwd(const twell_ffn_shape* sh, const void* x, const void* W1T, const void* b1,
+                                      const void* W2, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  twell_status st = check_shape(sh);
+  if (st) return st;
+  if (sh->in_dt != TWELL_BF16) return fail(TWELL_EUNSUPPORTED, "the dense baseline is bf16 only");
+  if (sh->T > 0 && (!x || !W1T || !W2 || !y)) return fail(TWELL_EINVAL, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(W1T) || !aligned16(W2) || !aligned16(y) || !aligned16(b1))
+    return fail(TWELL_EINVAL, "tensors must be 16-byte aligned");
+  if (sh->F % 128 != 0) return fail(TWELL_EUNSUPPORTED, "the dense baseline needs F %% 128 == 0");
+  const size_t need = twell_relu_ffn_dense_fwd_workspace(sh);
+  if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (sh->T == 0) return TWELL_OK;
+  return hip_status(launch_dense_relu_fwd(x, W1T, b1, W2, sh->T, sh->d, sh->F, ws,
+                                          sh->out_dt == TWELL_BF16 ? DT_BF16 : DT_F32, y, stream),
+                    "dense ReLU FFN");
+}
+
 // The dense baseline takes the few-token kernels where the TwELL forward does.
 bool dense_few_tokens(const twell_ffn_shape* sh) { return sh->T > 0 && sh->T <= DECODE_T_MAX; }
 

@@ -119,7 +119,9 @@ __global__ __launch_bounds__(256) void union_list_kernel(UnionArgs a, const uint
 constexpr int POSCAP = 12288;         // neuron span of a position tile covered by the LDS position map
 
 // Up-projection over the union, one (row block b, position tile pt) tile.
-template <class Cfg>
+// GATED = false: the non-gated ReLU FFN, a = h (no up GEMM; the tile only
+// lays h out over the union positions for the down GEMM).
+template <class Cfg, bool GATED>
 __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt, char* st0, char* st1,
                                               int16_t* posmap) {
   static_assert(Cfg::BM == UB, "one row block per M tile");
@@ -174,7 +176,7 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
     }
   }
 
-  g.run(A, &B, m0, p0, a.d, st0, st1);
+  if constexpr (GATED) g.run(A, &B, m0, p0, a.d, st0, st1);
 
   // epilogue: a = h * u on stored pairs, else 0, stored as fp16 into
   // adense[t][p] (32 consecutive positions per half-wave store).  Positions in
@@ -269,7 +271,8 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
         float v[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          v[k] = hv[k] != 0.f ? hv[k] * g.acc[0][i][j][4 * qq + k] : 0.f;
+          if constexpr (GATED) v[k] = hv[k] != 0.f ? hv[k] * g.acc[0][i][j][4 * qq + k] : 0.f;
+          else v[k] = hv[k];
           vbits = max(vbits, __float_as_uint(v[k]) & 0x7fffffffu);
         }
         // stores of position pairs: lanes l and l^1 hold positions p and
@@ -305,7 +308,7 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
 // position tile by position tile, so the WuT rows of neighbouring blocks'
 // unions (largely the same neurons) are reused from that XCD's L2 (measured
 // faster than keeping each block's x rows in L2 instead).
-template <class Cfg>
+template <class Cfg, bool GATED>
 __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   for (int k = blockIdx.x >> 3; k < ntile; k += gridDim.x >> 3) {
     const int pt = k / nbx;
     const int b = x + 8 * (k - pt * nbx);
-    up_union_tile<Cfg>(a, b, pt, st0, st1, posmap);
+    up_union_tile<Cfg, GATED>(a, b, pt, st0, st1, posmap);
     __syncthreads();                                   // stage buffers and position map free again
   }
 }
@@ -483,7 +486,12 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
   // never more than the tiles of the busiest XCD need
   const int cus = device_cus();
   auto grid_for = [&](int tiles_per_xcd) { return (unsigned)(8 * std::max(1, std::min(cus / 8, tiles_per_xcd))); };
-  hipLaunchKernelGGL((up_union_kernel<UpUnionCfg>), dim3(grid_for(nbx_max * npt)), dim3(UpUnionCfg::NTH), 0, s, a);
+  if (WuT)
+    hipLaunchKernelGGL((up_union_kernel<UpUnionCfg, true>), dim3(grid_for(nbx_max * npt)), dim3(UpUnionCfg::NTH), 0,
+                       s, a);
+  else   // non-gated layer: a = h
+    hipLaunchKernelGGL((up_union_kernel<UpUnionCfg, false>), dim3(grid_for(nbx_max * npt)), dim3(UpUnionCfg::NTH),
+                       0, s, a);
   if (ev_up) (void)hipEventRecord(ev_up, s);
   if (d % 256 == 0)
     hipLaunchKernelGGL((down_union_kernel<DownUnionCfg>), dim3(grid_for(nbx_max * (d / 256))), dim3(DownUnionCfg::NTH),

@@ -263,6 +263,42 @@ twell_status twell_ffn_dense_fwd(const twell_ffn_shape *sh, const void *x, const
                                  const void *WuT, const void *Wd, void *y, void *ws, size_t ws_bytes,
                                  hipStream_t stream);
 
+/* Workspace bytes for twell_relu_ffn_fwd (0 for an invalid shape). */
+size_t twell_relu_ffn_fwd_workspace(const twell_ffn_shape *sh);
+
+/*
+ * twell_relu_ffn_fwd: the non-gated ReLU FFN y = ReLU(x.W1T^T + b1) . W2
+ * through TwELL.  The pages' method targets gated FFNs (intellectnews.ru
+ * TwELL article, section "Ограничения и открытые вопросы"); a plain ReLU FFN
+ * has the same exact zeros in its hidden layer but no up-projection to skip.
+ * The gate GEMM packs h = ReLU(x.W1T^T + b1) into TwELL in its epilogue (as
+ * in twell_ffn_fwd), then the down-projection visits only the stored pairs:
+ * for bf16 inputs an fp16 MFMA GEMM over each 128-token block's union of
+ * active neurons with h in fp16 (h beyond the fp16 range: recomputed per pair
+ * in fp32), for fp32 inputs the per-pair kernel in fp32.
+ *   x    [T][d] in_dt;  W1T, W2 [F][d] in_dt (neuron-major);  b1 [F] or NULL
+ *   y    [T][d] out_dt (overwritten)
+ *   saved_h  NULL or a caller-allocated twell_mat (fp32 values, mask
+ *            required) that receives h
+ *   ws, ws_bytes  workspace of at least twell_relu_ffn_fwd_workspace(sh)
+ * Errors as for twell_ffn_fwd.
+ */
+twell_status twell_relu_ffn_fwd(const twell_ffn_shape *sh, const void *x, const void *W1T, const void *b1,
+                                const void *W2, void *y, twell_mat *saved_h, void *ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* Workspace bytes for twell_relu_ffn_dense_fwd. */
+size_t twell_relu_ffn_dense_fwd_workspace(const twell_ffn_shape *sh);
+
+/*
+ * twell_relu_ffn_dense_fwd: the same non-gated layer computed densely (the
+ * library's own dense MFMA baseline for it, bf16 only): a GEMM writes
+ * act = bf16(ReLU(x.W1T^T + b1)) for every (t, n), then y = act . W2.
+ * EUNSUPPORTED unless F % 128 == 0.  Other arguments as twell_relu_ffn_fwd.
+ */
+twell_status twell_relu_ffn_dense_fwd(const twell_ffn_shape *sh, const void *x, const void *W1T, const void *b1,
+                                      const void *W2, void *y, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes for twell_ffn_dense_bwd. */
 size_t twell_ffn_dense_bwd_workspace(const twell_ffn_shape *sh);
 
