@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--ffn", choices=["gated", "relu"], default="gated",
+                    help="relu: the non-gated ReLU FFN y = ReLU(x.W1 + b1).W2 (the workload's gate weights and "
+                         "bias as W1, b1, its down weights as W2)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the PMC byte counters)")
     return ap.parse_args()
@@ -128,6 +131,82 @@ def copy_calibration(steps: int) -> int:
     return 0
 
 
+def relu_bench(args) -> int:
+    """The non-gated ReLU FFN: whole-layer timing against its own dense
+    baseline (no per-kernel events: the entry point records none)."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_feedforward_gate_amd as tw
+    import oracle
+    from workloads import CONFIGS, make_workload
+
+    cfg = CONFIGS[args.config]
+    if cfg.dtype != "bf16" or cfg.tau_frac is not None:
+        print(json.dumps({"error": "--ffn relu runs the bf16 inference workloads (0.5b, 1.5b, 2b)"}))
+        return 2
+    w = make_workload(args.config, decode=args.decode)
+    T, d, f = w.T, w.d, w.f
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def dt(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
+
+    x, W1T, b1, W2 = dt(w.x), dt(w.WgT), dt(w.bg), dt(w.Wd)
+    shape = tw.ffn_shape(T, d, f, tw.TWELL_BF16, tw.TWELL_F32)
+    h = tw.alloc_twell_mat(T, f, tw.TWELL_F32, device=dev)
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, tw.twell_relu_ffn_fwd_workspace(shape)), dtype=torch.uint8, device=dev)
+    wsd = torch.empty(max(1, tw.twell_relu_ffn_dense_fwd_workspace(shape)), dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    ms = timed(lambda: tw.twell_relu_ffn_fwd(shape, x, W1T, b1, W2, y, h, ws, stream))
+    nnz = int(h.cnt.to(torch.int64).sum().item())
+    work = 2.0 * T * d * f + 2.0 * nnz * d              # gate GEMM + useful down-projection flops
+    achieved = work / (ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; shapes, densities and neuron-popularity structure of the workload)",
+        "config": {"workload": cfg.description + " -- non-gated ReLU FFN (W1 = gate weights, W2 = down weights)",
+                   "name": args.config, "ffn": "relu", "T": T, "d_model": d, "d_ff": f,
+                   "realised_density": nnz / (T * f), "pass": "fwd"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK["bf16_mfma_tflops"], "unit": "TFLOP/s",
+                     "frac": achieved / PEAK["bf16_mfma_tflops"], "traffic": None,
+                     "kernel": "whole layer (gate GEMM + pack + union down-projection)"},
+    }
+    if not args.no_dense:
+        dms = timed(lambda: tw.twell_relu_ffn_dense_fwd(shape, x, W1T, b1, W2, y, wsd, stream))
+        out["dense_baseline"] = {"tokens_per_s": T / (dms * 1e-3), "ms_per_step": dms,
+                                 "what": "dense ReLU FFN, bf16 act"}
+        out["speedup_vs_dense"] = dms / ms
+    if not args.no_cpu:
+        chunk, done, t0 = 256, 0, time.perf_counter()
+        while done < T and time.perf_counter() - t0 < args.cpu_seconds:
+            rows = slice(done, min(done + chunk, T))
+            oracle.relu_ffn_dense_fwd(w.x[rows], w.WgT, w.bg, w.Wd)
+            done = rows.stop
+        el = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": done / el, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"first {done} of {T} token rows, float64 numpy dense ReLU FFN, {el:.1f} s"}
+    print(json.dumps(out))
+    return 0
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -136,6 +215,8 @@ def main() -> int:
         return 2
     if args.copy_calibration:
         return copy_calibration(max(1, args.steps))
+    if args.ffn == "relu":
+        return relu_bench(args)
     import numpy as np
     import torch
 
