@@ -59,6 +59,14 @@ hipError_t launch_sddmm_bwd(int in_dt, const void* x, const void* dY, const void
                             int d, int F, const TwellView& h, float* aval, float* dgval, float* duval,
                             const uint8_t* skip, hipStream_t s, float l1 = 0.f);
 
+// The same for bf16 inputs as MFMA GEMMs over each 128-row block's union of
+// the live rows' active neurons (rows with skip[t] != 0 excluded); ws holds
+// union_bwd_ws_bytes(T, F) bytes.
+size_t union_bwd_ws_bytes(int T, int F);
+hipError_t launch_union_sddmm_bwd(const void* x, const void* dY, const void* WuT, const void* Wd, int T, int d, int F,
+                                  const TwellView& h, const uint8_t* skip, void* ws, float* aval, float* dgval,
+                                  float* duval, float l1, hipStream_t s);
+
 // Backward SpMM: dX_t = sum over stored n of dg*WgT[n] + du*WuT[n] (fp32),
 // rows with skip[t] != 0 not written.
 hipError_t launch_spmm_dx(int in_dt, const float* dgval, const float* duval, const void* WgT, const void* WuT,

@@ -143,6 +143,7 @@ struct BwdWs {
   int* part;         // [ceil(T/256)][F]
   int* start;        // [F+1]
   uint32_t* entries; // one per stored pair of a sparse row
+  void* uni;         // bf16 inputs: union lists of the sparse rows
 };
 
 size_t bwd_layout(const twell_ffn_shape* sh, int32_t tau, void* ws, BwdWs* out) {
@@ -164,6 +165,7 @@ size_t bwd_layout(const twell_ffn_shape* sh, int32_t tau, void* ws, BwdWs* out) 
   w.part = (int*)c.take((size_t)(((T + 255) / 256) * F) * 4);
   w.start = (int*)c.take((size_t)(F + 1) * 4);
   w.entries = (uint32_t*)c.take((size_t)(T * per_row) * 4);
+  if (sh->in_dt == TWELL_BF16) w.uni = c.take(union_bwd_ws_bytes((int)T, (int)F));
   if (out) *out = w;
   return c.off;
 }
@@ -350,7 +352,10 @@ twell_status twell_ffn_bwd_hybrid_l1(const twell_ffn_shape* sh, const void* x, c
   e = launch_dense_rows_bwd(in_dt, x, WgT, bg, WuT, Wd, dY, T, d, F, w.list, w.nD, w.buf3, w.dbg_part, dX, dWgT,
                             dWuT, dWd, dbg, stream, l1);
   if (e != hipSuccess) return hip_status(e, "dense-row backward");
-  e = launch_sddmm_bwd(in_dt, x, dY, WuT, Wd, T, d, F, h, w.aval, w.dgval, w.duval, w.flag, stream, l1);
+  if (in_dt == DT_BF16)
+    e = launch_union_sddmm_bwd(x, dY, WuT, Wd, T, d, F, h, w.flag, w.uni, w.aval, w.dgval, w.duval, l1, stream);
+  else
+    e = launch_sddmm_bwd(in_dt, x, dY, WuT, Wd, T, d, F, h, w.aval, w.dgval, w.duval, w.flag, stream, l1);
   if (e != hipSuccess) return hip_status(e, "sparse backward SDDMM");
   e = launch_spmm_dx(in_dt, w.dgval, w.duval, WgT, WuT, T, d, F, h, dX, w.flag, stream);
   if (e != hipSuccess) return hip_status(e, "sparse backward dX");

@@ -55,6 +55,12 @@ struct UnionArgs {
   int* flag;              // fp16 overflow flag
   void* y;
   int out_bf16;
+  // backward SDDMM over the union
+  const void* dY;         // [T][d]
+  float* aval;            // TwELL-shaped outputs: a = h*u, dg = da*u + l1, du = da*h
+  float* dgval;
+  float* duval;
+  float l1;
 };
 
 __device__ __forceinline__ bool live(const UnionArgs& a, int t) {
@@ -326,6 +332,136 @@ __global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
   }
 }
 
+// Backward SDDMM of the hybrid format's sparse rows over the union, one
+// (row block b, position tile pt) tile: U = x.WuT[ulist]^T and
+// DA = dY.Wd[ulist]^T (two bf16 MFMA GEMMs, fp32 accumulation), then for
+// every stored pair (t, n) of a live row in the tile: a = h*u, dg = da*u + l1,
+// du = da*h at the pair's TwELL slot.  The products at the union's other
+// positions are computed and dropped: at a uniform 1% density a 128-row
+// block's union holds about 72% of the neurons, and the dense MFMA GEMMs over
+// it run far faster than per-pair dot products.  The pairs reach the
+// accumulator layout through an LDS tile of slot numbers (256 positions x 128
+// rows, one byte each, 4-row groups XOR-swizzled by position), filled like the
+// up-projection's h tile.
+template <class Cfg>
+__device__ __forceinline__ void bwd_union_tile(const UnionArgs& a, int b, int pt, char* st0, char* st1,
+                                               int16_t* posmap) {
+  static_assert(Cfg::BM == UB && Cfg::BM == 128 && Cfg::BN == 256 && Cfg::NW == 8, "slot tile layout");
+  static_assert(Cfg::STAGE >= 256 * 128, "slot tile: 256 positions x 128 rows of bytes");
+  const int nb = a.ucount[b];
+  const int p0 = pt * Cfg::BN;
+  if (p0 >= nb) return;
+  const int m0 = b * UB;
+  const int* ul = a.ulist + (int64_t)b * a.F;
+  typedef DmaTile<Cfg> Tile;
+  Tile gu, gd;
+  const int tid = threadIdx.x;
+  const int pl = min(p0 + Cfg::BN, nb) - 1;
+  const int nlo = ul[p0], nhi = ul[pl];
+  const bool use_map = nhi - nlo < POSCAP;
+  if (use_map)
+    for (int p = p0 + tid; p <= pl; p += Cfg::NTH) posmap[ul[p] - nlo] = (int16_t)(p - p0);
+  const int tjf = nlo >> 6, S = (nhi >> 6) - tjf + 1;
+  {
+    const Operand A{a.x, a.d, nullptr, a.T};
+    const Operand B{a.WuT, a.d, ul, nb};
+    gu.run(A, &B, m0, p0, a.d, st0, st1);
+  }
+  {
+    const Operand A{a.dY, a.d, nullptr, a.T};
+    const Operand B{a.Wd, a.d, ul, nb};
+    gd.run(A, &B, m0, p0, a.d, st0, st1);
+  }
+  auto soff = [](int pr, int r) { return pr * 128 + (((r >> 2) ^ (pr & 31)) << 2) + (r & 3); };
+#pragma unroll
+  for (int o = 0; o < 256 * 128 / (16 * Cfg::NTH); ++o) ((uint4*)st0)[o * Cfg::NTH + tid] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  // scatter slot + 1 of every stored pair in the tile's neuron span: a 16-lane
+  // group per (row tile, column tile) block, lane piece c = slot c/4, rows
+  // 4*(c%4)..+3
+  constexpr int NG = Cfg::NTH / 16;
+  constexpr int NRT = Cfg::BM / 16;
+  const int grp = tid >> 4, gl = tid & 15;
+  for (int q = grp; q < NRT * S; q += NG) {
+    const int i = q / S, sj = q - i * S;
+    const int rt = (m0 >> 4) + i;
+    if (rt * 16 >= a.T) continue;
+    const int tj = tjf + sj;
+    const int64_t blk = (int64_t)rt * a.NT + tj;
+    const int w = a.hwidth[blk];
+    for (int c = gl; c < w * 4; c += 16) {
+      const float4 v4 = ((const float4*)(a.hval + blk * 1024))[c];
+      const uint32_t i4 = ((const uint32_t*)(a.hidx + blk * 1024))[c];
+      const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int rl = 4 * (c & 3) + k;
+        const int n = tj * 64 + (int)((i4 >> (8 * k)) & 255u);
+        if (vv[k] > 0.f && n >= nlo && n <= nhi && live(a, rt * 16 + rl)) {
+          int pr;
+          if (use_map) {
+            pr = posmap[n - nlo];
+          } else {
+            int lo = p0, hi = pl;
+            while (lo < hi) {
+              const int mid = (lo + hi) >> 1;
+              if (ul[mid] < n) lo = mid + 1; else hi = mid;
+            }
+            pr = lo - p0;
+          }
+          st0[soff(pr, i * 16 + rl)] = (char)((c >> 2) + 1);
+        }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < Cfg::TN; ++j) {
+    const int pr = Tile::col_of(j);
+    if (p0 + pr >= nb) continue;
+    const int tj = ul[p0 + pr] >> 6;
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int r0 = Tile::row_of(i, 4 * qq);                   // 4 consecutive rows r0..r0+3
+        const uint32_t s4 = *(const uint32_t*)(st0 + soff(pr, r0));
+        if (s4 == 0u) continue;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int sl = (int)((s4 >> (8 * k)) & 255u);
+          if (sl) {
+            const int t = m0 + r0 + k;
+            const int64_t off = (((int64_t)(t >> 4) * a.NT + tj) * 64 + (sl - 1)) * 16 + (t & 15);
+            const float h = a.hval[off];
+            const float u = gu.acc[0][i][j][4 * qq + k], da = gd.acc[0][i][j][4 * qq + k];
+            a.aval[off] = h * u;
+            a.dgval[off] = da * u + a.l1;
+            a.duval[off] = da * h;
+          }
+        }
+      }
+  }
+}
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTH) void bwd_union_kernel(UnionArgs a) {
+  __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
+  __shared__ int16_t posmap[POSCAP];
+  const int npt = (a.F + Cfg::BN - 1) / Cfg::BN;
+  const int nblk = (a.T + UB - 1) / UB;
+  const int x = blockIdx.x & 7;
+  const int nbx = (nblk - x + 7) / 8;
+  const int ntile = nbx * npt;
+  for (int k = blockIdx.x >> 3; k < ntile; k += gridDim.x >> 3) {
+    const int pt = k / nbx;
+    const int b = x + 8 * (k - pt * nbx);
+    bwd_union_tile<Cfg>(a, b, pt, st0, st1, posmap);
+    __syncthreads();
+  }
+}
+
 // fp16 copy of Wd for the down GEMM (exact for every bf16 value inside the
 // fp16 range); a value beyond that range raises the flag, and the layer then
 // takes the fp32 path.
@@ -502,6 +638,36 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
   else
     hipLaunchKernelGGL((down_union_kernel<DownUnionCfg64>), dim3(grid_for(nbx_max * (d / 64))),
                        dim3(DownUnionCfg64::NTH), 0, s, a);
+  return hipGetLastError();
+}
+
+size_t union_bwd_ws_bytes(int T, int F) {
+  const size_t nblk = (size_t)(T + UB - 1) / UB;
+  const size_t nslab = (size_t)(T + 63) / 64;
+  return nblk * F * 4 + nblk * 4 + 256 + nslab * (F / 64) * 8 + 256 * 4;
+}
+
+hipError_t launch_union_sddmm_bwd(const void* x, const void* dY, const void* WuT, const void* Wd, int T, int d, int F,
+                                  const TwellView& h, const uint8_t* skip, void* ws, float* aval, float* dgval,
+                                  float* duval, float l1, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int nblk = (T + UB - 1) / UB;
+  char* w = (char*)ws;
+  UnionArgs a{};
+  a.x = x; a.WuT = WuT; a.Wd = Wd; a.dY = dY; a.T = T; a.d = d; a.F = F; a.NT = F / 64;
+  a.mask = h.mask; a.skip = skip; a.hval = (const float*)h.val; a.hidx = h.idx; a.hwidth = h.width;
+  a.ulist = (int*)w;
+  a.ucount = (int*)(w + (size_t)nblk * F * 4);
+  uint64_t* U = (uint64_t*)(w + (((size_t)nblk * F * 4 + (size_t)nblk * 4 + 255) & ~(size_t)255));
+  a.flag = (int*)((char*)U + (((size_t)((T + 63) / 64) * a.NT * 8 + 255) & ~(size_t)255));   // the list kernel clears it
+  a.lrows = UB;
+  a.aval = aval; a.dgval = dgval; a.duval = duval; a.l1 = l1;
+  union_lists_launch(a, U, s);
+  using BwdUnionCfg = DmaCfg<UB, 256, 2, 4>;
+  const int npt = (F + BwdUnionCfg::BN - 1) / BwdUnionCfg::BN;
+  const int tiles_per_xcd = ((nblk + 7) / 8) * npt;
+  const unsigned grid = (unsigned)(8 * std::max(1, std::min(device_cus() / 8, tiles_per_xcd)));
+  hipLaunchKernelGGL((bwd_union_kernel<BwdUnionCfg>), dim3(grid), dim3(BwdUnionCfg::NTH), 0, s, a);
   return hipGetLastError();
 }
 
