@@ -60,12 +60,16 @@ hipError_t launch_sddmm_bwd(int in_dt, const void* x, const void* dY, const void
                             const uint8_t* skip, hipStream_t s, float l1 = 0.f);
 
 // The same for bf16 inputs as MFMA GEMMs over each 128-row block's union of
-// the live rows' active neurons (rows with skip[t] != 0 excluded); ws holds
-// union_bwd_ws_bytes(T, F) bytes.
-size_t union_bwd_ws_bytes(int T, int F);
-hipError_t launch_union_sddmm_bwd(const void* x, const void* dY, const void* WuT, const void* Wd, int T, int d, int F,
-                                  const TwellView& h, const uint8_t* skip, void* ws, float* aval, float* dgval,
-                                  float* duval, float l1, hipStream_t s);
+// the live rows' active neurons (rows with skip[t] != 0 excluded), followed by
+// dX of the live rows = dG.WgT + dU.WuT as an fp16 MFMA GEMM over the same
+// unions (dG, dU and the weights in fp16).  *flag_out receives the device flag
+// that is set when a value exceeds the fp16 range: the dX GEMM then stands
+// down and the per-pair dX kernel gated on the flag must run.  ws holds
+// union_bwd_ws_bytes(T, d, F) bytes.
+size_t union_bwd_ws_bytes(int T, int d, int F);
+hipError_t launch_union_bwd(const void* x, const void* dY, const void* WgT, const void* WuT, const void* Wd, int T,
+                            int d, int F, const TwellView& h, const uint8_t* skip, void* ws, float* aval,
+                            float* dgval, float* duval, float l1, float* dX, int** flag_out, hipStream_t s);
 
 // Backward SpMM: dX_t = sum over stored n of dg*WgT[n] + du*WuT[n] (fp32),
 // rows with skip[t] != 0 not written.

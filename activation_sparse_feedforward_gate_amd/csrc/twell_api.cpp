@@ -165,7 +165,7 @@ size_t bwd_layout(const twell_ffn_shape* sh, int32_t tau, void* ws, BwdWs* out) 
   w.part = (int*)c.take((size_t)(((T + 255) / 256) * F) * 4);
   w.start = (int*)c.take((size_t)(F + 1) * 4);
   w.entries = (uint32_t*)c.take((size_t)(T * per_row) * 4);
-  if (sh->in_dt == TWELL_BF16) w.uni = c.take(union_bwd_ws_bytes((int)T, (int)F));
+  if (sh->in_dt == TWELL_BF16) w.uni = c.take(union_bwd_ws_bytes((int)T, sh->d, (int)F));
   if (out) *out = w;
   return c.off;
 }
@@ -352,13 +352,20 @@ twell_status twell_ffn_bwd_hybrid_l1(const twell_ffn_shape* sh, const void* x, c
   e = launch_dense_rows_bwd(in_dt, x, WgT, bg, WuT, Wd, dY, T, d, F, w.list, w.nD, w.buf3, w.dbg_part, dX, dWgT,
                             dWuT, dWd, dbg, stream, l1);
   if (e != hipSuccess) return hip_status(e, "dense-row backward");
-  if (in_dt == DT_BF16)
-    e = launch_union_sddmm_bwd(x, dY, WuT, Wd, T, d, F, h, w.flag, w.uni, w.aval, w.dgval, w.duval, l1, stream);
-  else
+  if (in_dt == DT_BF16) {
+    int* ovf = nullptr;
+    e = launch_union_bwd(x, dY, WgT, WuT, Wd, T, d, F, h, w.flag, w.uni, w.aval, w.dgval, w.duval, l1, dX, &ovf,
+                         stream);
+    if (e != hipSuccess) return hip_status(e, "sparse backward union GEMMs");
+    // a value beyond the fp16 range: dX of the sparse rows per pair in fp32 (does nothing unless the flag is set)
+    e = launch_down_bf16(w.dgval, w.duval, WgT, WuT, T, d, F, h, dX, DT_F32, w.flag, stream, ovf);
+    if (e != hipSuccess) return hip_status(e, "sparse backward dX fallback");
+  } else {
     e = launch_sddmm_bwd(in_dt, x, dY, WuT, Wd, T, d, F, h, w.aval, w.dgval, w.duval, w.flag, stream, l1);
-  if (e != hipSuccess) return hip_status(e, "sparse backward SDDMM");
-  e = launch_spmm_dx(in_dt, w.dgval, w.duval, WgT, WuT, T, d, F, h, dX, w.flag, stream);
-  if (e != hipSuccess) return hip_status(e, "sparse backward dX");
+    if (e != hipSuccess) return hip_status(e, "sparse backward SDDMM");
+    e = launch_spmm_dx(in_dt, w.dgval, w.duval, WgT, WuT, T, d, F, h, dX, w.flag, stream);
+    if (e != hipSuccess) return hip_status(e, "sparse backward dX");
+  }
   e = launch_sparse_wgrad(in_dt, x, dY, T, d, F, h, w.flag, w.part, w.start, w.entries, w.aval, w.dgval,
                           w.duval, dWgT, dWuT, dWd, dbg, stream);
   return hip_status(e, "sparse weight gradients");

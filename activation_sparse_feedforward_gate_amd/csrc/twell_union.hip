@@ -61,6 +61,8 @@ struct UnionArgs {
   float* dgval;
   float* duval;
   float l1;
+  _Float16* dU16;         // backward: dU over the union positions (dG goes to adense)
+  const _Float16* Wu16;   // backward: fp16 copy of WuT (WgT's goes to Wd16)
 };
 
 __device__ __forceinline__ bool live(const UnionArgs& a, int t) {
@@ -415,33 +417,50 @@ __device__ __forceinline__ void bwd_union_tile(const UnionArgs& a, int b, int pt
     }
   }
   __syncthreads();
+  // per element: the stored pairs' a, dg, du at their TwELL slots, and dG, dU
+  // as fp16 over the union positions (zeros elsewhere, and in the positions
+  // [n_b, roundup64(n_b)) that the dX GEMM reads as whole K tiles); any value
+  // beyond the fp16 range raises the flag (the per-pair dX path then runs)
+  uint32_t vbits = 0;
+  const int pend = (nb + 63) & ~63;
 #pragma unroll
   for (int j = 0; j < Cfg::TN; ++j) {
     const int pr = Tile::col_of(j);
-    if (p0 + pr >= nb) continue;
-    const int tj = ul[p0 + pr] >> 6;
+    const int p = p0 + pr;
+    if (p >= pend) continue;
+    const bool inu = p < nb;
+    const int tj = inu ? ul[p] >> 6 : 0;
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int r0 = Tile::row_of(i, 4 * qq);                   // 4 consecutive rows r0..r0+3
-        const uint32_t s4 = *(const uint32_t*)(st0 + soff(pr, r0));
-        if (s4 == 0u) continue;
+        const uint32_t s4 = inu ? *(const uint32_t*)(st0 + soff(pr, r0)) : 0u;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int sl = (int)((s4 >> (8 * k)) & 255u);
+          const int t = m0 + r0 + k;
+          float dg = 0.f, du = 0.f;
           if (sl) {
-            const int t = m0 + r0 + k;
             const int64_t off = (((int64_t)(t >> 4) * a.NT + tj) * 64 + (sl - 1)) * 16 + (t & 15);
             const float h = a.hval[off];
             const float u = gu.acc[0][i][j][4 * qq + k], da = gd.acc[0][i][j][4 * qq + k];
+            dg = da * u + a.l1;
+            du = da * h;
             a.aval[off] = h * u;
-            a.dgval[off] = da * u + a.l1;
-            a.duval[off] = da * h;
+            a.dgval[off] = dg;
+            a.duval[off] = du;
+            vbits = max(vbits, max(__float_as_uint(dg), __float_as_uint(du)) & 0x7fffffffu);
+          }
+          if (t < a.T) {
+            a.adense[(int64_t)t * a.F + p] = (_Float16)dg;
+            a.dU16[(int64_t)t * a.F + p] = (_Float16)du;
           }
         }
       }
   }
+  const bool over = vbits > 0x477fe000u;   // above 65504, the largest finite fp16
+  if (__builtin_amdgcn_ballot_w64(over) != 0ull && (tid & 63) == 0) atomicOr(a.flag, 1);
 }
 
 template <class Cfg>
@@ -487,7 +506,9 @@ __global__ __launch_bounds__(256) void wd_to_f16_kernel(const uint16_t* Wd, _Flo
 // Down-projection over the union: y rows of the block, one column tile.  K
 // runs over the block's n_b positions; A = adense holds zeros in the
 // positions past n_b of the last K tile.
-template <class Cfg>
+// TWO: the backward's dX = dG.WgT + dU.WuT over the union (A = adense with
+// B = Wd16 holding WgT's fp16 copy, then A = dU16 with B = Wu16).
+template <class Cfg, bool TWO>
 __device__ __forceinline__ void down_union_tile(const UnionArgs& a, int b, int ct, char* st0, char* st1) {
   static_assert(Cfg::BM == UB, "one row block per M tile");
   const int nb = a.ucount[b];
@@ -497,6 +518,11 @@ __device__ __forceinline__ void down_union_tile(const UnionArgs& a, int b, int c
   const Operand A{a.adense, a.F, nullptr, a.T};
   const Operand B{a.Wd16, a.d, a.ulist + (int64_t)b * a.F, a.F};
   g.run(A, &B, m0, n0, nb, st0, st1);
+  if constexpr (TWO) {
+    const Operand A2{a.dU16, a.F, nullptr, a.T};
+    const Operand B2{a.Wu16, a.d, a.ulist + (int64_t)b * a.F, a.F};
+    g.run(A2, &B2, m0, n0, nb, st0, st1, false);
+  }
 #pragma unroll
   for (int j = 0; j < Cfg::TN; ++j) {
     const int col = n0 + Tile::col_of(j);
@@ -517,7 +543,7 @@ __device__ __forceinline__ void down_union_tile(const UnionArgs& a, int b, int c
 // Persistent workgroups walk the (row block, column tile) tiles; the
 // workgroups of XCD x take the row blocks b = x (mod 8), all column tiles of
 // a block together, so the block's adense rows are reused from that XCD's L2.
-template <class Cfg>
+template <class Cfg, bool TWO = false>
 __global__ __launch_bounds__(Cfg::NTH) void down_union_kernel(UnionArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
@@ -529,7 +555,7 @@ __global__ __launch_bounds__(Cfg::NTH) void down_union_kernel(UnionArgs a) {
   const int ntile = nbx * nct;
   for (int k = blockIdx.x >> 3; k < ntile; k += gridDim.x >> 3) {
     const int bi = k / nct;
-    down_union_tile<Cfg>(a, x + 8 * bi, k - bi * nct, st0, st1);
+    down_union_tile<Cfg, TWO>(a, x + 8 * bi, k - bi * nct, st0, st1);
     __syncthreads();
   }
 }
@@ -641,33 +667,65 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
   return hipGetLastError();
 }
 
-size_t union_bwd_ws_bytes(int T, int F) {
+size_t union_bwd_ws_bytes(int T, int d, int F) {
   const size_t nblk = (size_t)(T + UB - 1) / UB;
   const size_t nslab = (size_t)(T + 63) / 64;
-  return nblk * F * 4 + nblk * 4 + 256 + nslab * (F / 64) * 8 + 256 * 4;
+  auto r = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  return r(nblk * F * 4 + nblk * 4) + r(nslab * (F / 64) * 8) + 256 + 2 * r((size_t)T * F * 2) +
+         2 * r((size_t)F * d * 2);
 }
 
-hipError_t launch_union_sddmm_bwd(const void* x, const void* dY, const void* WuT, const void* Wd, int T, int d, int F,
-                                  const TwellView& h, const uint8_t* skip, void* ws, float* aval, float* dgval,
-                                  float* duval, float l1, hipStream_t s) {
+hipError_t launch_union_bwd(const void* x, const void* dY, const void* WgT, const void* WuT, const void* Wd, int T,
+                            int d, int F, const TwellView& h, const uint8_t* skip, void* ws, float* aval,
+                            float* dgval, float* duval, float l1, float* dX, int** flag_out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nblk = (T + UB - 1) / UB;
   char* w = (char*)ws;
   UnionArgs a{};
   a.x = x; a.WuT = WuT; a.Wd = Wd; a.dY = dY; a.T = T; a.d = d; a.F = F; a.NT = F / 64;
   a.mask = h.mask; a.skip = skip; a.hval = (const float*)h.val; a.hidx = h.idx; a.hwidth = h.width;
+  auto r = [](size_t v) { return (v + 255) & ~(size_t)255; };
   a.ulist = (int*)w;
   a.ucount = (int*)(w + (size_t)nblk * F * 4);
-  uint64_t* U = (uint64_t*)(w + (((size_t)nblk * F * 4 + (size_t)nblk * 4 + 255) & ~(size_t)255));
-  a.flag = (int*)((char*)U + (((size_t)((T + 63) / 64) * a.NT * 8 + 255) & ~(size_t)255));   // the list kernel clears it
+  w += r((size_t)nblk * F * 4 + (size_t)nblk * 4);
+  uint64_t* U = (uint64_t*)w;
+  w += r((size_t)((T + 63) / 64) * a.NT * 8);
+  a.flag = (int*)w;                         // the list kernel clears it
+  w += 256;
+  a.adense = (_Float16*)w;                  // dG over the union positions
+  w += r((size_t)T * F * 2);
+  a.dU16 = (_Float16*)w;
+  w += r((size_t)T * F * 2);
+  a.Wd16 = (const _Float16*)w;              // fp16 copy of WgT
+  w += r((size_t)F * d * 2);
+  a.Wu16 = (const _Float16*)w;              // fp16 copy of WuT
   a.lrows = UB;
   a.aval = aval; a.dgval = dgval; a.duval = duval; a.l1 = l1;
+  a.y = dX; a.out_bf16 = 0;
+  if (flag_out) *flag_out = a.flag;
   union_lists_launch(a, U, s);
   using BwdUnionCfg = DmaCfg<UB, 256, 2, 4>;
   const int npt = (F + BwdUnionCfg::BN - 1) / BwdUnionCfg::BN;
-  const int tiles_per_xcd = ((nblk + 7) / 8) * npt;
-  const unsigned grid = (unsigned)(8 * std::max(1, std::min(device_cus() / 8, tiles_per_xcd)));
-  hipLaunchKernelGGL((bwd_union_kernel<BwdUnionCfg>), dim3(grid), dim3(BwdUnionCfg::NTH), 0, s, a);
+  const int nbx_max = (nblk + 7) / 8;
+  const int cus = device_cus();
+  auto grid_for = [&](int tiles_per_xcd) { return (unsigned)(8 * std::max(1, std::min(cus / 8, tiles_per_xcd))); };
+  hipLaunchKernelGGL((bwd_union_kernel<BwdUnionCfg>), dim3(grid_for(nbx_max * npt)), dim3(BwdUnionCfg::NTH), 0, s, a);
+  // fp16 copies of WgT and WuT for the dX GEMM (a value beyond the fp16 range raises the flag)
+  const int64_t n8 = (int64_t)F * d / 8;
+  hipLaunchKernelGGL(wd_to_f16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, (const uint16_t*)WgT,
+                     (_Float16*)a.Wd16, n8, a.flag);
+  hipLaunchKernelGGL(wd_to_f16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, (const uint16_t*)WuT,
+                     (_Float16*)a.Wu16, n8, a.flag);
+  // dX of the live rows = dG.WgT + dU.WuT over the union (stands down when the flag is set)
+  if (d % 256 == 0)
+    hipLaunchKernelGGL((down_union_kernel<DownUnionCfg, true>), dim3(grid_for(nbx_max * (d / 256))),
+                       dim3(DownUnionCfg::NTH), 0, s, a);
+  else if (d % 128 == 0)
+    hipLaunchKernelGGL((down_union_kernel<DownUnionCfg128, true>), dim3(grid_for(nbx_max * (d / 128))),
+                       dim3(DownUnionCfg128::NTH), 0, s, a);
+  else
+    hipLaunchKernelGGL((down_union_kernel<DownUnionCfg64, true>), dim3(grid_for(nbx_max * (d / 64))),
+                       dim3(DownUnionCfg64::NTH), 0, s, a);
   return hipGetLastError();
 }
 

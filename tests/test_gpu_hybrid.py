@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from workloads import make_workload
+from workloads import make_workload, round_bf16
 
 from gpu_util import log, mat_to_numpy, rel_fro, to_dev
 
@@ -200,3 +200,16 @@ def test_hybrid_l1_penalty(torch, tw, name, kw, mean):
     check_full(w, got, w.tau, l1c=O.l1_coefficient(lam, w.T, mean))
     if name == "hybrid":
         assert 0 < got["nD"] < w.T                                             # both branches ran
+
+
+def test_hybrid_fp16_overflow_falls_back(torch, tw):
+    """dG or dU beyond the fp16 range (dY scaled up) makes the union dX GEMM
+    stand down for the per-pair fp32 kernel; every gradient must still match."""
+    w = make_workload("hybrid", T=520, d=256, f=1280)
+    w.dY[:] = round_bf16(np.asarray(w.dY, dtype=np.float32) * np.float32(1.0e5))
+    ref = O.ffn_dense_bwd(w.x, w.WgT, w.bg, w.WuT, w.Wd, w.dY)
+    dA = np.asarray(w.dY, dtype=np.float64) @ np.asarray(w.Wd, dtype=np.float64).T
+    assert np.abs(dA * ref["fwd"]["u"]).max() > 65504.0           # the case really overflows fp16
+    log("[hybrid] fp16 overflow in the backward")
+    got = run_train(torch, tw, w, w.tau)
+    check_full(w, got, w.tau)
