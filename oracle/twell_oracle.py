@@ -49,6 +49,7 @@ __all__ = [
     "ffn_sparse_fwd", "ffn_sparse_fwd_loops", "classify_rows",
     "hybrid_fwd_bwd", "hybrid_fwd_bwd_loops", "ffn_fwd_rows", "ffn_bwd_sampled",
     "relu_ffn_dense_fwd", "relu_ffn_sparse_fwd",
+    "CompactTwell", "twell_compact", "twell_expand",
 ]
 
 
@@ -535,3 +536,53 @@ def relu_ffn_sparse_fwd(x, W1T, b1, W2, R: int = 16, C: int = 64) -> dict:
         order = np.argsort(n[sel], kind="stable")
         y[tt] = (h[sel][order][:, None] * W2[n[sel][order]]).sum(axis=0)
     return {"y": y, "twell": m}
+
+
+# --------------------------------------------------------------------------
+# Compact TwELL: capacity W < C slots per (row, tile)
+# --------------------------------------------------------------------------
+
+@dataclass
+class CompactTwell:
+    """TwELL with capacity W slots per (row, tile) instead of C.
+
+    [IN] section "Слитые CUDA-ядра для инференса и гибрид для обучения": in
+    training, well-sparse rows are kept in a compact sparse matrix and rows
+    with many active values go to a dense branch; [GE] paragraph 1 and [GI]
+    paragraph 1 report reduced peak memory.  Reading: a fixed capacity W per
+    (row, tile), so tile (i, j) sits at a fixed offset (i*NT + j)*W*R and needs
+    no offset table; a row with more than W non-zeros in some tile cannot be
+    stored whole and is flagged (ovf) for the dense branch.
+    cnt [T, NT] true counts; width [NR, NT] = min(full width, W); val, idx
+    [NR, NT, W, R] = the first W slots of the full form; ovf [T] bool.
+    """
+    T: int
+    F: int
+    R: int
+    C: int
+    W: int
+    cnt: np.ndarray
+    width: np.ndarray
+    val: np.ndarray
+    idx: np.ndarray
+    ovf: np.ndarray
+
+
+def twell_compact(m: TwellMat, W: int) -> CompactTwell:
+    """Keep the first W slots of every (row, tile); flag the rows that have
+    more than W non-zeros in some tile."""
+    assert 1 <= W <= m.C
+    ovf = (m.cnt > W).any(axis=1) if m.cnt.size else np.zeros(m.T, dtype=bool)
+    return CompactTwell(m.T, m.F, m.R, m.C, W, m.cnt.copy(), np.minimum(m.width, W),
+                        m.val[:, :, :W, :].copy(), m.idx[:, :, :W, :].copy(), ovf)
+
+
+def twell_expand(c: CompactTwell) -> TwellMat:
+    """Back to the capacity-C form: the stored slots in place, the others zero.
+    Rows flagged in ovf keep their true counts but only W slots per tile."""
+    NR, NT = c.width.shape
+    val = np.zeros((NR, NT, c.C, c.R), dtype=c.val.dtype)
+    idx = np.zeros((NR, NT, c.C, c.R), dtype=c.idx.dtype)
+    val[:, :, :c.W, :] = c.val
+    idx[:, :, :c.W, :] = c.idx
+    return TwellMat(c.T, c.F, c.R, c.C, c.cnt.copy(), c.width.copy(), val, idx)

@@ -461,3 +461,53 @@ def test_relu_ffn_bias_only_closed_form():
         y = fn(rng.standard_normal((T, d)), np.zeros((f, d)), b1, W2)["y"]
         for t in range(T):
             np.testing.assert_allclose(y[t], want, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ compact TwELL
+
+def test_compact_full_capacity_is_identity():
+    rng = np.random.default_rng(40)
+    G = rng.standard_normal((37, 200)) - 0.5
+    m = O.twell_pack(G, R=16, C=64)
+    c = O.twell_compact(m, 64)
+    assert not c.ovf.any()
+    e = O.twell_expand(c)
+    np.testing.assert_array_equal(e.width, m.width)
+    np.testing.assert_array_equal(e.val.view(np.uint64), m.val.view(np.uint64))
+    np.testing.assert_array_equal(e.idx, m.idx)
+
+
+@pytest.mark.parametrize("W", [1, 4, 8])
+def test_compact_keeps_every_row_that_fits(W):
+    """Rows flagged exactly when some tile holds more than W non-zeros; every
+    other row's entries survive compact -> expand bit-exactly; the value
+    arrays shrink by W / C."""
+    rng = np.random.default_rng(41 + W)
+    T, F = 70, 320
+    G = rng.standard_normal((T, F)) - 1.6          # about 5% positive
+    G[::9] += 2.2                                  # some much denser rows
+    m = O.twell_pack(G, R=16, C=64)
+    c = O.twell_compact(m, W)
+    counts = np.array([[int((G[t, j * 64:(j + 1) * 64] > 0).sum()) for j in range(F // 64)] for t in range(T)])
+    np.testing.assert_array_equal(c.ovf, (counts > W).any(axis=1))
+    assert c.ovf.any() and not c.ovf.all()
+    assert c.val.nbytes * 64 == m.val.nbytes * W
+    keep = np.nonzero(~c.ovf)[0]
+    t0, n0, v0 = O.twell_entries(m, rows=keep)
+    t1, n1, v1 = O.twell_entries(O.twell_expand(c), rows=keep)
+    np.testing.assert_array_equal(t0, t1)
+    np.testing.assert_array_equal(n0, n1)
+    np.testing.assert_array_equal(v0.view(np.uint64), v1.view(np.uint64))
+    for t in keep:
+        for j in range(F // 64):
+            row = [G[t, j * 64 + c_] for c_ in range(64) if G[t, j * 64 + c_] > 0]
+            assert len(row) == counts[t, j] <= W
+
+
+def test_compact_bruteforce_overflow_flags():
+    """All 2^8 sign patterns of a 1x8 tile (C = 8), capacity 3: the row is
+    flagged iff more than 3 entries are positive."""
+    for bits in range(256):
+        G = np.array([[1.0 if (bits >> k) & 1 else -1.0 for k in range(8)]])
+        c = O.twell_compact(O.twell_pack(G, R=1, C=8), 3)
+        assert bool(c.ovf[0]) == (bin(bits).count("1") > 3)
