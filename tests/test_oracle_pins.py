@@ -477,14 +477,14 @@ def test_compact_full_capacity_is_identity():
     np.testing.assert_array_equal(e.idx, m.idx)
 
 
-@pytest.mark.parametrize("W", [1, 4, 8])
+@pytest.mark.parametrize("W", [2, 4, 8])
 def test_compact_keeps_every_row_that_fits(W):
     """Rows flagged exactly when some tile holds more than W non-zeros; every
     other row's entries survive compact -> expand bit-exactly; the value
     arrays shrink by W / C."""
     rng = np.random.default_rng(41 + W)
     T, F = 70, 320
-    G = rng.standard_normal((T, F)) - 1.6          # about 5% positive
+    G = rng.standard_normal((T, F)) - 2.3          # about 1% positive
     G[::9] += 2.2                                  # some much denser rows
     m = O.twell_pack(G, R=16, C=64)
     c = O.twell_compact(m, W)
