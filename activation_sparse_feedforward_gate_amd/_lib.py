@@ -31,6 +31,12 @@ class c_twell_mat(ctypes.Structure):
                 ("val", ctypes.c_void_p), ("idx", ctypes.c_void_p), ("mask", ctypes.c_void_p)]
 
 
+class c_twell_cmat(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("F", ctypes.c_int32), ("W", ctypes.c_int32),
+                ("cnt", ctypes.c_void_p), ("width", ctypes.c_void_p), ("val", ctypes.c_void_p),
+                ("idx", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("ovf", ctypes.c_void_p)]
+
+
 class c_twell_ffn_shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("F", ctypes.c_int32),
                 ("in_dt", ctypes.c_int), ("out_dt", ctypes.c_int)]
@@ -80,12 +86,21 @@ def lib() -> ctypes.CDLL:
         L.twell_ffn_dense_bwd_workspace.restype = sz
         L.twell_ffn_dense_bwd.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                           sz, vp]
+        L.twell_cmat_bytes.argtypes = [i32, i32, i32, P(sz)]
+        L.twell_cmat_bytes.restype = sz
+        L.twell_compact.argtypes = [P(c_twell_mat), P(c_twell_cmat), vp]
+        L.twell_expand.argtypes = [P(c_twell_cmat), P(c_twell_mat), vp]
+        L.twell_ffn_bwd_compact_workspace.argtypes = [P(c_twell_ffn_shape), i32]
+        L.twell_ffn_bwd_compact_workspace.restype = sz
+        L.twell_ffn_bwd_hybrid_compact.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_cmat),
+                                                   i32, ctypes.c_float, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.twell_status_string.argtypes = [ctypes.c_int]
         L.twell_status_string.restype = ctypes.c_char_p
         L.twell_last_error.argtypes = []
         L.twell_last_error.restype = ctypes.c_char_p
         for name in ("twell_pack", "twell_unpack", "twell_ffn_fwd", "twell_ffn_fwd_ex", "twell_ffn_bwd_hybrid",
-                     "twell_ffn_bwd_hybrid_l1", "twell_relu_ffn_fwd", "twell_relu_ffn_dense_fwd",
+                     "twell_ffn_bwd_hybrid_l1", "twell_compact", "twell_expand", "twell_ffn_bwd_hybrid_compact",
+                     "twell_relu_ffn_fwd", "twell_relu_ffn_dense_fwd",
                      "twell_ffn_dense_fwd", "twell_ffn_dense_bwd",
                      "twell_gate_pack",
                      "twell_sparse_up", "twell_sparse_down"):
@@ -174,6 +189,39 @@ def alloc_twell_mat(T: int, F: int, vdtype: int = TWELL_F32, device="cuda", with
     )
 
 
+@dataclass
+class TwellCMat:
+    """Device arrays of one compact TwELL matrix (see twell_cmat in include/twell.h)."""
+    T: int
+    F: int
+    W: int
+    cnt: object
+    width: object
+    val: object
+    idx: object
+    mask: object
+    ovf: object
+
+    def c(self) -> c_twell_cmat:
+        return c_twell_cmat(self.T, self.F, self.W, _ptr(self.cnt), _ptr(self.width), _ptr(self.val),
+                            _ptr(self.idx), _ptr(self.mask), _ptr(self.ovf))
+
+
+def alloc_twell_cmat(T: int, F: int, W: int, device="cuda") -> TwellCMat:
+    """Allocate the arrays of a T x F compact TwELL matrix of capacity W with torch (plumbing only)."""
+    import torch
+    NR, NT = -(-T // R_TILE), -(-F // C_TILE)
+    return TwellCMat(
+        T, F, W,
+        cnt=torch.empty((T, NT), dtype=torch.uint8, device=device),
+        width=torch.empty((NR, NT), dtype=torch.uint8, device=device),
+        val=torch.empty((NR, NT, W, R_TILE), dtype=torch.float32, device=device),
+        idx=torch.empty((NR, NT, W, R_TILE), dtype=torch.uint8, device=device),
+        mask=torch.empty((T, NT), dtype=torch.int64, device=device),
+        ovf=torch.empty((T,), dtype=torch.uint8, device=device),
+    )
+
+
 def ffn_shape(T: int, d: int, F: int, in_dt: int, out_dt: int) -> c_twell_ffn_shape:
     return c_twell_ffn_shape(T, d, F, in_dt, out_dt)
 
@@ -254,6 +302,38 @@ def twell_ffn_bwd_hybrid_l1(shape, x, WgT, bg, WuT, Wd, dY, saved_h: TwellMat, d
                                          _ptr(dbg), _ptr(n_dense_rows), _ptr(ws),
                                          ws.numel() * ws.element_size() if ws is not None else 0,
                                          _stream(stream)))
+
+
+def twell_cmat_bytes(T: int, F: int, W: int):
+    parts = (ctypes.c_size_t * 6)()
+    total = lib().twell_cmat_bytes(T, F, W, parts)
+    return int(total), [int(p) for p in parts]
+
+
+def twell_compact(full: TwellMat, out: TwellCMat, stream=None) -> None:
+    fm, cm = full.c(), out.c()
+    _check(lib().twell_compact(ctypes.byref(fm), ctypes.byref(cm), _stream(stream)))
+
+
+def twell_expand(c: TwellCMat, full: TwellMat, stream=None) -> None:
+    cm, fm = c.c(), full.c()
+    _check(lib().twell_expand(ctypes.byref(cm), ctypes.byref(fm), _stream(stream)))
+
+
+def twell_ffn_bwd_compact_workspace(shape: c_twell_ffn_shape, dense_row_threshold: int) -> int:
+    return int(lib().twell_ffn_bwd_compact_workspace(ctypes.byref(shape), int(dense_row_threshold)))
+
+
+def twell_ffn_bwd_hybrid_compact(shape, x, WgT, bg, WuT, Wd, dY, saved: TwellCMat, dense_row_threshold: int,
+                                 l1_lambda: float, l1_per_token_mean: bool, dX, dWgT, dWuT, dWd, dbg, n_dense_rows,
+                                 ws, stream=None) -> None:
+    cm = saved.c()
+    _check(lib().twell_ffn_bwd_hybrid_compact(ctypes.byref(shape), _ptr(x), _ptr(WgT), _ptr(bg), _ptr(WuT),
+                                              _ptr(Wd), _ptr(dY), ctypes.byref(cm), int(dense_row_threshold),
+                                              float(l1_lambda), int(bool(l1_per_token_mean)), _ptr(dX), _ptr(dWgT),
+                                              _ptr(dWuT), _ptr(dWd), _ptr(dbg), _ptr(n_dense_rows), _ptr(ws),
+                                              ws.numel() * ws.element_size() if ws is not None else 0,
+                                              _stream(stream)))
 
 
 def twell_ffn_fwd_ex(shape, x, WgT, bg, WuT, Wd, y, saved_h: Optional[TwellMat], dense_row_threshold: int,

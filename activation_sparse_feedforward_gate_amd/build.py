@@ -26,7 +26,7 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function",
 ]
-SOURCES = ["twell_api.cpp", "twell_gate.hip", "twell_sparse.hip", "twell_sparse_bf16.hip", "twell_union.hip", "twell_hybrid.hip", "dense_ffn.hip", "dense_train.hip", "twell_decode.hip"]
+SOURCES = ["twell_api.cpp", "twell_gate.hip", "twell_sparse.hip", "twell_sparse_bf16.hip", "twell_union.hip", "twell_hybrid.hip", "dense_ffn.hip", "dense_train.hip", "twell_decode.hip", "twell_compact.hip"]
 
 
 def _compile(src: str) -> str:

@@ -77,10 +77,31 @@ hipError_t launch_spmm_dx(int in_dt, const float* dgval, const float* duval, con
                           int T, int d, int F, const TwellView& pat, float* dX, const uint8_t* skip,
                           hipStream_t s);
 
-// Row classification of the hybrid format: flag[t] = (sum_j cnt[t][j] > tau);
+// Compact TwELL (capacity W per (row, tile)) <-> the capacity-64 form; see
+// twell_compact.hip.  Full side: cnt, width, val (fp32), idx, mask; compact
+// side: ccnt, cwidth, cval, cidx, cmask, ovf (flags written when compacting).
+struct CompactArgs {
+  int T, NT, W;
+  int64_t ntiles;
+  uint8_t* cnt;
+  uint8_t* width;
+  float* val;
+  uint8_t* idx;
+  uint64_t* mask;
+  uint8_t* ccnt;
+  uint8_t* cwidth;
+  float* cval;
+  uint8_t* cidx;
+  uint64_t* cmask;
+  uint8_t* ovf;
+};
+hipError_t launch_compact(const CompactArgs& a, bool expand, hipStream_t s);
+
+// Row classification of the hybrid format: flag[t] = (sum_j cnt[t][j] > tau)
+// or force[t] (force may be null);
 // list[0..n) = flagged rows ascending; *n_out = n (and *n_copy if non-null).
 hipError_t launch_classify(const TwellView& h, int tau, uint8_t* flag, int* list, int* n_out, int* n_copy,
-                           hipStream_t s);
+                           hipStream_t s, const uint8_t* force = nullptr);
 
 // Dense-branch forward on the listed rows: actbuf [T][F] (rows < n used)
 // receives ReLU(g)*u, then y[list[r]] = actbuf[r].Wd.

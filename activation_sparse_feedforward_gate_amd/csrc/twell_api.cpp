@@ -80,6 +80,27 @@ twell_status check_mat(const twell_mat* m, bool need_mask) {
   return TWELL_OK;
 }
 
+void cmat_parts(int64_t T, int64_t F, int64_t W, size_t parts[6]) {
+  const int64_t NR = (T + GPU_R - 1) / GPU_R, NT = F / GPU_C;
+  parts[0] = (size_t)(T * NT);
+  parts[1] = (size_t)(NR * NT);
+  parts[2] = (size_t)(NR * NT * W * GPU_R) * 4;
+  parts[3] = (size_t)(NR * NT * W * GPU_R);
+  parts[4] = (size_t)(T * NT) * 8;
+  parts[5] = (size_t)T;
+}
+
+twell_status check_cmat(const twell_cmat* m) {
+  if (!m) return fail(TWELL_EINVAL, "twell_cmat is NULL");
+  if (m->T < 0 || m->F <= 0) return fail(TWELL_EINVAL, "bad twell_cmat shape T=%d F=%d", m->T, m->F);
+  if (m->F % GPU_C != 0) return fail(TWELL_EUNSUPPORTED, "F=%d is not a multiple of 64", m->F);
+  if (m->W < 1 || m->W > GPU_C) return fail(TWELL_EINVAL, "capacity W=%d outside 1..64", m->W);
+  if (m->T > 0 && (!m->cnt || !m->width || !m->val || !m->idx || !m->mask || !m->ovf))
+    return fail(TWELL_EINVAL, "twell_cmat array is NULL");
+  if (!aligned16(m->val) || !aligned16(m->mask)) return fail(TWELL_EINVAL, "twell_cmat arrays must be 16-byte aligned");
+  return TWELL_OK;
+}
+
 TwellView view_of(const twell_mat* m) {
   TwellView v;
   v.T = m->T; v.F = m->F; v.NT = m->F / GPU_C; v.NR = (m->T + GPU_R - 1) / GPU_R;
@@ -304,6 +325,34 @@ size_t twell_ffn_bwd_workspace(const twell_ffn_shape* sh, int32_t dense_row_thre
   return bwd_layout(sh, dense_row_threshold, nullptr, nullptr);
 }
 
+static twell_status bwd_run(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
+                            const void* WuT, const void* Wd, const void* dY, const TwellView& h,
+                            const uint8_t* force, int32_t dense_row_threshold, float l1_lambda,
+                            int32_t l1_per_token_mean, float* dX, float* dWgT, float* dWuT, float* dWd, float* dbg,
+                            int32_t* n_dense_rows, const BwdWs& w, hipStream_t stream);
+
+// Checks shared by the hybrid backward entry points (all but the saved state).
+static twell_status check_bwd_args(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
+                                   const void* WuT, const void* Wd, const void* dY, float l1_lambda,
+                                   int32_t l1_per_token_mean, float* dX, float* dWgT, float* dWuT, float* dWd,
+                                   float* dbg) {
+  twell_status st = check_shape(sh);
+  if (!(l1_lambda >= 0.f) || l1_lambda > 3.0e38f)
+    return fail(TWELL_EINVAL, "l1_lambda must be finite and >= 0 (got %g)", (double)l1_lambda);
+  if (l1_per_token_mean != 0 && l1_per_token_mean != 1)
+    return fail(TWELL_EINVAL, "l1_per_token_mean must be 0 or 1");
+  if (st) return st;
+  if (!WgT || !WuT || !Wd || !dWgT || !dWuT || !dWd) return fail(TWELL_EINVAL, "NULL weight or gradient argument");
+  if (sh->T > 0 && (!x || !dY || !dX)) return fail(TWELL_EINVAL, "NULL tensor argument");
+  for (const void* p : {x, WgT, bg, WuT, Wd, dY, (const void*)dX, (const void*)dWgT, (const void*)dWuT,
+                        (const void*)dWd, (const void*)dbg})
+    if (!aligned16(p)) return fail(TWELL_EINVAL, "tensors must be 16-byte aligned");
+  const int64_t NR = (sh->T + GPU_R - 1) / GPU_R;
+  if (NR * (sh->F / GPU_C) * GPU_C * GPU_R >= ((int64_t)1 << 32))
+    return fail(TWELL_EUNSUPPORTED, "T x F too large for 32-bit TwELL slot offsets");
+  return TWELL_OK;
+}
+
 twell_status twell_ffn_bwd_hybrid(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
                                   const void* WuT, const void* Wd, const void* dY, const twell_mat* saved_h,
                                   int32_t dense_row_threshold, float* dX, float* dWgT, float* dWuT, float* dWd,
@@ -318,36 +367,36 @@ twell_status twell_ffn_bwd_hybrid_l1(const twell_ffn_shape* sh, const void* x, c
                                      int32_t dense_row_threshold, float l1_lambda, int32_t l1_per_token_mean,
                                      float* dX, float* dWgT, float* dWuT, float* dWd, float* dbg,
                                      int32_t* n_dense_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
-  twell_status st = check_shape(sh);
-  if (!(l1_lambda >= 0.f) || l1_lambda > 3.0e38f)
-    return fail(TWELL_EINVAL, "l1_lambda must be finite and >= 0 (got %g)", (double)l1_lambda);
-  if (l1_per_token_mean != 0 && l1_per_token_mean != 1)
-    return fail(TWELL_EINVAL, "l1_per_token_mean must be 0 or 1");
+  twell_status st = check_bwd_args(sh, x, WgT, bg, WuT, Wd, dY, l1_lambda, l1_per_token_mean, dX, dWgT, dWuT, dWd,
+                                   dbg);
   if (st) return st;
-  if (!WgT || !WuT || !Wd || !dWgT || !dWuT || !dWd) return fail(TWELL_EINVAL, "NULL weight or gradient argument");
-  if (sh->T > 0 && (!x || !dY || !dX)) return fail(TWELL_EINVAL, "NULL tensor argument");
-  for (const void* p : {x, WgT, bg, WuT, Wd, dY, (const void*)dX, (const void*)dWgT, (const void*)dWuT,
-                        (const void*)dWd, (const void*)dbg})
-    if (!aligned16(p)) return fail(TWELL_EINVAL, "tensors must be 16-byte aligned");
   st = check_mat(saved_h, true);
   if (st) return st;
   if (saved_h->T != sh->T || saved_h->F != sh->F || saved_h->vdtype != TWELL_F32)
     return fail(TWELL_EINVAL, "saved_h must be T x F with fp32 values");
-  const int64_t NR = (sh->T + GPU_R - 1) / GPU_R;
-  if (NR * (sh->F / GPU_C) * GPU_C * GPU_R >= ((int64_t)1 << 32))
-    return fail(TWELL_EUNSUPPORTED, "T x F too large for 32-bit TwELL slot offsets");
   const size_t need = bwd_layout(sh, dense_row_threshold, nullptr, nullptr);
   if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
 
   BwdWs w;
   bwd_layout(sh, dense_row_threshold, ws, &w);
+  return bwd_run(sh, x, WgT, bg, WuT, Wd, dY, view_of(saved_h), nullptr, dense_row_threshold, l1_lambda,
+                 l1_per_token_mean, dX, dWgT, dWuT, dWd, dbg, n_dense_rows, w, stream);
+}
+
+// Both hybrid backward entry points after their checks: h is the capacity-64
+// TwELL of the forward's activations; rows with force[t] set (may be null)
+// take the dense branch whatever their count.
+static twell_status bwd_run(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
+                            const void* WuT, const void* Wd, const void* dY, const TwellView& h,
+                            const uint8_t* force, int32_t dense_row_threshold, float l1_lambda,
+                            int32_t l1_per_token_mean, float* dX, float* dWgT, float* dWuT, float* dWd, float* dbg,
+                            int32_t* n_dense_rows, const BwdWs& w, hipStream_t stream) {
   const int in_dt = sh->in_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
-  const TwellView h = view_of(saved_h);
   const int T = sh->T, d = sh->d, F = sh->F;
   // gradient coefficient of the penalty: lambda for a sum over the
   // activations, lambda / T for a mean over tokens
   const float l1 = (l1_per_token_mean && T > 0) ? l1_lambda / (float)T : l1_lambda;
-  hipError_t e = launch_classify(h, dense_row_threshold, w.flag, w.list, w.nD, n_dense_rows, stream);
+  hipError_t e = launch_classify(h, dense_row_threshold, w.flag, w.list, w.nD, n_dense_rows, stream, force);
   if (e != hipSuccess) return hip_status(e, "row classification");
   e = launch_dense_rows_bwd(in_dt, x, WgT, bg, WuT, Wd, dY, T, d, F, w.list, w.nD, w.buf3, w.dbg_part, dX, dWgT,
                             dWuT, dWd, dbg, stream, l1);
@@ -369,6 +418,103 @@ twell_status twell_ffn_bwd_hybrid_l1(const twell_ffn_shape* sh, const void* x, c
   e = launch_sparse_wgrad(in_dt, x, dY, T, d, F, h, w.flag, w.part, w.start, w.entries, w.aval, w.dgval,
                           w.duval, dWgT, dWuT, dWd, dbg, stream);
   return hip_status(e, "sparse weight gradients");
+}
+
+// ------------------------------------------------------------------ compact TwELL
+
+size_t twell_cmat_bytes(int32_t T, int32_t F, int32_t W, size_t parts[6]) {
+  size_t p[6] = {0, 0, 0, 0, 0, 0};
+  if (T >= 0 && F > 0 && F % GPU_C == 0 && W >= 1 && W <= GPU_C) cmat_parts(T, F, W, p);
+  if (parts) memcpy(parts, p, sizeof(p));
+  return p[0] + p[1] + p[2] + p[3] + p[4] + p[5];
+}
+
+static CompactArgs compact_args(const twell_mat* full, const twell_cmat* c) {
+  CompactArgs a{};
+  a.T = c->T; a.NT = c->F / GPU_C; a.W = c->W;
+  a.ntiles = (int64_t)((c->T + GPU_R - 1) / GPU_R) * a.NT;
+  a.cnt = full->cnt; a.width = full->width; a.val = (float*)full->val; a.idx = full->idx; a.mask = full->mask;
+  a.ccnt = c->cnt; a.cwidth = c->width; a.cval = c->val; a.cidx = c->idx; a.cmask = c->mask; a.ovf = c->ovf;
+  return a;
+}
+
+static twell_status check_pair(const twell_mat* full, const twell_cmat* c) {
+  twell_status st = check_mat(full, true);
+  if (st) return st;
+  st = check_cmat(c);
+  if (st) return st;
+  if (full->vdtype != TWELL_F32) return fail(TWELL_EINVAL, "compact TwELL holds fp32 values");
+  if (full->T != c->T || full->F != c->F)
+    return fail(TWELL_EINVAL, "shape mismatch: %d x %d vs %d x %d", full->T, full->F, c->T, c->F);
+  return TWELL_OK;
+}
+
+twell_status twell_compact(const twell_mat* full, twell_cmat* out, hipStream_t stream) {
+  twell_status st = check_pair(full, out);
+  if (st) return st;
+  if (out->T == 0) return TWELL_OK;
+  return hip_status(launch_compact(compact_args(full, out), false, stream), "twell_compact");
+}
+
+twell_status twell_expand(const twell_cmat* in, twell_mat* full, hipStream_t stream) {
+  twell_status st = check_pair(full, in);
+  if (st) return st;
+  if (in->T == 0) return TWELL_OK;
+  return hip_status(launch_compact(compact_args(full, in), true, stream), "twell_expand");
+}
+
+// The compact backward's workspace: the hybrid backward's, then a
+// capacity-64 value and index array that the stored slots are moved into.
+static size_t bwd_compact_layout(const twell_ffn_shape* sh, int32_t tau, void* ws, BwdWs* out, float** val,
+                                 uint8_t** idx) {
+  size_t parts[5];
+  mat_parts(sh->T, sh->F, GPU_R, GPU_C, TWELL_F32, parts);
+  Carver c(ws);
+  c.take(bwd_layout(sh, tau, nullptr, nullptr));
+  if (ws) bwd_layout(sh, tau, ws, out);
+  float* v = (float*)c.take(parts[2]);
+  uint8_t* ix = (uint8_t*)c.take(parts[3]);
+  if (val) *val = v;
+  if (idx) *idx = ix;
+  return c.off;
+}
+
+size_t twell_ffn_bwd_compact_workspace(const twell_ffn_shape* sh, int32_t dense_row_threshold) {
+  if (!sh || check_shape(sh) != TWELL_OK) return 0;
+  return bwd_compact_layout(sh, dense_row_threshold, nullptr, nullptr, nullptr, nullptr);
+}
+
+twell_status twell_ffn_bwd_hybrid_compact(const twell_ffn_shape* sh, const void* x, const void* WgT,
+                                          const void* bg, const void* WuT, const void* Wd, const void* dY,
+                                          const twell_cmat* saved, int32_t dense_row_threshold, float l1_lambda,
+                                          int32_t l1_per_token_mean, float* dX, float* dWgT, float* dWuT,
+                                          float* dWd, float* dbg, int32_t* n_dense_rows, void* ws,
+                                          size_t ws_bytes, hipStream_t stream) {
+  twell_status st = check_bwd_args(sh, x, WgT, bg, WuT, Wd, dY, l1_lambda, l1_per_token_mean, dX, dWgT, dWuT, dWd,
+                                   dbg);
+  if (st) return st;
+  st = check_cmat(saved);
+  if (st) return st;
+  if (saved->T != sh->T || saved->F != sh->F)
+    return fail(TWELL_EINVAL, "saved must be T x F (T=%d F=%d)", sh->T, sh->F);
+  const size_t need = bwd_compact_layout(sh, dense_row_threshold, nullptr, nullptr, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+
+  BwdWs w;
+  float* val = nullptr;
+  uint8_t* idx = nullptr;
+  bwd_compact_layout(sh, dense_row_threshold, ws, &w, &val, &idx);
+  // capacity-64 view: counts, widths and masks are the compact arrays
+  // themselves; only the stored slots move
+  twell_mat full{saved->T, saved->F, GPU_R, GPU_C, TWELL_F32, saved->cnt, saved->width, val, idx, saved->mask};
+  if (sh->T > 0) {
+    CompactArgs a = compact_args(&full, saved);
+    a.T = 0;  // the per-row arrays are shared: only the tiles move
+    hipError_t e = launch_compact(a, true, stream);
+    if (e != hipSuccess) return hip_status(e, "compact TwELL expansion");
+  }
+  return bwd_run(sh, x, WgT, bg, WuT, Wd, dY, view_of(&full), saved->ovf, dense_row_threshold, l1_lambda,
+                 l1_per_token_mean, dX, dWgT, dWuT, dWd, dbg, n_dense_rows, w, stream);
 }
 
 static twell_status check_tensors(const twell_ffn_shape* sh, std::initializer_list<const void*> ptrs) {

@@ -31,7 +31,7 @@ namespace twell {
 
 // One wave per row: nnz = sum of the row's per-tile counts; flag = nnz > tau.
 __global__ __launch_bounds__(256) void row_classify_kernel(const uint8_t* cnt, int T, int NT, int tau,
-                                                           uint8_t* flag) {
+                                                           const uint8_t* force, uint8_t* flag) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void row_classify_kernel(const uint8_t* cnt, i
   for (int j = lane; j < NT; j += 64) s += cnt[(int64_t)t * NT + j];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-  if (lane == 0) flag[t] = (s > tau) ? 1 : 0;
+  if (lane == 0) flag[t] = (s > tau || (force && force[t])) ? 1 : 0;
 }
 
 // Single workgroup: stable compaction of the flagged rows into list[0..n).
@@ -69,9 +69,10 @@ __global__ __launch_bounds__(1024) void row_compact_kernel(const uint8_t* flag, 
 }
 
 hipError_t launch_classify(const TwellView& h, int tau, uint8_t* flag, int* list, int* n_out, int* n_copy,
-                           hipStream_t s) {
+                           hipStream_t s, const uint8_t* force) {
   if (h.T > 0)
-    hipLaunchKernelGGL(row_classify_kernel, dim3((h.T + 3) / 4), dim3(256), 0, s, h.cnt, h.T, h.NT, tau, flag);
+    hipLaunchKernelGGL(row_classify_kernel, dim3((h.T + 3) / 4), dim3(256), 0, s, h.cnt, h.T, h.NT, tau, force,
+                       flag);
   hipLaunchKernelGGL(row_compact_kernel, dim3(1), dim3(1024), 0, s, flag, h.T, list, n_out, n_copy);
   return hipGetLastError();
 }

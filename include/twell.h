@@ -200,6 +200,74 @@ twell_status twell_ffn_bwd_hybrid_l1(const twell_ffn_shape *sh, const void *x, c
                                      int32_t *n_dense_rows, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Compact TwELL for the saved state of training (intellectnews.ru TwELL
+ * article, section "Слитые CUDA-ядра для инференса и гибрид для обучения":
+ * well-sparse rows in a compact sparse matrix, the others in a dense branch;
+ * gate.com ES / ID, first paragraph: lower peak memory).  The same tiles as
+ * twell_mat (R = 16, C = 64, fp32 values) with room for only W slots per
+ * tile, so that tile (i, j) starts at (i*NT + j)*W*16 with no offset table:
+ *   cnt   uint8  [T][NT]        true number of entries of row t in tile j
+ *   width uint8  [NR][NT]       min(ELL width of the tile, W)
+ *   val   float  [NR][NT][W][R] slots 0..W-1 of the capacity-64 layout
+ *   idx   uint8  [NR][NT][W][R]
+ *   mask  uint64 [T][NT]        as in twell_mat (required)
+ *   ovf   uint8  [T]            1 iff some tile of row t holds more than W
+ *                               entries: the row's stored slots are then
+ *                               incomplete and its backward takes the dense
+ *                               branch, which recomputes h from x
+ * A row with ovf = 0 keeps every entry, bit for bit.  1 <= W <= 64; W = 64
+ * is the full form.  The caller allocates every array (twell_cmat_bytes).
+ */
+typedef struct {
+  int32_t T, F, W;
+  uint8_t *cnt;
+  uint8_t *width;
+  float *val;
+  uint8_t *idx;
+  uint64_t *mask;
+  uint8_t *ovf;
+} twell_cmat;
+
+/* Bytes of each compact array (parts: cnt, width, val, idx, mask, ovf) for a
+ * T x F matrix of capacity W; returns their sum, 0 for an invalid shape.
+ * parts may be NULL.  Pure host arithmetic. */
+size_t twell_cmat_bytes(int32_t T, int32_t F, int32_t W, size_t parts[6]);
+
+/*
+ * twell_compact: full (fp32 values, mask required, same T and F) -> out.
+ *   Writes every array of out (val and idx slots >= out->width excepted).
+ * twell_expand: in -> full, the capacity-64 form: cnt, width and mask copied,
+ *   the W stored slots of each tile moved to their capacity-64 positions,
+ *   slots >= width unwritten.  For a row with ovf = 1, cnt stays the true
+ *   count while only W slots of a tile survive.
+ * Both are one pass over the stored arrays; EINVAL for NULL arrays, shape
+ * mismatch, W outside 1..64 or misaligned (16 bytes) val / mask.
+ */
+twell_status twell_compact(const twell_mat *full, twell_cmat *out, hipStream_t stream);
+twell_status twell_expand(const twell_cmat *in, twell_mat *full, hipStream_t stream);
+
+/* Workspace bytes for twell_ffn_bwd_hybrid_compact: that of
+ * twell_ffn_bwd_workspace plus a capacity-64 value and index array. */
+size_t twell_ffn_bwd_compact_workspace(const twell_ffn_shape *sh, int32_t dense_row_threshold);
+
+/*
+ * twell_ffn_bwd_hybrid_compact: twell_ffn_bwd_hybrid_l1 with the saved state
+ * in compact form (saved: fp32, T x F, the twell_compact of the forward's
+ * saved_h).  Row t takes the dense branch when its count exceeds
+ * dense_row_threshold or when saved->ovf[t] is set; every other row keeps all
+ * its entries and takes the sparse branch as before, so the gradients equal
+ * those of twell_ffn_bwd_hybrid_l1 up to fp32 rounding.  n_dense_rows counts
+ * both kinds.  ws: at least twell_ffn_bwd_compact_workspace(sh, thr) bytes.
+ * Other arguments, outputs and errors as for twell_ffn_bwd_hybrid_l1.
+ */
+twell_status twell_ffn_bwd_hybrid_compact(const twell_ffn_shape *sh, const void *x, const void *WgT,
+                                          const void *bg, const void *WuT, const void *Wd, const void *dY,
+                                          const twell_cmat *saved, int32_t dense_row_threshold, float l1_lambda,
+                                          int32_t l1_per_token_mean, float *dX, float *dWgT, float *dWuT,
+                                          float *dWd, float *dbg, int32_t *n_dense_rows, void *ws,
+                                          size_t ws_bytes, hipStream_t stream);
+
+/*
  * twell_ffn_fwd_ex: twell_ffn_fwd that also records up to n_events caller-
  * created HIP events on the stream at its stage boundaries, for timing:
  *   [0] start

@@ -157,6 +157,67 @@ def test_bwd_l1_argument_errors():
     assert b"l1" in L.twell_last_error()
 
 
+def test_cmat_bytes():
+    total, parts = tw.twell_cmat_bytes(33, 128, 5)
+    NR, NT = 3, 2
+    assert parts == [33 * NT, NR * NT, NR * NT * 5 * 16 * 4, NR * NT * 5 * 16, 33 * NT * 8, 33]
+    assert total == sum(parts)
+    full, fparts = tw.twell_mat_bytes(33, 128)
+    assert tw.twell_cmat_bytes(33, 128, 64)[1][:5] == fparts                   # W = 64 is the full layout
+    for bad in ((33, 128, 0), (33, 128, 65), (33, 100, 4), (-1, 128, 4)):
+        assert tw.twell_cmat_bytes(*bad)[0] == 0
+
+
+def test_compact_argument_errors():
+    """twell_compact / twell_expand check shapes, capacity and pointers
+    before any launch (so these calls need no GPU)."""
+    L = tw.lib()
+    full = tw.c_twell_mat(64, 512, 16, 64, tw.TWELL_F32, 16, 16, 16, 16, 16)
+
+    def cm(T=64, F=512, W=4, ovf=16, val=16):
+        return tw.c_twell_cmat(T, F, W, 16, 16, val, 16, 16, ovf)
+
+    for f in (L.twell_compact, L.twell_expand):
+        def a(m, c, f=f):
+            return (m, c) if f is L.twell_compact else (c, m)
+        for c in (cm(W=0), cm(W=65), cm(T=32), cm(F=448), cm(ovf=None), cm(val=24)):
+            x, y = a(ctypes.byref(full), ctypes.byref(c))
+            assert f(x, y, None) == tw.TWELL_EINVAL, (f, c.T, c.F, c.W)
+        x, y = a(None, ctypes.byref(cm()))
+        assert f(x, y, None) == tw.TWELL_EINVAL
+        bf = tw.c_twell_mat(64, 512, 16, 64, tw.TWELL_BF16, 16, 16, 16, 16, 16)
+        x, y = a(ctypes.byref(bf), ctypes.byref(cm()))
+        assert f(x, y, None) == tw.TWELL_EINVAL                                # fp32 values only
+        nomask = tw.c_twell_mat(64, 512, 16, 64, tw.TWELL_F32, 16, 16, 16, 16, None)
+        x, y = a(ctypes.byref(nomask), ctypes.byref(cm()))
+        assert f(x, y, None) == tw.TWELL_EINVAL
+    empty_full = tw.c_twell_mat(0, 512, 16, 64, tw.TWELL_F32, None, None, None, None, None)
+    empty = tw.c_twell_cmat(0, 512, 4, None, None, None, None, None, None)
+    assert L.twell_compact(ctypes.byref(empty_full), ctypes.byref(empty), None) == tw.TWELL_OK
+
+
+def test_bwd_compact_argument_errors():
+    L = tw.lib()
+    sh = tw.ffn_shape(64, 128, 512, tw.TWELL_BF16, tw.TWELL_F32)
+    c = tw.c_twell_cmat(64, 512, 4, 16, 16, 16, 16, 16, 16)
+    need = tw.twell_ffn_bwd_compact_workspace(sh, 51)
+    full_val = tw.twell_mat_bytes(64, 512)[1][2]
+    assert need >= tw.twell_ffn_bwd_workspace(sh, 51) + full_val
+
+    def call(cmat=c, lam=0.0, ws_bytes=need, dY=16):
+        return L.twell_ffn_bwd_hybrid_compact(ctypes.byref(sh), 16, 16, None, 16, 16, dY,
+                                              ctypes.byref(cmat) if cmat is not None else None, 51,
+                                              ctypes.c_float(lam), 0, 16, 16, 16, 16, None, None, 4096, ws_bytes,
+                                              None)
+    assert call(cmat=None) == tw.TWELL_EINVAL
+    assert call(cmat=tw.c_twell_cmat(64, 512, 4, 16, 16, 16, 16, 16, None)) == tw.TWELL_EINVAL   # ovf required
+    assert call(cmat=tw.c_twell_cmat(64, 512, 70, 16, 16, 16, 16, 16, 16)) == tw.TWELL_EINVAL
+    assert call(cmat=tw.c_twell_cmat(32, 512, 4, 16, 16, 16, 16, 16, 16)) == tw.TWELL_EINVAL
+    assert call(lam=-1.0) == tw.TWELL_EINVAL
+    assert call(dY=None) == tw.TWELL_EINVAL
+    assert call(ws_bytes=need - 1) == tw.TWELL_EWORKSPACE
+
+
 def test_hybrid_fwd_needs_saved_h():
     sh = tw.ffn_shape(64, 128, 512, tw.TWELL_BF16, tw.TWELL_F32)
     need = tw.twell_ffn_fwd_workspace(sh, True)
