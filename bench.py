@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--compact-w", type=int, default=8,
+                    help="training workloads: also time the step with the saved state in compact TwELL of this "
+                         "capacity (twell_compact + twell_ffn_bwd_hybrid_compact); 0 skips it")
     ap.add_argument("--ffn", choices=["gated", "relu"], default="gated",
                     help="relu: the non-gated ReLU FFN y = ReLU(x.W1 + b1).W2 (the workload's gate weights and "
                          "bias as W1, b1, its down weights as W2)")
@@ -388,6 +391,35 @@ def main() -> int:
                                  "tflops": 18.0 * T * d * f / (dms * 1e-3) / 1e12,
                                  "what": "dense forward + backward, bf16 intermediates"}
         out["speedup_vs_dense"] = dms / ms_step
+
+    if training and args.compact_w > 0:
+        # the same step with the state saved between forward and backward in
+        # compact TwELL: forward, compaction, backward from the compact form
+        W = args.compact_w
+        c = tw.alloc_twell_cmat(T, f, W, device=dev)
+        wsc = torch.empty(max(1, tw.twell_ffn_bwd_compact_workspace(shape, tau)), dtype=torch.uint8, device=dev)
+
+        def compact_step():
+            tw.twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, h, tau, wsf, stream)
+            tw.twell_compact(h, c, stream)
+            tw.twell_ffn_bwd_hybrid_compact(shape, x, WgT, bg, WuT, Wd, dY, c, tau, 0.0, False, dX, dW[0], dW[1],
+                                            dW[2], dbg, nD, wsc, stream)
+        for _ in range(args.warmup):
+            compact_step()
+        torch.cuda.synchronize()
+        a0, a1 = ev(), ev()
+        a0.record(stream)
+        for _ in range(args.steps):
+            compact_step()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        cms = a0.elapsed_time(a1) / args.steps
+        out["compact_twell"] = {
+            "W": W, "ms_per_step": cms, "tokens_per_s": T / (cms * 1e-3),
+            "overflow_rows": int(c.ovf.to(torch.int64).sum().item()), "dense_rows": int(nD.item()),
+            "saved_state_bytes": tw.twell_cmat_bytes(T, f, W)[0],
+            "full_saved_state_bytes": tw.twell_mat_bytes(T, f)[0],
+        }
 
     if not args.no_dense and cfg.dtype == "bf16" and not training:
         dws = torch.empty(tw.twell_ffn_dense_fwd_workspace(shape), dtype=torch.uint8, device=dev)
