@@ -138,7 +138,7 @@ hipError_t launch_down_bf16(const float* v0, const float* v1, const void* W, con
                             const TwellView& pat, void* y, int out_dt, const uint8_t* skip, hipStream_t s,
                             const int* gate = nullptr);
 
-// Forward up/down over each 256-token row block's union of active neurons
+// Forward up/down over each 128-token row block's union of active neurons
 // (bf16 inputs): union lists, up GEMM writing a as fp16 over the union, down
 // GEMM into y (rows with skip[t] != 0 untouched).  ws holds
 // union_ws_bytes(T, d, F).  *flag_out receives the device flag that is set when
