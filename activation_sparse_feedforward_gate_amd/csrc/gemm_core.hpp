@@ -20,6 +20,8 @@
 // transposed kinds zero-fill past K and read whole row blocks, so the caller
 // launches them only on matrices whose row count is a multiple of the block.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace twell {
@@ -311,6 +313,7 @@ struct GemmCfg {
   static constexpr int NTH = WM * WN * WAVE;
   static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   static_assert(TM >= 1 && TN >= 1, "wave tile must hold whole 32x32 blocks");
+  static constexpr bool SINGLE = false;
   static constexpr bool ASPLIT = KindInfo<AKIND>::split;
   static constexpr bool F32MMA = KindInfo<AKIND>::f32mma;
   static constexpr bool F16MMA = KindInfo<AKIND>::f16;
@@ -474,6 +477,7 @@ struct DmaCfg {
   static constexpr bool F16MMA = F16_;
   static constexpr bool BT = BT_;                  // B given as [K][N] (see DmaTile)
   static constexpr bool AT = AT_;                  // A given as [K][M], never gathered
+  static constexpr bool SINGLE = false;            // one stage buffer (DmaCfg1)
   static_assert(!BT || NB == 1, "a transposed B operand comes alone");
   static constexpr int NW = WM * WN, NTH = NW * WAVE;
   static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
@@ -486,6 +490,21 @@ struct DmaCfg {
   static constexpr int LA = BM / (8 * NW), LB = BN / (8 * NW);   // 1 KB loads per wave per operand
   static_assert(LA * 8 * NW == BM && LB * 8 * NW == BN, "block rows must split into whole 1 KB loads per wave");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// Single-stage variant: one stage buffer (a 128x256 tile needs 48 KB), so
+// that two workgroups share a CU.  Inside a workgroup the loads of a K tile
+// no longer run under the MFMAs of the previous one; the other workgroup's
+// MFMAs fill that time, and each workgroup's output stores drain while the
+// other one computes.  Kernels built on it declare __launch_bounds__(NTH,
+// WPE): registers for two workgroups.
+template <int BM_, int BN_, int WM_, int WN_, int NB_ = 1, bool F16_ = false, bool BT_ = false, bool AT_ = false>
+struct DmaCfg1 : DmaCfg<BM_, BN_, WM_, WN_, NB_, F16_, BT_, AT_> {
+  typedef DmaCfg<BM_, BN_, WM_, WN_, NB_, F16_, BT_, AT_> Base;
+  static constexpr bool SINGLE = true;
+  static constexpr int LDS_BYTES = Base::STAGE;
+  static constexpr int WPE = 2 * Base::NW / 4;
+  static_assert(2 * Base::STAGE <= 160 * 1024, "two workgroups per CU");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -719,14 +738,31 @@ struct DmaTile {
         }
       }
     };
-    if (nk > 0) issue(0, st0);
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      step(kt, st0, st1);
-      step(kt + 1, st1, st0);
+    if constexpr (Cfg::SINGLE) {
+      // one buffer: load, hand over, compute, and let every wave finish its
+      // fragment reads before the next tile's loads overwrite it
+      for (int kt = 0; kt < nk; ++kt) {
+        issue(kt, st0);
+        stage_barrier();
+        compute(st0);
+        if constexpr (Cfg::BT) {
+          if (bgat) {
+#pragma unroll
+            for (int q = 0; q < Cfg::LB; ++q) asm volatile("" ::"v"(bvo[q]));
+          }
+        }
+        __syncthreads();
+      }
+    } else {
+      if (nk > 0) issue(0, st0);
+      int kt = 0;
+      for (; kt + 1 < nk; kt += 2) {
+        step(kt, st0, st1);
+        step(kt + 1, st1, st0);
+      }
+      if (kt < nk) step(kt, st0, st1);
+      __syncthreads();
     }
-    if (kt < nk) step(kt, st0, st1);
-    __syncthreads();
   }
 
   __device__ static int row_of(int i, int e) {
@@ -739,11 +775,22 @@ struct DmaTile {
   }
 };
 
+// Waves per SIMD a kernel on this configuration is compiled for (the second
+// __launch_bounds__ argument): WPE for the single-stage configurations, else
+// no constraint.
+template <class C, class = void> struct WavesPerEU { static constexpr int value = 1; };
+template <class C> struct WavesPerEU<C, std::void_t<decltype(C::WPE)>> { static constexpr int value = C::WPE; };
+
 // Mainloop type of a configuration.
 template <class Cfg> struct TileFor { typedef GemmTile<Cfg> type; static constexpr bool dma = false; };
 template <int BM, int BN, int WM, int WN, int NB, bool F16, bool BT, bool AT>
 struct TileFor<DmaCfg<BM, BN, WM, WN, NB, F16, BT, AT>> {
   typedef DmaTile<DmaCfg<BM, BN, WM, WN, NB, F16, BT, AT>> type;
+  static constexpr bool dma = true;
+};
+template <int BM, int BN, int WM, int WN, int NB, bool F16, bool BT, bool AT>
+struct TileFor<DmaCfg1<BM, BN, WM, WN, NB, F16, BT, AT>> {
+  typedef DmaTile<DmaCfg1<BM, BN, WM, WN, NB, F16, BT, AT>> type;
   static constexpr bool dma = true;
 };
 

@@ -544,9 +544,10 @@ __device__ __forceinline__ void down_union_tile(const UnionArgs& a, int b, int c
 // workgroups of XCD x take the row blocks b = x (mod 8), all column tiles of
 // a block together, so the block's adense rows are reused from that XCD's L2.
 template <class Cfg, bool TWO = false>
-__global__ __launch_bounds__(Cfg::NTH) void down_union_kernel(UnionArgs a) {
+__global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void down_union_kernel(UnionArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1_[Cfg::SINGLE ? 16 : Cfg::STAGE];
+  char* st1 = Cfg::SINGLE ? st0 : st1_;
   if (*a.flag) return;                              // fp16 overflow: the fallback path writes y
   const int nct = a.d / Cfg::BN;
   const int nblk = (a.T + UB - 1) / UB;
@@ -561,7 +562,7 @@ __global__ __launch_bounds__(Cfg::NTH) void down_union_kernel(UnionArgs a) {
 }
 
 using UpUnionCfg = DmaCfg<UB, 256, 2, 4>;
-using DownUnionCfg = DmaCfg<UB, 256, 2, 4, 1, true, true>;
+using DownUnionCfg = DmaCfg1<UB, 256, 2, 4, 1, true, true>;
 using DownUnionCfg128 = DmaCfg<UB, 128, 4, 2, 1, true, true>;
 using DownUnionCfg64 = DmaCfg<UB, 64, 4, 2, 1, true, true>;
 
@@ -647,7 +648,9 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
   // persistent grids: one workgroup per CU (multiples of 8, one row of XCDs),
   // never more than the tiles of the busiest XCD need
   const int cus = device_cus();
-  auto grid_for = [&](int tiles_per_xcd) { return (unsigned)(8 * std::max(1, std::min(cus / 8, tiles_per_xcd))); };
+  auto grid_for = [&](int tiles_per_xcd, int per_cu = 1) {
+    return (unsigned)(8 * std::max(1, std::min(per_cu * cus / 8, tiles_per_xcd)));
+  };
   if (WuT)
     hipLaunchKernelGGL((up_union_kernel<UpUnionCfg, true>), dim3(grid_for(nbx_max * npt)), dim3(UpUnionCfg::NTH), 0,
                        s, a);
@@ -656,8 +659,8 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
                        0, s, a);
   if (ev_up) (void)hipEventRecord(ev_up, s);
   if (d % 256 == 0)
-    hipLaunchKernelGGL((down_union_kernel<DownUnionCfg>), dim3(grid_for(nbx_max * (d / 256))), dim3(DownUnionCfg::NTH),
-                       0, s, a);
+    hipLaunchKernelGGL((down_union_kernel<DownUnionCfg>), dim3(grid_for(nbx_max * (d / 256), 2)),
+                       dim3(DownUnionCfg::NTH), 0, s, a);
   else if (d % 128 == 0)
     hipLaunchKernelGGL((down_union_kernel<DownUnionCfg128>), dim3(grid_for(nbx_max * (d / 128))),
                        dim3(DownUnionCfg128::NTH), 0, s, a);
@@ -708,7 +711,9 @@ hipError_t launch_union_bwd(const void* x, const void* dY, const void* WgT, cons
   const int npt = (F + BwdUnionCfg::BN - 1) / BwdUnionCfg::BN;
   const int nbx_max = (nblk + 7) / 8;
   const int cus = device_cus();
-  auto grid_for = [&](int tiles_per_xcd) { return (unsigned)(8 * std::max(1, std::min(cus / 8, tiles_per_xcd))); };
+  auto grid_for = [&](int tiles_per_xcd, int per_cu = 1) {
+    return (unsigned)(8 * std::max(1, std::min(per_cu * cus / 8, tiles_per_xcd)));
+  };
   hipLaunchKernelGGL((bwd_union_kernel<BwdUnionCfg>), dim3(grid_for(nbx_max * npt)), dim3(BwdUnionCfg::NTH), 0, s, a);
   // fp16 copies of WgT and WuT for the dX GEMM (a value beyond the fp16 range raises the flag)
   const int64_t n8 = (int64_t)F * d / 8;
@@ -718,7 +723,7 @@ hipError_t launch_union_bwd(const void* x, const void* dY, const void* WgT, cons
                      (_Float16*)a.Wu16, n8, a.flag);
   // dX of the live rows = dG.WgT + dU.WuT over the union (stands down when the flag is set)
   if (d % 256 == 0)
-    hipLaunchKernelGGL((down_union_kernel<DownUnionCfg, true>), dim3(grid_for(nbx_max * (d / 256))),
+    hipLaunchKernelGGL((down_union_kernel<DownUnionCfg, true>), dim3(grid_for(nbx_max * (d / 256), 2)),
                        dim3(DownUnionCfg::NTH), 0, s, a);
   else if (d % 128 == 0)
     hipLaunchKernelGGL((down_union_kernel<DownUnionCfg128, true>), dim3(grid_for(nbx_max * (d / 128))),
