@@ -158,13 +158,15 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
     for (int p = p0 + tid; p <= pl; p += Cfg::NTH) posmap[ul[p] - nlo] = (int16_t)(p - p0);
   const int tjf = nlo >> 6, S = (nhi >> 6) - tjf + 1;
   constexpr int NG = Cfg::NTH / 16;        // 16-lane groups
-  constexpr int NPRE = 4;                  // blocks per group fetched ahead
+  // blocks per group fetched ahead (none with one stage buffer: the other
+  // workgroup on the CU covers the latency, and the registers are needed)
+  constexpr int NPRE = Cfg::SINGLE ? 0 : 4;
   const int grp = tid >> 4, gl = tid & 15;
   // first piece (slots 0-3) of the group's first NPRE (row tile, column tile)
   // blocks; the whole 4 KB block is allocated, so the reads need no width check
   constexpr int NRT = Cfg::BM / 16;        // TwELL row tiles of the block
   struct Piece { int w; float4 v; uint32_t i; };
-  Piece pre[NPRE];
+  Piece pre[NPRE > 0 ? NPRE : 1];
 #pragma unroll
   for (int it = 0; it < NPRE; ++it) {
     const int q = grp + it * NG;
@@ -204,15 +206,14 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
     const int pb = pr & 127;
     return pb * (2 * Cfg::BM) + (((r >> 2) ^ (pb & 31)) << 3) + ((r & 3) << 1);
   };
-#pragma unroll
-  for (int o = 0; o < 128 * 2 * Cfg::BM / (16 * Cfg::NTH); ++o) {
-    ((float4*)st0)[o * Cfg::NTH + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
-    ((float4*)st1)[o * Cfg::NTH + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  __syncthreads();
+  // With one stage buffer the h tile is built and consumed in two passes of
+  // 128 positions (32 KB each); with two, in one pass over both buffers.
+  constexpr bool SPLIT = Cfg::SINGLE;
+  constexpr int NPASS = SPLIT ? 2 : 1;
+  auto hbuf_of = [&](int pr) -> char* { return (SPLIT || !(pr >> 7)) ? st0 : st1; };
   // scatter: a 16-lane group per (row tile, column tile) block; lane piece c
   // holds slot c/4, rows 4*(c%4)..+3 of the block
-  auto scatter = [&](int i, int tj, int rt, int c, const float4& v4, uint32_t i4) {
+  auto scatter = [&](int hp, int i, int tj, int rt, int c, const float4& v4, uint32_t i4) {
     const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -230,80 +231,90 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
           }
           pr = lo - p0;
         }
-        char* hbuf = (pr >> 7) ? st1 : st0;
-        *(_Float16*)(hbuf + hoff(pr, i * 16 + rl)) = (_Float16)vv[k];
+        if (!SPLIT || (pr >> 7) == hp) *(_Float16*)(hbuf_of(pr) + hoff(pr, i * 16 + rl)) = (_Float16)vv[k];
       }
     }
   };
-#pragma unroll
-  for (int it = 0; it < NPRE; ++it) {
-    const int q = grp + it * NG;
-    if (q >= NRT * S) break;
-    const int i = q / S, sj = q - i * S;
-    const int rt = (m0 >> 4) + i;
-    const Piece& pc = pre[it];
-    if (gl < pc.w * 4) scatter(i, tjf + sj, rt, gl, pc.v, pc.i);
-    const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
-    for (int c = gl + 16; c < pc.w * 4; c += 16)
-      scatter(i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
-              ((const uint32_t*)(a.hidx + blk * 1024))[c]);
-  }
-  for (int q = grp + NPRE * NG; q < NRT * S; q += NG) {
-    const int i = q / S, sj = q - i * S;
-    const int rt = (m0 >> 4) + i;
-    if (rt * 16 >= a.T) continue;
-    const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
-    const int w = a.hwidth[blk];
-    for (int c = gl; c < w * 4; c += 16)
-      scatter(i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
-              ((const uint32_t*)(a.hidx + blk * 1024))[c]);
-  }
-  __syncthreads();
   const int wrow = (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
 #pragma unroll
-  for (int j = 0; j < Cfg::TN; ++j) {
-    const int pr = Tile::col_of(j);
-    const int p = p0 + pr;
-    const bool wr = p < ((nb + 63) & ~63);
-    const char* hbuf = (pr >> 7) ? st1 : st0;
+  for (int hp = 0; hp < NPASS; ++hp) {
 #pragma unroll
-    for (int i = 0; i < Cfg::TM; ++i)
+    for (int o = 0; o < 128 * 2 * Cfg::BM / (16 * Cfg::NTH); ++o) {
+      ((float4*)st0)[o * Cfg::NTH + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (!SPLIT) ((float4*)st1)[o * Cfg::NTH + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const uint2 h2 = *(const uint2*)(hbuf + hoff(pr, wrow + i * 32 + 8 * qq + 4 * hl));
-        const float hv[4] = {(float)__builtin_bit_cast(_Float16, (uint16_t)(h2.x & 0xffffu)),
-                             (float)__builtin_bit_cast(_Float16, (uint16_t)(h2.x >> 16)),
-                             (float)__builtin_bit_cast(_Float16, (uint16_t)(h2.y & 0xffffu)),
-                             (float)__builtin_bit_cast(_Float16, (uint16_t)(h2.y >> 16))};
-        const int t0 = m0 + Tile::row_of(i, 4 * qq);
-        float v[4];
+    for (int it = 0; it < NPRE; ++it) {
+      const int q = grp + it * NG;
+      if (q >= NRT * S) break;
+      const int i = q / S, sj = q - i * S;
+      const int rt = (m0 >> 4) + i;
+      const Piece& pc = pre[it];
+      if (gl < pc.w * 4) scatter(hp, i, tjf + sj, rt, gl, pc.v, pc.i);
+      const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
+      for (int c = gl + 16; c < pc.w * 4; c += 16)
+        scatter(hp, i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
+                ((const uint32_t*)(a.hidx + blk * 1024))[c]);
+    }
+    for (int q = grp + NPRE * NG; q < NRT * S; q += NG) {
+      const int i = q / S, sj = q - i * S;
+      const int rt = (m0 >> 4) + i;
+      if (rt * 16 >= a.T) continue;
+      const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
+      const int w = a.hwidth[blk];
+      for (int c = gl; c < w * 4; c += 16)
+        scatter(hp, i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
+                ((const uint32_t*)(a.hidx + blk * 1024))[c]);
+    }
+    __syncthreads();
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if constexpr (GATED) v[k] = hv[k] != 0.f ? hv[k] * g.acc[0][i][j][4 * qq + k] : 0.f;
-          else v[k] = hv[k];
-          vbits = max(vbits, __float_as_uint(v[k]) & 0x7fffffffu);
+    for (int j = 0; j < Cfg::TN; ++j) {
+      const int pr = Tile::col_of(j);
+      if (SPLIT && (pr >> 7) != hp) continue;            // wave-uniform: the wave's columns lie in one half
+      const int p = p0 + pr;
+      const bool wr = p < ((nb + 63) & ~63);
+      const char* hbuf = hbuf_of(pr);
+#pragma unroll
+      for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const uint2 h2 = *(const uint2*)(hbuf + hoff(pr, wrow + i * 32 + 8 * qq + 4 * hl));
+          const float hv[4] = {(float)__builtin_bit_cast(_Float16, (uint16_t)(h2.x & 0xffffu)),
+                               (float)__builtin_bit_cast(_Float16, (uint16_t)(h2.x >> 16)),
+                               (float)__builtin_bit_cast(_Float16, (uint16_t)(h2.y & 0xffffu)),
+                               (float)__builtin_bit_cast(_Float16, (uint16_t)(h2.y >> 16))};
+          const int t0 = m0 + Tile::row_of(i, 4 * qq);
+          float v[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            if constexpr (GATED) v[k] = hv[k] != 0.f ? hv[k] * g.acc[0][i][j][4 * qq + k] : 0.f;
+            else v[k] = hv[k];
+            vbits = max(vbits, __float_as_uint(v[k]) & 0x7fffffffu);
+          }
+          // stores of position pairs: lanes l and l^1 hold positions p and
+          // p^1 of the same rows; for rows k and k+1 the even lane stores
+          // (its k, the odd lane's k) at p, the odd lane (the even lane's k+1,
+          // its k+1) at p-1: one 4-byte store per two elements.  Element
+          // offsets stay below 2^32 (the matrix holds fewer elements); pairs
+          // that are not written go to the spare slot past the matrix, so the
+          // stores need no branches.
+          const bool odd = lane & 1;
+#pragma unroll
+          for (int k = 0; k < 4; k += 2) {
+            const float send = odd ? v[k] : v[k + 1];
+            const float recv = __shfl_xor(send, 1);
+            const int kr = odd ? k + 1 : k;                   // row this lane stores
+            const _Float16 lo = (_Float16)(odd ? recv : v[k]), hi = (_Float16)(odd ? v[k + 1] : recv);
+            const uint32_t pair = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            const uint32_t keep = 0u - (uint32_t)(wr && t0 + kr < a.T);
+            const uint32_t o = (((uint32_t)(t0 + kr) * (uint32_t)a.F + (uint32_t)(p & ~1)) & keep) | (a.spare & ~keep);
+            *(uint32_t*)(a.adense + o) = pair;
+          }
         }
-        // stores of position pairs: lanes l and l^1 hold positions p and
-        // p^1 of the same rows; for rows k and k+1 the even lane stores
-        // (its k, the odd lane's k) at p, the odd lane (the even lane's k+1,
-        // its k+1) at p-1: one 4-byte store per two elements.  Element
-        // offsets stay below 2^32 (the matrix holds fewer elements); pairs
-        // that are not written go to the spare slot past the matrix, so the
-        // stores need no branches.
-        const bool odd = lane & 1;
-#pragma unroll
-        for (int k = 0; k < 4; k += 2) {
-          const float send = odd ? v[k] : v[k + 1];
-          const float recv = __shfl_xor(send, 1);
-          const int kr = odd ? k + 1 : k;                   // row this lane stores
-          const _Float16 lo = (_Float16)(odd ? recv : v[k]), hi = (_Float16)(odd ? v[k + 1] : recv);
-          const uint32_t pair = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-          const uint32_t keep = 0u - (uint32_t)(wr && t0 + kr < a.T);
-          const uint32_t o = (((uint32_t)(t0 + kr) * (uint32_t)a.F + (uint32_t)(p & ~1)) & keep) | (a.spare & ~keep);
-          *(uint32_t*)(a.adense + o) = pair;
-        }
-      }
+    }
+    if (SPLIT && hp + 1 < NPASS) __syncthreads();         // every wave done reading before the next pass
   }
   const bool over = vbits > 0x477fe000u;   // above 65504, the largest finite fp16
   if (__builtin_amdgcn_ballot_w64(over) != 0ull && lane == 0) atomicOr(a.flag, 1);
@@ -317,9 +328,10 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
 // unions (largely the same neurons) are reused from that XCD's L2 (measured
 // faster than keeping each block's x rows in L2 instead).
 template <class Cfg, bool GATED>
-__global__ __launch_bounds__(Cfg::NTH) void up_union_kernel(UnionArgs a) {
+__global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void up_union_kernel(UnionArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1_[Cfg::SINGLE ? 16 : Cfg::STAGE];
+  char* st1 = Cfg::SINGLE ? st0 : st1_;
   __shared__ int16_t posmap[POSCAP];
   const int npt = (a.F + Cfg::BN - 1) / Cfg::BN;
   const int nblk = (a.T + UB - 1) / UB;
@@ -561,7 +573,7 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void down_union_k
   }
 }
 
-using UpUnionCfg = DmaCfg<UB, 256, 2, 4>;
+using UpUnionCfg = DmaCfg1<UB, 256, 2, 4>;
 using DownUnionCfg = DmaCfg1<UB, 256, 2, 4, 1, true, true>;
 using DownUnionCfg128 = DmaCfg<UB, 128, 4, 2, 1, true, true>;
 using DownUnionCfg64 = DmaCfg<UB, 64, 4, 2, 1, true, true>;
@@ -652,10 +664,10 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
     return (unsigned)(8 * std::max(1, std::min(per_cu * cus / 8, tiles_per_xcd)));
   };
   if (WuT)
-    hipLaunchKernelGGL((up_union_kernel<UpUnionCfg, true>), dim3(grid_for(nbx_max * npt)), dim3(UpUnionCfg::NTH), 0,
-                       s, a);
+    hipLaunchKernelGGL((up_union_kernel<UpUnionCfg, true>), dim3(grid_for(nbx_max * npt, 2)), dim3(UpUnionCfg::NTH),
+                       0, s, a);
   else   // non-gated layer: a = h
-    hipLaunchKernelGGL((up_union_kernel<UpUnionCfg, false>), dim3(grid_for(nbx_max * npt)), dim3(UpUnionCfg::NTH),
+    hipLaunchKernelGGL((up_union_kernel<UpUnionCfg, false>), dim3(grid_for(nbx_max * npt, 2)), dim3(UpUnionCfg::NTH),
                        0, s, a);
   if (ev_up) (void)hipEventRecord(ev_up, s);
   if (d % 256 == 0)
