@@ -145,8 +145,8 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
   const Operand B{a.WuT, a.d, ul, nb};
 
   // epilogue set-up, issued before the mainloop so that its global reads
-  // (the position map, and the first TwELL pieces) complete under the MFMAs:
-  // see the epilogue below
+  // (the position map, and with two stage buffers the first TwELL pieces)
+  // complete under the MFMAs: see the epilogue below
   static_assert(Cfg::BN == 256 && Cfg::NW == 8 && Cfg::BM % 128 == 0 && Cfg::BM <= 256, "epilogue layout");
   static_assert(Cfg::STAGE >= 128 * 2 * Cfg::BM, "h tile: 128 positions x BM rows of fp16 per stage buffer");
   const int tid = threadIdx.x;
