@@ -131,7 +131,7 @@ constexpr int POSCAP = 12288;         // neuron span of a position tile covered 
 // lays h out over the union positions for the down GEMM).
 template <class Cfg, bool GATED>
 __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt, char* st0, char* st1,
-                                              int16_t* posmap) {
+                                              int16_t* posmap, int* lcount) {
   static_assert(Cfg::BM == UB, "one row block per M tile");
   const int nb = a.ucount[b];
   const int p0 = pt * Cfg::BN;
@@ -211,6 +211,12 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
   constexpr bool SPLIT = Cfg::SINGLE;
   constexpr int NPASS = SPLIT ? 2 : 1;
   auto hbuf_of = [&](int pr) -> char* { return (SPLIT || !(pr >> 7)) ? st0 : st1; };
+  // Two passes: the pairs of the second half found while scanning for the
+  // first are kept in a list in the buffer's last 16 KB (h-tile offset << 16
+  // | fp16 bits), so the second pass replays the list instead of scanning the
+  // TwELL again; only when the list overflows does it scan again.
+  constexpr int LCAP = SPLIT ? (Cfg::STAGE - 128 * 2 * Cfg::BM) / 4 : 0;
+  uint32_t* plist = (uint32_t*)(st0 + 128 * 2 * Cfg::BM);
   // scatter: a 16-lane group per (row tile, column tile) block; lane piece c
   // holds slot c/4, rows 4*(c%4)..+3 of the block
   auto scatter = [&](int hp, int i, int tj, int rt, int c, const float4& v4, uint32_t i4) {
@@ -231,7 +237,14 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
           }
           pr = lo - p0;
         }
-        if (!SPLIT || (pr >> 7) == hp) *(_Float16*)(hbuf_of(pr) + hoff(pr, i * 16 + rl)) = (_Float16)vv[k];
+        if (!SPLIT || (pr >> 7) == hp) {
+          *(_Float16*)(hbuf_of(pr) + hoff(pr, i * 16 + rl)) = (_Float16)vv[k];
+        } else if (hp == 0) {
+          const int k2 = atomicAdd(lcount, 1);
+          if (k2 < LCAP)
+            plist[k2] = ((uint32_t)hoff(pr, i * 16 + rl) << 16) |
+                        (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)vv[k]);
+        }
       }
     }
   };
@@ -243,7 +256,15 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
       ((float4*)st0)[o * Cfg::NTH + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
       if constexpr (!SPLIT) ((float4*)st1)[o * Cfg::NTH + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    if (SPLIT && hp == 0 && tid == 0) *lcount = 0;
     __syncthreads();
+    const int nl = (SPLIT && hp == 1) ? *lcount : 0;
+    if (SPLIT && hp == 1 && nl <= LCAP) {
+      for (int k2 = tid; k2 < nl; k2 += Cfg::NTH) {
+        const uint32_t e = plist[k2];
+        *(uint16_t*)(st0 + (e >> 16)) = (uint16_t)(e & 0xffffu);
+      }
+    } else {
 #pragma unroll
     for (int it = 0; it < NPRE; ++it) {
       const int q = grp + it * NG;
@@ -266,6 +287,7 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
       for (int c = gl; c < w * 4; c += 16)
         scatter(hp, i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
                 ((const uint32_t*)(a.hidx + blk * 1024))[c]);
+    }
     }
     __syncthreads();
 #pragma unroll
@@ -333,6 +355,7 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void up_union_ker
   __shared__ __attribute__((aligned(1024))) char st1_[Cfg::SINGLE ? 16 : Cfg::STAGE];
   char* st1 = Cfg::SINGLE ? st0 : st1_;
   __shared__ int16_t posmap[POSCAP];
+  __shared__ int lcount;                               // pairs in the second-pass list
   const int npt = (a.F + Cfg::BN - 1) / Cfg::BN;
   const int nblk = (a.T + UB - 1) / UB;
   const int x = blockIdx.x & 7;
@@ -341,7 +364,7 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void up_union_ker
   for (int k = blockIdx.x >> 3; k < ntile; k += gridDim.x >> 3) {
     const int pt = k / nbx;
     const int b = x + 8 * (k - pt * nbx);
-    up_union_tile<Cfg, GATED>(a, b, pt, st0, st1, posmap);
+    up_union_tile<Cfg, GATED>(a, b, pt, st0, st1, posmap, &lcount);
     __syncthreads();                                   // stage buffers and position map free again
   }
 }
