@@ -30,8 +30,11 @@ struct TwellView {
 // Gate GEMM g = x.WgT^T + bg, h = ReLU(g), packed into TwELL in the epilogue
 // (values fp32).  row_skip (optional, u8 [T]) marks rows whose mask must be
 // stored as empty for the consumers (never used by the gate itself).
+// slabs (bf16 only; nullable): the epilogue also writes the union of every
+// 64-row slab's masks, slabs[t / 64][j], and workgroup 0 clears *flag.
 hipError_t launch_gate_twell(int in_dt, const void* x, const void* WgT, const void* bg,
-                             int T, int d, int F, const TwellView& out, hipStream_t s);
+                             int T, int d, int F, const TwellView& out, hipStream_t s,
+                             uint64_t* slabs = nullptr, int* flag = nullptr);
 
 // Standalone pack of a [T][F] matrix with leading dimension ldg.
 hipError_t launch_pack(const void* G, int gdt, int64_t ldg, const TwellView& out, hipStream_t s);
@@ -169,7 +172,11 @@ hipError_t launch_decode_fwd(const void* x, const void* WgT, const void* bg, con
 hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int T, int d, int F,
                             const TwellView& h, const uint8_t* skip, void* ws, void* y, int out_dt,
                             int** flag_out, hipStream_t s, hipEvent_t ev_lists = nullptr,
-                            hipEvent_t ev_up = nullptr);
+                            hipEvent_t ev_up = nullptr, bool slabs_ready = false);
+// The union workspace's slab unions and fp16-overflow flag, for a gate GEMM
+// that writes the former and clears the latter (then launch_union_fwd runs
+// with slabs_ready and skip == nullptr).
+void union_slabs_and_flag(int T, int F, void* ws, uint64_t** slabs, int** flag);
 
 // Dense non-gated ReLU FFN baseline: act = bf16(ReLU(x.W1T^T + b1)), then
 // y = act.W2.  act is a [T][F] bf16 workspace; needs F % 128 == 0.

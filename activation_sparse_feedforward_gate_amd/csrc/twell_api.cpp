@@ -276,7 +276,13 @@ twell_status twell_ffn_fwd_ex(const twell_ffn_shape* sh, const void* x, const vo
     mark(6);
     return TWELL_OK;
   }
-  hipError_t e = launch_gate_twell(in_dt, x, WgT, bg, sh->T, sh->d, sh->F, h, stream);
+  // inference with bf16 inputs: the gate epilogue also writes the slab unions
+  // the up/down GEMMs' lists are built from (and clears their overflow flag)
+  const bool slabs_ready = !training && in_dt == DT_BF16;
+  uint64_t* slabs = nullptr;
+  int* uflag = nullptr;
+  if (slabs_ready) union_slabs_and_flag(sh->T, sh->F, w.uni, &slabs, &uflag);
+  hipError_t e = launch_gate_twell(in_dt, x, WgT, bg, sh->T, sh->d, sh->F, h, stream, slabs, uflag);
   if (e != hipSuccess) return hip_status(e, "gate GEMM");
   const uint8_t* skip = nullptr;
   if (training) {
@@ -287,7 +293,8 @@ twell_status twell_ffn_fwd_ex(const twell_ffn_shape* sh, const void* x, const vo
   mark(1);                                                            // gate GEMM + pack done
   if (in_dt == DT_BF16) {
     int* ovf = nullptr;
-    e = launch_union_fwd(x, WuT, Wd, sh->T, sh->d, sh->F, h, skip, w.uni, y, out_dt, &ovf, stream, evt(2), evt(3));
+    e = launch_union_fwd(x, WuT, Wd, sh->T, sh->d, sh->F, h, skip, w.uni, y, out_dt, &ovf, stream, evt(2), evt(3),
+                         slabs_ready);
     if (e != hipSuccess) return hip_status(e, "union up/down GEMMs");
     mark(4);                                                          // down-projection done
     // fp16 overflow fallback (does nothing unless the flag is set)
@@ -619,12 +626,15 @@ twell_status twell_relu_ffn_fwd(const twell_ffn_shape* sh, const void* x, const 
   const int in_dt = sh->in_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
   const int out_dt = sh->out_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
   const TwellView h = saved_h ? view_of(saved_h) : w.h;
-  hipError_t e = launch_gate_twell(in_dt, x, W1T, b1, sh->T, sh->d, sh->F, h, stream);
+  uint64_t* slabs = nullptr;
+  int* uflag = nullptr;
+  if (in_dt == DT_BF16) union_slabs_and_flag(sh->T, sh->F, w.uni, &slabs, &uflag);
+  hipError_t e = launch_gate_twell(in_dt, x, W1T, b1, sh->T, sh->d, sh->F, h, stream, slabs, uflag);
   if (e != hipSuccess) return hip_status(e, "gate GEMM");
   if (in_dt == DT_BF16) {
     int* ovf = nullptr;
     e = launch_union_fwd(x, nullptr, W2, sh->T, sh->d, sh->F, h, nullptr, w.uni, y, out_dt, &ovf, stream, nullptr,
-                         nullptr);
+                         nullptr, true);
     if (e != hipSuccess) return hip_status(e, "union down GEMM");
     // h beyond the fp16 range: the per-pair kernel with fp32 h (does nothing unless the flag is set)
     e = launch_down_bf16((const float*)h.val, nullptr, W2, nullptr, sh->T, sh->d, sh->F, h, y, out_dt, nullptr,

@@ -28,6 +28,8 @@ struct GateArgs {
   float* val;
   uint8_t* idx;
   uint64_t* mask;
+  uint64_t* slabs;   // nullable: union of each 64-row slab's masks, [ceil(T/64)][NT]
+  int* flag;         // nullable: cleared by workgroup 0
 };
 
 template <bool BF16IN>
@@ -53,6 +55,8 @@ __device__ __forceinline__ void tile_coords(int id, int nbm, int nbn, int& bm, i
 template <class Cfg, bool BF16IN>
 __global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
   static_assert((Cfg::BN / Cfg::WN) % 64 == 0 && Cfg::TN % 2 == 0, "whole 64-column TwELL tiles per wave");
+  static_assert((Cfg::BM / Cfg::WM) % 64 == 0, "whole 64-row slabs per wave");
+  if (a.flag && blockIdx.x == 0 && threadIdx.x == 0) *a.flag = 0;
   const int nbm = (a.T + Cfg::BM - 1) / Cfg::BM;
   const int nbn = a.F / Cfg::BN;
   int bm, bn;
@@ -87,7 +91,7 @@ __global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
   constexpr int STG = 16 * 64 * 4 + 16 * 8;                 // dense tile + row masks, per wave
   static_assert(Cfg::EPI_BYTES >= Cfg::NTH / 64 * STG, "epilogue staging");
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = m0 + (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
   const int hl = lane >> 5;
   const int cl = lane & 31;
@@ -99,6 +103,7 @@ __global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
     const int j = wc >> 6;
     const float b0 = load_bias<BF16IN>(a.bg, wc + cl);
     const float b1 = load_bias<BF16IN>(a.bg, wc + 32 + cl);
+    uint64_t sor = 0;                               // union of the masks of the current 64-row slab
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm) {
 #pragma unroll
@@ -110,16 +115,20 @@ __global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
         for (int q = 0; q < 8; ++q) {
           const int e = half * 8 + q;
           const int rl = 8 * (q >> 2) + 4 * hl + (q & 3);
-          const bool rowok = rt0 + rl < a.T;
+          // rows past T (a ragged last tile) leave the ballots through a
+          // wave-uniform mask: lanes 0-31 hold row rq, lanes 32-63 row rq + 4
+          const int rq = rt0 + 8 * (q >> 2) + (q & 3);
+          const uint64_t rowmask = (rq < a.T ? 0xffffffffull : 0ull) | (rq + 4 < a.T ? 0xffffffff00000000ull : 0ull);
           const float v0 = g.acc[0][tm][2 * tc][e] + b0;
           const float v1 = g.acc[0][tm][2 * tc + 1][e] + b1;
-          const uint64_t B0 = __builtin_amdgcn_ballot_w64(rowok && v0 > 0.f);
-          const uint64_t B1 = __builtin_amdgcn_ballot_w64(rowok && v1 > 0.f);
+          const uint64_t B0 = __builtin_amdgcn_ballot_w64(v0 > 0.f) & rowmask;
+          const uint64_t B1 = __builtin_amdgcn_ballot_w64(v1 > 0.f) & rowmask;
           sd[rl * 64 + cl] = v0;
           sd[rl * 64 + 32 + cl] = v1;
           const uint64_t mA = (B0 & 0xffffffffull) | (B1 << 32);               // row 8*(q/4) + q%4
           const uint64_t mB = (B0 >> 32) | (B1 & 0xffffffff00000000ull);        // that row + 4
           width = max(width, max(popc64(mA), popc64(mB)));
+          sor |= mA | mB;
           if (lane == 0) {
             const int r0 = 8 * (q >> 2) + (q & 3);
             sm[r0] = mA;
@@ -159,6 +168,13 @@ __global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
         if (lane == 0) a.width[tix] = (uint8_t)width;
         __builtin_amdgcn_wave_barrier();
       }
+      // a wave's rows start on a multiple of 64, so row blocks tm - 1 and tm
+      // (tm odd) are one whole 64-row slab
+      if ((tm & 1) && a.slabs) {
+        const int s0 = wr + (tm - 1) * 32;
+        if (s0 < a.T && lane == 0) a.slabs[(int64_t)(s0 >> 6) * a.NT + j] = sor;
+        sor = 0;
+      }
     }
   }
 }
@@ -179,8 +195,9 @@ static hipError_t launch_gate_cfg(const GateArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gate_twell(int in_dt, const void* x, const void* WgT, const void* bg, int T,
-                             int d, int F, const TwellView& out, hipStream_t s) {
-  GateArgs a{x, WgT, bg, T, d, F, F / 64, out.cnt, out.width, (float*)out.val, out.idx, out.mask};
+                             int d, int F, const TwellView& out, hipStream_t s, uint64_t* slabs, int* flag) {
+  GateArgs a{x, WgT, bg, T, d, F, F / 64, out.cnt, out.width, (float*)out.val, out.idx, out.mask,
+             in_dt == DT_BF16 ? slabs : nullptr, in_dt == DT_BF16 ? flag : nullptr};
   const bool big = T >= 512 && F % 256 == 0;
   if (in_dt == DT_BF16)
     return big ? launch_gate_cfg<GateBigBf16, true>(a, s) : launch_gate_cfg<GateSmallBf16, true>(a, s);

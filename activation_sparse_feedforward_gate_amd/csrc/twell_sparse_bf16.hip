@@ -31,6 +31,8 @@
 //       gfx950 transpose load (ds_read_b64_tr_b16); the A operand is each
 //       token's a values at those positions (zero where not stored), fp32
 //       split into bf16 hi + lo, fetched one step ahead.
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -68,22 +70,25 @@ struct SpArgs {
   int out_bf16;
   int S;                // slices
   int ngroups;          // ceil(NR / GW)
+  int nvb;              // virtual workgroups: ngroups * S (a grid may be smaller and loop over them)
   const int* gate;      // null, or a device flag: the kernel runs only if it is non-zero
   float l1;             // up backward: added to dg on every stored pair (activation penalty)
 };
 
-// Workgroup -> (token group g, slice s).  With S a multiple of 8, slice s runs
-// on XCD s % 8 (ids go round-robin over the XCDs), phase by phase.
-__device__ __forceinline__ void group_and_slice(const SpArgs& a, int& g, int& s) {
+// Virtual workgroup vb -> (token group g, slice s).  With S a multiple of 8,
+// slice s runs on XCD s % 8 (ids go round-robin over the XCDs, and a grid
+// that loops over the virtual workgroups has a multiple of 8 workgroups),
+// phase by phase.
+__device__ __forceinline__ void group_and_slice(const SpArgs& a, int vb, int& g, int& s) {
   if ((a.S & 7) == 0) {
     const int per_phase = a.ngroups * 8;
-    const int phase = blockIdx.x / per_phase;
-    const int r = blockIdx.x - phase * per_phase;
+    const int phase = vb / per_phase;
+    const int r = vb - phase * per_phase;
     g = r >> 3;
     s = phase * 8 + (r & 7);
   } else {
-    g = blockIdx.x / a.S;
-    s = blockIdx.x - g * a.S;
+    g = vb / a.S;
+    s = vb - g * a.S;
   }
 }
 
@@ -298,14 +303,11 @@ __device__ __forceinline__ void up_pass(const SpArgs& a, const UnionLds& L, char
 }
 
 template <int NP>
-__global__ __launch_bounds__(256) void up_bf16_kernel(SpArgs a) {
-  __shared__ UnionLds L;
-  __shared__ __attribute__((aligned(16))) char sw[NP][UP_CAP * 128];
-  if (a.gate && *a.gate == 0) return;
-
+__device__ __forceinline__ void up_bf16_block(const SpArgs& a, int vb, UnionLds& L,
+                                              char (*sw)[UP_CAP * 128]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int g, s;
-  group_and_slice(a, g, s);
+  group_and_slice(a, vb, g, s);
   const int j0 = (int)((int64_t)s * a.NT / a.S), j1 = (int)((int64_t)(s + 1) * a.NT / a.S);
   const int t0 = g * GT;
   build_union(a, L, t0, j0, j1 - j0);
@@ -331,17 +333,25 @@ __global__ __launch_bounds__(256) void up_bf16_kernel(SpArgs a) {
   }
 }
 
+template <int NP>
+__global__ __launch_bounds__(256) void up_bf16_kernel(SpArgs a) {
+  __shared__ UnionLds L;
+  __shared__ __attribute__((aligned(16))) char sw[NP][UP_CAP * 128];
+  if (a.gate && *a.gate == 0) return;
+  for (int vb = blockIdx.x; vb < a.nvb; vb += gridDim.x) {
+    up_bf16_block<NP>(a, vb, L, sw);
+    __syncthreads();                                 // LDS free for the next virtual workgroup
+  }
+}
+
 // ------------------------------------------------------------------ down
 
 template <int NV, int NCB>
-__global__ __launch_bounds__(256) void down_bf16_kernel(SpArgs a) {
-  __shared__ UnionLds L;
-  __shared__ __attribute__((aligned(16))) char sb[NV][DN_KC * DN_PITCH_MAX];
-  if (a.gate && *a.gate == 0) return;
-
+__device__ __forceinline__ void down_bf16_block(const SpArgs& a, int vb, UnionLds& L,
+                                                char (*sb)[DN_KC * DN_PITCH_MAX]) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int g, s;
-  group_and_slice(a, g, s);
+  group_and_slice(a, vb, g, s);
   constexpr int ncb = NCB;                       // every slice has NCB 16-column blocks
   const int c0 = s * NCB * 16, ncol = NCB * 16;
   const int pitch = (ncol * 2 + 127) / 128 * 128 + 32;   // row pitch: rows 32 bytes apart mod 128
@@ -474,6 +484,17 @@ __global__ __launch_bounds__(256) void down_bf16_kernel(SpArgs a) {
   }
 }
 
+template <int NV, int NCB>
+__global__ __launch_bounds__(256) void down_bf16_kernel(SpArgs a) {
+  __shared__ UnionLds L;
+  __shared__ __attribute__((aligned(16))) char sb[NV][DN_KC * DN_PITCH_MAX];
+  if (a.gate && *a.gate == 0) return;
+  for (int vb = blockIdx.x; vb < a.nvb; vb += gridDim.x) {
+    down_bf16_block<NV, NCB>(a, vb, L, sb);
+    __syncthreads();                                 // LDS free for the next virtual workgroup
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 
 namespace {
@@ -481,6 +502,17 @@ namespace {
 // Slices: a multiple of 8 (one per XCD per phase), enough that one slice's
 // weights (bytes_per_unit * units / S) stay within ~3 MB of L2, that no slice
 // has more than max_units, and that small batches still fill the chip.
+// Grid of a launch over nvb virtual workgroups.  A launch gated by a device
+// flag (a fallback that is almost never taken) gets one workgroup per CU,
+// rounded down to a multiple of 8 so that slices keep their XCD, and the
+// workgroups loop over the virtual ones: when the flag is clear the launch
+// costs one short wave of workgroups instead of the full grid.
+int gated_grid(int nvb, const int* gate) {
+  if (!gate) return nvb;
+  const int g = std::max(8, device_cus() / 8 * 8);
+  return std::min(nvb, g);
+}
+
 int pick_slices(int units, int max_units, double bytes_per_unit, int ngroups) {
   int S = 8;
   auto ok = [&](int s) {
@@ -508,7 +540,8 @@ hipError_t launch_up_bf16(const void* x, const void* dY, const void* WuT, const 
   const int NP = dY ? 2 : 1;
   a.S = pick_slices(a.NT, CT, 64.0 * d * 2 * NP, a.ngroups);
   if ((a.NT + a.S - 1) / a.S > CT) return hipErrorInvalidValue;
-  const int grid = a.ngroups * a.S;
+  a.nvb = a.ngroups * a.S;
+  const int grid = gated_grid(a.nvb, gate);
   if (NP == 2) hipLaunchKernelGGL(up_bf16_kernel<2>, dim3(grid), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(up_bf16_kernel<1>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -555,7 +588,8 @@ hipError_t launch_down_bf16(const float* v0, const float* v1, const void* W, con
     for (int c = 1; c <= ncb_all && S == 0; ++c)
       if (ncb_all % c == 0 && ncb_all / c <= DN_MAXCB) S = c;
   a.S = S;
-  const dim3 grid(a.ngroups * S);
+  a.nvb = a.ngroups * S;
+  const dim3 grid(gated_grid(a.nvb, gate));
   if (NV == 2) launch_down_ncb<2>(ncb_all / S, grid, a, s);
   else launch_down_ncb<1>(ncb_all / S, grid, a, s);
   return hipGetLastError();

@@ -92,20 +92,18 @@ __global__ __launch_bounds__(256) void union_or_kernel(UnionArgs a, uint64_t* Us
 }
 
 // Lists: one workgroup per row block; ascending positions via a scan of the
-// per-tile popcounts.
-__global__ __launch_bounds__(256) void union_list_kernel(UnionArgs a, const uint64_t* U) {
-  __shared__ int scan[256];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  if (b == 0 && tid == 0) *a.flag = 0;
+// per-tile popcounts, then each wave writes whole tiles, one set bit per lane.
+__device__ __forceinline__ void union_list_block(const UnionArgs& a, const uint64_t* U, int b, int* scan,
+                                                 int* start, uint64_t* su) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int base = 0;
   int* ul = a.ulist + (int64_t)b * a.F;
+  const int s0 = b * (a.lrows / 64), s1 = min((a.T + 63) / 64, s0 + a.lrows / 64);
   for (int j0 = 0; j0 < a.NT; j0 += 256) {
     const int j = j0 + tid;
     uint64_t u = 0;
-    if (j < a.NT) {
-      const int s0 = b * (a.lrows / 64), s1 = min((a.T + 63) / 64, s0 + a.lrows / 64);
+    if (j < a.NT)
       for (int sl = s0; sl < s1; ++sl) u |= U[(int64_t)sl * a.NT + j];
-    }
     const int c = popc64(u);
     scan[tid] = c;
     __syncthreads();
@@ -115,13 +113,26 @@ __global__ __launch_bounds__(256) void union_list_kernel(UnionArgs a, const uint
       scan[tid] += v;
       __syncthreads();
     }
-    int p = base + scan[tid] - c;
+    start[tid] = base + scan[tid] - c;
+    su[tid] = u;
     const int total = scan[255];
     __syncthreads();
-    for (uint64_t m = u; m; m &= m - 1) ul[p++] = j * 64 + __ffsll((long long)m) - 1;
+    const int nj = min(256, a.NT - j0);
+    for (int jj = w; jj < nj; jj += 4) {
+      const uint64_t m = su[jj];
+      if ((m >> lane) & 1ull) ul[start[jj] + popc64(m & below(lane))] = (j0 + jj) * 64 + lane;
+    }
     base += total;
+    __syncthreads();                                   // scan, start and su are rewritten next
   }
   if (tid == 0) a.ucount[b] = base;
+}
+
+__global__ __launch_bounds__(256) void union_list_kernel(UnionArgs a, const uint64_t* U) {
+  __shared__ int scan[256], start[256];
+  __shared__ uint64_t su[256];
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.flag = 0;
+  union_list_block(a, U, blockIdx.x, scan, start, su);
 }
 
 constexpr int POSCAP = 12288;         // neuron span of a position tile covered by the LDS position map
@@ -519,8 +530,9 @@ __global__ __launch_bounds__(Cfg::NTH) void bwd_union_kernel(UnionArgs a) {
 // fp16 copy of Wd for the down GEMM (exact for every bf16 value inside the
 // fp16 range); a value beyond that range raises the flag, and the layer then
 // takes the fp32 path.
-__global__ __launch_bounds__(256) void wd_to_f16_kernel(const uint16_t* Wd, _Float16* W16, int64_t n8, int* flag) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void wd_to_f16_block(const uint16_t* Wd, _Float16* W16, int64_t n8, int* flag,
+                                                int64_t blk) {
+  const int64_t i = blk * 256 + threadIdx.x;
   bool over = false;
   if (i < n8) {
     const uint4 w = ((const uint4*)Wd)[i];
@@ -536,6 +548,20 @@ __global__ __launch_bounds__(256) void wd_to_f16_kernel(const uint16_t* Wd, _Flo
     ((uint4*)W16)[i] = make_uint4(o[0], o[1], o[2], o[3]);
   }
   if (__builtin_amdgcn_ballot_w64(over) != 0ull && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
+}
+
+__global__ __launch_bounds__(256) void wd_to_f16_kernel(const uint16_t* Wd, _Float16* W16, int64_t n8, int* flag) {
+  wd_to_f16_block(Wd, W16, n8, flag, blockIdx.x);
+}
+
+// The row blocks' lists (workgroups [0, nlist)) and the fp16 copy of Wd (the
+// rest) in one launch, when the gate GEMM has written the slab unions and
+// cleared the flag.
+__global__ __launch_bounds__(256) void union_list_f16_kernel(UnionArgs a, const uint64_t* U, int nlist, int64_t n8) {
+  __shared__ int scan[256], start[256];
+  __shared__ uint64_t su[256];
+  if ((int)blockIdx.x < nlist) union_list_block(a, U, blockIdx.x, scan, start, su);
+  else wd_to_f16_block((const uint16_t*)a.Wd, (_Float16*)a.Wd16, n8, a.flag, (int64_t)blockIdx.x - nlist);
 }
 
 // Down-projection over the union: y rows of the block, one column tile.  K
@@ -637,6 +663,14 @@ void union_lists_launch(const UnionArgs& a, const uint64_t* U, hipStream_t s) {
 
 }  // namespace
 
+void union_slabs_and_flag(int T, int F, void* ws, uint64_t** slabs, int** flag) {
+  uint64_t* U;
+  const TwellView none{};
+  const UnionArgs a = union_setup(nullptr, nullptr, nullptr, T, 0, F, none, nullptr, ws, nullptr, DT_F32, &U);
+  *slabs = U;
+  *flag = a.flag;
+}
+
 void union_lists_only(int T, int F, const TwellView& h, void* ws, int** ulist, int** ucount, uint64_t** slabs) {
   uint64_t* U;
   const UnionArgs a = union_setup(nullptr, nullptr, nullptr, T, 0, F, h, nullptr, ws, nullptr, DT_F32, &U);
@@ -661,7 +695,7 @@ hipError_t launch_union_lists(int T, int F, const TwellView& h, void* ws, hipStr
 
 hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int T, int d, int F,
                             const TwellView& h, const uint8_t* skip, void* ws, void* y, int out_dt,
-                            int** flag_out, hipStream_t s, hipEvent_t ev_lists, hipEvent_t ev_up) {
+                            int** flag_out, hipStream_t s, hipEvent_t ev_lists, hipEvent_t ev_up, bool slabs_ready) {
   if (T == 0) {
     if (ev_lists) (void)hipEventRecord(ev_lists, s);
     if (ev_up) (void)hipEventRecord(ev_up, s);
@@ -671,11 +705,17 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
   uint64_t* U;
   const UnionArgs a = union_setup(x, WuT, Wd, T, d, F, h, skip, ws, y, out_dt, &U);
   if (flag_out) *flag_out = a.flag;
-  union_lists_launch(a, U, s);
   {
     const int64_t n8 = (int64_t)F * d / 8;
-    hipLaunchKernelGGL(wd_to_f16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, (const uint16_t*)Wd,
-                       (_Float16*)a.Wd16, n8, a.flag);
+    const unsigned nconv = (unsigned)((n8 + 255) / 256);
+    if (slabs_ready && !skip) {
+      hipLaunchKernelGGL(union_list_f16_kernel, dim3((unsigned)nblk + nconv), dim3(256), 0, s, a,
+                         (const uint64_t*)U, nblk, n8);
+    } else {
+      union_lists_launch(a, U, s);
+      hipLaunchKernelGGL(wd_to_f16_kernel, dim3(nconv), dim3(256), 0, s, (const uint16_t*)Wd, (_Float16*)a.Wd16,
+                         n8, a.flag);
+    }
   }
   if (ev_lists) (void)hipEventRecord(ev_lists, s);
   const int npt = (F + UpUnionCfg::BN - 1) / UpUnionCfg::BN;
