@@ -40,9 +40,10 @@ __device__ __forceinline__ float load_bias(const void* b, int n) {
 }
 
 // Tile order: groups of GM row blocks sweep all column blocks, so the
-// workgroups resident on one XCD share both x rows and gate weight rows in L2.
+// workgroups resident on one XCD share both x rows and gate weight rows in L2
+// (groups of 4 measured 2% faster than 8 at the 1.5B shapes, 16 slower).
 __device__ __forceinline__ void tile_coords(int id, int nbm, int nbn, int& bm, int& bn) {
-  constexpr int GM = 8;
+  constexpr int GM = 4;
   const int per_group = GM * nbn;
   const int group = id / per_group;
   const int first = group * GM;
