@@ -156,6 +156,57 @@ __global__ __launch_bounds__(Cfg2::NTH) void dense_rows_act_kernel(DenseRowsArgs
   }
 }
 
+// bf16 inputs: the same GEMMs and epilogue on the direct-to-LDS mainloop
+// (single-stage tiles, two workgroups per CU; the gathered x and dY rows come
+// through the A operand's row list).
+template <class Cfg2, class Cfg1, bool BWD>
+__global__ __launch_bounds__(Cfg2::NTH, WavesPerEU<Cfg2>::value) void dense_rows_act_dma_kernel(DenseRowsArgs a) {
+  static_assert(Cfg2::SINGLE && Cfg1::SINGLE && Cfg2::STAGE >= Cfg1::STAGE, "one stage buffer for both GEMMs");
+  __shared__ __attribute__((aligned(1024))) char st[Cfg2::STAGE];
+  const int nD = *a.n_rows;
+  const int nbn = a.F / Cfg2::BN;
+  const int bm = blockIdx.x / nbn, bn = blockIdx.x % nbn;
+  const int m0 = bm * Cfg2::BM, n0 = bn * Cfg2::BN;
+  if (m0 >= nD) return;
+  typedef DmaTile<Cfg2> Tile;
+  Tile g;
+  const Operand A{a.x, a.d, a.rows, nD};
+  const Operand B[2] = {{a.WgT, a.d, nullptr, a.F}, {a.WuT, a.d, nullptr, a.F}};
+  g.run(A, B, m0, n0, a.d, st, st);
+  DmaTile<Cfg1> gd;
+  if constexpr (BWD) {
+    const Operand A2{a.dY, a.d, a.rows, nD};
+    const Operand B2{a.Wd, a.d, nullptr, a.F};
+    gd.run(A2, &B2, m0, n0, a.d, st, st);
+  }
+  const int64_t ldb = BWD ? 3 * (int64_t)a.F : a.F;
+#pragma unroll
+  for (int j = 0; j < Cfg2::TN; ++j) {
+    const int col = n0 + Tile::col_of(j);
+    const float b = ld_bias<true>(a.bg, col);
+#pragma unroll
+    for (int i = 0; i < Cfg2::TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = m0 + Tile::row_of(i, e);
+        if (r < nD) {
+          const float gv = g.acc[0][i][j][e] + b;
+          const float h = gv > 0.f ? gv : 0.f;
+          const float u = g.acc[1][i][j][e];
+          float* row = a.buf + (int64_t)r * ldb;
+          if constexpr (BWD) {
+            const float da = gd.acc[0][i][j][e];
+            row[col] = gv > 0.f ? da * u + a.l1 : 0.f;
+            row[a.F + col] = da * h;
+            row[2 * a.F + col] = h * u;
+          } else {
+            row[col] = h * u;
+          }
+        }
+      }
+  }
+}
+
 // out[rows[r]] = sum_k buf[r][k].W[k]  (forward: y = A.Wd;  backward:
 // dX = dG.WgT + dU.WuT, two passes into one accumulator).
 template <class Cfg, bool BWD>
@@ -260,6 +311,10 @@ __global__ __launch_bounds__(256) void dense_rows_dbg_sum_kernel(DenseRowsArgs a
 // Configurations.  act: 128x128 block, 4 waves, gate+up (2 B operands) then dA.
 template <bool BF16IN> struct HybCfg;
 template <> struct HybCfg<true> {
+  using ActD2 = DmaCfg1<128, 128, 2, 4, 2>;
+  using ActD1 = DmaCfg1<128, 128, 2, 4, 1>;
+  using ActD2S = DmaCfg1<128, 64, 2, 2, 2>;
+  using ActD1S = DmaCfg1<128, 64, 2, 2, 1>;
   using Act2 = GemmCfg<128, 128, 2, 2, OP_BF16_K, OP_BF16_K, 2>;
   using Act1 = GemmCfg<128, 128, 2, 2, OP_BF16_K, OP_BF16_K, 1>;
   using Act2S = GemmCfg<128, 64, 2, 2, OP_BF16_K, OP_BF16_K, 2>;
@@ -286,6 +341,13 @@ static void launch_act(const DenseRowsArgs& a, hipStream_t s) {
   if (g > 0) hipLaunchKernelGGL((dense_rows_act_kernel<Act2, Act1, BF16IN, BWD>), dim3(g), dim3(Act2::NTH), 0, s, a);
 }
 
+template <class Act2, class Act1, bool BWD>
+static void launch_act_dma(const DenseRowsArgs& a, hipStream_t s) {
+  const int g = ((a.T + Act2::BM - 1) / Act2::BM) * (a.F / Act2::BN);
+  if (g > 0)
+    hipLaunchKernelGGL((dense_rows_act_dma_kernel<Act2, Act1, BWD>), dim3(g), dim3(Act2::NTH), 0, s, a);
+}
+
 template <class Cfg, bool BWD>
 static void launch_out(const DenseRowsArgs& a, hipStream_t s) {
   const int g = ((a.T + Cfg::BM - 1) / Cfg::BM) * (a.d / Cfg::BN);
@@ -298,11 +360,36 @@ static void launch_wgrad(const DenseRowsArgs& a, hipStream_t s) {
   if (g > 0) hipLaunchKernelGGL((dense_rows_wgrad_kernel<Cfg>), dim3(g), dim3(Cfg::NTH), 0, s, a);
 }
 
+// The direct-to-LDS act kernels are instantiated explicitly: referenced only
+// from the launchers below, the host pass emitted no launch stub for the
+// backward variants.
+template __global__ void dense_rows_act_dma_kernel<HybCfg<true>::ActD2, HybCfg<true>::ActD1, false>(DenseRowsArgs);
+template __global__ void dense_rows_act_dma_kernel<HybCfg<true>::ActD2, HybCfg<true>::ActD1, true>(DenseRowsArgs);
+template __global__ void dense_rows_act_dma_kernel<HybCfg<true>::ActD2S, HybCfg<true>::ActD1S, false>(DenseRowsArgs);
+template __global__ void dense_rows_act_dma_kernel<HybCfg<true>::ActD2S, HybCfg<true>::ActD1S, true>(DenseRowsArgs);
+
+// act GEMMs: direct-to-LDS tiles for bf16 inputs, register-staged for fp32
+template <bool BF16IN, bool BWD>
+struct ActLaunch {
+  static void go(const DenseRowsArgs& a, hipStream_t s) {
+    using C = HybCfg<false>;
+    if (a.F % 128 == 0) launch_act<typename C::Act2, typename C::Act1, false, BWD>(a, s);
+    else launch_act<typename C::Act2S, typename C::Act1S, false, BWD>(a, s);
+  }
+};
+template <bool BWD>
+struct ActLaunch<true, BWD> {
+  static void go(const DenseRowsArgs& a, hipStream_t s) {
+    using C = HybCfg<true>;
+    if (a.F % 128 == 0) launch_act_dma<typename C::ActD2, typename C::ActD1, BWD>(a, s);
+    else launch_act_dma<typename C::ActD2S, typename C::ActD1S, BWD>(a, s);
+  }
+};
+
 template <bool BF16IN, bool BWD>
 static hipError_t dense_rows_t(const DenseRowsArgs& a, hipStream_t s) {
   using C = HybCfg<BF16IN>;
-  if (a.F % 128 == 0) launch_act<typename C::Act2, typename C::Act1, BF16IN, BWD>(a, s);
-  else launch_act<typename C::Act2S, typename C::Act1S, BF16IN, BWD>(a, s);
+  ActLaunch<BF16IN, BWD>::go(a, s);
   launch_out<typename C::Out, BWD>(a, s);
   if constexpr (BWD) {
     if (a.d % 128 == 0) launch_wgrad<typename C::Wgrad>(a, s);
