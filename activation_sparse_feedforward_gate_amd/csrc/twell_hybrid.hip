@@ -434,25 +434,41 @@ hipError_t launch_dense_rows_bwd(int in_dt, const void* x, const void* WgT, cons
 
 constexpr int CSC_CHUNK = 256;   // tokens per count/fill chunk
 
-// part[c][n] = number of sparse rows t in chunk c with (t, n) stored.  The
-// loop takes 16 tokens at a time so their loads are in flight together.
-__global__ __launch_bounds__(64) void csc_count_kernel(const uint64_t* mask, const uint8_t* skip, int T,
-                                                       int NT, int F, int* part) {
-  const int lane = threadIdx.x;
-  const int j = blockIdx.x, c = blockIdx.y;
-  const int t0 = c * CSC_CHUNK, t1 = min(T, t0 + CSC_CHUNK);
-  int k = 0;
-  for (int tb = t0; tb < t1; tb += 16) {
-    uint64_t m[16];
+// The count and fill kernels stage the masks of one chunk of CSC_CHUNK rows
+// and CSC_JG column tiles in LDS (skipped rows and tiles past NT as zeros):
+// consecutive threads read consecutive tiles of a row, every load of a
+// thread in flight before the first LDS store.  Each wave then takes whole
+// tiles, lane = neuron bit, reading each row's word as an LDS broadcast.
+constexpr int CSC_JG = 16;       // column tiles per count/fill workgroup
+
+__device__ __forceinline__ void csc_stage(const uint64_t* mask, const uint8_t* skip, int T, int NT, int t0, int j0,
+                                          uint64_t* sm) {
+  constexpr int PER = CSC_CHUNK * CSC_JG / 256;
+  uint64_t m[PER];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int t = tb + q;
-      m[q] = (t < t1 && !(skip && skip[t])) ? mask[(int64_t)t * NT + j] : 0ull;
-    }
-#pragma unroll
-    for (int q = 0; q < 16; ++q) k += (int)((m[q] >> lane) & 1ull);
+  for (int q = 0; q < PER; ++q) {
+    const int i = threadIdx.x + q * 256;
+    const int t = t0 + i / CSC_JG, j = j0 + i % CSC_JG;
+    m[q] = (t < T && j < NT && !(skip && skip[t])) ? mask[(int64_t)t * NT + j] : 0ull;
   }
-  part[(int64_t)c * F + j * 64 + lane] = k;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) sm[threadIdx.x + q * 256] = m[q];
+  __syncthreads();
+}
+
+// part[c][n] = number of sparse rows t in chunk c with (t, n) stored.
+__global__ __launch_bounds__(256) void csc_count_kernel(const uint64_t* mask, const uint8_t* skip, int T,
+                                                        int NT, int F, int* part) {
+  __shared__ uint64_t sm[CSC_CHUNK * CSC_JG];
+  const int c = blockIdx.y, j0 = blockIdx.x * CSC_JG;
+  const int t0 = c * CSC_CHUNK, nr = min(T, t0 + CSC_CHUNK) - t0;
+  csc_stage(mask, skip, T, NT, t0, j0, sm);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int jj = w; jj < CSC_JG && j0 + jj < NT; jj += 4) {
+    int k = 0;
+    for (int r = 0; r < nr; ++r) k += (int)((sm[r * CSC_JG + jj] >> lane) & 1ull);
+    part[(int64_t)c * F + (j0 + jj) * 64 + lane] = k;
+  }
 }
 
 // Per neuron n (one thread each): part[c][n] becomes the exclusive prefix of
@@ -505,25 +521,22 @@ __global__ __launch_bounds__(1024) void csc_total_scan_kernel(int F, int* start)
 // entries[pos] = flat TwELL slot offset of each stored pair of a sparse row,
 // grouped by neuron, tokens ascending within a neuron; the neuron's block
 // starts at start[n], chunk c's part at part[c][n] within it.
-__global__ __launch_bounds__(64) void csc_fill_kernel(const uint64_t* mask, const uint8_t* skip, int T, int NT,
-                                                      int F, const int* part, const int* start, uint32_t* entries) {
-  const int lane = threadIdx.x;
-  const int j = blockIdx.x, c = blockIdx.y;
-  const int t0 = c * CSC_CHUNK, t1 = min(T, t0 + CSC_CHUNK);
-  int pos = start[j * 64 + lane] + part[(int64_t)c * F + j * 64 + lane];
+__global__ __launch_bounds__(256) void csc_fill_kernel(const uint64_t* mask, const uint8_t* skip, int T, int NT,
+                                                       int F, const int* part, const int* start, uint32_t* entries) {
+  __shared__ uint64_t sm[CSC_CHUNK * CSC_JG];
+  const int c = blockIdx.y, j0 = blockIdx.x * CSC_JG;
+  const int t0 = c * CSC_CHUNK, nr = min(T, t0 + CSC_CHUNK) - t0;
+  csc_stage(mask, skip, T, NT, t0, j0, sm);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint64_t lower = below(lane);
-  for (int tb = t0; tb < t1; tb += 16) {
-    uint64_t m[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int t = tb + q;
-      m[q] = (t < t1 && !(skip && skip[t])) ? mask[(int64_t)t * NT + j] : 0ull;
-    }
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      if ((m[q] >> lane) & 1ull) {
-        const int t = tb + q;
-        const uint32_t slot = (uint32_t)popc64(m[q] & lower);
+  for (int jj = w; jj < CSC_JG && j0 + jj < NT; jj += 4) {
+    const int j = j0 + jj;
+    int pos = start[j * 64 + lane] + part[(int64_t)c * F + j * 64 + lane];
+    for (int r = 0; r < nr; ++r) {
+      const uint64_t m = sm[r * CSC_JG + jj];
+      if ((m >> lane) & 1ull) {
+        const int t = t0 + r;
+        const uint32_t slot = (uint32_t)popc64(m & lower);
         entries[pos++] = ((uint32_t)((t >> 4) * NT + j) * 64u + slot) * 16u + (uint32_t)(t & 15);
       }
     }
@@ -607,12 +620,14 @@ hipError_t launch_sparse_wgrad(int in_dt, const void* x, const void* dY, int T, 
   const int NT = F / 64;
   const int nchunk = (T + CSC_CHUNK - 1) / CSC_CHUNK;
   if (nchunk > 0) {
-    hipLaunchKernelGGL(csc_count_kernel, dim3(NT, nchunk), dim3(64), 0, s, h.mask, skip, T, NT, F, part);
+    hipLaunchKernelGGL(csc_count_kernel, dim3((NT + CSC_JG - 1) / CSC_JG, nchunk), dim3(256), 0, s, h.mask, skip, T,
+                       NT, F, part);
   }
   hipLaunchKernelGGL(csc_chunk_scan_kernel, dim3((F + 255) / 256), dim3(256), 0, s, part, nchunk, F, start);
   hipLaunchKernelGGL(csc_total_scan_kernel, dim3(1), dim3(1024), 0, s, F, start);
   if (nchunk > 0) {
-    hipLaunchKernelGGL(csc_fill_kernel, dim3(NT, nchunk), dim3(64), 0, s, h.mask, skip, T, NT, F, part, start,
+    hipLaunchKernelGGL(csc_fill_kernel, dim3((NT + CSC_JG - 1) / CSC_JG, nchunk), dim3(256), 0, s, h.mask, skip, T,
+                       NT, F, part, start,
                        entries);
   }
   WgradArgs a{x, dY, T, d, F, NT, start, entries, aval, dgval, duval, dWgT, dWuT, dWd, dbg};
