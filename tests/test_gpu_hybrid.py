@@ -97,12 +97,13 @@ def check_full(w, got, tau, bias=True, l1c=0.0):
 SMALL = [
     ("hybrid", dict(T=520, d=256, f=1280)),
     ("hybrid", dict(T=333, d=128, f=640)),
+    ("hybrid", dict(T=300, d=192, f=704)),
     ("0.5b", dict(T=300, d=256, f=1024, grad=True)),
     ("tiny_f32", dict(grad=True)),
 ]
 
 
-@pytest.mark.parametrize("name,kw", SMALL, ids=["hybrid-520", "hybrid-333", "0.5b-300", "tiny_f32"])
+@pytest.mark.parametrize("name,kw", SMALL, ids=["hybrid-520", "hybrid-333", "hybrid-d192-f704", "0.5b-300", "tiny_f32"])
 def test_hybrid_small(torch, tw, name, kw):
     w = make_workload(name, **kw)
     log(f"[hybrid] {name} T={w.T} d={w.d} f={w.f} tau={w.tau}")
