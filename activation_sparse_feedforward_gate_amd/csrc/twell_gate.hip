@@ -54,7 +54,7 @@ __device__ __forceinline__ void tile_coords(int id, int nbm, int nbn, int& bm, i
 }
 
 template <class Cfg, bool BF16IN>
-__global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
+__global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_kernel(GateArgs a) {
   static_assert((Cfg::BN / Cfg::WN) % 64 == 0 && Cfg::TN % 2 == 0, "whole 64-column TwELL tiles per wave");
   static_assert((Cfg::BM / Cfg::WM) % 64 == 0, "whole 64-row slabs per wave");
   if (a.flag && blockIdx.x == 0 && threadIdx.x == 0) *a.flag = 0;
@@ -70,7 +70,8 @@ __global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
   char* lds;
   if constexpr (TileFor<Cfg>::dma) {
     __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
-    __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
+    __shared__ __attribute__((aligned(1024))) char st1_[Cfg::SINGLE ? 16 : Cfg::STAGE];
+    char* st1 = Cfg::SINGLE ? st0 : st1_;
     g.run(A, &B, m0, n0, a.d, st0, st1);
     lds = st0;
   } else {
@@ -181,6 +182,10 @@ __global__ __launch_bounds__(Cfg::NTH) void gate_twell_kernel(GateArgs a) {
 }
 
 using GateBigBf16 = DmaCfg<256, 256, 2, 4>;
+// K = d <= 1024: single-stage 128x256 tiles, two workgroups per CU, so one
+// workgroup's TwELL epilogue runs under the other's MFMAs (0.5b gate 159 ->
+// 149 us; at d = 2048 the double-buffered 256x256 tile is 4% faster)
+using GateMidBf16 = DmaCfg1<128, 256, 2, 4>;
 using GateSmallBf16 = GemmCfg<64, 64, 1, 1, OP_BF16_K, OP_BF16_K>;
 using GateBigF32 = GemmCfg<256, 256, 2, 4, OP_F32_K, OP_F32_K>;
 using GateSmallF32 = GemmCfg<64, 64, 1, 1, OP_F32_K, OP_F32_K>;
@@ -200,8 +205,10 @@ hipError_t launch_gate_twell(int in_dt, const void* x, const void* WgT, const vo
   GateArgs a{x, WgT, bg, T, d, F, F / 64, out.cnt, out.width, (float*)out.val, out.idx, out.mask,
              in_dt == DT_BF16 ? slabs : nullptr, in_dt == DT_BF16 ? flag : nullptr};
   const bool big = T >= 512 && F % 256 == 0;
-  if (in_dt == DT_BF16)
-    return big ? launch_gate_cfg<GateBigBf16, true>(a, s) : launch_gate_cfg<GateSmallBf16, true>(a, s);
+  if (in_dt == DT_BF16) {
+    if (!big) return launch_gate_cfg<GateSmallBf16, true>(a, s);
+    return d <= 1024 ? launch_gate_cfg<GateMidBf16, true>(a, s) : launch_gate_cfg<GateBigBf16, true>(a, s);
+  }
   return big ? launch_gate_cfg<GateBigF32, false>(a, s) : launch_gate_cfg<GateSmallF32, false>(a, s);
 }
 
