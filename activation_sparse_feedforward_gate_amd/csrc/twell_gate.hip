@@ -41,7 +41,8 @@ __device__ __forceinline__ float load_bias(const void* b, int n) {
 
 // Tile order: groups of GM row blocks sweep all column blocks, so the
 // workgroups resident on one XCD share both x rows and gate weight rows in L2
-// (groups of 4 measured 2% faster than 8 at the 1.5B shapes, 16 slower).
+// (groups of 4 measured 2% faster than 8 at T = 32768, d = 2048, F = 5632;
+// 16 slower).
 __device__ __forceinline__ void tile_coords(int id, int nbm, int nbn, int& bm, int& bn) {
   constexpr int GM = 4;
   const int per_group = GM * nbn;
@@ -183,8 +184,9 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
 
 using GateBigBf16 = DmaCfg<256, 256, 2, 4>;
 // K = d <= 1024: single-stage 128x256 tiles, two workgroups per CU, so one
-// workgroup's TwELL epilogue runs under the other's MFMAs (0.5b gate 159 ->
-// 149 us; at d = 2048 the double-buffered 256x256 tile is 4% faster)
+// workgroup's TwELL epilogue runs under the other's MFMAs (T = 16384,
+// d = 1024, F = 4096: 159 -> 148 us; at d = 2048 the double-buffered 256x256
+// tile is 4% faster)
 using GateMidBf16 = DmaCfg1<128, 256, 2, 4>;
 using GateSmallBf16 = GemmCfg<64, 64, 1, 1, OP_BF16_K, OP_BF16_K>;
 using GateBigF32 = GemmCfg<256, 256, 2, 4, OP_F32_K, OP_F32_K>;

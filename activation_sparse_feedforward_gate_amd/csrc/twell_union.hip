@@ -30,9 +30,10 @@ namespace twell {
 namespace {
 
 // Tokens per row block.  Smaller blocks give smaller unions (less executed
-// work) but smaller GEMM tiles: 128 rows measured faster than 256 overall on
-// the 1.5B and 2B shapes (union fractions 42% / 26% against 58% / 38%, tile
-// throughput about 10% lower).
+// work) but smaller GEMM tiles: 128 rows measured faster than 256 overall at
+// T = 32768 with d = 2048, F = 5632 (1.5% density) and d = 2304, F = 9216
+// (0.93%): union fractions 42% / 26% against 58% / 38%, tile throughput about
+// 10% lower.
 constexpr int UB = 128;
 constexpr int RT = UB / 16;            // TwELL row tiles per row block
 
