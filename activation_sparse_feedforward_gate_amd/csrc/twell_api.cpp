@@ -63,6 +63,13 @@ twell_status check_shape(const twell_ffn_shape* sh) {
   if (sh->d % 64 != 0 || sh->F % 64 != 0)
     return fail(TWELL_EUNSUPPORTED, "GPU path needs d %% 64 == 0 and F %% 64 == 0 (d=%d F=%d)", sh->d, sh->F);
   if (sh->F > 65472) return fail(TWELL_EUNSUPPORTED, "F=%d too large (max 65472)", sh->F);
+  // The GEMM mainloops address a 16-bit operand ([T][d] activations, [F][d]
+  // weights, the [T][F] fp16/bf16 intermediates) with 32-bit per-lane BYTE
+  // offsets, so each such matrix must hold fewer than 2^31 elements.
+  constexpr int64_t LIM = (int64_t)1 << 31;
+  if ((int64_t)sh->T * sh->d >= LIM || (int64_t)sh->F * sh->d >= LIM || (int64_t)sh->T * sh->F >= LIM)
+    return fail(TWELL_EUNSUPPORTED, "T*d, F*d and T*F must each be below 2^31 (T=%d d=%d F=%d)", sh->T, sh->d,
+                sh->F);
   return TWELL_OK;
 }
 
@@ -243,9 +250,6 @@ twell_status twell_ffn_fwd_ex(const twell_ffn_shape* sh, const void* x, const vo
       return fail(TWELL_EINVAL, "saved_h must be T x F with fp32 values");
   }
   if (n_events < 0 || (n_events > 0 && !stage_events)) return fail(TWELL_EINVAL, "bad stage event array");
-  if ((int64_t)sh->T * sh->d >= ((int64_t)1 << 32) || (int64_t)sh->F * sh->d >= ((int64_t)1 << 32) ||
-      (int64_t)sh->T * sh->F >= ((int64_t)1 << 32))
-    return fail(TWELL_EUNSUPPORTED, "matrices must hold fewer than 2^32 elements");
   const bool training = dense_row_threshold >= 0;
   if (training && !saved_h) return fail(TWELL_EINVAL, "the hybrid forward (dense_row_threshold >= 0) needs saved_h");
   const size_t need = fwd_layout(sh, training, nullptr, nullptr);
@@ -357,6 +361,9 @@ static twell_status check_bwd_args(const twell_ffn_shape* sh, const void* x, con
   const int64_t NR = (sh->T + GPU_R - 1) / GPU_R;
   if (NR * (sh->F / GPU_C) * GPU_C * GPU_R >= ((int64_t)1 << 32))
     return fail(TWELL_EUNSUPPORTED, "T x F too large for 32-bit TwELL slot offsets");
+  // the dense branch's [rows][3F] fp32 buffer is read with 32-bit element offsets
+  if ((int64_t)sh->T * 3 * sh->F >= ((int64_t)1 << 32))
+    return fail(TWELL_EUNSUPPORTED, "3*T*F must be below 2^32 for the backward (T=%d F=%d)", sh->T, sh->F);
   return TWELL_OK;
 }
 
@@ -615,9 +622,6 @@ twell_status twell_relu_ffn_fwd(const twell_ffn_shape* sh, const void* x, const 
     if (saved_h->T != sh->T || saved_h->F != sh->F || saved_h->vdtype != TWELL_F32)
       return fail(TWELL_EINVAL, "saved_h must be T x F with fp32 values");
   }
-  if ((int64_t)sh->T * sh->d >= ((int64_t)1 << 32) || (int64_t)sh->F * sh->d >= ((int64_t)1 << 32) ||
-      (int64_t)sh->T * sh->F >= ((int64_t)1 << 32))
-    return fail(TWELL_EUNSUPPORTED, "matrices must hold fewer than 2^32 elements");
   const size_t need = relu_layout(sh, nullptr, nullptr);
   if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
   if (sh->T == 0) return TWELL_OK;
@@ -719,8 +723,6 @@ twell_status twell_ffn_dense_bwd(const twell_ffn_shape* sh, const void* x, const
     if (!aligned16(p)) return fail(TWELL_EINVAL, "tensors must be 16-byte aligned");
   if (sh->T % 64 != 0 || sh->d % 256 != 0 || sh->F % 256 != 0)
     return fail(TWELL_EUNSUPPORTED, "the dense training baseline needs T %% 64 == 0, d %% 256 == 0, F %% 256 == 0");
-  if ((int64_t)sh->T * sh->F * 2 >= ((int64_t)1 << 32) || (int64_t)sh->T * sh->d * 2 >= ((int64_t)1 << 32))
-    return fail(TWELL_EUNSUPPORTED, "[T][F] and [T][d] bf16 matrices must be under 4 GB");
   const size_t need = dense_train_ws_bytes(sh->T, sh->d, sh->F);
   if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
   if (sh->T == 0) {

@@ -528,9 +528,13 @@ __global__ __launch_bounds__(Cfg::NTH) void bwd_union_kernel(UnionArgs a) {
   }
 }
 
-// fp16 copy of Wd for the down GEMM (exact for every bf16 value inside the
-// fp16 range); a value beyond that range raises the flag, and the layer then
-// takes the fp32 path.
+// fp16 copy of Wd for the down GEMM.  A bf16 value of magnitude in
+// [2^-14, 65504] is exact in fp16 (8 significant bits fit in 11); below 2^-14
+// fp16 is subnormal with spacing 2^-24, so a weight under 2^-17 keeps fewer
+// than 8 bits and is rounded to the nearest multiple of 2^-24 (absolute error
+// at most 2^-25, far below the rounding of a = h*u to fp16).  That underflow
+// raises no flag; a value beyond 65504 does, and the layer then takes the fp32
+// path.
 __device__ __forceinline__ void wd_to_f16_block(const uint16_t* Wd, _Float16* W16, int64_t n8, int* flag,
                                                 int64_t blk) {
   const int64_t i = blk * 256 + threadIdx.x;

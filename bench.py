@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """FFN-layer throughput of the TwELL ReLU-gated FFN on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0.5b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2b]
 
 One step is one pass of the whole hot path over the workload's token batch,
 inputs already resident in HBM:
@@ -36,11 +36,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="0.5b")
+    ap.add_argument("--config", default="2b",
+                    help="headline workload: 2b (T=32768, d=2304, F=9216, 0.93%% density) by default")
     ap.add_argument("--decode", action="store_true", help="use the workload's decode-shaped pass")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-extras", action="store_true", help="skip the short runs of the other workloads")
+    ap.add_argument("--cold-iters", type=int, default=5,
+                    help="steps timed one by one after a 512 MiB scratch write (cold cache); 0 skips")
     ap.add_argument("--compact-w", type=int, default=8,
                     help="training workloads: also time the step with the saved state in compact TwELL of this "
                          "capacity (twell_compact + twell_ffn_bwd_hybrid_compact); 0 skips it")
@@ -77,8 +81,10 @@ def cpu_baseline(w, budget_s: float, training: bool) -> dict:
     dt = time.perf_counter() - t0
     what = ("hybrid forward + backward (row classification, dense and sparse branches)" if training
             else "sparse forward (gate GEMM, TwELL pack, per-pair up/down)")
-    return {"value": done / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"first {done} of {w.T} token rows, float64 numpy {what}, {dt:.1f} s"}
+    return {"value": done / dt, "unit": "tokens/s", "cores": blas_threads(), "host_cpu_count": os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"first {done} of {w.T} token rows, float64 numpy {what}, {dt:.1f} s; cores = the BLAS "
+                      f"threads the oracle ran on"}
 
 
 # tokens per row block of the union up/down GEMMs (the library's row blocks)
@@ -210,25 +216,55 @@ def relu_bench(args) -> int:
     return 0
 
 
-def main() -> int:
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only (the library has no multi-GPU path); "
-                                   "use --gpus 1", "n_gpus": args.gpus}))
-        return 2
-    if args.copy_calibration:
-        return copy_calibration(max(1, args.steps))
-    if args.ffn == "relu":
-        return relu_bench(args)
+def _ev():
+    import torch
+    return torch.cuda.Event(enable_timing=True)
+
+
+def _timed(fn, steps: int, warmup: int, stream) -> float:
+    """Mean ms per call of fn over exactly `steps` calls after `warmup` untimed
+    ones, between two events on the launch stream, synchronized on both sides."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0, t1 = _ev(), _ev()
+    t0.record(stream)
+    for _ in range(steps):
+        fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def union_sizes(mask: "np.ndarray", T: int, live=None):
+    """Union size of every UNION_BLOCK-token row block (live rows only)."""
+    import numpy as np
+    m = mask.copy()
+    if live is not None:
+        m[~live] = 0
+    ub = UNION_BLOCK
+    if T == 0:
+        return np.zeros(0, dtype=np.int64)
+    pad = (-T) % ub
+    mm = np.concatenate([m, np.zeros((pad, m.shape[1]), np.uint64)]) if pad else m
+    u = np.bitwise_or.reduce(mm.reshape(-1, ub, m.shape[1]), axis=1)
+    return np.unpackbits(u.view(np.uint8), axis=1).sum(axis=1).astype(np.int64)
+
+
+def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool) -> dict:
+    """Time one workload: the TwELL step, the library's own dense step beside
+    it, per-stage HIP events, and (full) the roofline of every forward kernel,
+    a cold-cache figure and the workspace bytes of both paths."""
     import numpy as np
     import torch
 
     import activation_sparse_feedforward_gate_amd as tw
     from workloads import CONFIGS, make_workload
 
-    cfg = CONFIGS[args.config]
+    cfg = CONFIGS[name]
     training = cfg.tau_frac is not None
-    w = make_workload(args.config, decode=args.decode)
+    w = make_workload(name, decode=decode)
     T, d, f = w.T, w.d, w.f
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -241,26 +277,28 @@ def main() -> int:
     x, WgT, bg, WuT, Wd = dt(w.x), dt(w.WgT), dt(w.bg), dt(w.WuT), dt(w.Wd)
     in_dt = tw.TWELL_BF16 if cfg.dtype == "bf16" else tw.TWELL_F32
     shape = tw.ffn_shape(T, d, f, in_dt, tw.TWELL_F32)
-    h = tw.alloc_twell_mat(T, f, tw.TWELL_F32, device=dev)
     y = torch.empty((T, d), dtype=torch.float32, device=dev)
     tau = w.tau if training else -1
-    wsf = torch.empty(max(1, tw.twell_ffn_fwd_workspace(shape, training)), dtype=torch.uint8, device=dev)
+    ws_fwd_bytes = tw.twell_ffn_fwd_workspace(shape, training)
+    wsf = torch.empty(max(1, ws_fwd_bytes), dtype=torch.uint8, device=dev)
+    # inference keeps no TwELL for a backward pass: the step passes no saved_h
+    # and the TwELL lives in the workspace; training saves h for the backward
+    h = tw.alloc_twell_mat(T, f, tw.TWELL_F32, device=dev)
+    saved = h if training else None
     if training:
         dY = dt(w.dY)
         dX = torch.empty((T, d), dtype=torch.float32, device=dev)
         dW = [torch.empty((f, d), dtype=torch.float32, device=dev) for _ in range(3)]
         dbg = torch.empty((f,), dtype=torch.float32, device=dev)
         nD = torch.empty((1,), dtype=torch.int32, device=dev)
-        wsb = torch.empty(max(1, tw.twell_ffn_bwd_workspace(shape, tau)), dtype=torch.uint8, device=dev)
-
-    def ev():
-        return torch.cuda.Event(enable_timing=True)
+        ws_bwd_bytes = tw.twell_ffn_bwd_workspace(shape, tau)
+        wsb = torch.empty(max(1, ws_bwd_bytes), dtype=torch.uint8, device=dev)
 
     def step(evs=None):
         if evs is None:
-            tw.twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, h, tau, wsf, stream)
+            tw.twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, saved, tau, wsf, stream)
         else:
-            tw.twell_ffn_fwd_ex(shape, x, WgT, bg, WuT, Wd, y, h, tau, wsf, evs[:7], stream)
+            tw.twell_ffn_fwd_ex(shape, x, WgT, bg, WuT, Wd, y, saved, tau, wsf, evs[:7], stream)
         if training:
             if evs is not None:
                 evs[7].record(stream)
@@ -269,23 +307,14 @@ def main() -> int:
             if evs is not None:
                 evs[8].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # timed region: exactly K steps between two events, bracketed by synchronize
-    t0, t1 = ev(), ev()
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
+    # timed region: exactly `steps` steps between two events, bracketed by synchronize
+    ms_step = _timed(step, steps, warmup, stream)
 
     # per-stage durations from events recorded between the kernel launches
     nst = 9 if training else 7
-    recs = [[ev() for _ in range(nst)] for _ in range(args.steps)]
+    recs = [[_ev() for _ in range(nst)] for _ in range(steps)]
     torch.cuda.synchronize()
-    for k in range(args.steps):
+    for k in range(steps):
         step(recs[k])
     torch.cuda.synchronize()
     st = np.array([[r[i].elapsed_time(r[i + 1]) for i in range(nst - 1)] for r in recs]).mean(axis=0)
@@ -294,42 +323,87 @@ def main() -> int:
     if training:
         stages["dense_rows_fwd"] = st[5]
         stages["hybrid_bwd"] = st[7]
-    nnz = int(h.cnt.to(torch.int64).sum().item())
+    if not training:
+        # the TwELL of the step, for its statistics (one more call, untimed)
+        tw.twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, h, tau, wsf, stream)
+        torch.cuda.synchronize()
+    cnt = h.cnt.cpu().numpy().astype(np.int64)
+    nnz = int(cnt.sum())
+    mask = h.mask.cpu().numpy().view(np.uint64)
 
-    out = {
-        "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
-        "data": "synthetic (seeded; shapes, densities and neuron-popularity structure of the workload)",
-        "config": {"workload": cfg.description + (" (decode pass)" if args.decode else ""),
-                   "name": args.config, "T": T, "d_model": d, "d_ff": f, "tile": "16x64",
-                   "realised_density": nnz / (T * f), "pass": "fwd+bwd" if training else "fwd"},
-        "stages_ms": {k: float(v) for k, v in stages.items()},
-    }
+    out = {"ms_per_step": ms_step, "tokens_per_s": T / (ms_step * 1e-3),
+           "workload": cfg.description + (" (decode pass)" if decode else ""), "name": name,
+           "T": T, "d_model": d, "d_ff": f, "realised_density": nnz / max(1, T * f),
+           "pass": "fwd+bwd" if training else "fwd",
+           "stages_ms": {k: float(v) for k, v in stages.items()}}
+
+    bf = cfg.dtype == "bf16"
+    few_tokens = bf and not training and 0 < T <= 256
+    live = None
+    if training:
+        live = cnt.sum(axis=1) <= tau                  # the union GEMMs cover the sparse rows only
+        out["dense_rows"] = int((~live).sum())
+    if bf and not few_tokens:
+        nb = union_sizes(mask, T, live)
+        out["mean_union_fraction"] = float(nb.mean() / f) if len(nb) else 0.0
+    if few_tokens:
+        n_union = int(np.unpackbits(np.bitwise_or.reduce(mask, axis=0).view(np.uint8)).sum())
+        out["union_neurons"] = n_union
+
+    # the library's own dense step on the same inputs
+    if not args.no_dense and bf:
+        if training:
+            dws = torch.empty(tw.twell_ffn_dense_bwd_workspace(shape), dtype=torch.uint8, device=dev)
+            yd, dXd = torch.empty_like(y), torch.empty_like(dX)
+            dWd_ = [torch.empty_like(t) for t in dW]
+            dbgd = torch.empty_like(dbg)
+
+            def dense_step():
+                tw.twell_ffn_dense_bwd(shape, x, WgT, bg, WuT, Wd, dY, yd, dXd, dWd_[0], dWd_[1], dWd_[2], dbgd,
+                                       dws, stream)
+            dms = _timed(dense_step, steps, warmup, stream)
+            out["dense_baseline"] = {"tokens_per_s": T / (dms * 1e-3), "ms_per_step": dms,
+                                     "tflops": 18.0 * T * d * f / (dms * 1e-3) / 1e12,
+                                     "what": "dense forward + backward, bf16 intermediates"}
+            dense_ws = tw.twell_ffn_dense_bwd_workspace(shape)
+        else:
+            dense_ws = tw.twell_ffn_dense_fwd_workspace(shape)
+            dws = torch.empty(max(1, dense_ws), dtype=torch.uint8, device=dev)
+            yd = torch.empty_like(y)
+            dms = _timed(lambda: tw.twell_ffn_dense_fwd(shape, x, WgT, bg, WuT, Wd, yd, dws, stream), steps, warmup,
+                         stream)
+            out["dense_baseline"] = {"tokens_per_s": T / (dms * 1e-3), "ms_per_step": dms,
+                                     "tflops": 6.0 * T * d * f / (dms * 1e-3) / 1e12}
+            out["dense_vs_sparse_rel_diff"] = (y - yd).norm().item() / max(yd.norm().item(), 1e-30)
+        out["speedup_vs_dense"] = dms / ms_step
+        # device memory the step needs beyond its inputs and outputs
+        twell_ws = ws_fwd_bytes + (tw.twell_mat_bytes(T, f)[0] + ws_bwd_bytes if training else 0)
+        out["workspace_bytes"] = {"twell": int(twell_ws), "own_dense": int(dense_ws)}
+
+    out["_workload"] = w
+    if not full:
+        return out
 
     # roofline of each forward kernel: algorithmic work per launch / its duration
-    bf = cfg.dtype == "bf16"
     mma_peak = PEAK["bf16_mfma_tflops"] if bf else PEAK["fp32_vector_tflops"]
     gate_flops = 2.0 * T * d * f                       # 2 d F per token
     pair_flops = 2.0 * nnz * d                         # 2 d per stored (token, neuron) pair, each projection
+    if training:
+        pair_flops = 2.0 * float(cnt[live].sum()) * d  # the sparse rows' pairs
     lines = {
         "gate_gemm_twell_pack": {"bound": "mfma", "work": gate_flops, "ms": st[0]},
         "up_projection": {"bound": "mfma", "work": pair_flops, "ms": st[2]},
         "down_projection": {"bound": "mfma", "work": pair_flops, "ms": st[3]},
     }
-    few_tokens = bf and not training and 0 < T <= 256
     if few_tokens:
         # a few tokens make every phase a pass over weights: HBM-bound, with
         # algorithmic bytes Wg whole (+x), the union's Wu rows (+x), the
         # union's Wd rows (+y written)
-        m = h.mask.cpu().numpy().view(np.uint64)
-        n_union = int(np.unpackbits(np.bitwise_or.reduce(m, axis=0).view(np.uint8)).sum())
-        esz_y = 4
+        n_union = out["union_neurons"]
         lines["gate_gemm_twell_pack"].update(bound="hbm", work=2.0 * f * d + 2.0 * T * d)
         lines["up_projection"].update(bound="hbm", work=2.0 * n_union * d + 2.0 * T * d)
-        lines["down_projection"].update(bound="hbm", work=2.0 * n_union * d + esz_y * T * d)
-        out["config"]["union_neurons"] = n_union
-    traffic = load_traffic(args.config + ("_decode" if args.decode else ""))
+        lines["down_projection"].update(bound="hbm", work=2.0 * n_union * d + 4.0 * T * d)
+    traffic = load_traffic(name + ("_decode" if decode else ""))
     for k, v in lines.items():
         if v["bound"] == "hbm":
             v["achieved"] = v["work"] / (v["ms"] * 1e-3) / 1e9
@@ -341,23 +415,14 @@ def main() -> int:
             v["unit"] = "TFLOP/s"
         v["frac"] = v["achieved"] / v["peak"]
         v["traffic"] = traffic.get(k)
-    if bf and h.mask is not None and not few_tokens:
+    if bf and not few_tokens:
         # MFMA work the union GEMMs execute (all union positions of every
-        # UNION_BLOCK-token row block, in whole tiles), beside the useful work above
-        m = h.mask.cpu().numpy().view(np.uint64)
-        nb = np.zeros(0, dtype=np.int64)
-        ub = UNION_BLOCK
-        if T:
-            pad = (-T) % ub
-            mm = np.concatenate([m, np.zeros((pad, m.shape[1]), np.uint64)]) if pad else m
-            u = np.bitwise_or.reduce(mm.reshape(-1, ub, m.shape[1]), axis=1)
-            nb = np.unpackbits(u.view(np.uint8), axis=1).sum(axis=1).astype(np.int64)
-        up_exec = 2.0 * float((-(-nb // 256) * 256).sum()) * ub * d
-        dn_exec = 2.0 * float((-(-nb // 64) * 64).sum()) * ub * d
+        # row block, in whole tiles), beside the useful work above
+        up_exec = 2.0 * float((-(-nb // 256) * 256).sum()) * UNION_BLOCK * d
+        dn_exec = 2.0 * float((-(-nb // 64) * 64).sum()) * UNION_BLOCK * d
         for k, w_exec in (("up_projection", up_exec), ("down_projection", dn_exec)):
             lines[k]["executed_work"] = w_exec
             lines[k]["executed_tflops"] = w_exec / (lines[k]["ms"] * 1e-3) / 1e12
-        out["config"]["mean_union_fraction"] = float(nb.mean() / f) if len(nb) else 0.0
     dom = max(lines, key=lambda k: lines[k]["ms"])
     roof = {k2: lines[dom][k2] for k2 in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roof["kernel"] = dom
@@ -367,30 +432,22 @@ def main() -> int:
     out["stage_roofline"] = {k: {k2: (float(v2) if isinstance(v2, (np.floating, float)) else v2)
                                  for k2, v2 in v.items()} for k, v in lines.items()}
 
-    if not args.no_dense and cfg.dtype == "bf16" and training:
-        # own dense training step (forward + backward, bf16 intermediates)
-        dws = torch.empty(tw.twell_ffn_dense_bwd_workspace(shape), dtype=torch.uint8, device=dev)
-        yd, dXd = torch.empty_like(y), torch.empty_like(dX)
-        dWd_ = [torch.empty_like(t) for t in dW]
-        dbgd = torch.empty_like(dbg)
-
-        def dense_step():
-            tw.twell_ffn_dense_bwd(shape, x, WgT, bg, WuT, Wd, dY, yd, dXd, dWd_[0], dWd_[1], dWd_[2], dbgd, dws,
-                                   stream)
-        for _ in range(args.warmup):
-            dense_step()
-        torch.cuda.synchronize()
-        a0, a1 = ev(), ev()
-        a0.record(stream)
-        for _ in range(args.steps):
-            dense_step()
-        a1.record(stream)
-        torch.cuda.synchronize()
-        dms = a0.elapsed_time(a1) / args.steps
-        out["dense_baseline"] = {"tokens_per_s": T / (dms * 1e-3), "ms_per_step": dms,
-                                 "tflops": 18.0 * T * d * f / (dms * 1e-3) / 1e12,
-                                 "what": "dense forward + backward, bf16 intermediates"}
-        out["speedup_vs_dense"] = dms / ms_step
+    if args.cold_iters > 0:
+        # cold cache: a 512 MiB scratch write between steps evicts the 256 MB
+        # Infinity Cache (and every L2), so each step reads its inputs from HBM
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ms_cold = []
+        for k in range(args.cold_iters + 1):
+            scratch.fill_(k & 0xff)
+            e0, e1 = _ev(), _ev()
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if k:
+                ms_cold.append(e0.elapsed_time(e1))
+        out["cold_cache_ms_per_step"] = float(np.median(ms_cold))
+        del scratch
 
     if training and args.compact_w > 0:
         # the same step with the state saved between forward and backward in
@@ -404,43 +461,67 @@ def main() -> int:
             tw.twell_compact(h, c, stream)
             tw.twell_ffn_bwd_hybrid_compact(shape, x, WgT, bg, WuT, Wd, dY, c, tau, 0.0, False, dX, dW[0], dW[1],
                                             dW[2], dbg, nD, wsc, stream)
-        for _ in range(args.warmup):
-            compact_step()
-        torch.cuda.synchronize()
-        a0, a1 = ev(), ev()
-        a0.record(stream)
-        for _ in range(args.steps):
-            compact_step()
-        a1.record(stream)
-        torch.cuda.synchronize()
-        cms = a0.elapsed_time(a1) / args.steps
+        cms = _timed(compact_step, steps, warmup, stream)
         out["compact_twell"] = {
             "W": W, "ms_per_step": cms, "tokens_per_s": T / (cms * 1e-3),
             "overflow_rows": int(c.ovf.to(torch.int64).sum().item()), "dense_rows": int(nD.item()),
             "saved_state_bytes": tw.twell_cmat_bytes(T, f, W)[0],
             "full_saved_state_bytes": tw.twell_mat_bytes(T, f)[0],
         }
+    return out
 
-    if not args.no_dense and cfg.dtype == "bf16" and not training:
-        dws = torch.empty(tw.twell_ffn_dense_fwd_workspace(shape), dtype=torch.uint8, device=dev)
-        yd = torch.empty_like(y)
-        for _ in range(args.warmup):
-            tw.twell_ffn_dense_fwd(shape, x, WgT, bg, WuT, Wd, yd, dws, stream)
-        torch.cuda.synchronize()
-        a0, a1 = ev(), ev()
-        a0.record(stream)
-        for _ in range(args.steps):
-            tw.twell_ffn_dense_fwd(shape, x, WgT, bg, WuT, Wd, yd, dws, stream)
-        a1.record(stream)
-        torch.cuda.synchronize()
-        dms = a0.elapsed_time(a1) / args.steps
-        out["dense_baseline"] = {"tokens_per_s": T / (dms * 1e-3), "ms_per_step": dms,
-                                 "tflops": 6.0 * T * d * f / (dms * 1e-3) / 1e12}
-        out["speedup_vs_dense"] = dms / ms_step
-        out["dense_vs_sparse_rel_diff"] = (y - yd).norm().item() / max(yd.norm().item(), 1e-30)
 
+# the workloads the default run reports beside the headline, as (name, decode)
+EXTRA_WORKLOADS = [("1.5b", False), ("0.5b", False), ("2b", True), ("hybrid", False)]
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only (the library has no multi-GPU path); "
+                                   "use --gpus 1", "n_gpus": args.gpus}))
+        return 2
+    if args.copy_calibration:
+        return copy_calibration(max(1, args.steps))
+    if args.ffn == "relu":
+        return relu_bench(args)
+    from workloads import CONFIGS
+
+    cfg = CONFIGS[args.config]
+    training = cfg.tau_frac is not None
+    r = measure(args, args.config, args.decode, args.steps, args.warmup, full=True)
+    w = r.pop("_workload")
+    out = {
+        "metric": METRIC, "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded; shapes, densities and neuron-popularity structure of the workload)",
+        "config": {"workload": r["workload"], "name": args.config, "T": r["T"], "d_model": r["d_model"],
+                   "d_ff": r["d_ff"], "tile": "16x64", "realised_density": r["realised_density"],
+                   "pass": r["pass"]},
+    }
+    for k in ("mean_union_fraction", "union_neurons", "dense_rows"):
+        if k in r:
+            out["config"][k] = r[k]
+    for k in ("stages_ms", "roofline", "stage_roofline", "dense_baseline", "speedup_vs_dense",
+              "dense_vs_sparse_rel_diff", "workspace_bytes", "cold_cache_ms_per_step", "compact_twell"):
+        if k in r:
+            out[k] = r[k]
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, training)
+    del w
+    if not args.no_extras:
+        # the other workloads, each with a short timed run of its own
+        ex = {}
+        es, ew = max(1, min(args.steps, 10)), max(1, min(args.warmup, 3))
+        for name, dec in EXTRA_WORKLOADS:
+            if name == args.config and dec == args.decode:
+                continue
+            e = measure(args, name, dec, es, ew, full=False)
+            e.pop("_workload")
+            e["steps"], e["warmup"] = es, ew
+            ex[name + ("_decode" if dec else "")] = e
+        out["extra_workloads"] = ex
     print(json.dumps(out))
     return 0
 

@@ -35,7 +35,10 @@
  *     TWELL_EHIP.  twell_last_error() then gives a thread-local description.
  *   - Device arrays must be 16-byte aligned.  Dense matrices are row-major.
  *   - The GPU path needs d % 64 == 0 and F % 64 == 0 (64 <= F <= 65472); T may
- *     be any value >= 0 (ragged last tiles are handled).
+ *     be any value >= 0 (ragged last tiles are handled).  T*d, F*d and T*F
+ *     must each be below 2^31 (the GEMM mainloops address every 16-bit
+ *     operand with 32-bit byte offsets); a larger shape returns
+ *     TWELL_EUNSUPPORTED before anything is launched.
  */
 #ifndef TWELL_H
 #define TWELL_H
@@ -138,7 +141,6 @@ size_t twell_ffn_fwd_workspace(const twell_ffn_shape *sh, int32_t training);
  * 128-token block's union of active neurons, with a = h*u passed between them
  * in fp16 (if any |a| exceeds the fp16 range the layer is recomputed with a in
  * fp32 automatically); fp32 inputs keep h, u and a in fp32 throughout.
- * Matrices must hold fewer than 2^32 elements each.
  */
 twell_status twell_ffn_fwd(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
                            const void *WuT, const void *Wd, void *y, twell_mat *saved_h,
@@ -171,7 +173,7 @@ size_t twell_ffn_bwd_workspace(const twell_ffn_shape *sh, int32_t dense_row_thre
  * + du*WuT[n]; dWd[n] += h*u*dY_t, dWgT[n] += dg*x_t, dWuT[n] += du*x_t,
  * summed per neuron over its tokens in ascending order (deterministic).
  * Dense rows: the same gradient from gathered-row GEMMs.  fp32 accumulation
- * throughout; needs T*F < 2^32.
+ * throughout; needs 3*T*F < 2^32 (TWELL_EUNSUPPORTED otherwise).
  */
 twell_status twell_ffn_bwd_hybrid(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
                                   const void *WuT, const void *Wd, const void *dY, const twell_mat *saved_h,
@@ -286,8 +288,12 @@ twell_status twell_ffn_fwd_ex(const twell_ffn_shape *sh, const void *x, const vo
                               hipEvent_t *stage_events, int32_t n_events);
 
 /*
- * The three stages of twell_ffn_fwd, callable one by one (twell_ffn_fwd is
- * exactly these three calls in sequence):
+ * The three stages of the forward, callable one by one: the same layer as
+ * twell_ffn_fwd, computed by the per-pair kernels that twell_ffn_fwd keeps
+ * for fp32 inputs and for its fp16-overflow fallback.  For bf16 inputs
+ * twell_ffn_fwd itself runs other kernels (the union GEMMs with a in fp16, or
+ * the few-token kernels), so its bits differ from this sequence's; both meet
+ * the same tolerance against the definition.
  *
  * twell_gate_pack: gate GEMM g = x.WgT^T + bg with ReLU and the TwELL pack in
  *   its epilogue (intellectnews.ru TwELL article, TwELL section: the format is

@@ -214,3 +214,33 @@ def test_bwd_compact_empty(torch, tw):
     assert got["nD"] == 0
     for k in ("dWgT", "dWuT", "dWd", "dbg"):
         assert np.all(got[k] == 0), k
+
+
+def test_bwd_compact_full_size_sampled(torch, tw):
+    """The hybrid training workload at full size (T=16384, d=2048, F=5632)
+    with the saved state in compact TwELL of capacity 8: the 30%-density rows
+    overflow and take the dense branch, every 1% row fits.  Sampled tokens
+    (y, dX) and neurons (weight gradients) against the oracle."""
+    w = make_workload("hybrid")
+    W = 8
+    log(f"[bwd compact] full size T={w.T} d={w.d} f={w.f} tau={w.tau} W={W}")
+    got = _run_compact_train(torch, tw, w, w.tau, W)
+    cnt = got["h"]["cnt"]
+    ovf = (cnt > W).any(axis=1)
+    np.testing.assert_array_equal(got["ovf"], ovf)
+    dense = (cnt.sum(axis=1) > w.tau) | ovf
+    assert got["nD"] == int(dense.sum())
+    log(f"   dense rows {got['nD']} ({int(ovf.sum())} overflow)")
+    rng = np.random.default_rng(11)
+    toks = np.unique(np.concatenate([rng.choice(w.T, 192, replace=False), w.dense_rows[:32],
+                                     np.arange(w.T - 16, w.T)]))
+    neur = np.sort(rng.choice(w.f, 48, replace=False))
+    ref = O.ffn_bwd_sampled(w.x, w.WgT, w.bg, w.WuT, w.Wd, w.dY, toks, neur)
+    for k, g, r in (("y", got["y"][toks], ref["y_rows"]), ("dX", got["dX"][toks], ref["dX_rows"]),
+                    ("dWgT", got["dWgT"][neur], ref["dWgT_rows"]), ("dWuT", got["dWuT"][neur], ref["dWuT_rows"]),
+                    ("dWd", got["dWd"][neur], ref["dWd_rows"]), ("dbg", got["dbg"][neur], ref["dbg_rows"])):
+        e = rel_fro(g, r)
+        log(f"   {k} rel-Frobenius {e:.3e} (sampled)")
+        assert e <= TOL["bf16"], (k, e)
+    for k in ("dX", "dWgT", "dWuT", "dWd", "dbg"):
+        assert np.isfinite(got[k]).all(), k

@@ -228,3 +228,52 @@ def test_hybrid_fwd_needs_saved_h():
 def test_status_strings():
     for st in range(5):
         assert tw.twell_status_string(st)
+
+
+def test_shape_limits_of_32bit_offsets():
+    """Shapes whose [T][d], [F][d] or [T][F] 16-bit matrices reach 2^31
+    elements (the GEMM mainloops' 32-bit byte offsets) are refused before any
+    launch, by every entry point that takes a shape; one element fewer passes
+    the check (and then stops at the missing workspace)."""
+    L = tw.lib()
+    lim = 1 << 31
+    cases = [
+        (lim // 2048, 2048, 64),          # T*d == 2^31
+        (64, 2048, lim // 2048),          # F*d == 2^31 (F = 2^20 > 65472 is refused anyway)
+        (lim // 8192, 64, 8192),          # T*F == 2^31
+    ]
+    for T, d, F in cases:
+        sh = tw.ffn_shape(T, d, F, tw.TWELL_BF16, tw.TWELL_F32)
+        assert _call_fwd(sh, ws=4096, ws_bytes=1 << 40) == tw.TWELL_EUNSUPPORTED, (T, d, F)
+        assert tw.twell_ffn_fwd_workspace(sh) == 0
+        assert L.twell_ffn_dense_fwd(ctypes.byref(sh), 16, 16, None, 16, 16, 16, 4096, 1 << 40, None) \
+            == tw.TWELL_EUNSUPPORTED
+        assert L.twell_relu_ffn_fwd(ctypes.byref(sh), 16, 16, None, 16, 16, None, 4096, 1 << 40, None) \
+            == tw.TWELL_EUNSUPPORTED
+    # T*d one row below the limit: the shape passes, the call stops at the workspace
+    sh = tw.ffn_shape(lim // 2048 - 1, 2048, 64, tw.TWELL_BF16, tw.TWELL_F32)
+    assert _call_fwd(sh, ws=4096, ws_bytes=1) == tw.TWELL_EWORKSPACE
+    # T*F one row below the limit
+    sh = tw.ffn_shape(lim // 8192 - 1, 64, 8192, tw.TWELL_BF16, tw.TWELL_F32)
+    assert _call_fwd(sh, ws=4096, ws_bytes=1) == tw.TWELL_EWORKSPACE
+
+
+def test_bwd_shape_limit_of_dense_branch_buffer():
+    """The backward also needs 3*T*F < 2^32 (its dense-branch fp32 buffer is
+    read with 32-bit element offsets): T*F just under 2^31 passes the shape
+    check but is refused here."""
+    L = tw.lib()
+    F = 8192
+    T = (1 << 31) // F - 16                     # T*F < 2^31, 3*T*F > 2^32
+    sh = tw.ffn_shape(T, 64, F, tw.TWELL_BF16, tw.TWELL_F32)
+    h = tw.c_twell_mat(T, F, 16, 64, tw.TWELL_F32, 16, 16, 16, 16, 16)
+    st = L.twell_ffn_bwd_hybrid(ctypes.byref(sh), 16, 16, None, 16, 16, 16, ctypes.byref(h), 10, 16, 16, 16, 16,
+                                None, None, 4096, 1 << 40, None)
+    assert st == tw.TWELL_EUNSUPPORTED
+    assert b"3*T*F" in L.twell_last_error()
+    T = ((1 << 32) // 3) // F - 16              # 3*T*F < 2^32: passes, stops at the workspace
+    sh = tw.ffn_shape(T, 64, F, tw.TWELL_BF16, tw.TWELL_F32)
+    h = tw.c_twell_mat(T, F, 16, 64, tw.TWELL_F32, 16, 16, 16, 16, 16)
+    st = L.twell_ffn_bwd_hybrid(ctypes.byref(sh), 16, 16, None, 16, 16, 16, ctypes.byref(h), 10, 16, 16, 16, 16,
+                                None, None, 4096, 1, None)
+    assert st == tw.TWELL_EWORKSPACE
