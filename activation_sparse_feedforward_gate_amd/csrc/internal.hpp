@@ -148,6 +148,9 @@ hipError_t launch_down_bf16(const float* v0, const float* v1, const void* W, con
 // an a value overflows fp16; the caller then runs the pattern kernels gated on
 // it (they recompute and overwrite y).
 size_t union_ws_bytes(int T, int d, int F);
+// The leading part of that workspace the union lists alone use (lists,
+// counts, flag, slab unions): all the few-token path needs.
+size_t union_lists_ws_bytes(int T, int F);
 // The union lists alone (for the few-token path), in the same workspace:
 // pointers to the list and count of row block 0, and the two list kernels.
 // slabs: the 64-row slab unions u64 [ceil(T/64)][F/64] the list kernel reads;

@@ -150,10 +150,13 @@ size_t fwd_layout(const twell_ffn_shape* sh, bool training, void* ws, FwdWs* out
     w.nD = (int*)c.take(4);
     w.act = (float*)c.take((size_t)sh->T * sh->F * 4);
   }
-  if (sh->in_dt == TWELL_BF16) w.uni = c.take(union_ws_bytes(sh->T, sh->d, sh->F));
-  // reserved whatever the mode, so that a workspace sized for training also
-  // serves an inference call of the same shape
-  if (few_token_path(sh, false)) w.dec = c.take(decode_ws_bytes(sh->T, sh->d, sh->F));
+  if (few_token_path(sh, training)) {
+    // the few-token kernels use the union lists only (no adense, no fp16 Wd)
+    w.uni = c.take(union_lists_ws_bytes(sh->T, sh->F));
+    w.dec = c.take(decode_ws_bytes(sh->T, sh->d, sh->F));
+  } else if (sh->in_dt == TWELL_BF16) {
+    w.uni = c.take(union_ws_bytes(sh->T, sh->d, sh->F));
+  }
   if (out) *out = w;
   return c.off;
 }
@@ -231,7 +234,11 @@ twell_status twell_unpack(const twell_mat* in, void* H, int64_t ldh, hipStream_t
 
 size_t twell_ffn_fwd_workspace(const twell_ffn_shape* sh, int32_t training) {
   if (!sh || check_shape(sh) != TWELL_OK) return 0;
-  return fwd_layout(sh, training != 0, nullptr, nullptr);
+  // a workspace sized for training also serves an inference call of the same shape
+  const size_t inf = fwd_layout(sh, false, nullptr, nullptr);
+  if (!training) return inf;
+  const size_t tr = fwd_layout(sh, true, nullptr, nullptr);
+  return tr > inf ? tr : inf;
 }
 
 twell_status twell_ffn_fwd_ex(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,

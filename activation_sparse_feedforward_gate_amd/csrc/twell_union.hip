@@ -632,10 +632,18 @@ using DownUnionCfg = DmaCfg1<UB, 256, 2, 4, 1, true, true>;
 using DownUnionCfg128 = DmaCfg<UB, 128, 4, 2, 1, true, true>;
 using DownUnionCfg64 = DmaCfg<UB, 64, 4, 2, 1, true, true>;
 
-size_t union_ws_bytes(int T, int d, int F) {
+// Union workspace layout: lists, counts, flag and slab unions first (all the
+// few-token path uses), then adense and the fp16 copy of Wd.
+static size_t r256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+size_t union_lists_ws_bytes(int T, int F) {
   const size_t nblk = (size_t)(T + UB - 1) / UB;
   const size_t nslab = (size_t)(T + 63) / 64;
-  return nblk * F * 4 + nblk * 4 + (size_t)T * F * 2 + 256 + nslab * (F / 64) * 8 + (size_t)F * d * 2 + 256 * 5;
+  return r256(nblk * F * 4 + nblk * 4) + 256 + r256(nslab * (F / 64) * 8);
+}
+
+size_t union_ws_bytes(int T, int d, int F) {
+  return union_lists_ws_bytes(T, F) + r256((size_t)T * F * 2 + 256) + (size_t)F * d * 2;
 }
 
 namespace {
@@ -650,11 +658,15 @@ UnionArgs union_setup(const void* x, const void* WuT, const void* Wd, int T, int
   a.mask = h.mask; a.skip = skip; a.hval = (const float*)h.val; a.hidx = h.idx; a.hwidth = h.width;
   a.ulist = (int*)w;
   a.ucount = (int*)(w + (size_t)nblk * F * 4);
-  a.adense = (_Float16*)(w + (((size_t)nblk * F * 4 + (size_t)nblk * 4 + 255) & ~(size_t)255));
+  w += r256((size_t)nblk * F * 4 + (size_t)nblk * 4);
+  a.flag = (int*)w;
+  w += 256;
+  *U = (uint64_t*)w;
+  w += r256((size_t)((T + 63) / 64) * a.NT * 8);
+  a.adense = (_Float16*)w;                 // [T][F] and one spare slot
   a.spare = (uint32_t)((size_t)T * F);
-  a.flag = (int*)((char*)a.adense + (((size_t)T * F * 2 + 256 + 255) & ~(size_t)255));
-  *U = (uint64_t*)((char*)a.flag + 256);
-  a.Wd16 = (const _Float16*)((char*)*U + (((size_t)((T + 63) / 64) * a.NT * 8 + 255) & ~(size_t)255));
+  w += r256((size_t)T * F * 2 + 256);
+  a.Wd16 = (const _Float16*)w;
   a.y = y; a.out_bf16 = out_dt == DT_BF16;
   a.lrows = UB;
   return a;
