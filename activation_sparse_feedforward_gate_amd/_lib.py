@@ -94,6 +94,7 @@ def lib() -> ctypes.CDLL:
         L.twell_ffn_bwd_compact_workspace.restype = sz
         L.twell_ffn_bwd_hybrid_compact.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_cmat),
                                                    i32, ctypes.c_float, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.twell_ffn_fwd_noalloc.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_mat), i32, vp]
         L.twell_status_string.argtypes = [ctypes.c_int]
         L.twell_status_string.restype = ctypes.c_char_p
         L.twell_last_error.argtypes = []
@@ -103,7 +104,7 @@ def lib() -> ctypes.CDLL:
                      "twell_relu_ffn_fwd", "twell_relu_ffn_dense_fwd",
                      "twell_ffn_dense_fwd", "twell_ffn_dense_bwd",
                      "twell_gate_pack",
-                     "twell_sparse_up", "twell_sparse_down"):
+                     "twell_sparse_up", "twell_sparse_down", "twell_ffn_fwd_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -255,6 +256,18 @@ def twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, saved_h: Optional[TwellMat], de
                                ctypes.byref(sh) if sh is not None else None, dense_row_threshold,
                                _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
                                _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20        # TWELL_NOALLOC_SCRATCH_BYTES of include/twell.h
+
+
+def twell_ffn_fwd_noalloc(shape, x, WgT, bg, WuT, Wd, y, saved_h: Optional[TwellMat], dense_row_threshold: int,
+                          stream=None) -> None:
+    """twell_ffn_fwd on the library's static scratch (no workspace argument)."""
+    sh = saved_h.c() if saved_h is not None else None
+    _check(lib().twell_ffn_fwd_noalloc(ctypes.byref(shape), _ptr(x), _ptr(WgT), _ptr(bg), _ptr(WuT), _ptr(Wd),
+                                       _ptr(y), ctypes.byref(sh) if sh is not None else None, dense_row_threshold,
+                                       _stream(stream)))
 
 
 def twell_ffn_bwd_workspace(shape: c_twell_ffn_shape, dense_row_threshold: int) -> int:

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/twell.h"
 #include "internal.hpp"
@@ -745,6 +746,61 @@ twell_status twell_ffn_dense_bwd(const twell_ffn_shape* sh, const void* x, const
                                        sh->out_dt == TWELL_BF16 ? DT_BF16 : DT_F32, y, dX, dWgT, dWuT, dWd, dbg,
                                        stream),
                     "dense training baseline");
+}
+
+// ------------------------------------------------------------------ forward without allocation
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of twell_ffn_fwd_noalloc: one static array per device, held until
+// the process ends.  Host code never passes `scratch` itself to a kernel (on
+// the host that name is a stand-in, not a device address); it uses the
+// device address hipGetSymbolAddress returns, looked up once per device with
+// that device current.
+static_assert(TWELL_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+__device__ __align__(256) static char scratch[TWELL_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[MAX_DEVICES] = {};
+
+twell_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(TWELL_EUNSUPPORTED, "device %d beyond the %d supported", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(TWELL_EHIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return TWELL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+twell_status twell_ffn_fwd_noalloc(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
+                                   const void* WuT, const void* Wd, void* y, twell_mat* saved_h,
+                                   int32_t dense_row_threshold, hipStream_t stream) {
+  twell_status st = check_shape(sh);
+  if (st) return st;
+  const size_t need = fwd_layout(sh, dense_row_threshold >= 0, nullptr, nullptr);
+  if (need > TWELL_NOALLOC_SCRATCH_BYTES)
+    return fail(TWELL_EWORKSPACE, "this shape needs %zu bytes of scratch; the static scratch holds %zu",
+                need, (size_t)TWELL_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st) return st;
+  return twell_ffn_fwd_ex(sh, x, WgT, bg, WuT, Wd, y, saved_h, dense_row_threshold, ws,
+                          TWELL_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0);
 }
 
 const char* twell_status_string(twell_status st) {

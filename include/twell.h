@@ -400,6 +400,28 @@ twell_status twell_ffn_dense_bwd(const twell_ffn_shape *sh, const void *x, const
                                  float *dWuT, float *dWd, float *dbg, void *ws, size_t ws_bytes,
                                  hipStream_t stream);
 
+/*
+ * twell_ffn_fwd_noalloc: twell_ffn_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a static device array inside the
+ * library, TWELL_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held by each GPU the
+ * call runs on until the process ends; its device address is looked up on the
+ * first call on a device.  The call allocates and frees nothing.
+ *   Arguments as for twell_ffn_fwd, without ws and ws_bytes; the output and
+ *   numerics are those of twell_ffn_fwd with the same arguments.
+ *   TWELL_EWORKSPACE (nothing launched) when the shape needs more than the
+ *   scratch holds, i.e. when twell_ffn_fwd_workspace(sh, thr >= 0) would ask
+ *   for more than TWELL_NOALLOC_SCRATCH_BYTES: decode-shaped and small
+ *   batches fit (e.g. T = 64 tokens at d = 2304, F = 9216).
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind; nothing in it needs to start at zero.  Calls that overlap on one GPU
+ * (two streams, or two host threads) race on it: the caller serialises them.
+ */
+#define TWELL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+twell_status twell_ffn_fwd_noalloc(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
+                                   const void *WuT, const void *Wd, void *y, twell_mat *saved_h,
+                                   int32_t dense_row_threshold, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *twell_status_string(twell_status st);
 /* Thread-local description of the last error returned on this thread. */
