@@ -65,6 +65,16 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
   tile_coords(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, bm, bn);
   const int m0 = bm * Cfg::BM, n0 = bn * Cfg::BN;
 
+  // the bias of this lane's columns, loaded before the mainloop so that the
+  // epilogue does not start with a round trip to memory
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cl = lane & 31;
+  float bias[Cfg::TN];
+#pragma unroll
+  for (int t = 0; t < Cfg::TN; ++t)
+    bias[t] = load_bias<BF16IN>(a.bg, n0 + (wave % Cfg::WN) * (Cfg::BN / Cfg::WN) + t * 32 + cl);
+
   typename TileFor<Cfg>::type g;
   const Operand A{a.x, a.d, nullptr, a.T};
   const Operand B{a.WgT, a.d, nullptr, a.F};
@@ -93,19 +103,15 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
   // and masks.  The mainloop's LDS is free once it returns.
   constexpr int STG = 16 * 64 * 4 + 16 * 8;                 // dense tile + row masks, per wave
   static_assert(Cfg::EPI_BYTES >= Cfg::NTH / 64 * STG, "epilogue staging");
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = m0 + (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
   const int hl = lane >> 5;
-  const int cl = lane & 31;
   float* sd = (float*)(lds + wave * STG);                   // [16 rows][64 cols]
   uint64_t* sm = (uint64_t*)(lds + wave * STG + 16 * 64 * 4);
 #pragma unroll
   for (int tc = 0; tc < Cfg::TN / 2; ++tc) {
     const int wc = n0 + (wave % Cfg::WN) * (Cfg::BN / Cfg::WN) + tc * 64;
     const int j = wc >> 6;
-    const float b0 = load_bias<BF16IN>(a.bg, wc + cl);
-    const float b1 = load_bias<BF16IN>(a.bg, wc + 32 + cl);
+    const float b0 = bias[2 * tc], b1 = bias[2 * tc + 1];
     uint64_t sor = 0;                               // union of the masks of the current 64-row slab
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm) {
@@ -113,6 +119,7 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
       for (int half = 0; half < 2; ++half) {
         const int rt0 = wr + tm * 32 + half * 16;   // first row of this TwELL row tile
         if (rt0 >= a.T) continue;                   // wave-uniform
+        const bool full = rt0 + 16 <= a.T;          // every row of the tile exists
         int width = 0;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -121,7 +128,8 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
           // rows past T (a ragged last tile) leave the ballots through a
           // wave-uniform mask: lanes 0-31 hold row rq, lanes 32-63 row rq + 4
           const int rq = rt0 + 8 * (q >> 2) + (q & 3);
-          const uint64_t rowmask = (rq < a.T ? 0xffffffffull : 0ull) | (rq + 4 < a.T ? 0xffffffff00000000ull : 0ull);
+          const uint64_t rowmask = full ? ~0ull
+                                        : (rq < a.T ? 0xffffffffull : 0ull) | (rq + 4 < a.T ? 0xffffffff00000000ull : 0ull);
           const float v0 = g.acc[0][tm][2 * tc][e] + b0;
           const float v1 = g.acc[0][tm][2 * tc + 1][e] + b1;
           const uint64_t B0 = __builtin_amdgcn_ballot_w64(v0 > 0.f) & rowmask;
