@@ -158,16 +158,19 @@ size_t union_lists_ws_bytes(int T, int F);
 void union_lists_only(int T, int F, const TwellView& h, void* ws, int** ulist, int** ucount, uint64_t** slabs);
 hipError_t launch_union_lists(int T, int F, const TwellView& h, void* ws, hipStream_t s, bool slabs_ready = false);
 
-// Forward for few tokens (T <= DECODE_T_MAX, bf16, inference): GEMMs split
-// along K over many workgroups with fixed-order partial sums.  h receives the
-// TwELL of ReLU(g); uni_ws is the union workspace (union_ws_bytes), ws
-// decode_ws_bytes(T, d, F) bytes.  Events (nullable) after the gate + pack,
-// after the union lists, after the up-projection.
+// Forward for few tokens (T <= DECODE_T_MAX, bf16, inference): the gate GEMM
+// split along K over many workgroups with fixed-order partial sums, then one
+// kernel for the TwELL pack of ReLU(g) into h and the up-projection of every
+// stored pair, and one for the down-projection, both in fp32 (a kept in the
+// TwELL layout inside ws).  ws holds decode_ws_bytes(T, d, F) bytes.  Events
+// (nullable) after the gate GEMM, right after it again (the place of the
+// union lists, which this path does not build), and after the pack and
+// up-projection.
 constexpr int DECODE_T_MAX = 256;
 size_t decode_ws_bytes(int T, int d, int F);
 hipError_t launch_decode_fwd(const void* x, const void* WgT, const void* bg, const void* WuT, const void* Wd, int T,
-                             int d, int F, const TwellView& h, void* ws, void* uni_ws, void* y, int out_dt,
-                             hipStream_t s, hipEvent_t ev_gate, hipEvent_t ev_lists, hipEvent_t ev_up);
+                             int d, int F, const TwellView& h, void* ws, void* y, int out_dt, hipStream_t s,
+                             hipEvent_t ev_gate, hipEvent_t ev_lists, hipEvent_t ev_up);
 
 // ev_lists / ev_up (nullable) are recorded after the union lists and the fp16
 // copy of Wd, and after the up-projection.  WuT == null: the non-gated ReLU FFN

@@ -152,8 +152,6 @@ size_t fwd_layout(const twell_ffn_shape* sh, bool training, void* ws, FwdWs* out
     w.act = (float*)c.take((size_t)sh->T * sh->F * 4);
   }
   if (few_token_path(sh, training)) {
-    // the few-token kernels use the union lists only (no adense, no fp16 Wd)
-    w.uni = c.take(union_lists_ws_bytes(sh->T, sh->F));
     w.dec = c.take(decode_ws_bytes(sh->T, sh->d, sh->F));
   } else if (sh->in_dt == TWELL_BF16) {
     w.uni = c.take(union_ws_bytes(sh->T, sh->d, sh->F));
@@ -280,7 +278,7 @@ twell_status twell_ffn_fwd_ex(const twell_ffn_shape* sh, const void* x, const vo
   };
   mark(0);                                                            // start
   if (few_token_path(sh, training)) {
-    hipError_t e = launch_decode_fwd(x, WgT, bg, WuT, Wd, sh->T, sh->d, sh->F, h, w.dec, w.uni, y, out_dt, stream,
+    hipError_t e = launch_decode_fwd(x, WgT, bg, WuT, Wd, sh->T, sh->d, sh->F, h, w.dec, y, out_dt, stream,
                                      evt(1), evt(2), evt(3));
     if (e != hipSuccess) return hip_status(e, "few-token forward");
     mark(4);

@@ -98,7 +98,7 @@ TRAFFIC_SOURCES = {
     "down_projection": ["twell_union.hip", "gemm_core.hpp", "common.hpp"],
 }
 # the few-token (decode) path runs its own kernels
-TRAFFIC_SOURCES_DECODE = {k: ["twell_decode.hip", "twell_union.hip", "gemm_core.hpp", "common.hpp"]
+TRAFFIC_SOURCES_DECODE = {k: ["twell_decode.hip", "gemm_core.hpp", "common.hpp"]
                           for k in TRAFFIC_SOURCES}
 
 
@@ -349,6 +349,9 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool) 
     if few_tokens:
         n_union = int(np.unpackbits(np.bitwise_or.reduce(mask, axis=0).view(np.uint8)).sum())
         out["union_neurons"] = n_union
+        out["stage_note"] = ("few-token kernels: gate_gemm_twell_pack is the K-split gate GEMM alone, "
+                             "up_projection is the TwELL pack fused with the up-projection, "
+                             "union_lists_wd_fp16 and overflow_fallback_check are empty (event overhead)")
 
     # the library's own dense step on the same inputs
     if not args.no_dense and bf:
@@ -504,7 +507,7 @@ def main() -> int:
         if k in r:
             out["config"][k] = r[k]
     for k in ("stages_ms", "roofline", "stage_roofline", "dense_baseline", "speedup_vs_dense",
-              "dense_vs_sparse_rel_diff", "workspace_bytes", "cold_cache_ms_per_step", "compact_twell"):
+              "dense_vs_sparse_rel_diff", "workspace_bytes", "cold_cache_ms_per_step", "compact_twell", "stage_note"):
         if k in r:
             out[k] = r[k]
     if not args.no_cpu:

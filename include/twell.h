@@ -329,8 +329,9 @@ size_t twell_ffn_dense_fwd_workspace(const twell_ffn_shape *sh);
  * twell_ffn_dense_fwd: the same layer computed densely (the library's own
  * dense MFMA baseline, bf16 only): a fused gate/up GEMM writes
  * act = bf16(ReLU(g) * u) for every (t, n), then y = act . Wd.  For
- * 0 < T <= 256 it runs the same K-split GEMM blocks as the few-token TwELL
- * forward (partial sums added in a fixed order).
+ * 0 < T <= 256 every GEMM is split along K over many workgroups, with the
+ * same blocks as the few-token TwELL forward's gate (partial sums added in
+ * a fixed order).
  * Arguments as for twell_ffn_fwd.
  */
 twell_status twell_ffn_dense_fwd(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
