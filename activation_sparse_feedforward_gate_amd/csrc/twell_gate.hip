@@ -13,6 +13,8 @@
 //   width = max cnt over the 16 rows               (the tile's ELL width)
 // Values are stored [row tile][column tile][slot][row]; slots in
 // [cnt, width) hold (+0.0, index 0).
+#include <type_traits>
+
 #include "gemm_core.hpp"
 #include "internal.hpp"
 
@@ -95,24 +97,28 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
   // blocks 2*tc and 2*tc+1 of a wave hold the 64 columns of one TwELL tile;
   // register e of a 32x32 block holds row 8*(e/4) + 4*(lane/32) + e%4, column
   // lane%32.  For each 16-row tile: (1) every lane drops its biased values into
-  // a dense 16x64 LDS tile and two ballots per register give the 64-bit masks
-  // of two rows; (2) the width*16 output slots [slot][row] are produced one
-  // per lane: slot s of row r is the s-th set bit of r's mask (found by a
-  // branch-free binary search on popcounts), or padding (+0.0, index 0) past
-  // the row's count; (3) coalesced stores of the values, indices, row counts
-  // and masks.  The mainloop's LDS is free once it returns.
-  constexpr int STG = 16 * 64 * 4 + 16 * 8;                 // dense tile + row masks, per wave
+  // a dense 16x64 LDS tile, and two ballots per register give the masks of two
+  // rows, which lane selects collect so that lane r (r < 16) holds row r's
+  // 64-bit mask in two VGPRs (the mask bookkeeping stays on the vector unit:
+  // the scalar unit is shared by the CU's waves and would serialise it);
+  // (2) counts, the width (a 16-lane max) and the slab union (a 16-lane OR)
+  // come from those lanes; (3) the width*16 output slots [slot][row] are
+  // produced one per lane: slot s of row r is the s-th set bit of r's mask
+  // (found by a branch-free binary search on popcounts), or padding (+0.0,
+  // index 0) past the row's count; (4) coalesced stores of the values,
+  // indices, row counts and masks.  The mainloop's LDS is free once it
+  // returns.
+  constexpr int STG = 16 * 64 * 4;                          // dense tile, per wave
   static_assert(Cfg::EPI_BYTES >= Cfg::NTH / 64 * STG, "epilogue staging");
   const int wr = m0 + (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
-  const int hl = lane >> 5;
   float* sd = (float*)(lds + wave * STG);                   // [16 rows][64 cols]
-  uint64_t* sm = (uint64_t*)(lds + wave * STG + 16 * 64 * 4);
+  const int rsel = lane & 15;
 #pragma unroll
   for (int tc = 0; tc < Cfg::TN / 2; ++tc) {
     const int wc = n0 + (wave % Cfg::WN) * (Cfg::BN / Cfg::WN) + tc * 64;
     const int j = wc >> 6;
     const float b0 = bias[2 * tc], b1 = bias[2 * tc + 1];
-    uint64_t sor = 0;                               // union of the masks of the current 64-row slab
+    uint32_t sorl = 0, sorh = 0;                    // lanes 0-15: union of their rows' masks over the slab
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm) {
 #pragma unroll
@@ -120,71 +126,93 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
         const int rt0 = wr + tm * 32 + half * 16;   // first row of this TwELL row tile
         if (rt0 >= a.T) continue;                   // wave-uniform
         const bool full = rt0 + 16 <= a.T;          // every row of the tile exists
-        int width = 0;
+        uint32_t ml = 0, mh = 0;                    // lane r < 16: row r's mask, columns 0-31 / 32-63
+        // the ragged last tile takes a copy of the loop that masks rows past T
+        // out of the ballots; every other tile takes one without that work
+        auto collect = [&](auto full_c) {
+          constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int e = half * 8 + q;
-          const int rl = 8 * (q >> 2) + 4 * hl + (q & 3);
-          // rows past T (a ragged last tile) leave the ballots through a
-          // wave-uniform mask: lanes 0-31 hold row rq, lanes 32-63 row rq + 4
-          const int rq = rt0 + 8 * (q >> 2) + (q & 3);
-          const uint64_t rowmask = full ? ~0ull
-                                        : (rq < a.T ? 0xffffffffull : 0ull) | (rq + 4 < a.T ? 0xffffffff00000000ull : 0ull);
-          const float v0 = g.acc[0][tm][2 * tc][e] + b0;
-          const float v1 = g.acc[0][tm][2 * tc + 1][e] + b1;
-          const uint64_t B0 = __builtin_amdgcn_ballot_w64(v0 > 0.f) & rowmask;
-          const uint64_t B1 = __builtin_amdgcn_ballot_w64(v1 > 0.f) & rowmask;
-          sd[rl * 64 + cl] = v0;
-          sd[rl * 64 + 32 + cl] = v1;
-          const uint64_t mA = (B0 & 0xffffffffull) | (B1 << 32);               // row 8*(q/4) + q%4
-          const uint64_t mB = (B0 >> 32) | (B1 & 0xffffffff00000000ull);        // that row + 4
-          width = max(width, max(popc64(mA), popc64(mB)));
-          sor |= mA | mB;
-          if (lane == 0) {
-            const int r0 = 8 * (q >> 2) + (q & 3);
-            sm[r0] = mA;
-            sm[r0 + 4] = mB;
+          for (int q = 0; q < 8; ++q) {
+            const int e = half * 8 + q;
+            const int r0 = 8 * (q >> 2) + (q & 3);  // row of lanes 0-31; lanes 32-63 hold r0 + 4
+            const float v0 = g.acc[0][tm][2 * tc][e] + b0;
+            const float v1 = g.acc[0][tm][2 * tc + 1][e] + b1;
+            uint64_t B0 = __builtin_amdgcn_ballot_w64(v0 > 0.f);
+            uint64_t B1 = __builtin_amdgcn_ballot_w64(v1 > 0.f);
+            if constexpr (!FULL) {
+              const int rq = rt0 + r0;
+              const uint64_t rowmask =
+                  (rq < a.T ? 0xffffffffull : 0ull) | (rq + 4 < a.T ? 0xffffffff00000000ull : 0ull);
+              B0 &= rowmask;
+              B1 &= rowmask;
+            }
+            sd[(r0 + 4 * (lane >> 5)) * 64 + cl] = v0;
+            sd[(r0 + 4 * (lane >> 5)) * 64 + 32 + cl] = v1;
+            ml = lane == r0 ? (uint32_t)B0 : ml;
+            mh = lane == r0 ? (uint32_t)B1 : mh;
+            ml = lane == r0 + 4 ? (uint32_t)(B0 >> 32) : ml;
+            mh = lane == r0 + 4 ? (uint32_t)(B1 >> 32) : mh;
           }
-        }
+        };
+        if (full) collect(std::true_type{});
+        else collect(std::false_type{});
+        // lanes 0-15: counts; the tile's width is their maximum
+        const int c16 = __popc(ml) + __popc(mh);
+        int wm = c16;
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) wm = max(wm, __shfl_xor(wm, o));
+        const int width = __builtin_amdgcn_readfirstlane(wm);
+        sorl |= ml;
+        sorh |= mh;
         __builtin_amdgcn_wave_barrier();
         const int64_t tix = (int64_t)(rt0 >> 4) * a.NT + j;
         const int64_t tbase = tix * (64 * 16);
-        for (int i = lane; i < width * 16; i += 64) {
-          const int sl = i >> 4, r = i & 15;
-          uint64_t m = sm[r];
-          float v = 0.f;
-          int c = 0;
-          if (sl < popc64(m)) {
-            // position of the sl-th set bit of m
-            int k = sl;
+        if (width > 0) {
+          // this lane's slots all belong to row rsel
+          const uint64_t mrow = ((uint64_t)(uint32_t)__shfl((int)mh, rsel) << 32) | (uint32_t)__shfl((int)ml, rsel);
+          const int crow = popc64(mrow);
+          for (int i = lane; i < width * 16; i += 64) {
+            const int sl = i >> 4;
+            uint64_t m = mrow;
+            float v = 0.f;
+            int c = 0;
+            if (sl < crow) {
+              // position of the sl-th set bit of m
+              int k = sl;
 #pragma unroll
-            for (int w = 32; w >= 1; w >>= 1) {
-              const uint64_t lowmask = (w == 64) ? ~0ull : ((1ull << w) - 1ull);
-              const int pc = popc64(m & lowmask);
-              const bool up = k >= pc;
-              k = up ? k - pc : k;
-              c = up ? c + w : c;
-              m = up ? (m >> w) : m;
+              for (int w = 32; w >= 1; w >>= 1) {
+                const uint64_t lowmask = (1ull << w) - 1ull;
+                const int pc = popc64(m & lowmask);
+                const bool up = k >= pc;
+                k = up ? k - pc : k;
+                c = up ? c + w : c;
+                m = up ? (m >> w) : m;
+              }
+              v = sd[rsel * 64 + c];
             }
-            v = sd[r * 64 + c];
+            a.val[tbase + i] = v;
+            a.idx[tbase + i] = (uint8_t)c;
           }
-          a.val[tbase + i] = v;
-          a.idx[tbase + i] = (uint8_t)c;
         }
         if (lane < 16 && rt0 + lane < a.T) {
-          const uint64_t M = sm[lane];
-          a.cnt[(int64_t)(rt0 + lane) * a.NT + j] = (uint8_t)popc64(M);
-          if (a.mask) a.mask[(int64_t)(rt0 + lane) * a.NT + j] = M;
+          a.cnt[(int64_t)(rt0 + lane) * a.NT + j] = (uint8_t)c16;
+          if (a.mask) a.mask[(int64_t)(rt0 + lane) * a.NT + j] = ((uint64_t)mh << 32) | ml;
         }
         if (lane == 0) a.width[tix] = (uint8_t)width;
         __builtin_amdgcn_wave_barrier();
       }
       // a wave's rows start on a multiple of 64, so row blocks tm - 1 and tm
       // (tm odd) are one whole 64-row slab
-      if ((tm & 1) && a.slabs) {
+      if (tm & 1) {
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) {
+          sorl |= (uint32_t)__shfl_xor((int)sorl, o);
+          sorh |= (uint32_t)__shfl_xor((int)sorh, o);
+        }
         const int s0 = wr + (tm - 1) * 32;
-        if (s0 < a.T && lane == 0) a.slabs[(int64_t)(s0 >> 6) * a.NT + j] = sor;
-        sor = 0;
+        if (a.slabs && s0 < a.T && lane == 0) a.slabs[(int64_t)(s0 >> 6) * a.NT + j] = ((uint64_t)sorh << 32) | sorl;
+        sorl = 0;
+        sorh = 0;
       }
     }
   }
