@@ -4,9 +4,9 @@
 //
 //   g = x.WgT^T + b,  h = ReLU(g),  u = x.WuT^T,  a = h*u,  y = a.Wd
 //
-// with bf16 intermediates (h, u, a, dG, dU stored as bf16 [T][F]) and fp32
-// accumulation, nine GEMMs:
-//   1  g, u    (dual GEMM; epilogue stores h, u, a)
+// with bf16 intermediates (h, u, a, dG, dU stored as bf16 [T][F]; h and u
+// interleaved, one 32-bit word per element) and fp32 accumulation, nine GEMMs:
+//   1  g, u    (dual GEMM; epilogue stores (h, u) and a)
 //   2  y  = a.Wd
 //   3  dA = dY.Wd^T  (epilogue: dG = dA*u*[g>0], dU = dA*h, per-block dbg sums)
 //   4  dX = dG.WgT + dU.WuT
@@ -29,8 +29,7 @@ struct TrainArgs {
   const uint16_t* Wd;
   const uint16_t* dY;
   int T, d, F;
-  uint16_t* h16;    // [T][F]
-  uint16_t* u16;
+  uint32_t* hu32;   // [T][F]: bf16 h in the low half, bf16 u in the high half
   uint16_t* a16;
   uint16_t* dg16;
   uint16_t* du16;
@@ -79,8 +78,7 @@ __global__ __launch_bounds__(Cfg::NTH) void train_gateup_kernel(TrainArgs a) {
           const float h = gv > 0.f ? gv : 0.f;
           const float u = g.acc[1][i][j][e];
           const int64_t o = (int64_t)row * a.F + col;
-          a.h16[o] = bf(h);
-          a.u16[o] = bf(u);
+          a.hu32[o] = (uint32_t)bf(h) | ((uint32_t)bf(u) << 16);
           a.a16[o] = bf(h * u);
         }
       }
@@ -102,28 +100,59 @@ __global__ __launch_bounds__(Cfg::NTH) void train_da_kernel(TrainArgs a) {
   const Operand A{a.dY, a.d, nullptr, a.T};
   const Operand B{a.Wd, a.d, nullptr, a.F};
   g.run(A, &B, m0, n0, a.d, st0, st1);
-  // column sums of dG: per lane over its rows, then across the two row halves
-  // of the wave (lanes l and l^32) and across the waves of a column (LDS)
+  // Lanes l and l^1 hold neighbouring columns of the same rows: for each
+  // group of 4 rows, the even lane loads rows 0 and 2 of the column pair and
+  // the odd lane rows 1 and 3 (8-byte loads of two (h, u) words), one
+  // exchange gives each lane its own column, and dG, dU go out as 4-byte
+  // stores of column pairs (the even lane rows 0 and 2, the odd lane rows 1
+  // and 3).  Column sums of dG: per lane over its rows, then across the two
+  // row halves of the wave (lanes l and l^32) and across the waves of a
+  // column (LDS).
   float* csum = (float*)st0;                       // [WM][BN]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool odd = lane & 1;
 #pragma unroll
   for (int j = 0; j < Cfg::TN; ++j) {
     const int cl = Tile::col_of(j);
-    const int col = n0 + cl;
+    const int ce = n0 + (cl & ~1);                 // even column of the lane pair
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + Tile::row_of(i, e);
-        if (row < a.T) {
-          const int64_t o = (int64_t)row * a.F + col;
-          const float h = bf16_to_f32(a.h16[o]), u = bf16_to_f32(a.u16[o]);
-          const float dA = g.acc[0][i][j][e];
-          const float dG = h > 0.f ? dA * u : 0.f;
-          a.dg16[o] = bf(dG);
-          a.du16[o] = bf(dA * h);
-          s += dG;
+      for (int qq = 0; qq < 4; ++qq) {
+        const int r0 = m0 + Tile::row_of(i, 4 * qq);   // rows r0..r0+3
+        uint32_t own[4];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int r = r0 + 2 * m + (odd ? 1 : 0);
+          const uint2 L = r < a.T ? *(const uint2*)(a.hu32 + (int64_t)r * a.F + ce) : make_uint2(0u, 0u);
+          const uint32_t recv = (uint32_t)__shfl_xor((int)(odd ? L.x : L.y), 1);
+          own[2 * m] = odd ? recv : L.x;
+          own[2 * m + 1] = odd ? L.y : recv;
+        }
+        float dg[4], du[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float h = bf16_lo(own[k]), u = bf16_hi(own[k]);
+          const float dA = g.acc[0][i][j][4 * qq + k];
+          dg[k] = h > 0.f ? dA * u : 0.f;
+          du[k] = dA * h;
+          if (r0 + k < a.T) s += dg[k];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k += 2) {
+          const int kr = odd ? k + 1 : k;                  // row this lane stores
+          const float sg = __shfl_xor(odd ? dg[k] : dg[k + 1], 1);
+          const float su = __shfl_xor(odd ? du[k] : du[k + 1], 1);
+          if (r0 + kr < a.T) {
+            const uint32_t pg = odd ? ((uint32_t)bf(sg) | ((uint32_t)bf(dg[k + 1]) << 16))
+                                    : ((uint32_t)bf(dg[k]) | ((uint32_t)bf(sg) << 16));
+            const uint32_t pu = odd ? ((uint32_t)bf(su) | ((uint32_t)bf(du[k + 1]) << 16))
+                                    : ((uint32_t)bf(du[k]) | ((uint32_t)bf(su) << 16));
+            const int64_t o = (int64_t)(r0 + kr) * a.F + ce;
+            *(uint32_t*)(a.dg16 + o) = pg;
+            *(uint32_t*)(a.du16 + o) = pu;
+          }
         }
       }
     s += __shfl_xor(s, 32);
@@ -226,7 +255,7 @@ hipError_t launch_dense_train(const void* x, const void* WgT, const void* bg, co
   char* w = (char*)ws;
   TrainArgs a{(const uint16_t*)x, (const uint16_t*)WgT, (const uint16_t*)bg, (const uint16_t*)WuT,
               (const uint16_t*)Wd, (const uint16_t*)dY, T, d, F,
-              (uint16_t*)w, (uint16_t*)(w + tf), (uint16_t*)(w + 2 * tf), (uint16_t*)(w + 3 * tf),
+              (uint32_t*)w, (uint16_t*)(w + 2 * tf), (uint16_t*)(w + 3 * tf),
               (uint16_t*)(w + 4 * tf), (float*)(w + 5 * tf)};
   const int nbm = (T + 255) / 256;
   hipLaunchKernelGGL(train_gateup_kernel<TrainGateUp>, dim3(nbm * (F / TrainGateUp::BN)), dim3(TrainGateUp::NTH), 0,
