@@ -237,6 +237,27 @@ def _timed(fn, steps: int, warmup: int, stream) -> float:
     return t0.elapsed_time(t1) / steps
 
 
+def cold_cache_ms(fn, iters: int, stream) -> float:
+    """Median ms of fn over `iters` calls, each after a 512 MiB scratch write
+    that evicts the 256 MB Infinity Cache and every L2, so the call reads its
+    inputs from HBM."""
+    import numpy as np
+    import torch
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ms = []
+    for k in range(iters + 1):
+        scratch.fill_(k & 0xff)
+        e0, e1 = _ev(), _ev()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if k:
+            ms.append(e0.elapsed_time(e1))
+    del scratch
+    return float(np.median(ms))
+
+
 def union_sizes(mask: "np.ndarray", T: int, live=None):
     """Union size of every UNION_BLOCK-token row block (live rows only)."""
     import numpy as np
@@ -373,8 +394,10 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool) 
             dense_ws = tw.twell_ffn_dense_fwd_workspace(shape)
             dws = torch.empty(max(1, dense_ws), dtype=torch.uint8, device=dev)
             yd = torch.empty_like(y)
-            dms = _timed(lambda: tw.twell_ffn_dense_fwd(shape, x, WgT, bg, WuT, Wd, yd, dws, stream), steps, warmup,
-                         stream)
+
+            def dense_step():
+                tw.twell_ffn_dense_fwd(shape, x, WgT, bg, WuT, Wd, yd, dws, stream)
+            dms = _timed(dense_step, steps, warmup, stream)
             out["dense_baseline"] = {"tokens_per_s": T / (dms * 1e-3), "ms_per_step": dms,
                                      "tflops": 6.0 * T * d * f / (dms * 1e-3) / 1e12}
             out["dense_vs_sparse_rel_diff"] = (y - yd).norm().item() / max(yd.norm().item(), 1e-30)
@@ -383,6 +406,18 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool) 
         twell_ws = ws_fwd_bytes + (tw.twell_mat_bytes(T, f)[0] + ws_bwd_bytes if training else 0)
         out["workspace_bytes"] = {"twell": int(twell_ws), "own_dense": int(dense_ws)}
 
+    if training:
+        # state a layer keeps between its forward and its backward: TwELL of h
+        # (capacity 64, or compact with capacity W), against the own dense
+        # step's (h, u) words and a (bf16 [T][F] each; x and the weights are
+        # inputs either way)
+        out["saved_state_bytes"] = {
+            "twell_full": int(tw.twell_mat_bytes(T, f)[0]),
+            f"twell_compact_W{args.compact_w or 8}": int(tw.twell_cmat_bytes(T, f, args.compact_w or 8)[0]),
+            "own_dense_h_u_a_bf16": int(3 * T * f * 2)}
+    if few_tokens and not full and args.cold_iters > 0 and not args.no_dense:
+        out["cold_cache_ms_per_step"] = cold_cache_ms(step, args.cold_iters, stream)
+        out["dense_baseline"]["cold_cache_ms_per_step"] = cold_cache_ms(dense_step, args.cold_iters, stream)
     out["_workload"] = w
     if not full:
         return out
@@ -436,21 +471,21 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool) 
                                  for k2, v2 in v.items()} for k, v in lines.items()}
 
     if args.cold_iters > 0:
-        # cold cache: a 512 MiB scratch write between steps evicts the 256 MB
-        # Infinity Cache (and every L2), so each step reads its inputs from HBM
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        ms_cold = []
-        for k in range(args.cold_iters + 1):
-            scratch.fill_(k & 0xff)
-            e0, e1 = _ev(), _ev()
-            e0.record(stream)
-            step()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            if k:
-                ms_cold.append(e0.elapsed_time(e1))
-        out["cold_cache_ms_per_step"] = float(np.median(ms_cold))
-        del scratch
+        out["cold_cache_ms_per_step"] = cold_cache_ms(step, args.cold_iters, stream)
+        if "dense_step" in locals():
+            out["dense_baseline"]["cold_cache_ms_per_step"] = cold_cache_ms(dense_step, args.cold_iters, stream)
+
+    if bf and not few_tokens and not training:
+        # the library GEMM (hipBLASLt through torch.matmul) on the gate's shape,
+        # without any epilogue: a practical MFMA ceiling measured on the same
+        # box, beside the datasheet peak
+        C = torch.empty((T, f), dtype=torch.bfloat16, device=dev)
+        lib_ms = _timed(lambda: torch.matmul(x, WgT.t(), out=C), steps, warmup, stream)
+        del C
+        lib_tf = gate_flops / (lib_ms * 1e-3) / 1e12
+        out["library_gemm"] = {"what": "torch.matmul (hipBLASLt) x.WgT^T, the gate's GEMM without epilogue",
+                               "ms": lib_ms, "tflops": lib_tf, "frac_of_peak": lib_tf / PEAK["bf16_mfma_tflops"]}
+        out["roofline"]["frac_of_library_gemm"] = float(lines["gate_gemm_twell_pack"]["achieved"]) / lib_tf
 
     if training and args.compact_w > 0:
         # the same step with the state saved between forward and backward in
@@ -507,7 +542,8 @@ def main() -> int:
         if k in r:
             out["config"][k] = r[k]
     for k in ("stages_ms", "roofline", "stage_roofline", "dense_baseline", "speedup_vs_dense",
-              "dense_vs_sparse_rel_diff", "workspace_bytes", "cold_cache_ms_per_step", "compact_twell", "stage_note"):
+              "dense_vs_sparse_rel_diff", "workspace_bytes", "cold_cache_ms_per_step", "library_gemm",
+              "saved_state_bytes", "compact_twell", "stage_note"):
         if k in r:
             out[k] = r[k]
     if not args.no_cpu:
