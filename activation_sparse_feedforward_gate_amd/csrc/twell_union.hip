@@ -143,7 +143,7 @@ constexpr int POSCAP = 12288;         // neuron span of a position tile covered 
 // lays h out over the union positions for the down GEMM).
 template <class Cfg, bool GATED>
 __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt, char* st0, char* st1,
-                                              int16_t* posmap, int* lcount) {
+                                              int16_t* posmap, int* lcount, uint8_t* wl) {
   static_assert(Cfg::BM == UB, "one row block per M tile");
   const int nb = a.ucount[b];
   const int p0 = pt * Cfg::BN;
@@ -166,9 +166,20 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
   const int pl = min(p0 + Cfg::BN, nb) - 1;
   const int nlo = ul[p0], nhi = ul[pl];
   const bool use_map = nhi - nlo < POSCAP;
-  if (use_map)
-    for (int p = p0 + tid; p <= pl; p += Cfg::NTH) posmap[ul[p] - nlo] = (int16_t)(p - p0);
   const int tjf = nlo >> 6, S = (nhi >> 6) - tjf + 1;
+  constexpr int NRT0 = Cfg::BM / 16;
+  // the TwELL widths of the blocks in the span go to LDS with the position
+  // map (both wait for their loads here, before the mainloop), so the scan
+  // below starts without a dependent load
+  const bool wpre = NRT0 * S <= Cfg::NTH;
+  {
+    int wv = 0;
+    const int i = tid / S, sj = tid - (tid / S) * S;
+    if (wpre && tid < NRT0 * S && ((m0 >> 4) + i) * 16 < a.T) wv = a.hwidth[(int64_t)((m0 >> 4) + i) * a.NT + tjf + sj];
+    if (use_map)
+      for (int p = p0 + tid; p <= pl; p += Cfg::NTH) posmap[ul[p] - nlo] = (int16_t)(p - p0);
+    if (wpre && tid < NRT0 * S) wl[tid] = (uint8_t)wv;
+  }
   constexpr int NG = Cfg::NTH / 16;        // 16-lane groups
   // blocks per group fetched ahead (none with one stage buffer: the other
   // workgroup on the CU covers the latency, and the registers are needed)
@@ -290,12 +301,16 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
         scatter(hp, i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
                 ((const uint32_t*)(a.hidx + blk * 1024))[c]);
     }
+    // (row tile i, column tile sj) of block q, stepped without a division
+    int qi = (grp + NPRE * NG) / S, qs = grp + NPRE * NG - qi * S;
     for (int q = grp + NPRE * NG; q < NRT * S; q += NG) {
-      const int i = q / S, sj = q - i * S;
+      const int i = qi, sj = qs;
+      qs += NG;
+      while (qs >= S) { qs -= S; ++qi; }
       const int rt = (m0 >> 4) + i;
       if (rt * 16 >= a.T) continue;
       const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
-      const int w = a.hwidth[blk];
+      const int w = wpre ? (int)wl[q] : (int)a.hwidth[blk];
       for (int c = gl; c < w * 4; c += 16)
         scatter(hp, i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
                 ((const uint32_t*)(a.hidx + blk * 1024))[c]);
@@ -367,6 +382,7 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void up_union_ker
   __shared__ __attribute__((aligned(1024))) char st1_[Cfg::SINGLE ? 16 : Cfg::STAGE];
   char* st1 = Cfg::SINGLE ? st0 : st1_;
   __shared__ int16_t posmap[POSCAP];
+  __shared__ uint8_t wl[Cfg::NTH];                     // TwELL widths of the tile's blocks
   __shared__ int lcount;                               // pairs in the second-pass list
   const int npt = (a.F + Cfg::BN - 1) / Cfg::BN;
   const int nblk = (a.T + UB - 1) / UB;
@@ -376,7 +392,7 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void up_union_ker
   for (int k = blockIdx.x >> 3; k < ntile; k += gridDim.x >> 3) {
     const int pt = k / nbx;
     const int b = x + 8 * (k - pt * nbx);
-    up_union_tile<Cfg, GATED>(a, b, pt, st0, st1, posmap, &lcount);
+    up_union_tile<Cfg, GATED>(a, b, pt, st0, st1, posmap, &lcount, wl);
     __syncthreads();                                   // stage buffers and position map free again
   }
 }
