@@ -559,19 +559,37 @@ struct DmaTile {
     constexpr int BROWB = Cfg::BN * 2, KPI = 1024 / BROWB;   // transposed B: bytes per k-row, k-rows per load
     const int* bgat = Cfg::BT ? B[0].gather : nullptr;
     const int nk = (K + 63) / 64;
-    auto bt_krow = [&](int q) { return (q * NW + wave) * KPI + (16 * lane) / BROWB; };
-    // gathered k rows of the next tile to issue: one load carries KPI k-rows,
-    // so each wave needs KPI * LB indices per tile, all wave-uniform; they are
-    // read with scalar loads (constant address space) into SGPRs, which keeps
-    // them out of the vector memory counter the stage hand-over waits on
+    // a transposed B tile's 64 k-rows: wave w loads the KW = 64/NW k-rows
+    // KW*w..KW*w+KW-1 (LB loads of KPI k-rows each), so its gathered indices
+    // are KW consecutive list entries
+    constexpr int KW = Cfg::LB * KPI;
+    static_assert(!Cfg::BT || (KW * NW == 64 && KW % 8 == 0), "whole groups of eight k-rows per wave");
+    auto bt_krow = [&](int q) { return (wave * Cfg::LB + q) * KPI + (16 * lane) / BROWB; };
+    // gathered k rows of the next tile to issue, all wave-uniform: scalar
+    // loads of the wave's list entries, eight at a time (constant address
+    // space, into SGPRs, which keeps them out of the vector memory counter the
+    // stage hand-over waits on); in the last tile, entries at or past K are
+    // replaced by entry K-1 (a real row; A holds zeros in those K columns).
+    // The list must hold roundup64(K) readable entries.
     typedef __attribute__((address_space(4))) const int cint;
+    typedef int v8i __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(4))) const v8i cv8i;
     cint* cgat = (cint*)bgat;
     uint32_t gsc[Cfg::LB][KPI];
     auto bt_fetch = [&](int kt) {
+      const int k0 = kt * 64 + wave * KW;
+      const bool tail = k0 + KW > K;
+      const int last = tail ? cgat[K - 1] : 0;
 #pragma unroll
-      for (int q = 0; q < Cfg::LB; ++q)
+      for (int g8 = 0; g8 < KW / 8; ++g8) {
+        v8i v = *(cv8i*)(cgat + k0 + 8 * g8);
+        if (tail) {
 #pragma unroll
-        for (int j = 0; j < KPI; ++j) gsc[q][j] = (uint32_t)cgat[min(kt * 64 + (q * NW + wave) * KPI + j, K - 1)];
+          for (int j = 0; j < 8; ++j) v[j] = k0 + 8 * g8 + j < K ? v[j] : last;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gsc[(8 * g8 + j) / KPI][(8 * g8 + j) % KPI] = (uint32_t)v[j];
+      }
     };
     auto gidx = [&](int q) {
       const int kl = (16 * lane) / BROWB;
@@ -622,14 +640,14 @@ struct DmaTile {
 #pragma unroll
           for (int q = 0; q < Cfg::LB; ++q) {
             bvo[q] = gidx(q) * (uint32_t)B[0].ld * 2u + offb[0][q];
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[0], (lds_void*)(st + Cfg::A_BYTES + (q * NW + wave) * 1024),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[0], (lds_void*)(st + Cfg::A_BYTES + (wave * Cfg::LB + q) * 1024),
                                                      16, bvo[q], 0u, 0, 0);
           }
           if (kt + 1 < nk) bt_fetch(kt + 1);
         } else {
 #pragma unroll
           for (int q = 0; q < Cfg::LB; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[0], (lds_void*)(st + Cfg::A_BYTES + (q * NW + wave) * 1024),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[0], (lds_void*)(st + Cfg::A_BYTES + (wave * Cfg::LB + q) * 1024),
                                                      16, offb[0][q], (uint32_t)kt * 64u * (uint32_t)B[0].ld * 2u, 0, 0);
         }
       } else {
