@@ -97,8 +97,9 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
   // blocks 2*tc and 2*tc+1 of a wave hold the 64 columns of one TwELL tile;
   // register e of a 32x32 block holds row 8*(e/4) + 4*(lane/32) + e%4, column
   // lane%32.  For each 16-row tile: (1) every lane drops its biased values into
-  // a dense 16x64 LDS tile, and two ballots per register give the masks of two
-  // rows, which lane selects collect so that lane r (r < 16) holds row r's
+  // a dense 16x64 LDS tile (column pairs c, c + 32 side by side), and two
+  // ballots per register give the masks of two rows, which v_writelane
+  // collects so that lane r (r < 16) holds row r's
   // 64-bit mask in two VGPRs (the mask bookkeeping stays on the vector unit:
   // the scalar unit is shared by the CU's waves and would serialise it);
   // (2) counts, the width (a 16-lane max) and the slab union (a 16-lane OR)
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
   constexpr int STG = 16 * 64 * 4;                          // dense tile, per wave
   static_assert(Cfg::EPI_BYTES >= Cfg::NTH / 64 * STG, "epilogue staging");
   const int wr = m0 + (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
-  float* sd = (float*)(lds + wave * STG);                   // [16 rows][64 cols]
+  float* sd = (float*)(lds + wave * STG);                   // [16 rows][32][2]: (c, c + 32) pairs
   const int rsel = lane & 15;
 #pragma unroll
   for (int tc = 0; tc < Cfg::TN / 2; ++tc) {
@@ -131,12 +132,12 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
         // out of the ballots; every other tile takes one without that work
         auto collect = [&](auto full_c) {
           constexpr bool FULL = decltype(full_c)::value;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const int e = half * 8 + q;
-            const int r0 = 8 * (q >> 2) + (q & 3);  // row of lanes 0-31; lanes 32-63 hold r0 + 4
-            const float v0 = g.acc[0][tm][2 * tc][e] + b0;
-            const float v1 = g.acc[0][tm][2 * tc + 1][e] + b1;
+          auto one = [&](auto q_c) {
+            constexpr int q = decltype(q_c)::value;
+            constexpr int e = q;                    // register index within the half (+ 8 * half)
+            constexpr int r0 = 8 * (q >> 2) + (q & 3);  // row of lanes 0-31; lanes 32-63 hold r0 + 4
+            const float v0 = g.acc[0][tm][2 * tc][half * 8 + e] + b0;
+            const float v1 = g.acc[0][tm][2 * tc + 1][half * 8 + e] + b1;
             uint64_t B0 = __builtin_amdgcn_ballot_w64(v0 > 0.f);
             uint64_t B1 = __builtin_amdgcn_ballot_w64(v1 > 0.f);
             if constexpr (!FULL) {
@@ -146,13 +147,31 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
               B0 &= rowmask;
               B1 &= rowmask;
             }
-            sd[(r0 + 4 * (lane >> 5)) * 64 + cl] = v0;
-            sd[(r0 + 4 * (lane >> 5)) * 64 + 32 + cl] = v1;
-            ml = lane == r0 ? (uint32_t)B0 : ml;
-            mh = lane == r0 ? (uint32_t)B1 : mh;
-            ml = lane == r0 + 4 ? (uint32_t)(B0 >> 32) : ml;
-            mh = lane == r0 + 4 ? (uint32_t)(B1 >> 32) : mh;
-          }
+            *(float2*)(sd + ((r0 + 4 * (lane >> 5)) * 32 + cl) * 2) = make_float2(v0, v1);
+            // lane r0 (r0 + 4) of ml/mh takes row r0's (r0 + 4's) mask halves;
+            // the wait states cover the ballots' scalar results
+            const uint32_t b0l = (uint32_t)B0, b1l = (uint32_t)B1;
+            const uint32_t b0h = (uint32_t)(B0 >> 32), b1h = (uint32_t)(B1 >> 32);
+            uint32_t wl0 = ml, wl1 = mh;
+            asm volatile(
+                "s_nop 4\n\t"
+                "v_writelane_b32 %0, %2, %6\n\t"
+                "v_writelane_b32 %1, %3, %6\n\t"
+                "v_writelane_b32 %0, %4, %7\n\t"
+                "v_writelane_b32 %1, %5, %7"
+                : "+v"(wl0), "+v"(wl1)
+                : "s"(b0l), "s"(b1l), "s"(b0h), "s"(b1h), "i"(r0), "i"(r0 + 4));
+            ml = wl0;
+            mh = wl1;
+          };
+          one(std::integral_constant<int, 0>{});
+          one(std::integral_constant<int, 1>{});
+          one(std::integral_constant<int, 2>{});
+          one(std::integral_constant<int, 3>{});
+          one(std::integral_constant<int, 4>{});
+          one(std::integral_constant<int, 5>{});
+          one(std::integral_constant<int, 6>{});
+          one(std::integral_constant<int, 7>{});
         };
         if (full) collect(std::true_type{});
         else collect(std::false_type{});
@@ -188,7 +207,7 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
                 c = up ? c + w : c;
                 m = up ? (m >> w) : m;
               }
-              v = sd[rsel * 64 + c];
+              v = sd[(rsel * 32 + (c & 31)) * 2 + (c >> 5)];
             }
             a.val[tbase + i] = v;
             a.idx[tbase + i] = (uint8_t)c;
