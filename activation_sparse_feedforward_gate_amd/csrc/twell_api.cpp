@@ -302,16 +302,12 @@ twell_status twell_ffn_fwd_ex(const twell_ffn_shape* sh, const void* x, const vo
   }
   mark(1);                                                            // gate GEMM + pack done
   if (in_dt == DT_BF16) {
-    int* ovf = nullptr;
-    e = launch_union_fwd(x, WuT, Wd, sh->T, sh->d, sh->F, h, skip, w.uni, y, out_dt, &ovf, stream, evt(2), evt(3),
+    // a value beyond the fp16 range sets the overflow flag, and the down kernel
+    // then computes y per stored pair in fp32 instead (no extra launch)
+    e = launch_union_fwd(x, WuT, Wd, sh->T, sh->d, sh->F, h, skip, w.uni, y, out_dt, nullptr, stream, evt(2), evt(3),
                          slabs_ready);
     if (e != hipSuccess) return hip_status(e, "union up/down GEMMs");
     mark(4);                                                          // down-projection done
-    // fp16 overflow fallback (does nothing unless the flag is set)
-    e = launch_up_bf16(x, nullptr, WuT, nullptr, sh->T, sh->d, sh->F, h, aval, nullptr, nullptr, skip, stream, ovf);
-    if (e == hipSuccess)
-      e = launch_down_bf16(aval, nullptr, Wd, nullptr, sh->T, sh->d, sh->F, h, y, out_dt, skip, stream, ovf);
-    if (e != hipSuccess) return hip_status(e, "overflow fallback");
   } else {
     mark(2);
     e = launch_sddmm_up(in_dt, x, WuT, sh->T, sh->d, sh->F, h, aval, skip, stream);
@@ -642,14 +638,10 @@ twell_status twell_relu_ffn_fwd(const twell_ffn_shape* sh, const void* x, const 
   hipError_t e = launch_gate_twell(in_dt, x, W1T, b1, sh->T, sh->d, sh->F, h, stream, slabs, uflag);
   if (e != hipSuccess) return hip_status(e, "gate GEMM");
   if (in_dt == DT_BF16) {
-    int* ovf = nullptr;
-    e = launch_union_fwd(x, nullptr, W2, sh->T, sh->d, sh->F, h, nullptr, w.uni, y, out_dt, &ovf, stream, nullptr,
+    // h (or W2) beyond the fp16 range: the down kernel takes the per-pair fp32 path
+    e = launch_union_fwd(x, nullptr, W2, sh->T, sh->d, sh->F, h, nullptr, w.uni, y, out_dt, nullptr, stream, nullptr,
                          nullptr, true);
     if (e != hipSuccess) return hip_status(e, "union down GEMM");
-    // h beyond the fp16 range: the per-pair kernel with fp32 h (does nothing unless the flag is set)
-    e = launch_down_bf16((const float*)h.val, nullptr, W2, nullptr, sh->T, sh->d, sh->F, h, y, out_dt, nullptr,
-                         stream, ovf);
-    if (e != hipSuccess) return hip_status(e, "overflow fallback");
   } else {
     e = launch_spmm_down(in_dt, out_dt, (const float*)h.val, W2, sh->T, sh->d, sh->F, h, y, nullptr, stream);
     if (e != hipSuccess) return hip_status(e, "sparse down-projection");

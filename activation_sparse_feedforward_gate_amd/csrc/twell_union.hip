@@ -18,8 +18,8 @@
 // Neurons that no token of the block activates are skipped whole; the
 // products with the zero entries inside the union are computed and are exact
 // zeros.  a is fp16 for the down GEMM (relative rounding 2^-11, within the
-// 1e-3 output budget); if any |a| exceeds the fp16 range a device flag makes
-// the down GEMM stand down and the TwELL-pattern kernels recompute the layer.
+// 1e-3 output budget); if any |a| (or a weight of Wd) exceeds the fp16 range a
+// device flag makes the down kernel compute y per stored pair in fp32 instead.
 #include <algorithm>
 
 #include "gemm_core.hpp"
@@ -622,20 +622,86 @@ __device__ __forceinline__ void down_union_tile(const UnionArgs& a, int b, int c
   }
 }
 
+// The same y tile per stored pair in fp32, for the forward when the overflow
+// flag is set (a value of a, h or Wd beyond the fp16 range): for each live row
+// and each stored pair (n, h) in ascending neuron order, a = h * (x_t . WuT[n])
+// (bf16 products, fp32 sums, one fixed-order butterfly over the wave) or a = h
+// for the non-gated layer (WuT null), then y_t += a * Wd[n] over the tile's
+// columns (CPL per lane).  Every column tile recomputes its rows' dot
+// products: this path serves inputs outside the fp16 range, not speed.
+template <int CPL>
+__device__ void down_fallback_tile(const UnionArgs& a, int b, int n0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const uint16_t* x = (const uint16_t*)a.x;
+  const uint16_t* Wu = (const uint16_t*)a.WuT;
+  const uint16_t* Wd = (const uint16_t*)a.Wd;
+  const int c0 = n0 + lane * CPL;
+  for (int r = wave; r < UB; r += nw) {
+    const int t = b * UB + r;
+    if (!live(a, t)) continue;                      // wave-uniform
+    float acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+    const int64_t tile0 = (int64_t)(t >> 4) * a.NT;
+    for (int j = 0; j < a.NT; ++j) {
+      const int cnt = popc64(a.mask[(int64_t)t * a.NT + j]);
+      const int64_t sb = (tile0 + j) * 1024 + (t & 15);   // slot s of this row: sb + 16 s
+      for (int s = 0; s < cnt; ++s) {
+        const float hv = a.hval[sb + 16 * s];
+        const int64_t n = (int64_t)j * 64 + a.hidx[sb + 16 * s];
+        float av = hv;
+        if (Wu) {
+          float p = 0.f;
+          for (int e = lane * 8; e < a.d; e += 512) {
+            const uint4 xv = *(const uint4*)(x + (int64_t)t * a.d + e);
+            const uint4 wv = *(const uint4*)(Wu + n * a.d + e);
+            const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w}, ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              p = fmaf(bf16_lo(xs[q]), bf16_lo(ws[q]), p);
+              p = fmaf(bf16_hi(xs[q]), bf16_hi(ws[q]), p);
+            }
+          }
+          av = hv * wave_sum(p);
+        }
+        const uint16_t* wr = Wd + n * a.d + c0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] = fmaf(av, bf16_to_f32(wr[c]), acc[c]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      if (a.out_bf16) ((uint16_t*)a.y)[(int64_t)t * a.d + c0 + c] = (uint16_t)f32_to_bf16_bits(acc[c]);
+      else ((float*)a.y)[(int64_t)t * a.d + c0 + c] = acc[c];
+    }
+  }
+}
+
 // Persistent workgroups walk the (row block, column tile) tiles; the
 // workgroups of XCD x take the row blocks b = x (mod 8), all column tiles of
 // a block together, so the block's adense rows are reused from that XCD's L2.
+// In the forward, a set overflow flag sends every tile down the per-pair fp32
+// path above (no separate fallback launch); the backward (TWO) stands down
+// and leaves dX to its per-pair kernel.
 template <class Cfg, bool TWO = false>
 __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void down_union_kernel(UnionArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1_[Cfg::SINGLE ? 16 : Cfg::STAGE];
   char* st1 = Cfg::SINGLE ? st0 : st1_;
-  if (*a.flag) return;                              // fp16 overflow: the fallback path writes y
   const int nct = a.d / Cfg::BN;
   const int nblk = (a.T + UB - 1) / UB;
   const int x = blockIdx.x & 7;
   const int nbx = (nblk - x + 7) / 8;
   const int ntile = nbx * nct;
+  if (*a.flag) {
+    if constexpr (!TWO) {
+      for (int k = blockIdx.x >> 3; k < ntile; k += gridDim.x >> 3) {
+        const int bi = k / nct;
+        down_fallback_tile<Cfg::BN / 64>(a, x + 8 * bi, (k - bi * nct) * Cfg::BN);
+      }
+    }
+    return;
+  }
   for (int k = blockIdx.x >> 3; k < ntile; k += gridDim.x >> 3) {
     const int bi = k / nct;
     down_union_tile<Cfg, TWO>(a, x + 8 * bi, k - bi * nct, st0, st1);

@@ -35,7 +35,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps before the timed ones (the GPU clock settles over the first tens of ms)")
     ap.add_argument("--config", default="2b",
                     help="headline workload: 2b (T=32768, d=2304, F=9216, 0.93%% density) by default")
     ap.add_argument("--decode", action="store_true", help="use the workload's decode-shaped pass")
@@ -340,7 +341,7 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool) 
     torch.cuda.synchronize()
     st = np.array([[r[i].elapsed_time(r[i + 1]) for i in range(nst - 1)] for r in recs]).mean(axis=0)
     stages = {"gate_gemm_twell_pack": st[0], "union_lists_wd_fp16": st[1], "up_projection": st[2],
-              "down_projection": st[3], "overflow_fallback_check": st[4]}
+              "down_projection": st[3]}
     if training:
         stages["dense_rows_fwd"] = st[5]
         stages["hybrid_bwd"] = st[7]
@@ -372,7 +373,7 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool) 
         out["union_neurons"] = n_union
         out["stage_note"] = ("few-token kernels: gate_gemm_twell_pack is the K-split gate GEMM alone, "
                              "up_projection is the TwELL pack fused with the up-projection, "
-                             "union_lists_wd_fp16 and overflow_fallback_check are empty (event overhead)")
+                             "union_lists_wd_fp16 is empty (event overhead)")
 
     # the library's own dense step on the same inputs
     if not args.no_dense and bf:
@@ -552,7 +553,7 @@ def main() -> int:
     if not args.no_extras:
         # the other workloads, each with a short timed run of its own
         ex = {}
-        es, ew = max(1, min(args.steps, 10)), max(1, min(args.warmup, 3))
+        es, ew = max(1, min(args.steps, 10)), max(1, min(args.warmup, 10))
         for name, dec in EXTRA_WORKLOADS:
             if name == args.config and dec == args.decode:
                 continue

@@ -277,7 +277,8 @@ twell_status twell_ffn_bwd_hybrid_compact(const twell_ffn_shape *sh, const void 
  *   [2] row-block neuron unions and the fp16 copy of Wd done (bf16 inputs;
  *       for fp32 inputs recorded right after [1])
  *   [3] up-projection done   [4] down-projection done
- *   [5] sparse phases done (incl. the fp16-overflow fallback)
+ *   [5] sparse phases done (for bf16 inputs right after [4]: the fp16-
+ *       overflow fallback runs inside the down-projection kernel)
  *   [6] end (after the dense-row forward, training)
  * Arguments otherwise as for twell_ffn_fwd; events past n_events are not
  * recorded.
@@ -290,7 +291,7 @@ twell_status twell_ffn_fwd_ex(const twell_ffn_shape *sh, const void *x, const vo
 /*
  * The three stages of the forward, callable one by one: the same layer as
  * twell_ffn_fwd, computed by the per-pair kernels that twell_ffn_fwd keeps
- * for fp32 inputs and for its fp16-overflow fallback.  For bf16 inputs
+ * for fp32 inputs.  For bf16 inputs
  * twell_ffn_fwd itself runs other kernels (the union GEMMs with a in fp16, or
  * the few-token kernels), so its bits differ from this sequence's; both meet
  * the same tolerance against the definition.

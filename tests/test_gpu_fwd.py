@@ -374,10 +374,12 @@ def test_fwd_prefill_wide_sparse_union(torch, tw):
     check_fwd(w, y, m)
 
 
-def test_fwd_fp16_overflow_falls_back(torch, tw):
+@pytest.mark.parametrize("d,f", [(256, 1024), (384, 1024), (320, 640)], ids=["d256", "d384", "d320"])
+def test_fwd_fp16_overflow_falls_back(torch, tw, d, f):
     """a = h*u beyond the fp16 range (inputs scaled up) takes the fallback
-    path that keeps a in fp32; y must still match the oracle."""
-    w = make_workload("0.5b", T=300, d=256, f=1024)
+    path that keeps a in fp32; y must still match the oracle.  d = 256, 384
+    and 320 reach the down kernels with 256-, 128- and 64-column tiles."""
+    w = make_workload("0.5b", T=300, d=d, f=f)
     w.x[:] = round_bf16(w.x * np.float32(80.0))
     w.bg[:] = round_bf16(w.bg * np.float32(80.0))
     log("[fwd] fp16 overflow fallback")
