@@ -109,10 +109,15 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
   // index 0) past the row's count; (4) coalesced stores of the values,
   // indices, row counts and masks.  The mainloop's LDS is free once it
   // returns.
+  // Where the free LDS holds two dense tiles per wave, the two 16-row tiles
+  // of a 32-row accumulator block go through these steps together, with no
+  // barrier between them, so the latencies of one tile's shuffles, LDS reads
+  // and stores overlap the other's work.
   constexpr int STG = 16 * 64 * 4;                          // dense tile, per wave
-  static_assert(Cfg::EPI_BYTES >= Cfg::NTH / 64 * STG, "epilogue staging");
+  constexpr int NH = Cfg::EPI_BYTES >= Cfg::NTH / 64 * 2 * STG ? 2 : 1;
+  static_assert(Cfg::EPI_BYTES >= Cfg::NTH / 64 * NH * STG, "epilogue staging");
   const int wr = m0 + (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
-  float* sd = (float*)(lds + wave * STG);                   // [16 rows][32][2]: (c, c + 32) pairs
+  float* sdw = (float*)(lds + wave * NH * STG);             // NH x [16 rows][32][2]: (c, c + 32) pairs
   const int rsel = lane & 15;
 #pragma unroll
   for (int tc = 0; tc < Cfg::TN / 2; ++tc) {
@@ -123,36 +128,36 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int rt0 = wr + tm * 32 + half * 16;   // first row of this TwELL row tile
-        if (rt0 >= a.T) continue;                   // wave-uniform
-        const bool full = rt0 + 16 <= a.T;          // every row of the tile exists
-        uint32_t ml = 0, mh = 0;                    // lane r < 16: row r's mask, columns 0-31 / 32-63
-        // the ragged last tile takes a copy of the loop that masks rows past T
-        // out of the ballots; every other tile takes one without that work
+      for (int hb = 0; hb < 2; hb += NH) {
+        const int rtb = wr + tm * 32 + hb * 16;     // first row of the batch's first TwELL row tile
+        if (rtb >= a.T) continue;                   // wave-uniform
+        const bool full = rtb + 16 * NH <= a.T;     // every row of the batch exists
+        uint32_t ml[NH], mh[NH];                    // lane r < 16: row r's mask, columns 0-31 / 32-63
+        // a batch with rows past T takes a copy of the loop that masks them
+        // out of the ballots; every other batch takes one without that work
         auto collect = [&](auto full_c) {
           constexpr bool FULL = decltype(full_c)::value;
-          auto one = [&](auto q_c) {
+          auto one = [&](auto k_c, auto q_c) {
+            constexpr int k = decltype(k_c)::value;
             constexpr int q = decltype(q_c)::value;
-            constexpr int e = q;                    // register index within the half (+ 8 * half)
             constexpr int r0 = 8 * (q >> 2) + (q & 3);  // row of lanes 0-31; lanes 32-63 hold r0 + 4
-            const float v0 = g.acc[0][tm][2 * tc][half * 8 + e] + b0;
-            const float v1 = g.acc[0][tm][2 * tc + 1][half * 8 + e] + b1;
+            const float v0 = g.acc[0][tm][2 * tc][(hb + k) * 8 + q] + b0;
+            const float v1 = g.acc[0][tm][2 * tc + 1][(hb + k) * 8 + q] + b1;
             uint64_t B0 = __builtin_amdgcn_ballot_w64(v0 > 0.f);
             uint64_t B1 = __builtin_amdgcn_ballot_w64(v1 > 0.f);
             if constexpr (!FULL) {
-              const int rq = rt0 + r0;
+              const int rq = rtb + 16 * k + r0;
               const uint64_t rowmask =
                   (rq < a.T ? 0xffffffffull : 0ull) | (rq + 4 < a.T ? 0xffffffff00000000ull : 0ull);
               B0 &= rowmask;
               B1 &= rowmask;
             }
-            *(float2*)(sd + ((r0 + 4 * (lane >> 5)) * 32 + cl) * 2) = make_float2(v0, v1);
+            *(float2*)(sdw + k * (STG / 4) + ((r0 + 4 * (lane >> 5)) * 32 + cl) * 2) = make_float2(v0, v1);
             // lane r0 (r0 + 4) of ml/mh takes row r0's (r0 + 4's) mask halves;
             // the wait states cover the ballots' scalar results
             const uint32_t b0l = (uint32_t)B0, b1l = (uint32_t)B1;
             const uint32_t b0h = (uint32_t)(B0 >> 32), b1h = (uint32_t)(B1 >> 32);
-            uint32_t wl0 = ml, wl1 = mh;
+            uint32_t wl0 = ml[k], wl1 = mh[k];
             asm volatile(
                 "s_nop 4\n\t"
                 "v_writelane_b32 %0, %2, %6\n\t"
@@ -161,63 +166,89 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
                 "v_writelane_b32 %1, %5, %7"
                 : "+v"(wl0), "+v"(wl1)
                 : "s"(b0l), "s"(b1l), "s"(b0h), "s"(b1h), "i"(r0), "i"(r0 + 4));
-            ml = wl0;
-            mh = wl1;
+            ml[k] = wl0;
+            mh[k] = wl1;
           };
-          one(std::integral_constant<int, 0>{});
-          one(std::integral_constant<int, 1>{});
-          one(std::integral_constant<int, 2>{});
-          one(std::integral_constant<int, 3>{});
-          one(std::integral_constant<int, 4>{});
-          one(std::integral_constant<int, 5>{});
-          one(std::integral_constant<int, 6>{});
-          one(std::integral_constant<int, 7>{});
+          auto tile = [&](auto k_c) {
+            one(k_c, std::integral_constant<int, 0>{});
+            one(k_c, std::integral_constant<int, 1>{});
+            one(k_c, std::integral_constant<int, 2>{});
+            one(k_c, std::integral_constant<int, 3>{});
+            one(k_c, std::integral_constant<int, 4>{});
+            one(k_c, std::integral_constant<int, 5>{});
+            one(k_c, std::integral_constant<int, 6>{});
+            one(k_c, std::integral_constant<int, 7>{});
+          };
+          tile(std::integral_constant<int, 0>{});
+          if constexpr (NH == 2) tile(std::integral_constant<int, 1>{});
         };
+#pragma unroll
+        for (int k = 0; k < NH; ++k) ml[k] = mh[k] = 0;
         if (full) collect(std::true_type{});
         else collect(std::false_type{});
-        // lanes 0-15: counts; the tile's width is their maximum
-        const int c16 = __popc(ml) + __popc(mh);
-        int wm = c16;
+        // lanes 0-15: counts; each tile's width is their maximum
+        int c16[NH], width[NH];
 #pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) wm = max(wm, __shfl_xor(wm, o));
-        const int width = __builtin_amdgcn_readfirstlane(wm);
-        sorl |= ml;
-        sorh |= mh;
+        for (int k = 0; k < NH; ++k) c16[k] = __popc(ml[k]) + __popc(mh[k]);
+#pragma unroll
+        for (int k = 0; k < NH; ++k) {
+          int wm = c16[k];
+#pragma unroll
+          for (int o = 8; o >= 1; o >>= 1) wm = max(wm, __shfl_xor(wm, o));
+          width[k] = __builtin_amdgcn_readfirstlane(wm);
+          sorl |= ml[k];
+          sorh |= mh[k];
+        }
         __builtin_amdgcn_wave_barrier();
-        const int64_t tix = (int64_t)(rt0 >> 4) * a.NT + j;
-        const int64_t tbase = tix * (64 * 16);
-        if (width > 0) {
-          // this lane's slots all belong to row rsel
-          const uint64_t mrow = ((uint64_t)(uint32_t)__shfl((int)mh, rsel) << 32) | (uint32_t)__shfl((int)ml, rsel);
-          const int crow = popc64(mrow);
-          for (int i = lane; i < width * 16; i += 64) {
-            const int sl = i >> 4;
-            uint64_t m = mrow;
-            float v = 0.f;
-            int c = 0;
-            if (sl < crow) {
-              // position of the sl-th set bit of m
-              int k = sl;
+        // output slot i (lane + 64 m) of a tile is slot i >> 4 of row rsel:
+        // the (i >> 4)-th set bit of that row's mask, or padding
+        uint64_t mrow[NH];
+        int crow[NH];
 #pragma unroll
-              for (int w = 32; w >= 1; w >>= 1) {
-                const uint64_t lowmask = (1ull << w) - 1ull;
-                const int pc = popc64(m & lowmask);
-                const bool up = k >= pc;
-                k = up ? k - pc : k;
-                c = up ? c + w : c;
-                m = up ? (m >> w) : m;
-              }
-              v = sd[(rsel * 32 + (c & 31)) * 2 + (c >> 5)];
+        for (int k = 0; k < NH; ++k) {
+          mrow[k] = ((uint64_t)(uint32_t)__shfl((int)mh[k], rsel) << 32) | (uint32_t)__shfl((int)ml[k], rsel);
+          crow[k] = popc64(mrow[k]);
+        }
+        auto slot = [&](int k, int i) {
+          const int sl = i >> 4;
+          uint64_t m = mrow[k];
+          float v = 0.f;
+          int c = 0;
+          if (sl < crow[k]) {
+            // position of the sl-th set bit of m
+            int kk = sl;
+#pragma unroll
+            for (int w = 32; w >= 1; w >>= 1) {
+              const uint64_t lowmask = (1ull << w) - 1ull;
+              const int pc = popc64(m & lowmask);
+              const bool up = kk >= pc;
+              kk = up ? kk - pc : kk;
+              c = up ? c + w : c;
+              m = up ? (m >> w) : m;
             }
-            a.val[tbase + i] = v;
-            a.idx[tbase + i] = (uint8_t)c;
+            v = sdw[k * (STG / 4) + (rsel * 32 + (c & 31)) * 2 + (c >> 5)];
           }
+          const int64_t tbase = ((int64_t)((rtb >> 4) + k) * a.NT + j) * (64 * 16);
+          a.val[tbase + i] = v;
+          a.idx[tbase + i] = (uint8_t)c;
+        };
+        // the first 64 slots of every tile of the batch, one per lane, then
+        // the rest of the wider tiles
+#pragma unroll
+        for (int k = 0; k < NH; ++k)
+          if (lane < width[k] * 16) slot(k, lane);
+#pragma unroll
+        for (int k = 0; k < NH; ++k)
+          for (int i = lane + 64; i < width[k] * 16; i += 64) slot(k, i);
+#pragma unroll
+        for (int k = 0; k < NH; ++k) {
+          const int rt0 = rtb + 16 * k;
+          if (lane < 16 && rt0 + lane < a.T) {
+            a.cnt[(int64_t)(rt0 + lane) * a.NT + j] = (uint8_t)c16[k];
+            if (a.mask) a.mask[(int64_t)(rt0 + lane) * a.NT + j] = ((uint64_t)mh[k] << 32) | ml[k];
+          }
+          if (lane == 0 && rt0 < a.T) a.width[(int64_t)(rt0 >> 4) * a.NT + j] = (uint8_t)width[k];
         }
-        if (lane < 16 && rt0 + lane < a.T) {
-          a.cnt[(int64_t)(rt0 + lane) * a.NT + j] = (uint8_t)c16;
-          if (a.mask) a.mask[(int64_t)(rt0 + lane) * a.NT + j] = ((uint64_t)mh << 32) | ml;
-        }
-        if (lane == 0) a.width[tix] = (uint8_t)width;
         __builtin_amdgcn_wave_barrier();
       }
       // a wave's rows start on a multiple of 64, so row blocks tm - 1 and tm
