@@ -81,12 +81,14 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
   const Operand A{a.x, a.d, nullptr, a.T};
   const Operand B{a.WgT, a.d, nullptr, a.F};
   char* lds;
+  char* lds2 = nullptr;                             // a second free region (two-stage direct-to-LDS tiles)
   if constexpr (TileFor<Cfg>::dma) {
     __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
     __shared__ __attribute__((aligned(1024))) char st1_[Cfg::SINGLE ? 16 : Cfg::STAGE];
     char* st1 = Cfg::SINGLE ? st0 : st1_;
     g.run(A, &B, m0, n0, a.d, st0, st1);
     lds = st0;
+    lds2 = st1_;
   } else {
     __shared__ __attribute__((aligned(16))) char buf[Cfg::LDS_BYTES];
     g.run(A, &B, m0, n0, a.d, buf);
@@ -109,15 +111,22 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
   // index 0) past the row's count; (4) coalesced stores of the values,
   // indices, row counts and masks.  The mainloop's LDS is free once it
   // returns.
-  // Where the free LDS holds two dense tiles per wave, the two 16-row tiles
-  // of a 32-row accumulator block go through these steps together, with no
-  // barrier between them, so the latencies of one tile's shuffles, LDS reads
-  // and stores overlap the other's work.
+  // Where the free LDS holds several dense tiles per wave, NH consecutive
+  // 16-row tiles (four: one 64-row slab, with both stage buffers of a
+  // two-stage tile; else two: one 32-row accumulator block) go through these
+  // steps together, with no barrier between them, so the latencies of one
+  // tile's shuffles, LDS reads and stores overlap the others' work.
   constexpr int STG = 16 * 64 * 4;                          // dense tile, per wave
-  constexpr int NH = Cfg::EPI_BYTES >= Cfg::NTH / 64 * 2 * STG ? 2 : 1;
-  static_assert(Cfg::EPI_BYTES >= Cfg::NTH / 64 * NH * STG, "epilogue staging");
+  constexpr int NW = Cfg::NTH / 64;
+  constexpr bool TWO_REGIONS = TileFor<Cfg>::dma && !Cfg::SINGLE && NW % 2 == 0;
+  constexpr int NH = (TWO_REGIONS && Cfg::EPI_BYTES >= NW / 2 * 4 * STG) ? 4
+                     : Cfg::EPI_BYTES >= NW * 2 * STG ? 2 : 1;
+  static_assert(NH == 4 || Cfg::EPI_BYTES >= NW * NH * STG, "epilogue staging");
   const int wr = m0 + (wave / Cfg::WN) * (Cfg::BM / Cfg::WM);
-  float* sdw = (float*)(lds + wave * NH * STG);             // NH x [16 rows][32][2]: (c, c + 32) pairs
+  // NH x [16 rows][32][2]: (c, c + 32) pairs; with NH = 4 the first half of
+  // the waves stage in one stage buffer, the second half in the other
+  float* sdw = NH == 4 ? (float*)((wave < NW / 2 ? lds : lds2) + (wave % (NW / 2)) * NH * STG)
+                       : (float*)(lds + wave * NH * STG);
   const int rsel = lane & 15;
 #pragma unroll
   for (int tc = 0; tc < Cfg::TN / 2; ++tc) {
@@ -126,11 +135,9 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
     const float b0 = bias[2 * tc], b1 = bias[2 * tc + 1];
     uint32_t sorl = 0, sorh = 0;                    // lanes 0-15: union of their rows' masks over the slab
 #pragma unroll
-    for (int tm = 0; tm < Cfg::TM; ++tm) {
-#pragma unroll
-      for (int hb = 0; hb < 2; hb += NH) {
-        const int rtb = wr + tm * 32 + hb * 16;     // first row of the batch's first TwELL row tile
-        if (rtb >= a.T) continue;                   // wave-uniform
+    for (int kb = 0; kb < 2 * Cfg::TM; kb += NH) {  // 16-row tiles kb .. kb + NH - 1 of the wave
+      const int rtb = wr + kb * 16;                 // first row of the batch's first TwELL row tile
+      if (rtb < a.T) {                              // wave-uniform
         const bool full = rtb + 16 * NH <= a.T;     // every row of the batch exists
         uint32_t ml[NH], mh[NH];                    // lane r < 16: row r's mask, columns 0-31 / 32-63
         // a batch with rows past T takes a copy of the loop that masks them
@@ -141,8 +148,8 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
             constexpr int k = decltype(k_c)::value;
             constexpr int q = decltype(q_c)::value;
             constexpr int r0 = 8 * (q >> 2) + (q & 3);  // row of lanes 0-31; lanes 32-63 hold r0 + 4
-            const float v0 = g.acc[0][tm][2 * tc][(hb + k) * 8 + q] + b0;
-            const float v1 = g.acc[0][tm][2 * tc + 1][(hb + k) * 8 + q] + b1;
+            const float v0 = g.acc[0][(kb + k) >> 1][2 * tc][((kb + k) & 1) * 8 + q] + b0;
+            const float v1 = g.acc[0][(kb + k) >> 1][2 * tc + 1][((kb + k) & 1) * 8 + q] + b1;
             uint64_t B0 = __builtin_amdgcn_ballot_w64(v0 > 0.f);
             uint64_t B1 = __builtin_amdgcn_ballot_w64(v1 > 0.f);
             if constexpr (!FULL) {
@@ -180,7 +187,11 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
             one(k_c, std::integral_constant<int, 7>{});
           };
           tile(std::integral_constant<int, 0>{});
-          if constexpr (NH == 2) tile(std::integral_constant<int, 1>{});
+          if constexpr (NH >= 2) tile(std::integral_constant<int, 1>{});
+          if constexpr (NH == 4) {
+            tile(std::integral_constant<int, 2>{});
+            tile(std::integral_constant<int, 3>{});
+          }
         };
 #pragma unroll
         for (int k = 0; k < NH; ++k) ml[k] = mh[k] = 0;
@@ -251,15 +262,15 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
         }
         __builtin_amdgcn_wave_barrier();
       }
-      // a wave's rows start on a multiple of 64, so row blocks tm - 1 and tm
-      // (tm odd) are one whole 64-row slab
-      if (tm & 1) {
+      // a wave's rows start on a multiple of 64, so 16-row tiles 4s .. 4s + 3
+      // are one whole 64-row slab
+      if (((kb + NH) & 3) == 0) {
 #pragma unroll
         for (int o = 8; o >= 1; o >>= 1) {
           sorl |= (uint32_t)__shfl_xor((int)sorl, o);
           sorh |= (uint32_t)__shfl_xor((int)sorh, o);
         }
-        const int s0 = wr + (tm - 1) * 32;
+        const int s0 = wr + (kb + NH - 4) * 16;
         if (a.slabs && s0 < a.T && lane == 0) a.slabs[(int64_t)(s0 >> 6) * a.NT + j] = ((uint64_t)sorh << 32) | sorl;
         sorl = 0;
         sorh = 0;
