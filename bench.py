@@ -35,8 +35,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=20,
-                    help="untimed steps before the timed ones (the GPU clock settles over the first tens of ms)")
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps before the timed ones (the GPU clock takes a few hundred ms of work to settle)")
     ap.add_argument("--config", default="2b",
                     help="headline workload: 2b (T=32768, d=2304, F=9216, 0.93%% density) by default")
     ap.add_argument("--decode", action="store_true", help="use the workload's decode-shaped pass")
@@ -222,13 +222,22 @@ def _ev():
     return torch.cuda.Event(enable_timing=True)
 
 
-def _timed(fn, steps: int, warmup: int, stream) -> float:
+def _timed(fn, steps: int, warmup: int, stream, warm_s: float = 0.0) -> float:
     """Mean ms per call of fn over exactly `steps` calls after `warmup` untimed
-    ones, between two events on the launch stream, synchronized on both sides."""
+    ones (and, with warm_s > 0, more untimed calls until warm_s seconds have
+    passed), between two events on the launch stream, synchronized on both
+    sides."""
+    import time
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    if warm_s > 0:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warm_s:
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
     t0, t1 = _ev(), _ev()
     t0.record(stream)
     for _ in range(steps):
@@ -274,7 +283,7 @@ def union_sizes(mask: "np.ndarray", T: int, live=None):
     return np.unpackbits(u.view(np.uint8), axis=1).sum(axis=1).astype(np.int64)
 
 
-def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool) -> dict:
+def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool, warm_s: float = 0.0) -> dict:
     """Time one workload: the TwELL step, the library's own dense step beside
     it, per-stage HIP events, and (full) the roofline of every forward kernel,
     a cold-cache figure and the workspace bytes of both paths."""
@@ -330,7 +339,7 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool) 
                 evs[8].record(stream)
 
     # timed region: exactly `steps` steps between two events, bracketed by synchronize
-    ms_step = _timed(step, steps, warmup, stream)
+    ms_step = _timed(step, steps, warmup, stream, warm_s)
 
     # per-stage durations from events recorded between the kernel launches
     nst = 9 if training else 7
@@ -386,7 +395,7 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool) 
             def dense_step():
                 tw.twell_ffn_dense_bwd(shape, x, WgT, bg, WuT, Wd, dY, yd, dXd, dWd_[0], dWd_[1], dWd_[2], dbgd,
                                        dws, stream)
-            dms = _timed(dense_step, steps, warmup, stream)
+            dms = _timed(dense_step, steps, warmup, stream, warm_s)
             out["dense_baseline"] = {"tokens_per_s": T / (dms * 1e-3), "ms_per_step": dms,
                                      "tflops": 18.0 * T * d * f / (dms * 1e-3) / 1e12,
                                      "what": "dense forward + backward, bf16 intermediates"}
@@ -398,7 +407,7 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool) 
 
             def dense_step():
                 tw.twell_ffn_dense_fwd(shape, x, WgT, bg, WuT, Wd, yd, dws, stream)
-            dms = _timed(dense_step, steps, warmup, stream)
+            dms = _timed(dense_step, steps, warmup, stream, warm_s)
             out["dense_baseline"] = {"tokens_per_s": T / (dms * 1e-3), "ms_per_step": dms,
                                      "tflops": 6.0 * T * d * f / (dms * 1e-3) / 1e12}
             out["dense_vs_sparse_rel_diff"] = (y - yd).norm().item() / max(yd.norm().item(), 1e-30)
@@ -554,12 +563,14 @@ def main() -> int:
         # the other workloads, each with a short timed run of its own
         ex = {}
         es, ew = max(1, min(args.steps, 10)), max(1, min(args.warmup, 10))
+        # each extra workload follows seconds of host-side input generation with
+        # the GPU idle: its warmup runs until 0.25 s of steps have passed
         for name, dec in EXTRA_WORKLOADS:
             if name == args.config and dec == args.decode:
                 continue
-            e = measure(args, name, dec, es, ew, full=False)
+            e = measure(args, name, dec, es, ew, full=False, warm_s=0.25)
             e.pop("_workload")
-            e["steps"], e["warmup"] = es, ew
+            e["steps"], e["warmup"], e["warmup_min_s"] = es, ew, 0.25
             ex[name + ("_decode" if dec else "")] = e
         out["extra_workloads"] = ex
     print(json.dumps(out))

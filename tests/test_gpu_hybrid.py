@@ -203,6 +203,23 @@ def test_hybrid_l1_penalty(torch, tw, name, kw, mean):
         assert 0 < got["nD"] < w.T                                             # both branches ran
 
 
+def test_hybrid_fwd_fp16_overflow_falls_back(torch, tw):
+    """a = h*u beyond the fp16 range in the hybrid forward (x and the gate
+    bias scaled up, which keeps the sign pattern): the union down-projection
+    computes the sparse rows per stored pair in fp32 while the dense rows take
+    their own branch; y and every gradient must still match."""
+    w = make_workload("hybrid", T=520, d=256, f=1280)
+    w.x[:] = round_bf16(np.asarray(w.x, dtype=np.float32) * np.float32(120.0))
+    w.bg[:] = round_bf16(np.asarray(w.bg, dtype=np.float32) * np.float32(120.0))
+    fwd = O.ffn_dense_fwd(w.x, w.WgT, w.bg, w.WuT, w.Wd)
+    sparse = (fwd["h"] > 0).sum(axis=1) <= w.tau
+    assert sparse.any() and (~sparse).any()
+    assert np.abs(fwd["a"][sparse]).max() > 65504.0                # a sparse row really overflows fp16
+    log("[hybrid] fp16 overflow in the forward")
+    got = run_train(torch, tw, w, w.tau)
+    check_full(w, got, w.tau)
+
+
 def test_hybrid_fp16_overflow_falls_back(torch, tw):
     """dG or dU beyond the fp16 range (dY scaled up) makes the union dX GEMM
     stand down for the per-pair fp32 kernel; every gradient must still match."""
