@@ -12,6 +12,8 @@
 //   OP_F32_K   fp32 [rows][K] fed to fp32 MFMA (fp32 workloads)
 //   OP_F32_T   fp32 [K][rows] fed to fp32 MFMA
 //   OP_F16_K   fp16 [rows][K] fed to fp16 MFMA
+//   OP_BF16P_K bf16 [rows][K] hi values with their lo values pair_off elements
+//              further on (an fp32 quantity kept split), fed like OP_F32S_K
 //   OP_BF16_T16 bf16 [K][rows], optional K gather list, converted to fp16 as
 //              it is transposed into LDS (exact for |v| >= 2^-17; smaller
 //              magnitudes keep fp16's subnormal resolution), fed to fp16 MFMA
@@ -27,13 +29,14 @@
 namespace twell {
 
 enum OpKind { OP_BF16_K = 0, OP_BF16_T = 1, OP_F32S_K = 2, OP_F32S_T = 3, OP_F32_K = 4, OP_F32_T = 5,
-              OP_F16_K = 6, OP_BF16_T16 = 7 };
+              OP_F16_K = 6, OP_BF16_T16 = 7, OP_BF16P_K = 8 };
 
 struct Operand {
   const void* ptr;
   int64_t ld;          // elements between consecutive rows (K kinds) or K steps (T kinds)
   const int* gather;   // K kinds: row index list; T kinds: K index list; may be null
   int nrows;           // rows that exist (K kinds clamp to nrows-1)
+  int64_t pair_off;    // OP_BF16P_K: elements from a hi value to its lo value
 };
 
 template <int KIND> struct KindInfo;
@@ -45,6 +48,7 @@ template <> struct KindInfo<OP_F32_K>  { static constexpr bool split = false, f3
 template <> struct KindInfo<OP_F32_T>  { static constexpr bool split = false, f32mma = true,  f16 = false, trans = true;  static constexpr int esz = 4; };
 template <> struct KindInfo<OP_F16_K>  { static constexpr bool split = false, f32mma = false, f16 = true,  trans = false; static constexpr int esz = 2; };
 template <> struct KindInfo<OP_BF16_T16> { static constexpr bool split = false, f32mma = false, f16 = true, trans = true; static constexpr int esz = 2; };
+template <> struct KindInfo<OP_BF16P_K> { static constexpr bool split = true, f32mma = false, f16 = false, trans = false; static constexpr int esz = 2; };
 
 // K elements per LDS row (= per K tile).
 template <int KIND> constexpr int ktile() { return KindInfo<KIND>::f32mma ? 32 : 64; }
@@ -93,6 +97,45 @@ struct LoaderK {
 template <int ROWS, int NTH> struct Loader<OP_BF16_K, ROWS, NTH> : LoaderK<OP_BF16_K, ROWS, NTH> {};
 template <int ROWS, int NTH> struct Loader<OP_F32_K, ROWS, NTH> : LoaderK<OP_F32_K, ROWS, NTH> {};
 template <int ROWS, int NTH> struct Loader<OP_F16_K, ROWS, NTH> : LoaderK<OP_F16_K, ROWS, NTH> {};
+
+// bf16 pair, K contiguous: an fp32 quantity kept as two bf16 planes, its hi
+// values at the operand's rows and its lo values pair_off elements further
+// on; they go to the hi and lo tiles exactly as a split fp32 operand's do.
+template <int ROWS, int NTH>
+struct Loader<OP_BF16P_K, ROWS, NTH> {
+  static constexpr int CH = ROWS * 8 / NTH;
+  static_assert(CH * NTH == ROWS * 8, "tile rows must divide the thread count");
+  const char* base;
+  uint32_t lo;
+  uint32_t off[CH];
+  uint4 rh[CH], rl[CH];
+  __device__ void init(const Operand& op, int row0, int tid) {
+    base = (const char*)op.ptr;
+    lo = (uint32_t)op.pair_off;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      int id = tid + q * NTH;
+      int gr = min(row0 + (id >> 3), op.nrows - 1);
+      if (op.gather) gr = op.gather[gr];
+      off[q] = (uint32_t)gr * (uint32_t)op.ld + (uint32_t)(id & 7) * 8;
+    }
+  }
+  __device__ void load(int k0, int /*K*/) {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      rh[q] = *(const uint4*)(base + ((uint64_t)off[q] + (uint32_t)k0) * 2);
+      rl[q] = *(const uint4*)(base + ((uint64_t)off[q] + lo + (uint32_t)k0) * 2);
+    }
+  }
+  __device__ void store(char* lds, char* lds_lo, int tid) const {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      int id = tid + q * NTH;
+      *(uint4*)(lds + swz(id >> 3, id & 7)) = rh[q];
+      *(uint4*)(lds_lo + swz(id >> 3, id & 7)) = rl[q];
+    }
+  }
+};
 
 // 16-bit [K][rows] operands (used as B): each K tile is copied into LDS as it
 // is laid out in memory, [k][row] with a padded pitch of 2*ROWS + 32 bytes

@@ -15,7 +15,10 @@
 //              dX_D = dG.WgT + dU.WuT
 //              dWgT = dG^T.x_D, dWuT = dU^T.x_D, dWd = A^T.dY_D, dbg = sum dG
 // The fp32 intermediates (A, dG, dU) enter the bf16 matrix cores as a hi + lo
-// pair of bf16 values; x, dY and the weights are exact in bf16.
+// pair of bf16 values; x, dY and the weights are exact in bf16.  For bf16
+// inputs the act kernel's epilogue writes them split, as bf16 planes (per
+// dense row: dG hi, dG lo, dU hi, dU lo, A hi, A lo, F values each; the
+// forward keeps A hi, A lo), which the later GEMMs read directly.
 //
 // Sparse rows: the weight gradients are sums over the tokens that activate a
 // neuron, i.e. over a column of the TwELL pattern.  A column-major index of
@@ -96,8 +99,9 @@ struct DenseRowsArgs {
   float* dWgT;
   float* dWuT;
   float* dWd;
-  float* dbg_part;    // [ceil(T/64)][F]
+  float* dbg_part;    // [ceil(T/dbg_rows)][F]
   float* dbg;
+  int dbg_rows;       // rows per dbg partial
   float l1;           // backward: added to dG where g > 0 (activation penalty)
 };
 
@@ -179,11 +183,16 @@ __global__ __launch_bounds__(Cfg2::NTH, WavesPerEU<Cfg2>::value) void dense_rows
     const Operand B2{a.Wd, a.d, nullptr, a.F};
     gd.run(A2, &B2, m0, n0, a.d, st, st);
   }
-  const int64_t ldb = BWD ? 3 * (int64_t)a.F : a.F;
+  // bf16 planes: backward [dG hi | dG lo | dU hi | dU lo | A hi | A lo],
+  // forward [A hi | A lo], F values each
+  const int64_t ld16 = (BWD ? 6 : 2) * (int64_t)a.F;
+  uint16_t* buf16 = (uint16_t*)a.buf;
+  float dsum[Cfg2::TN];                             // backward: this lane's column sum of dG
 #pragma unroll
   for (int j = 0; j < Cfg2::TN; ++j) {
     const int col = n0 + Tile::col_of(j);
     const float b = ld_bias<true>(a.bg, col);
+    dsum[j] = 0.f;
 #pragma unroll
     for (int i = 0; i < Cfg2::TM; ++i)
 #pragma unroll
@@ -193,17 +202,148 @@ __global__ __launch_bounds__(Cfg2::NTH, WavesPerEU<Cfg2>::value) void dense_rows
           const float gv = g.acc[0][i][j][e] + b;
           const float h = gv > 0.f ? gv : 0.f;
           const float u = g.acc[1][i][j][e];
-          float* row = a.buf + (int64_t)r * ldb;
+          uint16_t* row = buf16 + (int64_t)r * ld16 + col;
+          uint32_t hi, lo;
           if constexpr (BWD) {
             const float da = gd.acc[0][i][j][e];
-            row[col] = gv > 0.f ? da * u + a.l1 : 0.f;
-            row[a.F + col] = da * h;
-            row[2 * a.F + col] = h * u;
+            const float dg = gv > 0.f ? da * u + a.l1 : 0.f;
+            dsum[j] += dg;
+            split_bf16(dg, hi, lo);
+            row[0] = (uint16_t)hi;
+            row[a.F] = (uint16_t)lo;
+            split_bf16(da * h, hi, lo);
+            row[2 * a.F] = (uint16_t)hi;
+            row[3 * a.F] = (uint16_t)lo;
+            split_bf16(h * u, hi, lo);
+            row[4 * a.F] = (uint16_t)hi;
+            row[5 * a.F] = (uint16_t)lo;
           } else {
-            row[col] = h * u;
+            split_bf16(h * u, hi, lo);
+            row[0] = (uint16_t)hi;
+            row[a.F] = (uint16_t)lo;
           }
         }
       }
+  }
+  if constexpr (BWD) {
+    if (a.dbg) {
+      // partial dbg of the tile's rows, in a fixed order: lanes l and l + 32
+      // hold the same column (rows 4 apart), the WM waves of a column range
+      // hold different rows (added through the free stage buffer)
+      const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) / Cfg2::WN;
+      float* red = (float*)st;                      // [WM][BN]
+#pragma unroll
+      for (int j = 0; j < Cfg2::TN; ++j) {
+        dsum[j] += __shfl_xor(dsum[j], 32);
+        if (lane < 32) red[wm * Cfg2::BN + Tile::col_of(j)] = dsum[j];
+      }
+      __syncthreads();
+      if (wm == 0 && lane < 32) {
+#pragma unroll
+        for (int j = 0; j < Cfg2::TN; ++j) {
+          float sum = 0.f;
+#pragma unroll
+          for (int q = 0; q < Cfg2::WM; ++q) sum += red[q * Cfg2::BN + Tile::col_of(j)];
+          a.dbg_part[(int64_t)(m0 / Cfg2::BM) * a.F + n0 + Tile::col_of(j)] = sum;
+        }
+      }
+    }
+  }
+}
+
+// bf16 inputs: out[rows[r]] from the bf16 planes (forward: y = A.Wd;
+// backward: dX = dG.WgT + dU.WuT), each intermediate read as a hi/lo plane
+// pair, so every weight tile serves both MFMAs as with the fp32 split.  The A
+// operand starts at the tile's first row, so its 32-bit element offsets stay
+// within one tile's rows.
+template <class Cfg, bool BWD>
+__global__ __launch_bounds__(Cfg::NTH) void dense_rows_out16_kernel(DenseRowsArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  const int nD = *a.n_rows;
+  const int nbn = a.d / Cfg::BN;
+  const int bm = blockIdx.x / nbn, bn = blockIdx.x % nbn;
+  const int m0 = bm * Cfg::BM, n0 = bn * Cfg::BN;
+  if (m0 >= nD) return;
+  const int64_t ld16 = (BWD ? 6 : 2) * (int64_t)a.F;
+  const uint16_t* tile = (const uint16_t*)a.buf + (int64_t)m0 * ld16;
+  auto pair = [&](int p) { return Operand{tile + (int64_t)p * a.F, ld16, nullptr, nD - m0, a.F}; };
+  GemmTile<Cfg> g;
+  if constexpr (BWD) {
+    const Operand Bg{a.WgT, a.d, nullptr, a.F}, Bu{a.WuT, a.d, nullptr, a.F};
+    g.run(pair(0), &Bg, 0, n0, a.F, lds);
+    g.run(pair(2), &Bu, 0, n0, a.F, lds, false);
+  } else {
+    const Operand Bd{a.Wd, a.d, nullptr, a.F};
+    g.run(pair(0), &Bd, 0, n0, a.F, lds);
+  }
+#pragma unroll
+  for (int j = 0; j < Cfg::TN; ++j) {
+    const int col = n0 + GemmTile<Cfg>::col_of(j);
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = m0 + GemmTile<Cfg>::row_of(i, e);
+        if (r < nD) {
+          const int64_t t = a.rows[r];
+          const float v = g.acc[0][i][j][e];
+          if constexpr (BWD) {
+            a.dX[t * a.d + col] = v;
+          } else {
+            if (a.out_bf16) ((uint16_t*)a.y)[t * a.d + col] = (uint16_t)f32_to_bf16_bits(v);
+            else ((float*)a.y)[t * a.d + col] = v;
+          }
+        }
+      }
+  }
+}
+
+// bf16 inputs: dense-row weight gradients from the bf16 planes on the
+// direct-to-LDS mainloop, written (not accumulated):
+//   C rows [0, F): dWgT = dG^T.x_D, [F, 2F): dWuT = dU^T.x_D, [2F, 3F): dWd = A^T.dY_D
+// A is a plane read as [K][M] (K = the dense rows), B the gathered x or dY
+// rows; K runs in chunks of WG_KCH rows (hi and lo pass each) so the 32-bit
+// byte offsets stay within one chunk; rows past n_D lie outside the A
+// operand's range and read as zeros.
+constexpr int WG_KCH = 1024;
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTH) void dense_rows_wgrad16_kernel(DenseRowsArgs a) {
+  __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
+  const int nD = *a.n_rows;
+  const int nbn = a.d / Cfg::BN;
+  const int tl = xcd_remap(blockIdx.x, gridDim.x);
+  const int bm = tl / nbn, bn = tl % nbn;
+  const int m0 = bm * Cfg::BM, n0 = bn * Cfg::BN;
+  const int part = m0 / a.F;                        // 0: dWgT, 1: dWuT, 2: dWd (tiles never straddle)
+  const int mp = m0 - part * a.F;
+  const int64_t ld16 = 6 * (int64_t)a.F;
+  const uint16_t* b16 = (const uint16_t*)a.buf;
+  const void* V = part == 2 ? a.dY : a.x;
+  typedef DmaTile<Cfg> Tile;
+  Tile g;
+  if (nD == 0) {
+    const Operand A{b16, ld16, nullptr, 0};
+    const Operand B{V, a.d, a.rows, a.T};
+    g.run(A, &B, mp, n0, 0, st0, st1);              // no K tiles: zeros
+  }
+  for (int k0 = 0; k0 < nD; k0 += WG_KCH) {
+    const int kn = min(WG_KCH, nD - k0);
+#pragma unroll
+    for (int lo = 0; lo < 2; ++lo) {
+      const Operand A{b16 + (int64_t)k0 * ld16 + (int64_t)(2 * part + lo) * a.F, ld16, nullptr, kn};
+      const Operand B{V, a.d, a.rows + k0, a.T};
+      g.run(A, &B, mp, n0, kn, st0, st1, k0 == 0 && lo == 0);
+    }
+  }
+  float* out = part == 0 ? a.dWgT : part == 1 ? a.dWuT : a.dWd;
+#pragma unroll
+  for (int j = 0; j < Cfg::TN; ++j) {
+    const int col = n0 + Tile::col_of(j);
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) out[(int64_t)(mp + Tile::row_of(i, e)) * a.d + col] = g.acc[0][i][j][e];
   }
 }
 
@@ -302,7 +442,7 @@ __global__ __launch_bounds__(256) void dense_rows_dbg_sum_kernel(DenseRowsArgs a
   const int nD = *a.n_rows;
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= a.F) return;
-  const int nc = (nD + 63) / 64;
+  const int nc = (nD + a.dbg_rows - 1) / a.dbg_rows;
   float s = 0.f;
   for (int c = 0; c < nc; ++c) s += a.dbg_part[(int64_t)c * a.F + n];
   a.dbg[n] = s;
@@ -319,10 +459,9 @@ template <> struct HybCfg<true> {
   using Act1 = GemmCfg<128, 128, 2, 2, OP_BF16_K, OP_BF16_K, 1>;
   using Act2S = GemmCfg<128, 64, 2, 2, OP_BF16_K, OP_BF16_K, 2>;
   using Act1S = GemmCfg<128, 64, 2, 2, OP_BF16_K, OP_BF16_K, 1>;
-  using Out = GemmCfg<64, 64, 2, 2, OP_F32S_K, OP_BF16_T>;
-  using WgradL = GemmCfg<128, 256, 2, 4, OP_F32S_T, OP_BF16_T>;   // F % 128 == 0, d % 256 == 0
-  using Wgrad = GemmCfg<64, 128, 2, 2, OP_F32S_T, OP_BF16_T>;
-  using WgradS = GemmCfg<64, 64, 2, 2, OP_F32S_T, OP_BF16_T>;
+  using Out16 = GemmCfg<64, 64, 2, 2, OP_BF16P_K, OP_BF16_T>;
+  using Wgrad16L = DmaCfg<256, 256, 2, 4, 1, false, true, true>;   // F % 256 == 0, d % 256 == 0
+  using Wgrad16S = DmaCfg<64, 64, 2, 2, 1, false, true, true>;
 };
 template <> struct HybCfg<false> {
   using Act2 = GemmCfg<128, 128, 2, 2, OP_F32_K, OP_F32_K, 2>;
@@ -330,7 +469,6 @@ template <> struct HybCfg<false> {
   using Act2S = GemmCfg<128, 64, 2, 2, OP_F32_K, OP_F32_K, 2>;
   using Act1S = GemmCfg<128, 64, 2, 2, OP_F32_K, OP_F32_K, 1>;
   using Out = GemmCfg<64, 64, 2, 2, OP_F32_K, OP_F32_T>;
-  using WgradL = GemmCfg<64, 128, 2, 2, OP_F32_T, OP_F32_T>;
   using Wgrad = GemmCfg<64, 128, 2, 2, OP_F32_T, OP_F32_T>;
   using WgradS = GemmCfg<64, 64, 2, 2, OP_F32_T, OP_F32_T>;
 };
@@ -388,17 +526,44 @@ struct ActLaunch<true, BWD> {
   }
 };
 
-template <bool BF16IN, bool BWD>
-static hipError_t dense_rows_t(const DenseRowsArgs& a, hipStream_t s) {
-  using C = HybCfg<BF16IN>;
-  ActLaunch<BF16IN, BWD>::go(a, s);
+template <class Cfg, bool BWD>
+static void launch_out16(const DenseRowsArgs& a, hipStream_t s) {
+  const int g = ((a.T + Cfg::BM - 1) / Cfg::BM) * (a.d / Cfg::BN);
+  if (g > 0) hipLaunchKernelGGL((dense_rows_out16_kernel<Cfg, BWD>), dim3(g), dim3(Cfg::NTH), 0, s, a);
+}
+
+template <class Cfg>
+static void launch_wgrad16(const DenseRowsArgs& a, hipStream_t s) {
+  const int g = (3 * a.F / Cfg::BM) * (a.d / Cfg::BN);
+  if (g > 0) hipLaunchKernelGGL((dense_rows_wgrad16_kernel<Cfg>), dim3(g), dim3(Cfg::NTH), 0, s, a);
+}
+
+// bf16 inputs: act kernel writing the bf16 planes (and, backward, the dbg
+// partials of its 128-row tiles), then the plane GEMMs
+template <bool BWD>
+static hipError_t dense_rows_bf16(DenseRowsArgs a, hipStream_t s) {
+  using C = HybCfg<true>;
+  static_assert(C::ActD2::BM == C::ActD2S::BM, "one dbg partial per act row tile");
+  a.dbg_rows = C::ActD2::BM;
+  ActLaunch<true, BWD>::go(a, s);
+  launch_out16<typename C::Out16, BWD>(a, s);
+  if constexpr (BWD) {
+    if (a.F % 256 == 0 && a.d % 256 == 0) launch_wgrad16<typename C::Wgrad16L>(a, s);
+    else launch_wgrad16<typename C::Wgrad16S>(a, s);
+    if (a.dbg) hipLaunchKernelGGL(dense_rows_dbg_sum_kernel, dim3((a.F + 255) / 256), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// fp32 inputs: the register-staged GEMMs on the fp32 intermediates
+template <bool BWD>
+static hipError_t dense_rows_f32(DenseRowsArgs a, hipStream_t s) {
+  using C = HybCfg<false>;
+  a.dbg_rows = 64;
+  ActLaunch<false, BWD>::go(a, s);
   launch_out<typename C::Out, BWD>(a, s);
   if constexpr (BWD) {
-    // 128-row tiles never straddle two of the three gradients when F % 128 == 0
-    // (128 x 256 measured 80 us faster than 64 x 128 at T = 16384, d = 2048,
-    // F = 5632 with 819 dense rows)
-    if (a.F % 128 == 0 && a.d % 256 == 0) launch_wgrad<typename C::WgradL>(a, s);
-    else if (a.d % 128 == 0) launch_wgrad<typename C::Wgrad>(a, s);
+    if (a.d % 128 == 0) launch_wgrad<typename C::Wgrad>(a, s);
     else launch_wgrad<typename C::WgradS>(a, s);
     if (a.dbg) {
       if (a.T > 0)
@@ -407,6 +572,12 @@ static hipError_t dense_rows_t(const DenseRowsArgs& a, hipStream_t s) {
     }
   }
   return hipGetLastError();
+}
+
+template <bool BF16IN, bool BWD>
+static hipError_t dense_rows_t(const DenseRowsArgs& a, hipStream_t s) {
+  if constexpr (BF16IN) return dense_rows_bf16<BWD>(a, s);
+  else return dense_rows_f32<BWD>(a, s);
 }
 
 hipError_t launch_dense_rows_fwd(int in_dt, const void* x, const void* WgT, const void* bg, const void* WuT,
