@@ -209,8 +209,15 @@ __device__ __forceinline__ void up_pass(const SpArgs& a, const UnionLds& L, char
     for (int i = 0; i < LDI; ++i) {
       const int q = tid + 256 * i;
       if (q < ROWS * 8) {
-        *(uint4*)(sw[0] + swz(q >> 3, q & 7)) = pre0[i];
-        if constexpr (NP == 2) *(uint4*)(sw[1] + swz(q >> 3, q & 7)) = pre1[i];
+        // two 8-byte stores per chunk: fewer bank conflicts in this swizzle
+        // than one 16-byte store
+        const int o = swz(q >> 3, q & 7);
+        *(uint2*)(sw[0] + o) = make_uint2(pre0[i].x, pre0[i].y);
+        *(uint2*)(sw[0] + o + 8) = make_uint2(pre0[i].z, pre0[i].w);
+        if constexpr (NP == 2) {
+          *(uint2*)(sw[1] + o) = make_uint2(pre1[i].x, pre1[i].y);
+          *(uint2*)(sw[1] + o + 8) = make_uint2(pre1[i].z, pre1[i].w);
+        }
       }
     }
   };
