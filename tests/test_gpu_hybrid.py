@@ -124,6 +124,18 @@ def test_hybrid_threshold_limits(torch, tw, tau_kind):
     check_full(w, got, tau)
 
 
+@pytest.mark.parametrize("d,f", [(128, 640), (256, 1280)], ids=["d128-f640", "d256-f1280"])
+def test_hybrid_all_dense_many_rows(torch, tw, d, f):
+    """Every row dense with more than 1024 of them: the dense-row weight
+    gradients run their K loop over the rows in two chunks (1024 + 76), on
+    the 64x64 (d = 128) and the 256x256 (d = 256, F = 1280) tiles."""
+    w = make_workload("hybrid", T=1100, d=d, f=f)
+    log(f"[hybrid] all dense T={w.T} d={w.d} f={w.f}")
+    got = run_train(torch, tw, w, -1)
+    assert got["nD"] == w.T
+    check_full(w, got, -1)
+
+
 def test_hybrid_no_bias_no_dbg(torch, tw):
     """Without the gate bias about half the gate values are positive; a
     threshold at half the width sends about half the rows to each branch."""
