@@ -16,4 +16,5 @@ from ._lib import (  # noqa: F401
     twell_relu_ffn_fwd, twell_relu_ffn_fwd_workspace, twell_relu_ffn_dense_fwd, twell_relu_ffn_dense_fwd_workspace,
     TwellCMat, alloc_twell_cmat, c_twell_cmat, twell_cmat_bytes, twell_compact, twell_expand,
     twell_ffn_bwd_compact_workspace, twell_ffn_bwd_hybrid_compact, twell_ffn_fwd_noalloc, NOALLOC_SCRATCH_BYTES,
+    twell_ffn_fwd_bounded_workspace, twell_ffn_fwd_bounded,
 )

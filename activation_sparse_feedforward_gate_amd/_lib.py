@@ -95,6 +95,9 @@ def lib() -> ctypes.CDLL:
         L.twell_ffn_bwd_hybrid_compact.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_cmat),
                                                    i32, ctypes.c_float, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.twell_ffn_fwd_noalloc.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_mat), i32, vp]
+        L.twell_ffn_fwd_bounded_workspace.argtypes = [P(c_twell_ffn_shape), i32, i32]
+        L.twell_ffn_fwd_bounded_workspace.restype = sz
+        L.twell_ffn_fwd_bounded.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
         L.twell_status_string.argtypes = [ctypes.c_int]
         L.twell_status_string.restype = ctypes.c_char_p
         L.twell_last_error.argtypes = []
@@ -104,7 +107,7 @@ def lib() -> ctypes.CDLL:
                      "twell_relu_ffn_fwd", "twell_relu_ffn_dense_fwd",
                      "twell_ffn_dense_fwd", "twell_ffn_dense_bwd",
                      "twell_gate_pack",
-                     "twell_sparse_up", "twell_sparse_down", "twell_ffn_fwd_noalloc"):
+                     "twell_sparse_up", "twell_sparse_down", "twell_ffn_fwd_noalloc", "twell_ffn_fwd_bounded"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -256,6 +259,19 @@ def twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, saved_h: Optional[TwellMat], de
                                ctypes.byref(sh) if sh is not None else None, dense_row_threshold,
                                _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
                                _stream(stream)))
+
+
+def twell_ffn_fwd_bounded_workspace(shape: c_twell_ffn_shape, tile_cap: int, union_cap: int) -> int:
+    return int(lib().twell_ffn_fwd_bounded_workspace(ctypes.byref(shape), int(tile_cap), int(union_cap)))
+
+
+def twell_ffn_fwd_bounded(shape, x, WgT, bg, WuT, Wd, y, tile_cap: int, union_cap: int, ws,
+                          n_over_blocks=None, stream=None) -> None:
+    """The capacity-bounded inference forward; n_over_blocks: optional device
+    int32 tensor of one element that receives the blocks computed per pair."""
+    _check(lib().twell_ffn_fwd_bounded(ctypes.byref(shape), _ptr(x), _ptr(WgT), _ptr(bg), _ptr(WuT), _ptr(Wd),
+                                       _ptr(y), int(tile_cap), int(union_cap), _ptr(n_over_blocks), _ptr(ws),
+                                       ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20        # TWELL_NOALLOC_SCRATCH_BYTES of include/twell.h

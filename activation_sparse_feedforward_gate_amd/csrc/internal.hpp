@@ -22,9 +22,11 @@ struct TwellView {
   int T, F, NT, NR;
   uint8_t* cnt;     // [T][NT]
   uint8_t* width;   // [NR][NT]
-  void* val;        // [NR][NT][64][16]
-  uint8_t* idx;     // [NR][NT][64][16]
+  void* val;        // [NR][NT][cap][16]
+  uint8_t* idx;     // [NR][NT][cap][16]
   uint64_t* mask;   // [T][NT] or null
+  int cap = 64;     // slots per tile in val and idx; a tile wider than cap keeps
+                    // its first cap slots (width still records the true width)
 };
 
 // Gate GEMM g = x.WgT^T + bg, h = ReLU(g), packed into TwELL in the epilogue
@@ -147,7 +149,10 @@ hipError_t launch_down_bf16(const float* v0, const float* v1, const void* W, con
 // union_ws_bytes(T, d, F).  *flag_out receives the device flag that is set when
 // an a value overflows fp16; the caller then runs the pattern kernels gated on
 // it (they recompute and overwrite y).
-size_t union_ws_bytes(int T, int d, int F);
+// ucap > 0: a holds ucap union positions per row (a multiple of 64, <= F);
+// a block whose union is longer, or whose TwELL tiles are wider than h.cap,
+// is computed per stored pair by the down kernel (h recomputed from WgT, bg).
+size_t union_ws_bytes(int T, int d, int F, int ucap = 0);
 // The leading part of that workspace the union lists alone use (lists,
 // counts, flag, slab unions): all the few-token path needs.
 size_t union_lists_ws_bytes(int T, int F);
@@ -178,7 +183,11 @@ hipError_t launch_decode_fwd(const void* x, const void* WgT, const void* bg, con
 hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int T, int d, int F,
                             const TwellView& h, const uint8_t* skip, void* ws, void* y, int out_dt,
                             int** flag_out, hipStream_t s, hipEvent_t ev_lists = nullptr,
-                            hipEvent_t ev_up = nullptr, bool slabs_ready = false);
+                            hipEvent_t ev_up = nullptr, bool slabs_ready = false, const void* WgT = nullptr,
+                            const void* bg = nullptr, int ucap = 0);
+// Writes to *out (device) the number of row blocks the last bounded forward
+// in ws (union_ws_bytes(T, d, F, ucap > 0)) computed per pair; 0 for ucap <= 0.
+hipError_t launch_union_over_count(int T, int F, void* ws, int ucap, int* out, hipStream_t s);
 // The union workspace's slab unions and fp16-overflow flag, for a gate GEMM
 // that writes the former and clears the latter (then launch_union_fwd runs
 // with slabs_ready and skip == nullptr).

@@ -160,6 +160,32 @@ size_t fwd_layout(const twell_ffn_shape* sh, bool training, void* ws, FwdWs* out
   return c.off;
 }
 
+// Workspace of the capacity-bounded forward (T > DECODE_T_MAX): the TwELL of
+// h with W slots per tile, then the union workspace whose a rows hold ucap
+// positions.  Few-token shapes take the ordinary inference layout.
+bool bounded_caps_ok(const twell_ffn_shape* sh, int32_t W, int32_t ucap) {
+  return W >= 4 && W <= GPU_C && W % 4 == 0 && ucap >= 64 && ucap <= sh->F && ucap % 64 == 0;
+}
+
+size_t bounded_layout(const twell_ffn_shape* sh, int32_t W, int32_t ucap, void* ws, FwdWs* out) {
+  if (few_token_path(sh, false)) return fwd_layout(sh, false, ws, out);
+  size_t parts[6];
+  cmat_parts(sh->T, sh->F, W, parts);
+  Carver c(ws);
+  FwdWs w{};
+  TwellView& v = w.h;
+  v.T = sh->T; v.F = sh->F; v.NT = sh->F / GPU_C; v.NR = (sh->T + GPU_R - 1) / GPU_R;
+  v.cap = W;
+  v.cnt = (uint8_t*)c.take(parts[0]);
+  v.width = (uint8_t*)c.take(parts[1]);
+  v.val = c.take(parts[2]);
+  v.idx = (uint8_t*)c.take(parts[3]);
+  v.mask = (uint64_t*)c.take(parts[4]);
+  w.uni = c.take(union_ws_bytes(sh->T, sh->d, sh->F, ucap));
+  if (out) *out = w;
+  return c.off;
+}
+
 // Workspace of the hybrid backward.
 struct BwdWs {
   uint8_t* flag;
@@ -331,6 +357,46 @@ twell_status twell_ffn_fwd(const twell_ffn_shape* sh, const void* x, const void*
                            const void* WuT, const void* Wd, void* y, twell_mat* saved_h,
                            int32_t dense_row_threshold, void* ws, size_t ws_bytes, hipStream_t stream) {
   return twell_ffn_fwd_ex(sh, x, WgT, bg, WuT, Wd, y, saved_h, dense_row_threshold, ws, ws_bytes, stream, nullptr, 0);
+}
+
+size_t twell_ffn_fwd_bounded_workspace(const twell_ffn_shape* sh, int32_t tile_cap, int32_t union_cap) {
+  if (!sh || check_shape(sh) != TWELL_OK || sh->in_dt != TWELL_BF16 || !bounded_caps_ok(sh, tile_cap, union_cap))
+    return 0;
+  return bounded_layout(sh, tile_cap, union_cap, nullptr, nullptr);
+}
+
+twell_status twell_ffn_fwd_bounded(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
+                                   const void* WuT, const void* Wd, void* y, int32_t tile_cap, int32_t union_cap,
+                                   int32_t* n_over_blocks, void* ws, size_t ws_bytes, hipStream_t stream) {
+  twell_status st = check_shape(sh);
+  if (st) return st;
+  if (sh->in_dt != TWELL_BF16) return fail(TWELL_EUNSUPPORTED, "the bounded forward takes bf16 inputs");
+  if (!bounded_caps_ok(sh, tile_cap, union_cap))
+    return fail(TWELL_EINVAL, "tile_cap=%d must be a multiple of 4 in 4..64 and union_cap=%d a multiple of 64 in "
+                "64..F=%d", tile_cap, union_cap, sh->F);
+  if (sh->T > 0 && (!x || !WgT || !WuT || !Wd || !y)) return fail(TWELL_EINVAL, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(WgT) || !aligned16(WuT) || !aligned16(Wd) || !aligned16(y) || !aligned16(bg))
+    return fail(TWELL_EINVAL, "tensors must be 16-byte aligned");
+  const size_t need = bounded_layout(sh, tile_cap, union_cap, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (few_token_path(sh, false) || sh->T == 0) {
+    st = twell_ffn_fwd_ex(sh, x, WgT, bg, WuT, Wd, y, nullptr, -1, ws, ws_bytes, stream, nullptr, 0);
+    if (st || !n_over_blocks) return st;
+    return hip_status(launch_union_over_count(0, sh->F, nullptr, 0, n_over_blocks, stream), "block count");
+  }
+  FwdWs w;
+  bounded_layout(sh, tile_cap, union_cap, ws, &w);
+  const int out_dt = sh->out_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
+  uint64_t* slabs = nullptr;
+  int* uflag = nullptr;
+  union_slabs_and_flag(sh->T, sh->F, w.uni, &slabs, &uflag);
+  hipError_t e = launch_gate_twell(DT_BF16, x, WgT, bg, sh->T, sh->d, sh->F, w.h, stream, slabs, uflag);
+  if (e != hipSuccess) return hip_status(e, "gate GEMM");
+  e = launch_union_fwd(x, WuT, Wd, sh->T, sh->d, sh->F, w.h, nullptr, w.uni, y, out_dt, nullptr, stream, nullptr,
+                       nullptr, true, WgT, bg, union_cap);
+  if (e != hipSuccess) return hip_status(e, "union up/down GEMMs");
+  if (n_over_blocks) e = launch_union_over_count(sh->T, sh->F, w.uni, union_cap, n_over_blocks, stream);
+  return hip_status(e, "block count");
 }
 
 size_t twell_ffn_bwd_workspace(const twell_ffn_shape* sh, int32_t dense_row_threshold) {

@@ -32,6 +32,7 @@ struct GateArgs {
   uint64_t* mask;
   uint64_t* slabs;   // nullable: union of each 64-row slab's masks, [ceil(T/64)][NT]
   int* flag;         // nullable: cleared by workgroup 0
+  int cap;           // slots per tile in val and idx (a wider tile keeps its first cap)
 };
 
 template <bool BF16IN>
@@ -239,18 +240,18 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void gate_twell_k
             }
             v = sdw[k * (STG / 4) + (rsel * 32 + (c & 31)) * 2 + (c >> 5)];
           }
-          const int64_t tbase = ((int64_t)((rtb >> 4) + k) * a.NT + j) * (64 * 16);
+          const int64_t tbase = ((int64_t)((rtb >> 4) + k) * a.NT + j) * (a.cap * 16);
           a.val[tbase + i] = v;
           a.idx[tbase + i] = (uint8_t)c;
         };
         // the first 64 slots of every tile of the batch, one per lane, then
-        // the rest of the wider tiles
+        // the rest of the wider tiles (up to the capacity)
 #pragma unroll
         for (int k = 0; k < NH; ++k)
-          if (lane < width[k] * 16) slot(k, lane);
+          if (lane < min(width[k], a.cap) * 16) slot(k, lane);
 #pragma unroll
         for (int k = 0; k < NH; ++k)
-          for (int i = lane + 64; i < width[k] * 16; i += 64) slot(k, i);
+          for (int i = lane + 64; i < min(width[k], a.cap) * 16; i += 64) slot(k, i);
 #pragma unroll
         for (int k = 0; k < NH; ++k) {
           const int rt0 = rtb + 16 * k;
@@ -302,7 +303,7 @@ static hipError_t launch_gate_cfg(const GateArgs& a, hipStream_t s) {
 hipError_t launch_gate_twell(int in_dt, const void* x, const void* WgT, const void* bg, int T,
                              int d, int F, const TwellView& out, hipStream_t s, uint64_t* slabs, int* flag) {
   GateArgs a{x, WgT, bg, T, d, F, F / 64, out.cnt, out.width, (float*)out.val, out.idx, out.mask,
-             in_dt == DT_BF16 ? slabs : nullptr, in_dt == DT_BF16 ? flag : nullptr};
+             in_dt == DT_BF16 ? slabs : nullptr, in_dt == DT_BF16 ? flag : nullptr, out.cap};
   const bool big = T >= 512 && F % 256 == 0;
   if (in_dt == DT_BF16) {
     if (!big) return launch_gate_cfg<GateSmallBf16, true>(a, s);

@@ -64,6 +64,12 @@ struct UnionArgs {
   float l1;
   _Float16* dU16;         // backward: dU over the union positions (dG goes to adense)
   const _Float16* Wu16;   // backward: fp16 copy of WuT (WgT's goes to Wd16)
+  // capacity-bounded forward
+  int hcap;               // slots per TwELL tile of h (64: the full form)
+  int ucap;               // row stride of adense: union positions a block may hold
+  uint8_t* bflag;         // [NBLK] or null: block b's TwELL or union exceeds its capacity
+  const void* WgT;        // gate weights and bias, to recompute h for such blocks
+  const void* bg;
 };
 
 __device__ __forceinline__ bool live(const UnionArgs& a, int t) {
@@ -98,6 +104,7 @@ __device__ __forceinline__ void union_list_block(const UnionArgs& a, const uint6
                                                  int* start, uint64_t* su) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int base = 0;
+  bool over = false;
   int* ul = a.ulist + (int64_t)b * a.F;
   const int s0 = b * (a.lrows / 64), s1 = min((a.T + 63) / 64, s0 + a.lrows / 64);
   for (int j0 = 0; j0 < a.NT; j0 += 256) {
@@ -116,6 +123,11 @@ __device__ __forceinline__ void union_list_block(const UnionArgs& a, const uint6
     }
     start[tid] = base + scan[tid] - c;
     su[tid] = u;
+    if (a.bflag && j < a.NT) {
+      // a tile of the block's rows wider than the TwELL capacity
+      const int r0 = b * (a.lrows / 16), r1 = min((a.T + 15) / 16, r0 + a.lrows / 16);
+      for (int r = r0; r < r1; ++r) over |= (int)a.hwidth[(int64_t)r * a.NT + j] > a.hcap;
+    }
     const int total = scan[255];
     __syncthreads();
     const int nj = min(256, a.NT - j0);
@@ -127,6 +139,11 @@ __device__ __forceinline__ void union_list_block(const UnionArgs& a, const uint6
     __syncthreads();                                   // scan, start and su are rewritten next
   }
   if (tid == 0) a.ucount[b] = base;
+  if (a.bflag) {
+    // or a union longer than adense's rows hold
+    const int ov = __syncthreads_or((int)over);
+    if (tid == 0) a.bflag[b] = (uint8_t)(ov || base > a.ucap);
+  }
 }
 
 __global__ __launch_bounds__(256) void union_list_kernel(UnionArgs a, const uint64_t* U) {
@@ -148,8 +165,10 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
   const int nb = a.ucount[b];
   const int p0 = pt * Cfg::BN;
   if (p0 >= nb) return;
+  if (a.bflag && a.bflag[b]) return;       // over capacity: the down kernel computes it per pair
   const int m0 = b * UB;
   const int* ul = a.ulist + (int64_t)b * a.F;
+  const int64_t hs = (int64_t)a.hcap * 16; // TwELL tile stride of h
 
   typedef DmaTile<Cfg> Tile;
   Tile g;
@@ -186,7 +205,7 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
   constexpr int NPRE = Cfg::SINGLE ? 0 : 4;
   const int grp = tid >> 4, gl = tid & 15;
   // first piece (slots 0-3) of the group's first NPRE (row tile, column tile)
-  // blocks; the whole 4 KB block is allocated, so the reads need no width check
+  // blocks; every tile holds at least 4 slots, so the reads need no width check
   constexpr int NRT = Cfg::BM / 16;        // TwELL row tiles of the block
   struct Piece { int w; float4 v; uint32_t i; };
   Piece pre[NPRE > 0 ? NPRE : 1];
@@ -203,8 +222,8 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
       if (rt * 16 < a.T) {
         const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
         pc.w = a.hwidth[blk];
-        pc.v = ((const float4*)(a.hval + blk * 1024))[gl];
-        pc.i = ((const uint32_t*)(a.hidx + blk * 1024))[gl];
+        pc.v = ((const float4*)(a.hval + blk * hs))[gl];
+        pc.i = ((const uint32_t*)(a.hidx + blk * hs))[gl];
       }
     }
   }
@@ -298,8 +317,8 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
       if (gl < pc.w * 4) scatter(hp, i, tjf + sj, rt, gl, pc.v, pc.i);
       const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
       for (int c = gl + 16; c < pc.w * 4; c += 16)
-        scatter(hp, i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
-                ((const uint32_t*)(a.hidx + blk * 1024))[c]);
+        scatter(hp, i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * hs))[c],
+                ((const uint32_t*)(a.hidx + blk * hs))[c]);
     }
     // (row tile i, column tile sj) of block q, stepped without a division
     int qi = (grp + NPRE * NG) / S, qs = grp + NPRE * NG - qi * S;
@@ -312,8 +331,8 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
       const int64_t blk = (int64_t)rt * a.NT + tjf + sj;
       const int w = wpre ? (int)wl[q] : (int)a.hwidth[blk];
       for (int c = gl; c < w * 4; c += 16)
-        scatter(hp, i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * 1024))[c],
-                ((const uint32_t*)(a.hidx + blk * 1024))[c]);
+        scatter(hp, i, tjf + sj, rt, c, ((const float4*)(a.hval + blk * hs))[c],
+                ((const uint32_t*)(a.hidx + blk * hs))[c]);
     }
     }
     __syncthreads();
@@ -358,7 +377,7 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
             const uint32_t pair = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                                   ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
             const uint32_t keep = 0u - (uint32_t)(wr && t0 + kr < a.T);
-            const uint32_t o = (((uint32_t)(t0 + kr) * (uint32_t)a.F + (uint32_t)(p & ~1)) & keep) | (a.spare & ~keep);
+            const uint32_t o = (((uint32_t)(t0 + kr) * (uint32_t)a.ucap + (uint32_t)(p & ~1)) & keep) | (a.spare & ~keep);
             *(uint32_t*)(a.adense + o) = pair;
           }
         }
@@ -597,7 +616,7 @@ __device__ __forceinline__ void down_union_tile(const UnionArgs& a, int b, int c
   const int m0 = b * UB, n0 = ct * Cfg::BN;
   typedef DmaTile<Cfg> Tile;
   Tile g;
-  const Operand A{a.adense, a.F, nullptr, a.T};
+  const Operand A{a.adense, a.ucap, nullptr, a.T};
   const Operand B{a.Wd16, a.d, a.ulist + (int64_t)b * a.F, a.F};
   g.run(A, &B, m0, n0, nb, st0, st1);
   if constexpr (TWO) {
@@ -623,47 +642,67 @@ __device__ __forceinline__ void down_union_tile(const UnionArgs& a, int b, int c
 }
 
 // The same y tile per stored pair in fp32, for the forward when the overflow
-// flag is set (a value of a, h or Wd beyond the fp16 range): for each live row
-// and each stored pair (n, h) in ascending neuron order, a = h * (x_t . WuT[n])
-// (bf16 products, fp32 sums, one fixed-order butterfly over the wave) or a = h
-// for the non-gated layer (WuT null), then y_t += a * Wd[n] over the tile's
-// columns (CPL per lane).  Every column tile recomputes its rows' dot
-// products: this path serves inputs outside the fp16 range, not speed.
+// flag is set (a value of a, h or Wd beyond the fp16 range) or when the block
+// is over capacity: for each live row and each stored pair (n, h) in
+// ascending neuron order, a = h * (x_t . WuT[n]) (bf16 products, fp32 sums,
+// one fixed-order butterfly over the wave) or a = h for the non-gated layer
+// (WuT null), then y_t += a * Wd[n] over the tile's columns (CPL per lane).
+// The pairs come from the TwELL slots, or, for a block over capacity (whose
+// tiles may have lost slots), from the row's mask with h = x_t . WgT[n] + bg[n]
+// recomputed the same way.  Every column tile recomputes its rows' dot
+// products: this path serves inputs outside the fp16 range or the capacities,
+// not speed.
+__device__ __forceinline__ float row_dot(const uint16_t* x, const uint16_t* w, int d, int lane) {
+  float p = 0.f;
+  for (int e = lane * 8; e < d; e += 512) {
+    const uint4 xv = *(const uint4*)(x + e);
+    const uint4 wv = *(const uint4*)(w + e);
+    const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w}, ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      p = fmaf(bf16_lo(xs[q]), bf16_lo(ws[q]), p);
+      p = fmaf(bf16_hi(xs[q]), bf16_hi(ws[q]), p);
+    }
+  }
+  return wave_sum(p);
+}
+
 template <int CPL>
 __device__ void down_fallback_tile(const UnionArgs& a, int b, int n0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const uint16_t* x = (const uint16_t*)a.x;
   const uint16_t* Wu = (const uint16_t*)a.WuT;
+  const uint16_t* Wg = (const uint16_t*)a.WgT;
   const uint16_t* Wd = (const uint16_t*)a.Wd;
+  const bool rec = a.bflag && a.bflag[b];
+  const int64_t hs = (int64_t)a.hcap * 16;
   const int c0 = n0 + lane * CPL;
   for (int r = wave; r < UB; r += nw) {
     const int t = b * UB + r;
     if (!live(a, t)) continue;                      // wave-uniform
+    const uint16_t* xt = x + (int64_t)t * a.d;
     float acc[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
     const int64_t tile0 = (int64_t)(t >> 4) * a.NT;
     for (int j = 0; j < a.NT; ++j) {
-      const int cnt = popc64(a.mask[(int64_t)t * a.NT + j]);
-      const int64_t sb = (tile0 + j) * 1024 + (t & 15);   // slot s of this row: sb + 16 s
+      uint64_t m = a.mask[(int64_t)t * a.NT + j];
+      const int cnt = popc64(m);
+      const int64_t sb = (tile0 + j) * hs + (t & 15);     // slot s of this row: sb + 16 s
       for (int s = 0; s < cnt; ++s) {
-        const float hv = a.hval[sb + 16 * s];
-        const int64_t n = (int64_t)j * 64 + a.hidx[sb + 16 * s];
-        float av = hv;
-        if (Wu) {
-          float p = 0.f;
-          for (int e = lane * 8; e < a.d; e += 512) {
-            const uint4 xv = *(const uint4*)(x + (int64_t)t * a.d + e);
-            const uint4 wv = *(const uint4*)(Wu + n * a.d + e);
-            const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w}, ws[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              p = fmaf(bf16_lo(xs[q]), bf16_lo(ws[q]), p);
-              p = fmaf(bf16_hi(xs[q]), bf16_hi(ws[q]), p);
-            }
-          }
-          av = hv * wave_sum(p);
+        float hv;
+        int64_t n;
+        if (rec) {
+          const int c = __builtin_ctzll(m);
+          m &= m - 1;
+          n = (int64_t)j * 64 + c;
+          hv = row_dot(xt, Wg + n * a.d, a.d, lane);
+          if (a.bg) hv += bf16_to_f32(((const uint16_t*)a.bg)[n]);
+        } else {
+          hv = a.hval[sb + 16 * s];
+          n = (int64_t)j * 64 + a.hidx[sb + 16 * s];
         }
+        const float av = Wu ? hv * row_dot(xt, Wu + n * a.d, a.d, lane) : hv;
         const uint16_t* wr = Wd + n * a.d + c0;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) acc[c] = fmaf(av, bf16_to_f32(wr[c]), acc[c]);
@@ -704,8 +743,17 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void down_union_k
   }
   for (int k = blockIdx.x >> 3; k < ntile; k += gridDim.x >> 3) {
     const int bi = k / nct;
+    if (!TWO && a.bflag && a.bflag[x + 8 * bi]) continue;   // workgroup-uniform
     down_union_tile<Cfg, TWO>(a, x + 8 * bi, k - bi * nct, st0, st1);
     __syncthreads();
+  }
+  if constexpr (!TWO) {
+    // blocks over capacity (bounded forward), per pair, after the GEMM tiles
+    if (a.bflag)
+      for (int k = blockIdx.x >> 3; k < ntile; k += gridDim.x >> 3) {
+        const int bi = k / nct;
+        if (a.bflag[x + 8 * bi]) down_fallback_tile<Cfg::BN / 64>(a, x + 8 * bi, (k - bi * nct) * Cfg::BN);
+      }
   }
 }
 
@@ -721,23 +769,26 @@ static size_t r256(size_t v) { return (v + 255) & ~(size_t)255; }
 size_t union_lists_ws_bytes(int T, int F) {
   const size_t nblk = (size_t)(T + UB - 1) / UB;
   const size_t nslab = (size_t)(T + 63) / 64;
-  return r256(nblk * F * 4 + nblk * 4) + 256 + r256(nslab * (F / 64) * 8);
+  return r256(nblk * F * 4 + nblk * 4) + 256 + r256(nslab * (F / 64) * 8) + r256(nblk);
 }
 
-size_t union_ws_bytes(int T, int d, int F) {
-  return union_lists_ws_bytes(T, F) + r256((size_t)T * F * 2 + 256) + (size_t)F * d * 2;
+size_t union_ws_bytes(int T, int d, int F, int ucap) {
+  if (ucap <= 0) ucap = F;
+  return union_lists_ws_bytes(T, F) + r256((size_t)T * ucap * 2 + 256) + (size_t)F * d * 2;
 }
 
 namespace {
 
 // Pointers into the union workspace (layout of union_ws_bytes).
 UnionArgs union_setup(const void* x, const void* WuT, const void* Wd, int T, int d, int F, const TwellView& h,
-                      const uint8_t* skip, void* ws, void* y, int out_dt, uint64_t** U) {
+                      const uint8_t* skip, void* ws, void* y, int out_dt, uint64_t** U, int ucap = 0) {
   const int nblk = (T + UB - 1) / UB;
   char* w = (char*)ws;
   UnionArgs a{};
   a.x = x; a.WuT = WuT; a.Wd = Wd; a.T = T; a.d = d; a.F = F; a.NT = F / 64;
   a.mask = h.mask; a.skip = skip; a.hval = (const float*)h.val; a.hidx = h.idx; a.hwidth = h.width;
+  a.hcap = h.cap;
+  a.ucap = ucap > 0 ? ucap : F;
   a.ulist = (int*)w;
   a.ucount = (int*)(w + (size_t)nblk * F * 4);
   w += r256((size_t)nblk * F * 4 + (size_t)nblk * 4);
@@ -745,9 +796,12 @@ UnionArgs union_setup(const void* x, const void* WuT, const void* Wd, int T, int
   w += 256;
   *U = (uint64_t*)w;
   w += r256((size_t)((T + 63) / 64) * a.NT * 8);
-  a.adense = (_Float16*)w;                 // [T][F] and one spare slot
-  a.spare = (uint32_t)((size_t)T * F);
-  w += r256((size_t)T * F * 2 + 256);
+  // block flags only where a capacity can be exceeded
+  if (ucap > 0) a.bflag = (uint8_t*)w;
+  w += r256((size_t)nblk);
+  a.adense = (_Float16*)w;                 // [T][ucap] and one spare slot
+  a.spare = (uint32_t)((size_t)T * a.ucap);
+  w += r256((size_t)T * a.ucap * 2 + 256);
   a.Wd16 = (const _Float16*)w;
   a.y = y; a.out_bf16 = out_dt == DT_BF16;
   a.lrows = UB;
@@ -761,6 +815,29 @@ void union_lists_launch(const UnionArgs& a, const uint64_t* U, hipStream_t s) {
 }
 
 }  // namespace
+
+// Number of row blocks over capacity in the bounded forward (one workgroup).
+__global__ __launch_bounds__(256) void count_flags_kernel(const uint8_t* f, int n, int* out) {
+  int c = 0;
+  for (int i = threadIdx.x; i < n; i += 256) c += f[i] != 0;
+  __shared__ int part[256];
+  part[threadIdx.x] = c;
+  __syncthreads();
+  for (int o = 128; o >= 1; o >>= 1) {
+    if ((int)threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = part[0];
+}
+
+hipError_t launch_union_over_count(int T, int F, void* ws, int ucap, int* out, hipStream_t s) {
+  uint64_t* U;
+  const TwellView none{};
+  const UnionArgs a = union_setup(nullptr, nullptr, nullptr, T, 0, F, none, nullptr, ws, nullptr, DT_F32, &U, ucap);
+  hipLaunchKernelGGL(count_flags_kernel, dim3(1), dim3(256), 0, s, (const uint8_t*)a.bflag, a.bflag ? (T + UB - 1) / UB : 0,
+                     out);
+  return hipGetLastError();
+}
 
 void union_slabs_and_flag(int T, int F, void* ws, uint64_t** slabs, int** flag) {
   uint64_t* U;
@@ -794,7 +871,8 @@ hipError_t launch_union_lists(int T, int F, const TwellView& h, void* ws, hipStr
 
 hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int T, int d, int F,
                             const TwellView& h, const uint8_t* skip, void* ws, void* y, int out_dt,
-                            int** flag_out, hipStream_t s, hipEvent_t ev_lists, hipEvent_t ev_up, bool slabs_ready) {
+                            int** flag_out, hipStream_t s, hipEvent_t ev_lists, hipEvent_t ev_up, bool slabs_ready,
+                            const void* WgT, const void* bg, int ucap) {
   if (T == 0) {
     if (ev_lists) (void)hipEventRecord(ev_lists, s);
     if (ev_up) (void)hipEventRecord(ev_up, s);
@@ -802,7 +880,9 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
   }
   const int nblk = (T + UB - 1) / UB;
   uint64_t* U;
-  const UnionArgs a = union_setup(x, WuT, Wd, T, d, F, h, skip, ws, y, out_dt, &U);
+  UnionArgs a = union_setup(x, WuT, Wd, T, d, F, h, skip, ws, y, out_dt, &U, ucap);
+  a.WgT = WgT;
+  a.bg = bg;
   if (flag_out) *flag_out = a.flag;
   {
     const int64_t n8 = (int64_t)F * d / 8;
@@ -861,6 +941,8 @@ hipError_t launch_union_bwd(const void* x, const void* dY, const void* WgT, cons
   UnionArgs a{};
   a.x = x; a.WuT = WuT; a.Wd = Wd; a.dY = dY; a.T = T; a.d = d; a.F = F; a.NT = F / 64;
   a.mask = h.mask; a.skip = skip; a.hval = (const float*)h.val; a.hidx = h.idx; a.hwidth = h.width;
+  a.hcap = 64;                              // the backward reads the full TwELL form
+  a.ucap = F;
   auto r = [](size_t v) { return (v + 255) & ~(size_t)255; };
   a.ulist = (int*)w;
   a.ucount = (int*)(w + (size_t)nblk * F * 4);

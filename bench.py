@@ -416,6 +416,30 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool, 
         twell_ws = ws_fwd_bytes + (tw.twell_mat_bytes(T, f)[0] + ws_bwd_bytes if training else 0)
         out["workspace_bytes"] = {"twell": int(twell_ws), "own_dense": int(dense_ws)}
 
+    caps = BOUNDED_CAPS.get(name)
+    if caps and bf and not training and not few_tokens:
+        # the capacity-bounded forward on the same inputs: its workspace against
+        # the full-capacity one and the own dense path's, and its time
+        Wc, Uc = caps
+        bws = tw.twell_ffn_fwd_bounded_workspace(shape, Wc, Uc)
+        wsb_ = torch.empty(bws, dtype=torch.uint8, device=dev)
+        yb = torch.empty_like(y)
+        nover = torch.zeros((1,), dtype=torch.int32, device=dev)
+
+        def bounded_step():
+            tw.twell_ffn_fwd_bounded(shape, x, WgT, bg, WuT, Wd, yb, Wc, Uc, wsb_, None, stream)
+        bms = _timed(bounded_step, steps, warmup, stream, warm_s)
+        tw.twell_ffn_fwd_bounded(shape, x, WgT, bg, WuT, Wd, yb, Wc, Uc, wsb_, nover, stream)
+        tw.twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, None, tau, wsf, stream)
+        torch.cuda.synchronize()
+        out["bounded_forward"] = {
+            "tile_cap": Wc, "union_cap": Uc, "ms_per_step": bms, "tokens_per_s": T / (bms * 1e-3),
+            "workspace_bytes": int(bws), "over_capacity_blocks": int(nover.item()),
+            "y_equals_full_forward": bool(torch.equal(yb, y))}
+        if "dense_baseline" in out:
+            out["bounded_forward"]["speedup_vs_dense"] = out["dense_baseline"]["ms_per_step"] / bms
+            out["bounded_forward"]["workspace_vs_own_dense"] = bws / max(1, out["workspace_bytes"]["own_dense"])
+        del wsb_
     if training:
         # state a layer keeps between its forward and its backward: TwELL of h
         # (capacity 64, or compact with capacity W), against the own dense
@@ -519,6 +543,13 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool, 
     return out
 
 
+# capacities (tile_cap, union_cap) of the bounded forward per workload: the
+# largest per-(row, tile) count of these inputs over every token is 8 (1.5b)
+# and 7 (2b), the largest 128-token block union 43.8% and 27.3% of d_ff; the
+# union capacity is that rounded up to a multiple of 64 with at least 1.5% of
+# d_ff to spare
+BOUNDED_CAPS = {"1.5b": (8, 2560), "2b": (8, 2816)}
+
 # the workloads the default run reports beside the headline, as (name, decode)
 EXTRA_WORKLOADS = [("1.5b", False), ("0.5b", False), ("2b", True), ("hybrid", False)]
 
@@ -553,7 +584,7 @@ def main() -> int:
             out["config"][k] = r[k]
     for k in ("stages_ms", "roofline", "stage_roofline", "dense_baseline", "speedup_vs_dense",
               "dense_vs_sparse_rel_diff", "workspace_bytes", "cold_cache_ms_per_step", "library_gemm",
-              "saved_state_bytes", "compact_twell", "stage_note"):
+              "saved_state_bytes", "compact_twell", "stage_note", "bounded_forward"):
         if k in r:
             out[k] = r[k]
     if not args.no_cpu:

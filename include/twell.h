@@ -289,6 +289,39 @@ twell_status twell_ffn_fwd_ex(const twell_ffn_shape *sh, const void *x, const vo
                               hipEvent_t *stage_events, int32_t n_events);
 
 /*
+ * Capacity-bounded inference forward (intellectnews.ru TwELL article, section
+ * "Слитые CUDA-ядра для инференса и гибрид для обучения": intermediates are
+ * not written to global memory beyond need; gate.com ES / ID, first
+ * paragraph: lower peak memory).  The same layer and the same kernels as
+ * twell_ffn_fwd for bf16 inputs, with the two per-call buffers that grow with
+ * T x F sized by capacities the caller picks instead of for the worst case:
+ *   tile_cap   slots per 16 x 64 TwELL tile of h (a multiple of 4, 4..64; the
+ *              full form has 64): h takes 5 * tile_cap / 64 bytes per (t, n)
+ *              instead of 5
+ *   union_cap  union positions per 128-token block that the fp16 buffer of
+ *              a = h * u holds (a multiple of 64, 64..F): 2 * union_cap bytes
+ *              per token instead of 2 * F
+ * A 128-token block with a tile wider than tile_cap, or with more than
+ * union_cap neurons active in its tokens, is computed per stored pair in fp32
+ * inside the down-projection, with h recomputed from x, WgT and bg for its
+ * pairs (the mask keeps every pair): exact for any input, slow for such
+ * blocks.  The caller picks the capacities from its activation statistics
+ * (e.g. the largest per-tile count and block union seen in calibration).
+ *   n_over_blocks  NULL, or a device int32 that receives the number of
+ *                  128-token blocks computed per pair (0: every block fit)
+ *   Other arguments as for twell_ffn_fwd with saved_h NULL and
+ *   dense_row_threshold < 0.  bf16 inputs only (EUNSUPPORTED otherwise);
+ *   EINVAL for capacities outside the ranges above.  For T <= 256 the call is
+ *   twell_ffn_fwd's few-token path, whose workspace is small already.
+ *   ws, ws_bytes  at least twell_ffn_fwd_bounded_workspace(sh, tile_cap,
+ *   union_cap) bytes (0 for an invalid shape or capacities).
+ */
+size_t twell_ffn_fwd_bounded_workspace(const twell_ffn_shape *sh, int32_t tile_cap, int32_t union_cap);
+twell_status twell_ffn_fwd_bounded(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
+                                   const void *WuT, const void *Wd, void *y, int32_t tile_cap, int32_t union_cap,
+                                   int32_t *n_over_blocks, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * The three stages of the forward, callable one by one: the same layer as
  * twell_ffn_fwd, computed by the per-pair kernels that twell_ffn_fwd keeps
  * for fp32 inputs.  For bf16 inputs

@@ -1,0 +1,200 @@
+"""GPU parity of the capacity-bounded inference forward (twell_ffn_fwd_bounded)
+against the CPU oracle and against the ordinary forward.
+
+* Capacities that every block fits: no block is computed per pair and y is
+  bit-identical to twell_ffn_fwd's (the same kernels and summation order;
+  only the strides of h and of a differ).
+* Capacities that some or all blocks exceed (a TwELL tile wider than
+  tile_cap, a block union longer than union_cap): those blocks are computed
+  per stored pair in fp32 with h recomputed; y within relative Frobenius error
+  1e-3 of the float64 oracle, and the reported count of such blocks equals
+  the oracle's where the case is built away from the zero band.
+Full-size workloads run with the capacities the benchmark uses.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from workloads import make_workload, round_bf16
+
+from gpu_util import log, rel_fro, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    assert _t.cuda.is_available(), "GPU tests need a GPU"
+    return _t
+
+
+@pytest.fixture(scope="module")
+def tw():
+    import activation_sparse_feedforward_gate_amd as _tw
+    _tw.lib()
+    return _tw
+
+
+def _dev(w):
+    return tuple(to_dev(a, "bf16") for a in (w.x, w.WgT, w.bg, w.WuT, w.Wd))
+
+
+def run_bounded(torch, tw, w, W, U, out_dt="f32"):
+    od = tw.TWELL_BF16 if out_dt == "bf16" else tw.TWELL_F32
+    shape = tw.ffn_shape(w.T, w.d, w.f, tw.TWELL_BF16, od)
+    nbytes = tw.twell_ffn_fwd_bounded_workspace(shape, W, U)
+    assert nbytes > 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty((w.T, w.d), dtype=torch.bfloat16 if out_dt == "bf16" else torch.float32, device="cuda")
+    cnt = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    x, WgT, bg, WuT, Wd = _dev(w)
+    tw.twell_ffn_fwd_bounded(shape, x, WgT, bg, WuT, Wd, y, W, U, ws, n_over_blocks=cnt)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy(), int(cnt.item())
+
+
+def run_full(torch, tw, w, out_dt="f32"):
+    od = tw.TWELL_BF16 if out_dt == "bf16" else tw.TWELL_F32
+    shape = tw.ffn_shape(w.T, w.d, w.f, tw.TWELL_BF16, od)
+    ws = torch.empty(max(1, tw.twell_ffn_fwd_workspace(shape)), dtype=torch.uint8, device="cuda")
+    y = torch.empty((w.T, w.d), dtype=torch.bfloat16 if out_dt == "bf16" else torch.float32, device="cuda")
+    x, WgT, bg, WuT, Wd = _dev(w)
+    tw.twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, None, -1, ws)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy()
+
+
+def block_stats(g, T, f):
+    """Largest per-(row, tile) count and per-128-token-block union sizes of
+    the pattern g > 0."""
+    pos = g > 0
+    cnt = pos.reshape(T, f // 64, 64).sum(axis=2)
+    unions = [int(pos[b:b + 128].any(axis=0).sum()) for b in range(0, T, 128)]
+    tilemax = [int(cnt[b:b + 128].max()) if cnt[b:b + 128].size else 0 for b in range(0, T, 128)]
+    return tilemax, unions
+
+
+def check_y(w, y, rows=None):
+    rows = np.arange(w.T) if rows is None else rows
+    ref = O.ffn_fwd_rows(w.x, w.WgT, w.bg, w.WuT, w.Wd, rows)
+    err = rel_fro(y[rows], ref["y"])
+    log(f"   y rel-Frobenius error {err:.3e} (tol {TOL:g}) over {len(rows)} rows")
+    assert err <= TOL, err
+    return ref
+
+
+def _pattern(w):
+    return O.ffn_fwd_rows(w.x, w.WgT, w.bg, w.WuT, w.Wd, np.arange(w.T))["g"]
+
+
+@pytest.mark.parametrize("name,kw", [("0.5b", dict(T=1000, d=256, f=1024)), ("2b", dict(T=777, d=384, f=1536))])
+def test_bounded_fits_equals_full_forward(torch, tw, name, kw):
+    w = make_workload(name, **kw)
+    tilemax, unions = block_stats(_pattern(w), w.T, w.f)
+    W = min(64, (max(tilemax) + 1 + 3) // 4 * 4)
+    U = min(w.f, (max(unions) + 64 + 63) // 64 * 64)
+    log(f"[bounded] {name} T={w.T} d={w.d} f={w.f} caps W={W} U={U} (max tile count {max(tilemax)}, "
+        f"max union {max(unions)})")
+    y, n_over = run_bounded(torch, tw, w, W, U)
+    assert n_over == 0
+    y_full = run_full(torch, tw, w)
+    assert np.array_equal(y, y_full), np.abs(y - y_full).max()
+    check_y(w, y)
+
+
+def test_bounded_tile_overflow(torch, tw):
+    """tile_cap = 4 at 3% density over 1024 neurons: some blocks hold a row
+    with more than 4 entries in one tile and are computed per pair."""
+    w = make_workload("0.5b", T=1000, d=256, f=1024)
+    tilemax, unions = block_stats(_pattern(w), w.T, w.f)
+    log(f"[bounded] tile overflow: per-block max tile count {tilemax}")
+    assert max(tilemax) >= 6
+    y, n_over = run_bounded(torch, tw, w, 4, w.f)
+    log(f"   blocks over capacity: {n_over} of {len(tilemax)}")
+    assert n_over >= sum(t >= 6 for t in tilemax)        # counts of 6+ are far from the zero band's reach
+    check_y(w, y)
+
+
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_bounded_union_overflow_everywhere(torch, tw, out_dt):
+    """union_cap = 64 below every block's union: the whole layer is computed
+    per pair, with a ragged last block (T = 600)."""
+    w = make_workload("2b", T=600, d=256, f=1024)
+    tilemax, unions = block_stats(_pattern(w), w.T, w.f)
+    log(f"[bounded] union overflow, out {out_dt}: unions {unions}")
+    assert min(unions) > 128
+    y, n_over = run_bounded(torch, tw, w, 64, 64, out_dt)
+    assert n_over == len(unions)
+    if out_dt == "bf16":
+        ref = O.ffn_fwd_rows(w.x, w.WgT, w.bg, w.WuT, w.Wd, np.arange(w.T))
+        err = rel_fro(y, ref["y"])
+        log(f"   y rel-Frobenius error {err:.3e}")
+        assert err <= 4e-3                               # one bf16 rounding of y
+    else:
+        check_y(w, y)
+
+
+def test_bounded_mixed_blocks(torch, tw):
+    """Odd 128-token blocks get x scaled up, so their unions are far larger
+    than the even blocks'; union_cap between the two sends exactly the odd
+    blocks down the per-pair path while the even ones take the GEMMs in the
+    same launches."""
+    w = make_workload("1.5b", T=1024 + 77, d=256, f=2048)
+    for b0 in range(128, w.T, 256):
+        w.x[b0:b0 + 128] = round_bf16(w.x[b0:b0 + 128] * np.float32(3.0))
+    tilemax, unions = block_stats(_pattern(w), w.T, w.f)
+    even, odd = unions[0::2], unions[1::2]
+    log(f"[bounded] mixed: even unions {even}, odd unions {odd}")
+    U = (max(even) + 64 + 63) // 64 * 64
+    assert max(even) + 64 <= U < min(odd) - 64                # away from the boundary
+    y, n_over = run_bounded(torch, tw, w, 64, U)
+    assert n_over == len(odd)
+    check_y(w, y)
+
+
+def test_bounded_with_fp16_overflow(torch, tw):
+    """a beyond the fp16 range sends every tile down the per-pair path; the
+    blocks over the tile capacity recompute h there."""
+    w = make_workload("0.5b", T=300, d=256, f=1024)
+    w.x[:] = round_bf16(w.x * np.float32(80.0))
+    w.bg[:] = round_bf16(w.bg * np.float32(80.0))
+    ref = O.ffn_fwd_rows(w.x, w.WgT, w.bg, w.WuT, w.Wd, np.arange(w.T))
+    assert np.abs(ref["a"]).max() > 65504.0
+    tilemax, _ = block_stats(ref["g"], w.T, w.f)
+    log(f"[bounded] fp16 overflow with tile cap 4: per-block max tile count {tilemax}")
+    y, n_over = run_bounded(torch, tw, w, 4, w.f)
+    assert n_over >= sum(t >= 6 for t in tilemax)
+    check_y(w, y)
+
+
+def test_bounded_few_tokens_and_empty(torch, tw):
+    w = make_workload("2b", T=64, d=256, f=1024)
+    log("[bounded] few-token path")
+    y, n_over = run_bounded(torch, tw, w, 8, 256)
+    assert n_over == 0
+    assert np.array_equal(y, run_full(torch, tw, w))
+    w0 = make_workload("2b", T=0, d=256, f=1024)
+    y0, n0 = run_bounded(torch, tw, w0, 8, 256)
+    assert y0.shape == (0, 256) and n0 == 0
+
+
+# capacities of the benchmark's bounded forward (per-tile counts and block
+# unions of these inputs measured with the oracle over every token)
+BENCH_CAPS = {"1.5b": (8, 2560), "2b": (8, 2816)}
+
+
+@pytest.mark.parametrize("name", sorted(BENCH_CAPS))
+def test_bounded_full_size(torch, tw, name):
+    w = make_workload(name)
+    W, U = BENCH_CAPS[name]
+    log(f"[bounded] full size {name} T={w.T} d={w.d} f={w.f} caps W={W} U={U}")
+    y, n_over = run_bounded(torch, tw, w, W, U)
+    assert n_over == 0
+    y_full = run_full(torch, tw, w)
+    assert np.array_equal(y, y_full), np.abs(y - y_full).max()
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([rng.choice(w.T, size=256, replace=False), np.arange(w.T - 16, w.T)]))
+    check_y(w, y, rows)

@@ -277,3 +277,36 @@ def test_bwd_shape_limit_of_dense_branch_buffer():
     st = L.twell_ffn_bwd_hybrid(ctypes.byref(sh), 16, 16, None, 16, 16, 16, ctypes.byref(h), 10, 16, 16, 16, 16,
                                 None, None, 4096, 1, None)
     assert st == tw.TWELL_EWORKSPACE
+
+
+def _call_bounded(shape, **kw):
+    L = tw.lib()
+    args = dict(x=16, WgT=32, bg=None, WuT=48, Wd=64, y=80, W=8, U=256, cnt=None, ws=None, ws_bytes=0)
+    args.update(kw)
+    return L.twell_ffn_fwd_bounded(ctypes.byref(shape), args["x"], args["WgT"], args["bg"], args["WuT"], args["Wd"],
+                                   args["y"], args["W"], args["U"], args["cnt"], args["ws"], args["ws_bytes"], None)
+
+
+def test_bounded_fwd_workspace_and_argument_errors():
+    T, d, F = 4096, 256, 1024
+    sh = tw.ffn_shape(T, d, F, tw.TWELL_BF16, tw.TWELL_F32)
+    full = tw.twell_ffn_fwd_workspace(sh)
+    w8 = tw.twell_ffn_fwd_bounded_workspace(sh, 8, 256)
+    w64 = tw.twell_ffn_fwd_bounded_workspace(sh, 64, F)
+    # capacities at their maxima: the ordinary forward's buffers (plus the block flags)
+    assert full <= w64 <= full + 1024
+    # h shrinks by 5 * (64 - 8) / 64 bytes per (t, n) and a by 2 * (F - 256) bytes per token, to 256-byte rounding
+    saved = 5 * T * F * (64 - 8) // 64 + 2 * T * (F - 256)
+    assert abs((w64 - w8) - saved) <= 2048
+    for W, U in [(0, 256), (3, 256), (6, 256), (68, 256), (8, 0), (8, 100), (8, F + 64)]:
+        assert tw.twell_ffn_fwd_bounded_workspace(sh, W, U) == 0
+        assert _call_bounded(sh, W=W, U=U, ws=256, ws_bytes=w8) == tw.TWELL_EINVAL
+    assert tw.twell_ffn_fwd_bounded_workspace(tw.ffn_shape(T, d, F, tw.TWELL_F32, tw.TWELL_F32), 8, 256) == 0
+    assert _call_bounded(tw.ffn_shape(T, d, F, tw.TWELL_F32, tw.TWELL_F32)) == tw.TWELL_EUNSUPPORTED
+    assert _call_bounded(sh, x=None, ws=256, ws_bytes=w8) == tw.TWELL_EINVAL
+    assert _call_bounded(sh, x=24, ws=256, ws_bytes=w8) == tw.TWELL_EINVAL          # misaligned
+    assert _call_bounded(sh, ws=256, ws_bytes=w8 - 1) == tw.TWELL_EWORKSPACE
+    assert _call_bounded(sh, ws=None, ws_bytes=w8) == tw.TWELL_EWORKSPACE
+    # few tokens: the ordinary few-token workspace
+    small = tw.ffn_shape(64, d, F, tw.TWELL_BF16, tw.TWELL_F32)
+    assert tw.twell_ffn_fwd_bounded_workspace(small, 8, 256) == tw.twell_ffn_fwd_workspace(small)
