@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--decode", action="store_true", help="use the workload's decode-shaped pass")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
+    ap.add_argument("--no-bounded", action="store_true", help="skip the capacity-bounded forward")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-extras", action="store_true", help="skip the short runs of the other workloads")
     ap.add_argument("--cold-iters", type=int, default=5,
@@ -416,7 +417,7 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool, 
         twell_ws = ws_fwd_bytes + (tw.twell_mat_bytes(T, f)[0] + ws_bwd_bytes if training else 0)
         out["workspace_bytes"] = {"twell": int(twell_ws), "own_dense": int(dense_ws)}
 
-    caps = BOUNDED_CAPS.get(name)
+    caps = None if args.no_bounded else BOUNDED_CAPS.get(name)
     if caps and bf and not training and not few_tokens:
         # the capacity-bounded forward on the same inputs: its workspace against
         # the full-capacity one and the own dense path's, and its time
