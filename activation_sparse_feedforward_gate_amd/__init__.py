@@ -17,4 +17,5 @@ from ._lib import (  # noqa: F401
     TwellCMat, alloc_twell_cmat, c_twell_cmat, twell_cmat_bytes, twell_compact, twell_expand,
     twell_ffn_bwd_compact_workspace, twell_ffn_bwd_hybrid_compact, twell_ffn_fwd_noalloc, NOALLOC_SCRATCH_BYTES,
     twell_ffn_fwd_bounded_workspace, twell_ffn_fwd_bounded,
+    twell_ffn_fwd_compact_workspace, twell_ffn_fwd_compact,
 )

@@ -90,11 +90,15 @@ def lib() -> ctypes.CDLL:
         L.twell_cmat_bytes.restype = sz
         L.twell_compact.argtypes = [P(c_twell_mat), P(c_twell_cmat), vp]
         L.twell_expand.argtypes = [P(c_twell_cmat), P(c_twell_mat), vp]
-        L.twell_ffn_bwd_compact_workspace.argtypes = [P(c_twell_ffn_shape), i32]
+        L.twell_ffn_bwd_compact_workspace.argtypes = [P(c_twell_ffn_shape), i32, i32]
         L.twell_ffn_bwd_compact_workspace.restype = sz
         L.twell_ffn_bwd_hybrid_compact.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_cmat),
                                                    i32, ctypes.c_float, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.twell_ffn_fwd_noalloc.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_mat), i32, vp]
+        L.twell_ffn_fwd_compact_workspace.argtypes = [P(c_twell_ffn_shape), i32]
+        L.twell_ffn_fwd_compact_workspace.restype = sz
+        L.twell_ffn_fwd_compact.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_cmat), i32, vp,
+                                            sz, vp]
         L.twell_ffn_fwd_bounded_workspace.argtypes = [P(c_twell_ffn_shape), i32, i32]
         L.twell_ffn_fwd_bounded_workspace.restype = sz
         L.twell_ffn_fwd_bounded.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
@@ -107,7 +111,8 @@ def lib() -> ctypes.CDLL:
                      "twell_relu_ffn_fwd", "twell_relu_ffn_dense_fwd",
                      "twell_ffn_dense_fwd", "twell_ffn_dense_bwd",
                      "twell_gate_pack",
-                     "twell_sparse_up", "twell_sparse_down", "twell_ffn_fwd_noalloc", "twell_ffn_fwd_bounded"):
+                     "twell_sparse_up", "twell_sparse_down", "twell_ffn_fwd_noalloc", "twell_ffn_fwd_bounded",
+                     "twell_ffn_fwd_compact"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -349,8 +354,21 @@ def twell_expand(c: TwellCMat, full: TwellMat, stream=None) -> None:
     _check(lib().twell_expand(ctypes.byref(cm), ctypes.byref(fm), _stream(stream)))
 
 
-def twell_ffn_bwd_compact_workspace(shape: c_twell_ffn_shape, dense_row_threshold: int) -> int:
-    return int(lib().twell_ffn_bwd_compact_workspace(ctypes.byref(shape), int(dense_row_threshold)))
+def twell_ffn_bwd_compact_workspace(shape: c_twell_ffn_shape, dense_row_threshold: int, W: int) -> int:
+    return int(lib().twell_ffn_bwd_compact_workspace(ctypes.byref(shape), int(dense_row_threshold), int(W)))
+
+
+def twell_ffn_fwd_compact_workspace(shape: c_twell_ffn_shape, W: int) -> int:
+    return int(lib().twell_ffn_fwd_compact_workspace(ctypes.byref(shape), int(W)))
+
+
+def twell_ffn_fwd_compact(shape, x, WgT, bg, WuT, Wd, y, saved: TwellCMat, dense_row_threshold: int, ws,
+                          stream=None) -> None:
+    """The hybrid training forward saving h straight into the compact form."""
+    cm = saved.c()
+    _check(lib().twell_ffn_fwd_compact(ctypes.byref(shape), _ptr(x), _ptr(WgT), _ptr(bg), _ptr(WuT), _ptr(Wd),
+                                       _ptr(y), ctypes.byref(cm), int(dense_row_threshold), _ptr(ws),
+                                       ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
 
 
 def twell_ffn_bwd_hybrid_compact(shape, x, WgT, bg, WuT, Wd, dY, saved: TwellCMat, dense_row_threshold: int,

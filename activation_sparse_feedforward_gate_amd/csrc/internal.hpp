@@ -101,6 +101,9 @@ struct CompactArgs {
   uint8_t* ovf;
 };
 hipError_t launch_compact(const CompactArgs& a, bool expand, hipStream_t s);
+// The compact arrays (ccnt, cwidth, ovf, W, T, NT, ntiles) after a gate GEMM
+// packed into them directly: ovf[t] = some ccnt[t][j] > W, widths clamped to W.
+hipError_t launch_compact_finish(const CompactArgs& a, hipStream_t s);
 
 // Row classification of the hybrid format: flag[t] = (sum_j cnt[t][j] > tau)
 // or force[t] (force may be null);

@@ -116,6 +116,15 @@ TwellView view_of(const twell_mat* m) {
   return v;
 }
 
+// The compact form read in place: the same arrays with W slots per tile.
+TwellView view_of(const twell_cmat* m) {
+  TwellView v;
+  v.T = m->T; v.F = m->F; v.NT = m->F / GPU_C; v.NR = (m->T + GPU_R - 1) / GPU_R;
+  v.cnt = m->cnt; v.width = m->width; v.val = m->val; v.idx = m->idx; v.mask = m->mask;
+  v.cap = m->W;
+  return v;
+}
+
 // Workspace of the forward: one TwELL (fp32 values, with mask; with saved_h
 // only its value array is used, for a); training adds the row classification
 // and the dense rows' activation buffer.
@@ -202,10 +211,10 @@ struct BwdWs {
   void* uni;         // bf16 inputs: union lists of the sparse rows
 };
 
-size_t bwd_layout(const twell_ffn_shape* sh, int32_t tau, void* ws, BwdWs* out) {
+size_t bwd_layout(const twell_ffn_shape* sh, int32_t tau, void* ws, BwdWs* out, int cap = GPU_C) {
   const int64_t T = sh->T, F = sh->F;
   const int64_t NR = (T + GPU_R - 1) / GPU_R, NT = F / GPU_C;
-  const size_t slots = (size_t)(NR * NT * GPU_C * GPU_R);
+  const size_t slots = (size_t)(NR * NT * cap * GPU_R);   // the value arrays follow h's capacity
   // a sparse row holds at most min(F, tau) pairs
   const int64_t per_row = tau < 0 ? 0 : (tau < F ? tau : F);
   Carver c(ws);
@@ -515,7 +524,9 @@ static CompactArgs compact_args(const twell_mat* full, const twell_cmat* c) {
   CompactArgs a{};
   a.T = c->T; a.NT = c->F / GPU_C; a.W = c->W;
   a.ntiles = (int64_t)((c->T + GPU_R - 1) / GPU_R) * a.NT;
-  a.cnt = full->cnt; a.width = full->width; a.val = (float*)full->val; a.idx = full->idx; a.mask = full->mask;
+  if (full) {   // null: the compact arrays alone (after a gate GEMM packed into them)
+    a.cnt = full->cnt; a.width = full->width; a.val = (float*)full->val; a.idx = full->idx; a.mask = full->mask;
+  }
   a.ccnt = c->cnt; a.cwidth = c->width; a.cval = c->val; a.cidx = c->idx; a.cmask = c->mask; a.ovf = c->ovf;
   return a;
 }
@@ -547,23 +558,9 @@ twell_status twell_expand(const twell_cmat* in, twell_mat* full, hipStream_t str
 
 // The compact backward's workspace: the hybrid backward's, then a
 // capacity-64 value and index array that the stored slots are moved into.
-static size_t bwd_compact_layout(const twell_ffn_shape* sh, int32_t tau, void* ws, BwdWs* out, float** val,
-                                 uint8_t** idx) {
-  size_t parts[5];
-  mat_parts(sh->T, sh->F, GPU_R, GPU_C, TWELL_F32, parts);
-  Carver c(ws);
-  c.take(bwd_layout(sh, tau, nullptr, nullptr));
-  if (ws) bwd_layout(sh, tau, ws, out);
-  float* v = (float*)c.take(parts[2]);
-  uint8_t* ix = (uint8_t*)c.take(parts[3]);
-  if (val) *val = v;
-  if (idx) *idx = ix;
-  return c.off;
-}
-
-size_t twell_ffn_bwd_compact_workspace(const twell_ffn_shape* sh, int32_t dense_row_threshold) {
-  if (!sh || check_shape(sh) != TWELL_OK) return 0;
-  return bwd_compact_layout(sh, dense_row_threshold, nullptr, nullptr, nullptr, nullptr);
+size_t twell_ffn_bwd_compact_workspace(const twell_ffn_shape* sh, int32_t dense_row_threshold, int32_t W) {
+  if (!sh || check_shape(sh) != TWELL_OK || W < 1 || W > GPU_C) return 0;
+  return bwd_layout(sh, dense_row_threshold, nullptr, nullptr, W);
 }
 
 twell_status twell_ffn_bwd_hybrid_compact(const twell_ffn_shape* sh, const void* x, const void* WgT,
@@ -579,24 +576,87 @@ twell_status twell_ffn_bwd_hybrid_compact(const twell_ffn_shape* sh, const void*
   if (st) return st;
   if (saved->T != sh->T || saved->F != sh->F)
     return fail(TWELL_EINVAL, "saved must be T x F (T=%d F=%d)", sh->T, sh->F);
-  const size_t need = bwd_compact_layout(sh, dense_row_threshold, nullptr, nullptr, nullptr, nullptr);
+  const size_t need = bwd_layout(sh, dense_row_threshold, nullptr, nullptr, saved->W);
   if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
-
   BwdWs w;
-  float* val = nullptr;
-  uint8_t* idx = nullptr;
-  bwd_compact_layout(sh, dense_row_threshold, ws, &w, &val, &idx);
-  // capacity-64 view: counts, widths and masks are the compact arrays
-  // themselves; only the stored slots move
-  twell_mat full{saved->T, saved->F, GPU_R, GPU_C, TWELL_F32, saved->cnt, saved->width, val, idx, saved->mask};
-  if (sh->T > 0) {
-    CompactArgs a = compact_args(&full, saved);
-    a.T = 0;  // the per-row arrays are shared: only the tiles move
-    hipError_t e = launch_compact(a, true, stream);
-    if (e != hipSuccess) return hip_status(e, "compact TwELL expansion");
-  }
-  return bwd_run(sh, x, WgT, bg, WuT, Wd, dY, view_of(&full), saved->ovf, dense_row_threshold, l1_lambda,
+  bwd_layout(sh, dense_row_threshold, ws, &w, saved->W);
+  // the compact arrays are read in place (W slots per tile); the per-pair
+  // values of the backward follow the same layout
+  return bwd_run(sh, x, WgT, bg, WuT, Wd, dY, view_of(saved), saved->ovf, dense_row_threshold, l1_lambda,
                  l1_per_token_mean, dX, dWgT, dWuT, dWd, dbg, n_dense_rows, w, stream);
+}
+
+// Workspace of the compact training forward: the row classification, the
+// dense rows' activation buffer, a at the stored pairs (capacity W; fp32
+// inputs) and the union workspace (bf16 inputs).
+static size_t fwd_compact_layout(const twell_ffn_shape* sh, int32_t W, void* ws, FwdWs* out, float** aval) {
+  Carver c(ws);
+  FwdWs w{};
+  w.flag = (uint8_t*)c.take((size_t)sh->T);
+  w.list = (int*)c.take((size_t)sh->T * 4);
+  w.nD = (int*)c.take(4);
+  w.act = (float*)c.take((size_t)sh->T * sh->F * 4);
+  float* av = nullptr;
+  if (sh->in_dt == TWELL_BF16) {
+    w.uni = c.take(union_ws_bytes(sh->T, sh->d, sh->F));
+  } else {
+    size_t parts[6];
+    cmat_parts(sh->T, sh->F, W, parts);
+    av = (float*)c.take(parts[2]);
+  }
+  if (out) *out = w;
+  if (aval) *aval = av;
+  return c.off;
+}
+
+size_t twell_ffn_fwd_compact_workspace(const twell_ffn_shape* sh, int32_t W) {
+  if (!sh || check_shape(sh) != TWELL_OK || W < 1 || W > GPU_C) return 0;
+  return fwd_compact_layout(sh, W, nullptr, nullptr, nullptr);
+}
+
+twell_status twell_ffn_fwd_compact(const twell_ffn_shape* sh, const void* x, const void* WgT, const void* bg,
+                                   const void* WuT, const void* Wd, void* y, twell_cmat* saved,
+                                   int32_t dense_row_threshold, void* ws, size_t ws_bytes, hipStream_t stream) {
+  twell_status st = check_shape(sh);
+  if (st) return st;
+  if (sh->T > 0 && (!x || !WgT || !WuT || !Wd || !y)) return fail(TWELL_EINVAL, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(WgT) || !aligned16(WuT) || !aligned16(Wd) || !aligned16(y) || !aligned16(bg))
+    return fail(TWELL_EINVAL, "tensors must be 16-byte aligned");
+  st = check_cmat(saved);
+  if (st) return st;
+  if (saved->T != sh->T || saved->F != sh->F)
+    return fail(TWELL_EINVAL, "saved must be T x F (T=%d F=%d)", sh->T, sh->F);
+  if (dense_row_threshold < 0) return fail(TWELL_EINVAL, "the compact forward is the hybrid one: threshold >= 0");
+  const size_t need = fwd_compact_layout(sh, saved->W, nullptr, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (sh->T == 0) return TWELL_OK;
+  FwdWs w;
+  float* aval = nullptr;
+  fwd_compact_layout(sh, saved->W, ws, &w, &aval);
+  const int in_dt = sh->in_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
+  const int out_dt = sh->out_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
+  const TwellView h = view_of(saved);
+  // the gate epilogue packs straight into the W slots of each tile; then the
+  // rows with a tile above W are flagged, widths clamped, and those rows go
+  // to the dense branch with the rows above the threshold
+  hipError_t e = launch_gate_twell(in_dt, x, WgT, bg, sh->T, sh->d, sh->F, h, stream);
+  if (e != hipSuccess) return hip_status(e, "gate GEMM");
+  e = launch_compact_finish(compact_args(nullptr, saved), stream);
+  if (e != hipSuccess) return hip_status(e, "compact overflow flags");
+  e = launch_classify(h, dense_row_threshold, w.flag, w.list, w.nD, nullptr, stream, saved->ovf);
+  if (e != hipSuccess) return hip_status(e, "row classification");
+  if (in_dt == DT_BF16) {
+    e = launch_union_fwd(x, WuT, Wd, sh->T, sh->d, sh->F, h, w.flag, w.uni, y, out_dt, nullptr, stream);
+    if (e != hipSuccess) return hip_status(e, "union up/down GEMMs");
+  } else {
+    e = launch_sddmm_up(in_dt, x, WuT, sh->T, sh->d, sh->F, h, aval, w.flag, stream);
+    if (e != hipSuccess) return hip_status(e, "sparse up-projection");
+    TwellView pat = h;
+    e = launch_spmm_down(in_dt, out_dt, aval, Wd, sh->T, sh->d, sh->F, pat, y, w.flag, stream);
+    if (e != hipSuccess) return hip_status(e, "sparse down-projection");
+  }
+  e = launch_dense_rows_fwd(in_dt, x, WgT, bg, WuT, Wd, sh->T, sh->d, sh->F, w.list, w.nD, w.act, out_dt, y, stream);
+  return hip_status(e, "dense-row forward");
 }
 
 static twell_status check_tensors(const twell_ffn_shape* sh, std::initializer_list<const void*> ptrs) {

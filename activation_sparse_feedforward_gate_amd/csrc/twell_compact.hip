@@ -62,6 +62,33 @@ __global__ __launch_bounds__(256) void compact_rows_kernel(CompactArgs a) {
   if (!EXPAND && lane == 0) a.ovf[t] = any ? 1 : 0;
 }
 
+// After a gate GEMM that packed straight into the capacity-W arrays (the
+// epilogue keeps the first W slots of every tile and records the true counts
+// and widths): the overflow flag of every row, and each tile's width clamped
+// to W, the convention of the compact form.  Workgroups [0, nrow) take four
+// rows each, the rest 256 tiles each.
+__global__ __launch_bounds__(256) void compact_finish_kernel(CompactArgs a, int nrow) {
+  if ((int)blockIdx.x < nrow) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.T) return;
+    bool over = false;
+    for (int j = lane; j < a.NT; j += 64) over |= a.ccnt[(int64_t)t * a.NT + j] > a.W;
+    const uint64_t any = ballot(over);
+    if (lane == 0) a.ovf[t] = any ? 1 : 0;
+  } else {
+    const int64_t tile = (int64_t)(blockIdx.x - nrow) * 256 + threadIdx.x;
+    if (tile < a.ntiles && a.cwidth[tile] > a.W) a.cwidth[tile] = (uint8_t)a.W;
+  }
+}
+
+hipError_t launch_compact_finish(const CompactArgs& a, hipStream_t s) {
+  const int nrow = (a.T + 3) / 4;
+  const int ntb = (int)((a.ntiles + 255) / 256);
+  if (nrow + ntb > 0) hipLaunchKernelGGL(compact_finish_kernel, dim3(nrow + ntb), dim3(256), 0, s, a, nrow);
+  return hipGetLastError();
+}
+
 hipError_t launch_compact(const CompactArgs& a, bool expand, hipStream_t s) {
   if (a.ntiles > 0) {
     const dim3 g((unsigned)((a.ntiles + 3) / 4));

@@ -700,7 +700,8 @@ __global__ __launch_bounds__(1024) void csc_total_scan_kernel(int F, int* start)
 // grouped by neuron, tokens ascending within a neuron; the neuron's block
 // starts at start[n], chunk c's part at part[c][n] within it.
 __global__ __launch_bounds__(256) void csc_fill_kernel(const uint64_t* mask, const uint8_t* skip, int T, int NT,
-                                                       int F, const int* part, const int* start, uint32_t* entries) {
+                                                       int F, const int* part, const int* start, uint32_t* entries,
+                                                       int cap) {
   __shared__ uint64_t sm[CSC_CHUNK * CSC_JG];
   const int c = blockIdx.y, j0 = blockIdx.x * CSC_JG;
   const int t0 = c * CSC_CHUNK, nr = min(T, t0 + CSC_CHUNK) - t0;
@@ -719,7 +720,7 @@ __global__ __launch_bounds__(256) void csc_fill_kernel(const uint64_t* mask, con
         if ((m[q] >> lane) & 1ull) {
           const int t = t0 + r0 + q;
           const uint32_t slot = (uint32_t)popc64(m[q] & lower);
-          entries[pos++] = ((uint32_t)((t >> 4) * NT + j) * 64u + slot) * 16u + (uint32_t)(t & 15);
+          entries[pos++] = ((uint32_t)((t >> 4) * NT + j) * (uint32_t)cap + slot) * 16u + (uint32_t)(t & 15);
         }
       }
     }
@@ -730,6 +731,7 @@ struct WgradArgs {
   const void* x;
   const void* dY;
   int T, d, F, NT;
+  int cap;                 // slots per TwELL tile of the value arrays
   const int* start;
   const uint32_t* entries;
   const float* aval;
@@ -759,7 +761,7 @@ __global__ __launch_bounds__(256) void wgrad_sparse_kernel(WgradArgs a) {
     for (int q = 0; q < EPC; ++q) accD[q] = accG[q] = accU[q] = 0.f;
     for (int e = e0; e < e1; ++e) {
       const uint32_t off = a.entries[e];
-      const int t = (int)(off / (uint32_t)(a.NT * 1024)) * 16 + (int)(off & 15u);
+      const int t = (int)(off / (uint32_t)(a.NT * a.cap * 16)) * 16 + (int)(off & 15u);
       const float av = a.aval[off], dg = a.dgval[off], du = a.duval[off];
       if (cb0 == 0) dsum += dg;
       if (on) {
@@ -810,10 +812,9 @@ hipError_t launch_sparse_wgrad(int in_dt, const void* x, const void* dY, int T, 
   hipLaunchKernelGGL(csc_total_scan_kernel, dim3(1), dim3(1024), 0, s, F, start);
   if (nchunk > 0) {
     hipLaunchKernelGGL(csc_fill_kernel, dim3((NT + CSC_JG - 1) / CSC_JG, nchunk), dim3(256), 0, s, h.mask, skip, T,
-                       NT, F, part, start,
-                       entries);
+                       NT, F, part, start, entries, h.cap);
   }
-  WgradArgs a{x, dY, T, d, F, NT, start, entries, aval, dgval, duval, dWgT, dWuT, dWd, dbg};
+  WgradArgs a{x, dY, T, d, F, NT, h.cap, start, entries, aval, dgval, duval, dWgT, dWuT, dWd, dbg};
   if (in_dt == DT_BF16) hipLaunchKernelGGL(wgrad_sparse_kernel<true>, dim3(F), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(wgrad_sparse_kernel<false>, dim3(F), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -45,6 +45,7 @@ struct SparseArgs {
   int out_bf16;
   int nslices;
   float l1;               // backward up: added to dg on every stored pair (activation penalty)
+  int cap;                // slots per TwELL tile of the value arrays
 };
 
 constexpr int SP_WPB = 4;        // waves (token groups) per workgroup
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256) void sddmm_up_kernel(SparseArgs a) {
           const uint64_t M = smask[w][r][j - j0];
           if ((M >> c) & 1ull) {
             const int slot = popc64(M & below(c));
-            const int64_t off = ((int64_t)grp * a.NT + j) * 1024 + slot * 16 + r;
+            const int64_t off = ((int64_t)grp * a.NT + j) * (a.cap * 16) + slot * 16 + r;
             const float h = a.hval[off];
             a.aval[off] = h * acc[b][i];
             if constexpr (BWD) {
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(256) void spmm_down_kernel(SparseArgs a) {
           const uint64_t M = smask[w][r_a][j - jc];
           if ((M >> c) & 1ull) {
             const int slot = popc64(M & below(c));
-            const int64_t off = ((int64_t)grp * a.NT + j) * 1024 + slot * 16 + r_a;
+            const int64_t off = ((int64_t)grp * a.NT + j) * (a.cap * 16) + slot * 16 + r_a;
 #pragma unroll
             for (int v = 0; v < NV; ++v) av[v] = vsrc[v][off];
           }
@@ -310,7 +311,7 @@ hipError_t launch_sddmm_up(int in_dt, const void* x, const void* WuT, int T, int
                            const TwellView& h, float* aval, const uint8_t* skip, hipStream_t s) {
   SparseArgs a{};
   a.x = x; a.W = WuT; a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
-  a.mask = h.mask; a.hval = (const float*)h.val; a.aval = aval; a.skip = skip;
+  a.mask = h.mask; a.hval = (const float*)h.val; a.aval = aval; a.skip = skip; a.cap = h.cap;
   if (in_dt == DT_BF16) return launch_up_bf16(x, nullptr, WuT, nullptr, T, d, F, h, aval, nullptr, nullptr, skip, s);
   a.nslices = choose_slices(a.NT, UP_MAXT);
   if (a.NR == 0) return hipSuccess;
@@ -326,6 +327,7 @@ hipError_t launch_sddmm_bwd(int in_dt, const void* x, const void* dY, const void
   a.l1 = l1;
   a.x = x; a.x2 = dY; a.W = WuT; a.W2 = Wd; a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
   a.mask = h.mask; a.hval = (const float*)h.val; a.aval = aval; a.dgval = dgval; a.duval = duval; a.skip = skip;
+  a.cap = h.cap;
   if (in_dt == DT_BF16) return launch_up_bf16(x, dY, WuT, Wd, T, d, F, h, aval, dgval, duval, skip, s, nullptr, l1);
   a.nslices = choose_slices(a.NT, UP_MAXT);
   if (a.NR == 0) return hipSuccess;
@@ -339,6 +341,7 @@ hipError_t launch_spmm_down(int in_dt, int out_dt, const float* aval, const void
   SparseArgs a{};
   a.W = Wd; a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
   a.mask = pat.mask; a.aval = (float*)aval; a.skip = skip; a.y = y; a.out_bf16 = out_dt == DT_BF16;
+  a.cap = pat.cap;
   if (in_dt == DT_BF16) return launch_down_bf16(aval, nullptr, Wd, nullptr, T, d, F, pat, y, out_dt, skip, s);
   a.nslices = choose_slices(d / 16, DN_MAXCB);
   if (d / 16 < a.nslices) a.nslices = d / 16;
@@ -354,6 +357,7 @@ hipError_t launch_spmm_dx(int in_dt, const float* dgval, const float* duval, con
   SparseArgs a{};
   a.W = WgT; a.W2 = WuT; a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
   a.mask = pat.mask; a.dgval = (float*)dgval; a.duval = (float*)duval; a.skip = skip; a.y = dX; a.out_bf16 = 0;
+  a.cap = pat.cap;
   if (in_dt == DT_BF16) return launch_down_bf16(dgval, duval, WgT, WuT, T, d, F, pat, dX, DT_F32, skip, s);
   a.nslices = choose_slices(d / 16, DN_MAXCB);
   if (d / 16 < a.nslices) a.nslices = d / 16;

@@ -73,6 +73,7 @@ struct SpArgs {
   int nvb;              // virtual workgroups: ngroups * S (a grid may be smaller and loop over them)
   const int* gate;      // null, or a device flag: the kernel runs only if it is non-zero
   float l1;             // up backward: added to dg on every stored pair (activation penalty)
+  int cap;              // slots per TwELL tile of the value arrays
 };
 
 // Virtual workgroup vb -> (token group g, slice s).  With S a multiple of 8,
@@ -294,7 +295,7 @@ __device__ __forceinline__ void up_pass(const SpArgs& a, const UnionLds& L, char
         const uint64_t P = L.pm[w * 16 + r][jj];
         if ((P >> qp) & 1ull) {
           const int slot = popc64(P & below(qp));
-          const int64_t off = (c.rt * a.NT + (c.j0 + jj)) * 1024 + slot * 16 + r;
+          const int64_t off = (c.rt * a.NT + (c.j0 + jj)) * (a.cap * 16) + slot * 16 + r;
           const float h = a.hval[off];
           const float u = acc[b][i];
           a.v0[off] = h * u;
@@ -424,7 +425,7 @@ __device__ __forceinline__ void down_bf16_block(const SpArgs& a, int vb, UnionLd
         const uint64_t P = L.pm[w * 16 + ra][jj];
         const uint32_t bits = (uint32_t)(P >> q0) & 0xFFu;
         if (bits) {
-          const int64_t tb = (rt * a.NT + (jc + jj)) * 1024 + ra;
+          const int64_t tb = (rt * a.NT + (jc + jj)) * (a.cap * 16) + ra;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             if ((bits >> e) & 1u) {
@@ -540,6 +541,7 @@ hipError_t launch_up_bf16(const void* x, const void* dY, const void* WuT, const 
   a.x = (const uint16_t*)x; a.x2 = (const uint16_t*)dY; a.W = (const uint16_t*)WuT; a.W2 = (const uint16_t*)Wd;
   a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
   a.mask = h.mask; a.skip = skip; a.hval = (const float*)h.val; a.v0 = aval; a.v1 = dgval; a.v2 = duval;
+  a.cap = h.cap;
   a.gate = gate;
   a.l1 = l1;
   if (a.NR == 0) return hipSuccess;
@@ -574,6 +576,7 @@ hipError_t launch_down_bf16(const float* v0, const float* v1, const void* W, con
   a.W = (const uint16_t*)W; a.W2 = (const uint16_t*)W2;
   a.T = T; a.d = d; a.F = F; a.NT = F / 64; a.NR = (T + 15) / 16;
   a.mask = pat.mask; a.skip = skip; a.v0 = (float*)v0; a.v1 = (float*)v1; a.y = y; a.out_bf16 = out_dt == DT_BF16;
+  a.cap = pat.cap;
   a.gate = gate;
   if (a.NR == 0) return hipSuccess;
   a.ngroups = (a.NR + GW - 1) / GW;

@@ -474,8 +474,8 @@ __device__ __forceinline__ void bwd_union_tile(const UnionArgs& a, int b, int pt
     const int64_t blk = (int64_t)rt * a.NT + tj;
     const int w = a.hwidth[blk];
     for (int c = gl; c < w * 4; c += 16) {
-      const float4 v4 = ((const float4*)(a.hval + blk * 1024))[c];
-      const uint32_t i4 = ((const uint32_t*)(a.hidx + blk * 1024))[c];
+      const float4 v4 = ((const float4*)(a.hval + blk * a.hcap * 16))[c];
+      const uint32_t i4 = ((const uint32_t*)(a.hidx + blk * a.hcap * 16))[c];
       const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -524,7 +524,7 @@ __device__ __forceinline__ void bwd_union_tile(const UnionArgs& a, int b, int pt
           const int t = m0 + r0 + k;
           float dg = 0.f, du = 0.f;
           if (sl) {
-            const int64_t off = (((int64_t)(t >> 4) * a.NT + tj) * 64 + (sl - 1)) * 16 + (t & 15);
+            const int64_t off = (((int64_t)(t >> 4) * a.NT + tj) * a.hcap + (sl - 1)) * 16 + (t & 15);
             const float h = a.hval[off];
             const float u = gu.acc[0][i][j][4 * qq + k], da = gd.acc[0][i][j][4 * qq + k];
             dg = da * u + a.l1;
@@ -941,7 +941,7 @@ hipError_t launch_union_bwd(const void* x, const void* dY, const void* WgT, cons
   UnionArgs a{};
   a.x = x; a.WuT = WuT; a.Wd = Wd; a.dY = dY; a.T = T; a.d = d; a.F = F; a.NT = F / 64;
   a.mask = h.mask; a.skip = skip; a.hval = (const float*)h.val; a.hidx = h.idx; a.hwidth = h.width;
-  a.hcap = 64;                              // the backward reads the full TwELL form
+  a.hcap = h.cap;                           // slot arrays in, and out (aval, dgval, duval)
   a.ucap = F;
   auto r = [](size_t v) { return (v + 255) & ~(size_t)255; };
   a.ulist = (int*)w;

@@ -453,6 +453,36 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool, 
     if few_tokens and not full and args.cold_iters > 0 and not args.no_dense:
         out["cold_cache_ms_per_step"] = cold_cache_ms(step, args.cold_iters, stream)
         out["dense_baseline"]["cold_cache_ms_per_step"] = cold_cache_ms(dense_step, args.cold_iters, stream)
+    if training and args.compact_w > 0:
+        # the same step with the state saved between forward and backward in
+        # compact TwELL of capacity W: the forward packs the gate output
+        # straight into it, the backward reads it in place
+        W = args.compact_w
+        c = tw.alloc_twell_cmat(T, f, W, device=dev)
+        fws = tw.twell_ffn_fwd_compact_workspace(shape, W)
+        bws = tw.twell_ffn_bwd_compact_workspace(shape, tau, W)
+        wfc = torch.empty(max(1, fws), dtype=torch.uint8, device=dev)
+        wsc = torch.empty(max(1, bws), dtype=torch.uint8, device=dev)
+
+        def compact_step():
+            tw.twell_ffn_fwd_compact(shape, x, WgT, bg, WuT, Wd, y, c, tau, wfc, stream)
+            tw.twell_ffn_bwd_hybrid_compact(shape, x, WgT, bg, WuT, Wd, dY, c, tau, 0.0, False, dX, dW[0], dW[1],
+                                            dW[2], dbg, nD, wsc, stream)
+        cms = _timed(compact_step, steps, warmup, stream, warm_s)
+        saved_c = tw.twell_cmat_bytes(T, f, W)[0]
+        out["compact_twell"] = {
+            "W": W, "ms_per_step": cms, "tokens_per_s": T / (cms * 1e-3),
+            "overflow_rows": int(c.ovf.to(torch.int64).sum().item()), "dense_rows": int(nD.item()),
+            "saved_state_bytes": saved_c,
+            "full_saved_state_bytes": tw.twell_mat_bytes(T, f)[0],
+            "workspace_bytes": {"forward": int(fws), "backward": int(bws), "saved_state": int(saved_c),
+                                "total": int(fws + bws + saved_c)},
+        }
+        if "dense_baseline" in out:
+            out["compact_twell"]["speedup_vs_dense"] = out["dense_baseline"]["ms_per_step"] / cms
+            out["compact_twell"]["workspace_vs_own_dense"] = (fws + bws + saved_c) / max(
+                1, out["workspace_bytes"]["own_dense"])
+        del wfc, wsc
     out["_workload"] = w
     if not full:
         return out
@@ -522,25 +552,6 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool, 
                                "ms": lib_ms, "tflops": lib_tf, "frac_of_peak": lib_tf / PEAK["bf16_mfma_tflops"]}
         out["roofline"]["frac_of_library_gemm"] = float(lines["gate_gemm_twell_pack"]["achieved"]) / lib_tf
 
-    if training and args.compact_w > 0:
-        # the same step with the state saved between forward and backward in
-        # compact TwELL: forward, compaction, backward from the compact form
-        W = args.compact_w
-        c = tw.alloc_twell_cmat(T, f, W, device=dev)
-        wsc = torch.empty(max(1, tw.twell_ffn_bwd_compact_workspace(shape, tau)), dtype=torch.uint8, device=dev)
-
-        def compact_step():
-            tw.twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, h, tau, wsf, stream)
-            tw.twell_compact(h, c, stream)
-            tw.twell_ffn_bwd_hybrid_compact(shape, x, WgT, bg, WuT, Wd, dY, c, tau, 0.0, False, dX, dW[0], dW[1],
-                                            dW[2], dbg, nD, wsc, stream)
-        cms = _timed(compact_step, steps, warmup, stream)
-        out["compact_twell"] = {
-            "W": W, "ms_per_step": cms, "tokens_per_s": T / (cms * 1e-3),
-            "overflow_rows": int(c.ovf.to(torch.int64).sum().item()), "dense_rows": int(nD.item()),
-            "saved_state_bytes": tw.twell_cmat_bytes(T, f, W)[0],
-            "full_saved_state_bytes": tw.twell_mat_bytes(T, f)[0],
-        }
     return out
 
 

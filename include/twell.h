@@ -248,19 +248,21 @@ size_t twell_cmat_bytes(int32_t T, int32_t F, int32_t W, size_t parts[6]);
 twell_status twell_compact(const twell_mat *full, twell_cmat *out, hipStream_t stream);
 twell_status twell_expand(const twell_cmat *in, twell_mat *full, hipStream_t stream);
 
-/* Workspace bytes for twell_ffn_bwd_hybrid_compact: that of
- * twell_ffn_bwd_workspace plus a capacity-64 value and index array. */
-size_t twell_ffn_bwd_compact_workspace(const twell_ffn_shape *sh, int32_t dense_row_threshold);
+/* Workspace bytes for twell_ffn_bwd_hybrid_compact with a saved state of
+ * capacity W: that of twell_ffn_bwd_workspace with its per-pair value arrays
+ * at W slots per tile instead of 64.  0 for an invalid shape or W. */
+size_t twell_ffn_bwd_compact_workspace(const twell_ffn_shape *sh, int32_t dense_row_threshold, int32_t W);
 
 /*
  * twell_ffn_bwd_hybrid_compact: twell_ffn_bwd_hybrid_l1 with the saved state
- * in compact form (saved: fp32, T x F, the twell_compact of the forward's
- * saved_h).  Row t takes the dense branch when its count exceeds
- * dense_row_threshold or when saved->ovf[t] is set; every other row keeps all
- * its entries and takes the sparse branch as before, so the gradients equal
- * those of twell_ffn_bwd_hybrid_l1 up to fp32 rounding.  n_dense_rows counts
- * both kinds.  ws: at least twell_ffn_bwd_compact_workspace(sh, thr) bytes.
- * Other arguments, outputs and errors as for twell_ffn_bwd_hybrid_l1.
+ * in compact form (saved: T x F, written by twell_ffn_fwd_compact or by
+ * twell_compact of a forward's saved_h), read in place.  Row t takes the
+ * dense branch when its count exceeds dense_row_threshold or when
+ * saved->ovf[t] is set; every other row keeps all its entries and takes the
+ * sparse branch as before, so the gradients equal those of
+ * twell_ffn_bwd_hybrid_l1 up to fp32 rounding.  n_dense_rows counts both
+ * kinds.  ws: at least twell_ffn_bwd_compact_workspace(sh, thr, saved->W)
+ * bytes.  Other arguments, outputs and errors as for twell_ffn_bwd_hybrid_l1.
  */
 twell_status twell_ffn_bwd_hybrid_compact(const twell_ffn_shape *sh, const void *x, const void *WgT,
                                           const void *bg, const void *WuT, const void *Wd, const void *dY,
@@ -268,6 +270,26 @@ twell_status twell_ffn_bwd_hybrid_compact(const twell_ffn_shape *sh, const void 
                                           int32_t l1_per_token_mean, float *dX, float *dWgT, float *dWuT,
                                           float *dWd, float *dbg, int32_t *n_dense_rows, void *ws,
                                           size_t ws_bytes, hipStream_t stream);
+
+/*
+ * twell_ffn_fwd_compact: the hybrid training forward (twell_ffn_fwd with
+ * dense_row_threshold >= 0) that saves h straight into compact form: the
+ * gate GEMM's epilogue packs every tile into the W slots of saved (keeping
+ * the first W entries of each row and the true counts and masks), then each
+ * row with more than W entries in some tile is flagged (saved->ovf) and
+ * joins the dense branch with the rows above the threshold; tile widths are
+ * clamped to W.  No capacity-64 form is ever held.  y is the same layer as
+ * twell_ffn_fwd's (the dense branch computes the same function), and saved
+ * equals twell_compact of twell_ffn_fwd's saved_h.
+ *   saved  caller-allocated twell_cmat (T and F of the shape; any W in 1..64)
+ *   dense_row_threshold  >= 0 (EINVAL otherwise)
+ *   ws, ws_bytes  at least twell_ffn_fwd_compact_workspace(sh, saved->W)
+ * Other arguments and errors as for twell_ffn_fwd.
+ */
+size_t twell_ffn_fwd_compact_workspace(const twell_ffn_shape *sh, int32_t W);
+twell_status twell_ffn_fwd_compact(const twell_ffn_shape *sh, const void *x, const void *WgT, const void *bg,
+                                   const void *WuT, const void *Wd, void *y, twell_cmat *saved,
+                                   int32_t dense_row_threshold, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * twell_ffn_fwd_ex: twell_ffn_fwd that also records up to n_events caller-

@@ -4,7 +4,9 @@ hybrid backward that reads it.
 twell_compact / twell_expand are byte work: they are compared bit for bit
 with the oracle's twell_compact / twell_expand of the oracle's own pack of the
 same seeded matrix G (the GPU side packs G with twell_pack, itself checked bit
-for bit elsewhere).  twell_ffn_bwd_hybrid_compact is compared with the float64
+for bit elsewhere).  twell_ffn_fwd_compact, which packs the gate GEMM's
+output straight into the compact form, must save exactly twell_compact of the
+full-capacity forward's h.  twell_ffn_bwd_hybrid_compact is compared with the float64
 oracle's gradients within the hybrid backward's tolerance (relative Frobenius
 1e-3 for bf16 inputs, 1e-5 for fp32), on the sparse and dense row sets
 separately; the rows the dense branch took must be exactly those of the GPU's
@@ -121,30 +123,41 @@ def test_compact_full_capacity_is_identity(torch, tw):
             np.testing.assert_array_equal(got["val_bits"][i, j, :w], f["val_bits"][i, j, :w])
 
 
-def _run_compact_train(torch, tw, w, tau, W, l1=(0.0, False), bias=True):
+def _run_compact_train(torch, tw, w, tau, W, l1=(0.0, False), bias=True, direct=False):
+    """direct: the compact forward writes the saved state; else the full
+    forward's saved h is compacted with twell_compact."""
     dt = w.cfg.dtype
     in_dt = tw.TWELL_BF16 if dt == "bf16" else tw.TWELL_F32
     x, WgT, WuT, Wd, dY = (to_dev(a, dt) for a in (w.x, w.WgT, w.WuT, w.Wd, w.dY))
     bg = to_dev(w.bg, dt) if bias else None
     T, d, F = w.T, w.d, w.f
     shape = tw.ffn_shape(T, d, F, in_dt, tw.TWELL_F32)
-    h = tw.alloc_twell_mat(T, F, tw.TWELL_F32)
     y = torch.empty((T, d), dtype=torch.float32, device="cuda")
-    wsf = torch.empty(max(1, tw.twell_ffn_fwd_workspace(shape, True)), dtype=torch.uint8, device="cuda")
-    tw.twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, h, tau, wsf)
     c = tw.alloc_twell_cmat(T, F, W)
-    tw.twell_compact(h, c)
-    torch.cuda.synchronize()
-    h_host = mat_to_numpy(h)
-    # the full form is no longer needed: scribble over it so that a backward
-    # that still read it would fail
-    h.val.fill_(float("nan"))
-    h.idx.fill_(0xEE)
+    if direct:
+        c.val.fill_(float("nan"))
+        c.idx.fill_(0xEE)
+        wsf = torch.empty(max(1, tw.twell_ffn_fwd_compact_workspace(shape, W)), dtype=torch.uint8, device="cuda")
+        wsf.fill_(0xFF)
+        tw.twell_ffn_fwd_compact(shape, x, WgT, bg, WuT, Wd, y, c, tau, wsf)
+        torch.cuda.synchronize()
+        h_host = {"cnt": c.cnt.cpu().numpy().astype(np.int64)}
+    else:
+        h = tw.alloc_twell_mat(T, F, tw.TWELL_F32)
+        wsf = torch.empty(max(1, tw.twell_ffn_fwd_workspace(shape, True)), dtype=torch.uint8, device="cuda")
+        tw.twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, h, tau, wsf)
+        tw.twell_compact(h, c)
+        torch.cuda.synchronize()
+        h_host = mat_to_numpy(h)
+        # the full form is no longer needed: scribble over it so that a backward
+        # that still read it would fail
+        h.val.fill_(float("nan"))
+        h.idx.fill_(0xEE)
     dX = torch.full((T, d), float("nan"), dtype=torch.float32, device="cuda")
     dW = [torch.full((F, d), float("nan"), dtype=torch.float32, device="cuda") for _ in range(3)]
     dbg = torch.full((F,), float("nan"), dtype=torch.float32, device="cuda")
     nD = torch.full((1,), -1, dtype=torch.int32, device="cuda")
-    wsb = torch.empty(max(1, tw.twell_ffn_bwd_compact_workspace(shape, tau)), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(max(1, tw.twell_ffn_bwd_compact_workspace(shape, tau, W)), dtype=torch.uint8, device="cuda")
     wsb.fill_(0xFF)
     tw.twell_ffn_bwd_hybrid_compact(shape, x, WgT, bg, WuT, Wd, dY, c, tau, l1[0], l1[1], dX, dW[0], dW[1], dW[2],
                                     dbg, nD, wsb)
@@ -187,11 +200,12 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("direct", [False, True], ids=["compacted", "direct"])
 @pytest.mark.parametrize("name,kw,W", CASES, ids=["520-W2", "333-W4", "200-W64", "130-W1", "tiny_f32-W3"])
-def test_bwd_compact(torch, tw, name, kw, W):
+def test_bwd_compact(torch, tw, name, kw, W, direct):
     w = make_workload(name, **kw)
-    log(f"[bwd compact] {name} T={w.T} d={w.d} f={w.f} tau={w.tau} W={W}")
-    got = _run_compact_train(torch, tw, w, w.tau, W)
+    log(f"[bwd compact] {name} T={w.T} d={w.d} f={w.f} tau={w.tau} W={W} direct={direct}")
+    got = _run_compact_train(torch, tw, w, w.tau, W, direct=direct)
     ovf = _check(w, got, w.tau, W)
     if W == 64:
         assert not ovf.any()
@@ -199,18 +213,20 @@ def test_bwd_compact(torch, tw, name, kw, W):
         assert ovf.any() and not ovf.all()
 
 
-def test_bwd_compact_l1_and_no_bias(torch, tw):
+@pytest.mark.parametrize("direct", [False, True], ids=["compacted", "direct"])
+def test_bwd_compact_l1_and_no_bias(torch, tw, direct):
     w = make_workload("hybrid", T=260, d=128, f=640)
     lam = 3e-3
-    log(f"[bwd compact] l1 lambda={lam} mean, no bias")
-    got = _run_compact_train(torch, tw, w, w.tau, 3, l1=(lam, True), bias=False)
+    log(f"[bwd compact] l1 lambda={lam} mean, no bias, direct={direct}")
+    got = _run_compact_train(torch, tw, w, w.tau, 3, l1=(lam, True), bias=False, direct=direct)
     _check(w, got, w.tau, 3, l1c=O.l1_coefficient(lam, w.T, True), bias=False)
 
 
-def test_bwd_compact_empty(torch, tw):
+@pytest.mark.parametrize("direct", [False, True], ids=["compacted", "direct"])
+def test_bwd_compact_empty(torch, tw, direct):
     w = make_workload("hybrid", T=0, d=128, f=640)
-    log("[bwd compact] T=0")
-    got = _run_compact_train(torch, tw, w, w.tau, 4)
+    log(f"[bwd compact] T=0, direct={direct}")
+    got = _run_compact_train(torch, tw, w, w.tau, 4, direct=direct)
     assert got["nD"] == 0
     for k in ("dWgT", "dWuT", "dWd", "dbg"):
         assert np.all(got[k] == 0), k
@@ -223,8 +239,8 @@ def test_bwd_compact_full_size_sampled(torch, tw):
     (y, dX) and neurons (weight gradients) against the oracle."""
     w = make_workload("hybrid")
     W = 8
-    log(f"[bwd compact] full size T={w.T} d={w.d} f={w.f} tau={w.tau} W={W}")
-    got = _run_compact_train(torch, tw, w, w.tau, W)
+    log(f"[bwd compact] full size T={w.T} d={w.d} f={w.f} tau={w.tau} W={W}, compact forward")
+    got = _run_compact_train(torch, tw, w, w.tau, W, direct=True)
     cnt = got["h"]["cnt"]
     ovf = (cnt > W).any(axis=1)
     np.testing.assert_array_equal(got["ovf"], ovf)
@@ -244,3 +260,57 @@ def test_bwd_compact_full_size_sampled(torch, tw):
         assert e <= TOL["bf16"], (k, e)
     for k in ("dX", "dWgT", "dWuT", "dWd", "dbg"):
         assert np.isfinite(got[k]).all(), k
+
+
+@pytest.mark.parametrize("name,kw,W", [("hybrid", dict(T=520, d=256, f=1280), 2),
+                                       ("hybrid", dict(T=777, d=256, f=1280), 8),
+                                       ("tiny_f32", dict(grad=True), 3),
+                                       ("0.5b", dict(T=600, d=256, f=1024), 5)],
+                         ids=["520-W2", "777-W8", "tiny_f32-W3", "0.5b-W5"])
+def test_fwd_compact_saves_compact_of_full(torch, tw, name, kw, W):
+    """The compact forward's saved state equals twell_compact of the full
+    forward's saved h, byte for byte (counts, masks, clamped widths, overflow
+    flags, the first min(width, W) slots of every tile); its y matches the
+    oracle on the sparse and dense rows alike."""
+    w = make_workload(name, **kw)
+    dt = w.cfg.dtype
+    in_dt = tw.TWELL_BF16 if dt == "bf16" else tw.TWELL_F32
+    x, WgT, bg, WuT, Wd = (to_dev(a, dt) for a in (w.x, w.WgT, w.bg, w.WuT, w.Wd))
+    T, d, F = w.T, w.d, w.f
+    tau = w.tau if w.tau is not None else 64
+    log(f"[fwd compact] {name} T={T} d={d} f={F} tau={tau} W={W}")
+    shape = tw.ffn_shape(T, d, F, in_dt, tw.TWELL_F32)
+    h = tw.alloc_twell_mat(T, F, tw.TWELL_F32)
+    y_full = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    wsf = torch.empty(max(1, tw.twell_ffn_fwd_workspace(shape, True)), dtype=torch.uint8, device="cuda")
+    tw.twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y_full, h, tau, wsf)
+    ref_c = tw.alloc_twell_cmat(T, F, W)
+    tw.twell_compact(h, ref_c)
+    c = tw.alloc_twell_cmat(T, F, W)
+    c.val.fill_(float("nan"))
+    c.idx.fill_(0xEE)
+    y = torch.full((T, d), float("nan"), dtype=torch.float32, device="cuda")
+    wsc = torch.empty(max(1, tw.twell_ffn_fwd_compact_workspace(shape, W)), dtype=torch.uint8, device="cuda")
+    wsc.fill_(0xFF)
+    tw.twell_ffn_fwd_compact(shape, x, WgT, bg, WuT, Wd, y, c, tau, wsc)
+    torch.cuda.synchronize()
+    got, want = _cmat_to_numpy(c), _cmat_to_numpy(ref_c)
+    for k in ("cnt", "width", "mask", "ovf"):
+        np.testing.assert_array_equal(got[k], want[k], err_msg=k)
+    log(f"   overflow rows {int(got['ovf'].sum())} of {T}")
+    NR, NT = want["width"].shape
+    for i in range(NR):
+        for j in range(NT):
+            wd = int(want["width"][i, j])
+            np.testing.assert_array_equal(got["idx"][i, j, :wd], want["idx"][i, j, :wd], err_msg=f"idx {i},{j}")
+            np.testing.assert_array_equal(got["val_bits"][i, j, :wd], want["val_bits"][i, j, :wd],
+                                          err_msg=f"val {i},{j}")
+    ref = O.ffn_fwd_rows(w.x, w.WgT, w.bg, w.WuT, w.Wd, np.arange(T))
+    yc = y.cpu().numpy()
+    e = rel_fro(yc, ref["y"])
+    log(f"   y rel-Frobenius {e:.3e}")
+    assert e <= TOL[dt], e
+    dense = (got["cnt"].sum(axis=1) > tau) | got["ovf"]
+    for nm, sel in (("dense rows", dense), ("sparse rows", ~dense)):
+        if sel.any():
+            assert rel_fro(yc[sel], ref["y"][sel]) <= TOL[dt], nm

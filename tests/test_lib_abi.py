@@ -200,9 +200,14 @@ def test_bwd_compact_argument_errors():
     L = tw.lib()
     sh = tw.ffn_shape(64, 128, 512, tw.TWELL_BF16, tw.TWELL_F32)
     c = tw.c_twell_cmat(64, 512, 4, 16, 16, 16, 16, 16, 16)
-    need = tw.twell_ffn_bwd_compact_workspace(sh, 51)
-    full_val = tw.twell_mat_bytes(64, 512)[1][2]
-    assert need >= tw.twell_ffn_bwd_workspace(sh, 51) + full_val
+    need = tw.twell_ffn_bwd_compact_workspace(sh, 51, 4)
+    # the three per-pair value arrays of the backward shrink from 64 to W slots per tile
+    full = tw.twell_ffn_bwd_workspace(sh, 51)
+    assert tw.twell_ffn_bwd_compact_workspace(sh, 51, 64) == full
+    slots = 4 * 8 * 16 * 4                         # NR * NT * 16 rows, per slot of a tile, fp32
+    assert abs((full - need) - 3 * slots * (64 - 4)) <= 3 * 256
+    assert tw.twell_ffn_bwd_compact_workspace(sh, 51, 0) == 0
+    assert tw.twell_ffn_bwd_compact_workspace(sh, 51, 65) == 0
 
     def call(cmat=c, lam=0.0, ws_bytes=need, dY=16):
         return L.twell_ffn_bwd_hybrid_compact(ctypes.byref(sh), 16, 16, None, 16, 16, dY,
@@ -310,3 +315,24 @@ def test_bounded_fwd_workspace_and_argument_errors():
     # few tokens: the ordinary few-token workspace
     small = tw.ffn_shape(64, d, F, tw.TWELL_BF16, tw.TWELL_F32)
     assert tw.twell_ffn_fwd_bounded_workspace(small, 8, 256) == tw.twell_ffn_fwd_workspace(small)
+
+
+def test_fwd_compact_argument_errors():
+    L = tw.lib()
+    sh = tw.ffn_shape(64, 128, 512, tw.TWELL_BF16, tw.TWELL_F32)
+    c = tw.c_twell_cmat(64, 512, 4, 16, 16, 16, 16, 16, 16)
+    need = tw.twell_ffn_fwd_compact_workspace(sh, 4)
+    assert 0 < need < tw.twell_ffn_fwd_workspace(sh, True)     # no capacity-64 TwELL in it
+    assert tw.twell_ffn_fwd_compact_workspace(sh, 0) == 0
+
+    def call(cmat=c, thr=51, ws_bytes=need, x=16):
+        return L.twell_ffn_fwd_compact(ctypes.byref(sh), x, 16, None, 16, 16, 16,
+                                       ctypes.byref(cmat) if cmat is not None else None, thr, 4096, ws_bytes, None)
+    assert call(cmat=None) == tw.TWELL_EINVAL
+    assert call(cmat=tw.c_twell_cmat(64, 512, 4, 16, 16, 16, 16, 16, None)) == tw.TWELL_EINVAL   # ovf required
+    assert call(cmat=tw.c_twell_cmat(64, 512, 0, 16, 16, 16, 16, 16, 16)) == tw.TWELL_EINVAL
+    assert call(cmat=tw.c_twell_cmat(32, 512, 4, 16, 16, 16, 16, 16, 16)) == tw.TWELL_EINVAL
+    assert call(thr=-1) == tw.TWELL_EINVAL
+    assert call(x=None) == tw.TWELL_EINVAL
+    assert call(x=24) == tw.TWELL_EINVAL
+    assert call(ws_bytes=need - 1) == tw.TWELL_EWORKSPACE
