@@ -20,6 +20,12 @@
 // zeros.  a is fp16 for the down GEMM (relative rounding 2^-11, within the
 // 1e-3 output budget); if any |a| (or a weight of Wd) exceeds the fp16 range a
 // device flag makes the down kernel compute y per stored pair in fp32 instead.
+//
+// The TwELL of h may hold fewer than 64 slots per tile (hcap), and adense may
+// hold fewer than F positions per row (ucap): with block flags (bounded
+// forward) a block whose tiles are wider than hcap or whose union is longer
+// than ucap skips the GEMMs and the down kernel computes it per stored pair,
+// with h recomputed from the gate weights (its tiles may have lost slots).
 #include <algorithm>
 
 #include "gemm_core.hpp"
@@ -205,7 +211,9 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
   constexpr int NPRE = Cfg::SINGLE ? 0 : 4;
   const int grp = tid >> 4, gl = tid & 15;
   // first piece (slots 0-3) of the group's first NPRE (row tile, column tile)
-  // blocks; every tile holds at least 4 slots, so the reads need no width check
+  // blocks, read before the width is known: only for tiles of at least 4
+  // slots, so the kernels that may see a smaller TwELL capacity are the
+  // single-stage ones, which read nothing ahead (checked where they launch)
   constexpr int NRT = Cfg::BM / 16;        // TwELL row tiles of the block
   struct Piece { int w; float4 v; uint32_t i; };
   Piece pre[NPRE > 0 ? NPRE : 1];
@@ -897,6 +905,7 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
     }
   }
   if (ev_lists) (void)hipEventRecord(ev_lists, s);
+  static_assert(UpUnionCfg::SINGLE, "TwELL capacities below 4 slots need the up kernel without read-ahead");
   const int npt = (F + UpUnionCfg::BN - 1) / UpUnionCfg::BN;
   const int nbx_max = (nblk + 7) / 8;
   // persistent grids: one workgroup per CU (multiples of 8, one row of XCDs),
