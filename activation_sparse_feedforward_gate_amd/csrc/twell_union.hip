@@ -22,10 +22,11 @@
 // device flag makes the down kernel compute y per stored pair in fp32 instead.
 //
 // The TwELL of h may hold fewer than 64 slots per tile (hcap), and adense may
-// hold fewer than F positions per row (ucap): with block flags (bounded
-// forward) a block whose tiles are wider than hcap or whose union is longer
-// than ucap skips the GEMMs and the down kernel computes it per stored pair,
-// with h recomputed from the gate weights (its tiles may have lost slots).
+// hold fewer than F positions per row (ucap).  With block flags (bounded
+// forward), a block whose tiles are wider than hcap but whose union fits
+// takes h from a gate GEMM over its union (up_union_rec_kernel) instead of
+// its incomplete TwELL; a block whose union is longer than ucap skips the
+// GEMMs and the down kernel computes it per stored pair, with h recomputed.
 #include <algorithm>
 
 #include "gemm_core.hpp"
@@ -73,7 +74,8 @@ struct UnionArgs {
   // capacity-bounded forward
   int hcap;               // slots per TwELL tile of h (64: the full form)
   int ucap;               // row stride of adense: union positions a block may hold
-  uint8_t* bflag;         // [NBLK] or null: block b's TwELL or union exceeds its capacity
+  uint8_t* bflag;         // [NBLK] or null: 1 if block b's TwELL tiles exceed hcap (its union fits
+                          // ucap), 2 if its union exceeds ucap, else 0
   const void* WgT;        // gate weights and bias, to recompute h for such blocks
   const void* bg;
 };
@@ -148,7 +150,7 @@ __device__ __forceinline__ void union_list_block(const UnionArgs& a, const uint6
   if (a.bflag) {
     // or a union longer than adense's rows hold
     const int ov = __syncthreads_or((int)over);
-    if (tid == 0) a.bflag[b] = (uint8_t)(ov || base > a.ucap);
+    if (tid == 0) a.bflag[b] = (uint8_t)(base > a.ucap ? 2 : ov ? 1 : 0);
   }
 }
 
@@ -171,7 +173,7 @@ __device__ __forceinline__ void up_union_tile(const UnionArgs& a, int b, int pt,
   const int nb = a.ucount[b];
   const int p0 = pt * Cfg::BN;
   if (p0 >= nb) return;
-  if (a.bflag && a.bflag[b]) return;       // over capacity: the down kernel computes it per pair
+  if (a.bflag && a.bflag[b]) return;       // over capacity: up_union_rec_kernel or the down kernel
   const int m0 = b * UB;
   const int* ul = a.ulist + (int64_t)b * a.F;
   const int64_t hs = (int64_t)a.hcap * 16; // TwELL tile stride of h
@@ -424,6 +426,69 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void up_union_ker
   }
 }
 
+// Up-projection of a block whose TwELL tiles are wider than the capacity
+// while its union fits (bounded forward, block flag 1): the stored slots are
+// incomplete, so h comes from the gate GEMM over the block's union, computed
+// beside the up GEMM on one tile with two B operands (x loaded once):
+// h = x_t . WgT[n] + bg[n] where the row's mask keeps (t, n), else 0, and
+// a = fp16(h) * u written to adense as in the TwELL path (zeros in the
+// positions [n_b, roundup64(n_b))).  About one more GEMM over the union for
+// such a block; the down kernel then treats it like any other.
+template <class Cfg>
+__device__ __forceinline__ void up_rec_tile(const UnionArgs& a, int b, int pt, char* st) {
+  static_assert(Cfg::BM == UB && Cfg::NB == 2, "one row block per M tile, gate and up products");
+  const int nb = a.ucount[b];
+  const int p0 = pt * Cfg::BN;
+  if (p0 >= nb) return;
+  const int m0 = b * UB;
+  const int* ul = a.ulist + (int64_t)b * a.F;
+  typedef DmaTile<Cfg> Tile;
+  Tile g;
+  const Operand A{a.x, a.d, nullptr, a.T};
+  const Operand B[2] = {{a.WgT, a.d, ul, nb}, {a.WuT, a.d, ul, nb}};
+  g.run(A, B, m0, p0, a.d, st, st);
+  uint32_t vbits = 0;
+  const int pend = (nb + 63) & ~63;
+#pragma unroll
+  for (int j = 0; j < Cfg::TN; ++j) {
+    const int p = p0 + Tile::col_of(j);
+    if (p >= pend) continue;
+    const bool inu = p < nb;
+    const int n = inu ? ul[p] : 0;
+    const float bias = (inu && a.bg) ? bf16_to_f32(((const uint16_t*)a.bg)[n]) : 0.f;
+    const uint64_t bit = 1ull << (n & 63);
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t = m0 + Tile::row_of(i, e);
+        if (t >= a.T) continue;
+        float v = 0.f;
+        if (inu && (a.mask[(int64_t)t * a.NT + (n >> 6)] & bit)) {
+          const _Float16 h16 = (_Float16)(g.acc[0][i][j][e] + bias);
+          v = (float)h16 * g.acc[1][i][j][e];
+        }
+        vbits = max(vbits, __float_as_uint(v) & 0x7fffffffu);
+        a.adense[(int64_t)t * a.ucap + p] = (_Float16)v;
+      }
+  }
+  const bool over = vbits > 0x477fe000u;   // above 65504, the largest finite fp16
+  if (__builtin_amdgcn_ballot_w64(over) != 0ull && (threadIdx.x & 63) == 0) atomicOr(a.flag, 1);
+}
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void up_union_rec_kernel(UnionArgs a) {
+  __shared__ __attribute__((aligned(1024))) char st[Cfg::STAGE];
+  const int npt = (a.F + Cfg::BN - 1) / Cfg::BN;
+  const int ntile = ((a.T + UB - 1) / UB) * npt;
+  for (int k = blockIdx.x; k < ntile; k += gridDim.x) {
+    const int b = k / npt;
+    if (a.bflag[b] != 1) continue;                     // workgroup-uniform
+    up_rec_tile<Cfg>(a, b, k - b * npt, st);
+    __syncthreads();                                   // the stage buffer is free again
+  }
+}
+
 // Backward SDDMM of the hybrid format's sparse rows over the union, one
 // (row block b, position tile pt) tile: U = x.WuT[ulist]^T and
 // DA = dY.Wd[ulist]^T (two bf16 MFMA GEMMs, fp32 accumulation), then for
@@ -655,7 +720,7 @@ __device__ __forceinline__ void down_union_tile(const UnionArgs& a, int b, int c
 // ascending neuron order, a = h * (x_t . WuT[n]) (bf16 products, fp32 sums,
 // one fixed-order butterfly over the wave) or a = h for the non-gated layer
 // (WuT null), then y_t += a * Wd[n] over the tile's columns (CPL per lane).
-// The pairs come from the TwELL slots, or, for a block over capacity (whose
+// The pairs come from the TwELL slots, or, for a block over a capacity (whose
 // tiles may have lost slots), from the row's mask with h = x_t . WgT[n] + bg[n]
 // recomputed the same way.  Every column tile recomputes its rows' dot
 // products: this path serves inputs outside the fp16 range or the capacities,
@@ -751,21 +816,25 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void down_union_k
   }
   for (int k = blockIdx.x >> 3; k < ntile; k += gridDim.x >> 3) {
     const int bi = k / nct;
-    if (!TWO && a.bflag && a.bflag[x + 8 * bi]) continue;   // workgroup-uniform
+    if (!TWO && a.bflag && a.bflag[x + 8 * bi] == 2) continue;   // workgroup-uniform
     down_union_tile<Cfg, TWO>(a, x + 8 * bi, k - bi * nct, st0, st1);
     __syncthreads();
   }
   if constexpr (!TWO) {
-    // blocks over capacity (bounded forward), per pair, after the GEMM tiles
+    // blocks over the union capacity (bounded forward), per pair, after the GEMM tiles
     if (a.bflag)
       for (int k = blockIdx.x >> 3; k < ntile; k += gridDim.x >> 3) {
         const int bi = k / nct;
-        if (a.bflag[x + 8 * bi]) down_fallback_tile<Cfg::BN / 64>(a, x + 8 * bi, (k - bi * nct) * Cfg::BN);
+        if (a.bflag[x + 8 * bi] == 2) down_fallback_tile<Cfg::BN / 64>(a, x + 8 * bi, (k - bi * nct) * Cfg::BN);
       }
   }
 }
 
 using UpUnionCfg = DmaCfg1<UB, 256, 2, 4>;
+// gate and up products on one x tile: 128 positions, so two workgroups share a
+// CU (two B operands of 256 positions took one CU each: 2b, every block
+// recomputed, 2.86 against 2.52 ms for the layer)
+using UpRecCfg = DmaCfg1<UB, 128, 2, 4, 2>;
 using DownUnionCfg = DmaCfg1<UB, 256, 2, 4, 1, true, true>;
 using DownUnionCfg128 = DmaCfg<UB, 128, 4, 2, 1, true, true>;
 using DownUnionCfg64 = DmaCfg<UB, 64, 4, 2, 1, true, true>;
@@ -920,6 +989,9 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
   else   // non-gated layer: a = h
     hipLaunchKernelGGL((up_union_kernel<UpUnionCfg, false>), dim3(grid_for(nbx_max * npt, 2)), dim3(UpUnionCfg::NTH),
                        0, s, a);
+  if (a.bflag && WuT)   // blocks over the tile capacity only: h from a gate GEMM over the union
+    hipLaunchKernelGGL((up_union_rec_kernel<UpRecCfg>), dim3(std::max(1, std::min(2 * cus, nblk * npt * 2))),
+                       dim3(UpRecCfg::NTH), 0, s, a);
   if (ev_up) (void)hipEventRecord(ev_up, s);
   if (d % 256 == 0)
     hipLaunchKernelGGL((down_union_kernel<DownUnionCfg>), dim3(grid_for(nbx_max * (d / 256), 2)),

@@ -323,14 +323,17 @@ twell_status twell_ffn_fwd_ex(const twell_ffn_shape *sh, const void *x, const vo
  *   union_cap  union positions per 128-token block that the fp16 buffer of
  *              a = h * u holds (a multiple of 64, 64..F): 2 * union_cap bytes
  *              per token instead of 2 * F
- * A 128-token block with a tile wider than tile_cap, or with more than
- * union_cap neurons active in its tokens, is computed per stored pair in fp32
+ * A 128-token block with a tile wider than tile_cap whose union fits takes
+ * h from a gate GEMM over its union instead of its incomplete TwELL (about
+ * one more GEMM over the union for that block); a block with more than
+ * union_cap neurons active in its tokens is computed per stored pair in fp32
  * inside the down-projection, with h recomputed from x, WgT and bg for its
- * pairs (the mask keeps every pair): exact for any input, slow for such
- * blocks.  The caller picks the capacities from its activation statistics
- * (e.g. the largest per-tile count and block union seen in calibration).
+ * pairs (the mask keeps every pair).  Both are exact for any input; the
+ * second is slow.  The caller picks the capacities from its activation
+ * statistics (e.g. the largest per-tile count and block union seen in
+ * calibration).
  *   n_over_blocks  NULL, or a device int32 that receives the number of
- *                  128-token blocks computed per pair (0: every block fit)
+ *                  128-token blocks over either capacity (0: every block fit)
  *   Other arguments as for twell_ffn_fwd with saved_h NULL and
  *   dense_row_threshold < 0.  bf16 inputs only (EUNSUPPORTED otherwise);
  *   EINVAL for capacities outside the ranges above.  For T <= 256 the call is

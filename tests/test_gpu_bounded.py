@@ -4,11 +4,12 @@ against the CPU oracle and against the ordinary forward.
 * Capacities that every block fits: no block is computed per pair and y is
   bit-identical to twell_ffn_fwd's (the same kernels and summation order;
   only the strides of h and of a differ).
-* Capacities that some or all blocks exceed (a TwELL tile wider than
-  tile_cap, a block union longer than union_cap): those blocks are computed
-  per stored pair in fp32 with h recomputed; y within relative Frobenius error
-  1e-3 of the float64 oracle, and the reported count of such blocks equals
-  the oracle's where the case is built away from the zero band.
+* Capacities that some or all blocks exceed: a block with a TwELL tile wider
+  than tile_cap (union within union_cap) takes h from a gate GEMM over its
+  union, a block whose union is longer than union_cap is computed per stored
+  pair in fp32 with h recomputed; y within relative Frobenius error 1e-3 of
+  the float64 oracle, and the reported count of such blocks equals the
+  oracle's where the case is built away from the zero band.
 Full-size workloads run with the capacities the benchmark uses.
 """
 import numpy as np
@@ -107,7 +108,8 @@ def test_bounded_fits_equals_full_forward(torch, tw, name, kw):
 
 def test_bounded_tile_overflow(torch, tw):
     """tile_cap = 4 at 3% density over 1024 neurons: some blocks hold a row
-    with more than 4 entries in one tile and are computed per pair."""
+    with more than 4 entries in one tile and take h from a gate GEMM over
+    their union."""
     w = make_workload("0.5b", T=1000, d=256, f=1024)
     tilemax, unions = block_stats(_pattern(w), w.T, w.f)
     log(f"[bounded] tile overflow: per-block max tile count {tilemax}")
@@ -152,6 +154,28 @@ def test_bounded_mixed_blocks(torch, tw):
     assert max(even) + 64 <= U < min(odd) - 64                # away from the boundary
     y, n_over = run_bounded(torch, tw, w, 64, U)
     assert n_over == len(odd)
+    check_y(w, y)
+
+
+def test_bounded_both_overflow_kinds(torch, tw):
+    """tile_cap = 4 (every block has a wider tile) with union_cap between the
+    even and the odd blocks' unions: the even blocks take h from the gate GEMM
+    over their union, the odd ones go per pair, in the same launches."""
+    w = make_workload("1.5b", T=1024 + 77, d=256, f=2048)
+    for b0 in range(128, w.T, 256):
+        w.x[b0:b0 + 128] = round_bf16(w.x[b0:b0 + 128] * np.float32(3.0))
+    tilemax, unions = block_stats(_pattern(w), w.T, w.f)
+    even, odd = unions[0::2], unions[1::2]
+    log(f"[bounded] both kinds: max tile counts {tilemax}, even unions {even}, odd unions {odd}")
+    U = (max(even) + 64 + 63) // 64 * 64
+    assert U < min(odd) - 64
+    y, n_over = run_bounded(torch, tw, w, 4, U)
+    # every odd block, and every even block with a count of 6 or more (far
+    # from the zero band's reach; counts of 5 are over the capacity too, but
+    # one entry in the band could bring them to 4)
+    sure = len(odd) + sum(t >= 6 for t in tilemax[0::2])
+    log(f"   blocks over capacity: {n_over} of {len(unions)} (at least {sure})")
+    assert sure <= n_over <= len(unions)
     check_y(w, y)
 
 
