@@ -179,6 +179,30 @@ def test_bounded_both_overflow_kinds(torch, tw):
     check_y(w, y)
 
 
+def test_bounded_tile_overflow_no_bias_bf16_out(torch, tw):
+    """The gate GEMM over the union without a bias (about half the gate
+    values positive, every block's union all of F, within union_cap = F),
+    and bf16 output: every block over the tile capacity of 4."""
+    w = make_workload("0.5b", T=700, d=256, f=1024)
+    w.bg = None
+    ref = O.ffn_fwd_rows(w.x, w.WgT, None, w.WuT, w.Wd, np.arange(w.T))
+    tilemax, unions = block_stats(ref["g"], w.T, w.f)
+    log(f"[bounded] no bias, bf16 out: per-block max tile count {tilemax}")
+    assert min(tilemax) >= 6
+    od = tw.TWELL_BF16
+    shape = tw.ffn_shape(w.T, w.d, w.f, tw.TWELL_BF16, od)
+    ws = torch.empty(tw.twell_ffn_fwd_bounded_workspace(shape, 4, w.f), dtype=torch.uint8, device="cuda")
+    y = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda")
+    cnt = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    x, WgT, WuT, Wd = (to_dev(a, "bf16") for a in (w.x, w.WgT, w.WuT, w.Wd))
+    tw.twell_ffn_fwd_bounded(shape, x, WgT, None, WuT, Wd, y, 4, w.f, ws, n_over_blocks=cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == len(tilemax)
+    err = rel_fro(y.float().cpu().numpy(), ref["y"])
+    log(f"   y rel-Frobenius error {err:.3e}")
+    assert err <= 4e-3                                   # one bf16 rounding of y
+
+
 def test_bounded_with_fp16_overflow(torch, tw):
     """a beyond the fp16 range sends every tile down the per-pair path; the
     blocks over the tile capacity recompute h there."""
@@ -220,5 +244,19 @@ def test_bounded_full_size(torch, tw, name):
     y_full = run_full(torch, tw, w)
     assert np.array_equal(y, y_full), np.abs(y - y_full).max()
     rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([rng.choice(w.T, size=256, replace=False), np.arange(w.T - 16, w.T)]))
+    check_y(w, y, rows)
+
+
+def test_bounded_full_size_tile_overflow(torch, tw):
+    """2b at full size with 4 slots per tile: nearly every block has a row
+    with more than 4 entries in some tile (up to 7 in these inputs), so h
+    comes from the gate GEMM over the blocks' unions."""
+    w = make_workload("2b")
+    log("[bounded] full size 2b, W=4 U=2816")
+    y, n_over = run_bounded(torch, tw, w, 4, 2816)
+    log(f"   blocks over capacity: {n_over} of {(w.T + 127) // 128}")
+    assert n_over > (w.T // 128) // 2
+    rng = np.random.default_rng(9)
     rows = np.unique(np.concatenate([rng.choice(w.T, size=256, replace=False), np.arange(w.T - 16, w.T)]))
     check_y(w, y, rows)
