@@ -260,3 +260,19 @@ def test_bounded_full_size_tile_overflow(torch, tw):
     rng = np.random.default_rng(9)
     rows = np.unique(np.concatenate([rng.choice(w.T, size=256, replace=False), np.arange(w.T - 16, w.T)]))
     check_y(w, y, rows)
+
+
+@pytest.mark.parametrize("W,U", [(4, 640), (64, 64)], ids=["tile-overflow", "union-overflow"])
+def test_bounded_odd_d(torch, tw, W, U):
+    """d = 320: the down kernel's 64-column tiles (per-pair path with one
+    column per lane) and a K of 320 in the gate GEMM over the union."""
+    w = make_workload("0.5b", T=513, d=320, f=640)
+    tilemax, unions = block_stats(_pattern(w), w.T, w.f)
+    log(f"[bounded] d=320 W={W} U={U}: max tile counts {tilemax}, unions {unions}")
+    y, n_over = run_bounded(torch, tw, w, W, U)
+    if W == 64:
+        # every block but the one-token last one (its union of about 20 fits)
+        assert n_over == sum(u > U + 8 for u in unions) and n_over == sum(u > U for u in unions)
+    else:
+        assert n_over >= sum(t >= 6 for t in tilemax)
+    check_y(w, y)
