@@ -18,4 +18,5 @@ from ._lib import (  # noqa: F401
     twell_ffn_bwd_compact_workspace, twell_ffn_bwd_hybrid_compact, twell_ffn_fwd_noalloc, NOALLOC_SCRATCH_BYTES,
     twell_ffn_fwd_bounded_workspace, twell_ffn_fwd_bounded,
     twell_ffn_fwd_compact_workspace, twell_ffn_fwd_compact,
+    twell_relu_ffn_fwd_bounded_workspace, twell_relu_ffn_fwd_bounded,
 )

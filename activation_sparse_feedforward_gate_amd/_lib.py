@@ -99,6 +99,10 @@ def lib() -> ctypes.CDLL:
         L.twell_ffn_fwd_compact_workspace.restype = sz
         L.twell_ffn_fwd_compact.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, P(c_twell_cmat), i32, vp,
                                             sz, vp]
+        L.twell_relu_ffn_fwd_bounded_workspace.argtypes = [P(c_twell_ffn_shape), i32, i32]
+        L.twell_relu_ffn_fwd_bounded_workspace.restype = sz
+        L.twell_relu_ffn_fwd_bounded.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, i32, i32, vp, vp, sz,
+                                                 vp]
         L.twell_ffn_fwd_bounded_workspace.argtypes = [P(c_twell_ffn_shape), i32, i32]
         L.twell_ffn_fwd_bounded_workspace.restype = sz
         L.twell_ffn_fwd_bounded.argtypes = [P(c_twell_ffn_shape), vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
@@ -112,7 +116,7 @@ def lib() -> ctypes.CDLL:
                      "twell_ffn_dense_fwd", "twell_ffn_dense_bwd",
                      "twell_gate_pack",
                      "twell_sparse_up", "twell_sparse_down", "twell_ffn_fwd_noalloc", "twell_ffn_fwd_bounded",
-                     "twell_ffn_fwd_compact"):
+                     "twell_ffn_fwd_compact", "twell_relu_ffn_fwd_bounded"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -264,6 +268,19 @@ def twell_ffn_fwd(shape, x, WgT, bg, WuT, Wd, y, saved_h: Optional[TwellMat], de
                                ctypes.byref(sh) if sh is not None else None, dense_row_threshold,
                                _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
                                _stream(stream)))
+
+
+def twell_relu_ffn_fwd_bounded_workspace(shape: c_twell_ffn_shape, tile_cap: int, union_cap: int) -> int:
+    return int(lib().twell_relu_ffn_fwd_bounded_workspace(ctypes.byref(shape), int(tile_cap), int(union_cap)))
+
+
+def twell_relu_ffn_fwd_bounded(shape, x, W1T, b1, W2, y, tile_cap: int, union_cap: int, ws, n_over_blocks=None,
+                               stream=None) -> None:
+    """The capacity-bounded non-gated layer (see twell_ffn_fwd_bounded)."""
+    _check(lib().twell_relu_ffn_fwd_bounded(ctypes.byref(shape), _ptr(x), _ptr(W1T), _ptr(b1), _ptr(W2), _ptr(y),
+                                            int(tile_cap), int(union_cap), _ptr(n_over_blocks), _ptr(ws),
+                                            ws.numel() * ws.element_size() if ws is not None else 0,
+                                            _stream(stream)))
 
 
 def twell_ffn_fwd_bounded_workspace(shape: c_twell_ffn_shape, tile_cap: int, union_cap: int) -> int:

@@ -775,6 +775,63 @@ twell_status twell_relu_ffn_fwd(const twell_ffn_shape* sh, const void* x, const 
   return TWELL_OK;
 }
 
+// The non-gated layer with the same capacities as twell_ffn_fwd_bounded.
+static size_t relu_bounded_layout(const twell_ffn_shape* sh, int32_t W, int32_t ucap, void* ws, FwdWs* out) {
+  size_t parts[6];
+  cmat_parts(sh->T, sh->F, W, parts);
+  Carver c(ws);
+  FwdWs w{};
+  TwellView& v = w.h;
+  v.T = sh->T; v.F = sh->F; v.NT = sh->F / GPU_C; v.NR = (sh->T + GPU_R - 1) / GPU_R;
+  v.cap = W;
+  v.cnt = (uint8_t*)c.take(parts[0]);
+  v.width = (uint8_t*)c.take(parts[1]);
+  v.val = c.take(parts[2]);
+  v.idx = (uint8_t*)c.take(parts[3]);
+  v.mask = (uint64_t*)c.take(parts[4]);
+  w.uni = c.take(union_ws_bytes(sh->T, sh->d, sh->F, ucap));
+  if (out) *out = w;
+  return c.off;
+}
+
+size_t twell_relu_ffn_fwd_bounded_workspace(const twell_ffn_shape* sh, int32_t tile_cap, int32_t union_cap) {
+  if (!sh || check_shape(sh) != TWELL_OK || sh->in_dt != TWELL_BF16 || !bounded_caps_ok(sh, tile_cap, union_cap))
+    return 0;
+  return relu_bounded_layout(sh, tile_cap, union_cap, nullptr, nullptr);
+}
+
+twell_status twell_relu_ffn_fwd_bounded(const twell_ffn_shape* sh, const void* x, const void* W1T, const void* b1,
+                                        const void* W2, void* y, int32_t tile_cap, int32_t union_cap,
+                                        int32_t* n_over_blocks, void* ws, size_t ws_bytes, hipStream_t stream) {
+  twell_status st = check_shape(sh);
+  if (st) return st;
+  if (sh->in_dt != TWELL_BF16) return fail(TWELL_EUNSUPPORTED, "the bounded forward takes bf16 inputs");
+  if (!bounded_caps_ok(sh, tile_cap, union_cap))
+    return fail(TWELL_EINVAL, "tile_cap=%d must be a multiple of 4 in 4..64 and union_cap=%d a multiple of 64 in "
+                "64..F=%d", tile_cap, union_cap, sh->F);
+  if (sh->T > 0 && (!x || !W1T || !W2 || !y)) return fail(TWELL_EINVAL, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(W1T) || !aligned16(W2) || !aligned16(y) || !aligned16(b1))
+    return fail(TWELL_EINVAL, "tensors must be 16-byte aligned");
+  const size_t need = relu_bounded_layout(sh, tile_cap, union_cap, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return fail(TWELL_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  hipError_t e = hipSuccess;
+  FwdWs w;
+  relu_bounded_layout(sh, tile_cap, union_cap, ws, &w);
+  if (sh->T > 0) {
+    const int out_dt = sh->out_dt == TWELL_BF16 ? DT_BF16 : DT_F32;
+    uint64_t* slabs = nullptr;
+    int* uflag = nullptr;
+    union_slabs_and_flag(sh->T, sh->F, w.uni, &slabs, &uflag);
+    e = launch_gate_twell(DT_BF16, x, W1T, b1, sh->T, sh->d, sh->F, w.h, stream, slabs, uflag);
+    if (e != hipSuccess) return hip_status(e, "gate GEMM");
+    e = launch_union_fwd(x, nullptr, W2, sh->T, sh->d, sh->F, w.h, nullptr, w.uni, y, out_dt, nullptr, stream, nullptr,
+                         nullptr, true, W1T, b1, union_cap);
+    if (e != hipSuccess) return hip_status(e, "union down GEMM");
+  }
+  if (n_over_blocks) e = launch_union_over_count(sh->T, sh->F, w.uni, sh->T > 0 ? union_cap : 0, n_over_blocks, stream);
+  return hip_status(e, "block count");
+}
+
 size_t twell_relu_ffn_dense_fwd_workspace(const twell_ffn_shape* sh) {
   if (!sh || check_shape(sh) != TWELL_OK) return 0;
   return round_up((size_t)sh->T * sh->F * 2, 256);

@@ -433,10 +433,11 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void up_union_ker
 // h = x_t . WgT[n] + bg[n] where the row's mask keeps (t, n), else 0, and
 // a = fp16(h) * u written to adense as in the TwELL path (zeros in the
 // positions [n_b, roundup64(n_b))).  About one more GEMM over the union for
-// such a block; the down kernel then treats it like any other.
-template <class Cfg>
+// such a block; the down kernel then treats it like any other.  GATED =
+// false: the non-gated layer, a = fp16(h) from the gate GEMM alone.
+template <class Cfg, bool GATED>
 __device__ __forceinline__ void up_rec_tile(const UnionArgs& a, int b, int pt, char* st) {
-  static_assert(Cfg::BM == UB && Cfg::NB == 2, "one row block per M tile, gate and up products");
+  static_assert(Cfg::BM == UB && Cfg::NB == (GATED ? 2 : 1), "one row block per M tile, gate (and up) products");
   const int nb = a.ucount[b];
   const int p0 = pt * Cfg::BN;
   if (p0 >= nb) return;
@@ -446,7 +447,7 @@ __device__ __forceinline__ void up_rec_tile(const UnionArgs& a, int b, int pt, c
   Tile g;
   const Operand A{a.x, a.d, nullptr, a.T};
   const Operand B[2] = {{a.WgT, a.d, ul, nb}, {a.WuT, a.d, ul, nb}};
-  g.run(A, B, m0, p0, a.d, st, st);
+  g.run(A, B, m0, p0, a.d, st, st);                  // with one B operand only the first is read
   uint32_t vbits = 0;
   const int pend = (nb + 63) & ~63;
 #pragma unroll
@@ -466,7 +467,7 @@ __device__ __forceinline__ void up_rec_tile(const UnionArgs& a, int b, int pt, c
         float v = 0.f;
         if (inu && (a.mask[(int64_t)t * a.NT + (n >> 6)] & bit)) {
           const _Float16 h16 = (_Float16)(g.acc[0][i][j][e] + bias);
-          v = (float)h16 * g.acc[1][i][j][e];
+          v = GATED ? (float)h16 * g.acc[GATED ? 1 : 0][i][j][e] : (float)h16;
         }
         vbits = max(vbits, __float_as_uint(v) & 0x7fffffffu);
         a.adense[(int64_t)t * a.ucap + p] = (_Float16)v;
@@ -476,7 +477,7 @@ __device__ __forceinline__ void up_rec_tile(const UnionArgs& a, int b, int pt, c
   if (__builtin_amdgcn_ballot_w64(over) != 0ull && (threadIdx.x & 63) == 0) atomicOr(a.flag, 1);
 }
 
-template <class Cfg>
+template <class Cfg, bool GATED>
 __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void up_union_rec_kernel(UnionArgs a) {
   __shared__ __attribute__((aligned(1024))) char st[Cfg::STAGE];
   const int npt = (a.F + Cfg::BN - 1) / Cfg::BN;
@@ -484,7 +485,7 @@ __global__ __launch_bounds__(Cfg::NTH, WavesPerEU<Cfg>::value) void up_union_rec
   for (int k = blockIdx.x; k < ntile; k += gridDim.x) {
     const int b = k / npt;
     if (a.bflag[b] != 1) continue;                     // workgroup-uniform
-    up_rec_tile<Cfg>(a, b, k - b * npt, st);
+    up_rec_tile<Cfg, GATED>(a, b, k - b * npt, st);
     __syncthreads();                                   // the stage buffer is free again
   }
 }
@@ -835,6 +836,7 @@ using UpUnionCfg = DmaCfg1<UB, 256, 2, 4>;
 // CU (two B operands of 256 positions took one CU each: 2b, every block
 // recomputed, 2.86 against 2.52 ms for the layer)
 using UpRecCfg = DmaCfg1<UB, 128, 2, 4, 2>;
+using UpRecReluCfg = DmaCfg1<UB, 128, 2, 4, 1>;
 using DownUnionCfg = DmaCfg1<UB, 256, 2, 4, 1, true, true>;
 using DownUnionCfg128 = DmaCfg<UB, 128, 4, 2, 1, true, true>;
 using DownUnionCfg64 = DmaCfg<UB, 64, 4, 2, 1, true, true>;
@@ -989,9 +991,11 @@ hipError_t launch_union_fwd(const void* x, const void* WuT, const void* Wd, int 
   else   // non-gated layer: a = h
     hipLaunchKernelGGL((up_union_kernel<UpUnionCfg, false>), dim3(grid_for(nbx_max * npt, 2)), dim3(UpUnionCfg::NTH),
                        0, s, a);
-  if (a.bflag && WuT)   // blocks over the tile capacity only: h from a gate GEMM over the union
-    hipLaunchKernelGGL((up_union_rec_kernel<UpRecCfg>), dim3(std::max(1, std::min(2 * cus, nblk * npt * 2))),
-                       dim3(UpRecCfg::NTH), 0, s, a);
+  if (a.bflag) {       // blocks over the tile capacity only: h from a gate GEMM over the union
+    const dim3 grid(std::max(1, std::min(2 * cus, nblk * npt * 2)));
+    if (WuT) hipLaunchKernelGGL((up_union_rec_kernel<UpRecCfg, true>), grid, dim3(UpRecCfg::NTH), 0, s, a);
+    else hipLaunchKernelGGL((up_union_rec_kernel<UpRecReluCfg, false>), grid, dim3(UpRecReluCfg::NTH), 0, s, a);
+  }
   if (ev_up) (void)hipEventRecord(ev_up, s);
   if (d % 256 == 0)
     hipLaunchKernelGGL((down_union_kernel<DownUnionCfg>), dim3(grid_for(nbx_max * (d / 256), 2)),

@@ -205,6 +205,24 @@ def relu_bench(args) -> int:
         out["dense_baseline"] = {"tokens_per_s": T / (dms * 1e-3), "ms_per_step": dms,
                                  "what": "dense ReLU FFN, bf16 act"}
         out["speedup_vs_dense"] = dms / ms
+        out["workspace_bytes"] = {"twell": int(ws.numel()), "own_dense": int(wsd.numel())}
+    caps = None if args.no_bounded else BOUNDED_CAPS.get(args.config)
+    if caps and not args.decode:
+        Wc, Uc = caps
+        bws = tw.twell_relu_ffn_fwd_bounded_workspace(shape, Wc, Uc)
+        wsb = torch.empty(bws, dtype=torch.uint8, device=dev)
+        yb = torch.empty_like(y)
+        nover = torch.zeros((1,), dtype=torch.int32, device=dev)
+        bms = timed(lambda: tw.twell_relu_ffn_fwd_bounded(shape, x, W1T, b1, W2, yb, Wc, Uc, wsb, None, stream))
+        tw.twell_relu_ffn_fwd_bounded(shape, x, W1T, b1, W2, yb, Wc, Uc, wsb, nover, stream)
+        tw.twell_relu_ffn_fwd(shape, x, W1T, b1, W2, y, None, ws, stream)
+        torch.cuda.synchronize()
+        out["bounded_forward"] = {"tile_cap": Wc, "union_cap": Uc, "ms_per_step": bms, "workspace_bytes": int(bws),
+                                  "over_capacity_blocks": int(nover.item()),
+                                  "y_equals_full_forward": bool(torch.equal(yb, y))}
+        if "dense_baseline" in out:
+            out["bounded_forward"]["speedup_vs_dense"] = out["dense_baseline"]["ms_per_step"] / bms
+            out["bounded_forward"]["workspace_vs_own_dense"] = bws / max(1, int(wsd.numel()))
     if not args.no_cpu:
         chunk, done, t0 = 256, 0, time.perf_counter()
         while done < T and time.perf_counter() - t0 < args.cpu_seconds:

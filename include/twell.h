@@ -421,6 +421,23 @@ twell_status twell_relu_ffn_fwd(const twell_ffn_shape *sh, const void *x, const 
                                 const void *W2, void *y, twell_mat *saved_h, void *ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/*
+ * twell_relu_ffn_fwd_bounded: the non-gated layer of twell_relu_ffn_fwd with
+ * the capacities of twell_ffn_fwd_bounded (gate.com ES / ID, first paragraph:
+ * lower peak memory): h in a TwELL of tile_cap slots per tile, a = h over at
+ * most union_cap union positions per 128-token block.  A block with a tile
+ * wider than tile_cap whose union fits takes h from a GEMM of x with its
+ * union's W1T rows; a block with a longer union is computed per stored pair
+ * in fp32 with h recomputed.  Exact for any input.  bf16 inputs only;
+ * capacities, n_over_blocks and errors as for twell_ffn_fwd_bounded, other
+ * arguments as for twell_relu_ffn_fwd (no saved_h).  ws: at least
+ * twell_relu_ffn_fwd_bounded_workspace(sh, tile_cap, union_cap) bytes.
+ */
+size_t twell_relu_ffn_fwd_bounded_workspace(const twell_ffn_shape *sh, int32_t tile_cap, int32_t union_cap);
+twell_status twell_relu_ffn_fwd_bounded(const twell_ffn_shape *sh, const void *x, const void *W1T, const void *b1,
+                                        const void *W2, void *y, int32_t tile_cap, int32_t union_cap,
+                                        int32_t *n_over_blocks, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes for twell_relu_ffn_dense_fwd. */
 size_t twell_relu_ffn_dense_fwd_workspace(const twell_ffn_shape *sh);
 

@@ -138,3 +138,40 @@ def test_relu_ffn_dense_baseline(torch, tw, name, kw):
     log(f"[relu dense] {name} T={w.T}")
     y, _ = run_relu(torch, tw, w, dense=True)
     check_relu(w, y, None, tol=5e-3)
+
+
+def run_relu_bounded(torch, tw, w, W, U):
+    x, W1T, b1, W2 = (to_dev(a, "bf16") for a in (w.x, w.WgT, w.bg, w.Wd))
+    shape = tw.ffn_shape(w.T, w.d, w.f, tw.TWELL_BF16, tw.TWELL_F32)
+    nbytes = tw.twell_relu_ffn_fwd_bounded_workspace(shape, W, U)
+    assert nbytes > 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty((w.T, w.d), dtype=torch.float32, device="cuda")
+    cnt = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    tw.twell_relu_ffn_fwd_bounded(shape, x, W1T, b1, W2, y, W, U, ws, n_over_blocks=cnt)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), int(cnt.item())
+
+
+@pytest.mark.parametrize("W,U,kind", [(64, 1024, "fits"), (4, 1024, "tile"), (64, 64, "union")])
+def test_relu_ffn_bounded(torch, tw, W, U, kind):
+    """The capacity-bounded non-gated layer: with capacities every block fits,
+    y equals twell_relu_ffn_fwd's bit for bit; over the tile capacity h comes
+    from a GEMM of x with the union's W1T rows; over the union capacity the
+    blocks go per pair.  y against the oracle in every case."""
+    w = make_workload("0.5b", T=600, d=256, f=1024)
+    g = w.x.astype(np.float64) @ w.WgT.astype(np.float64).T + w.bg.astype(np.float64)
+    pos = g > 0
+    tilemax = [int(pos[b:b + 128].reshape(-1, w.f // 64, 64).sum(axis=2).max()) for b in range(0, w.T, 128)]
+    unions = [int(pos[b:b + 128].any(axis=0).sum()) for b in range(0, w.T, 128)]
+    log(f"[relu bounded] {kind}: W={W} U={U}, max tile counts {tilemax}, unions {unions}")
+    y, n_over = run_relu_bounded(torch, tw, w, W, U)
+    if kind == "fits":
+        assert n_over == 0
+        y_full, _ = run_relu(torch, tw, w, saved=False)
+        assert np.array_equal(y, y_full)
+    elif kind == "tile":
+        assert n_over >= sum(t >= 6 for t in tilemax)
+    else:
+        assert n_over == sum(u > U for u in unions) and n_over == len(unions)
+    check_relu(w, y, None)

@@ -336,3 +336,23 @@ def test_fwd_compact_argument_errors():
     assert call(x=None) == tw.TWELL_EINVAL
     assert call(x=24) == tw.TWELL_EINVAL
     assert call(ws_bytes=need - 1) == tw.TWELL_EWORKSPACE
+
+
+def test_relu_bounded_workspace_and_errors():
+    L = tw.lib()
+    T, d, F = 4096, 256, 1024
+    sh = tw.ffn_shape(T, d, F, tw.TWELL_BF16, tw.TWELL_F32)
+    full = tw.twell_relu_ffn_fwd_workspace(sh)
+    w8 = tw.twell_relu_ffn_fwd_bounded_workspace(sh, 8, 256)
+    assert full <= tw.twell_relu_ffn_fwd_bounded_workspace(sh, 64, F) <= full + 1024
+    assert abs((full - w8) - (5 * T * F * (64 - 8) // 64 + 2 * T * (F - 256))) <= 2048
+    assert tw.twell_relu_ffn_fwd_bounded_workspace(sh, 6, 256) == 0
+    assert tw.twell_relu_ffn_fwd_bounded_workspace(tw.ffn_shape(T, d, F, tw.TWELL_F32, tw.TWELL_F32), 8, 256) == 0
+
+    def call(W=8, U=256, ws_bytes=w8, x=16, shape=sh):
+        return L.twell_relu_ffn_fwd_bounded(ctypes.byref(shape), x, 32, None, 48, 64, W, U, None, 256, ws_bytes, None)
+    assert call(W=2) == tw.TWELL_EINVAL
+    assert call(U=100) == tw.TWELL_EINVAL
+    assert call(x=None) == tw.TWELL_EINVAL
+    assert call(ws_bytes=w8 - 1) == tw.TWELL_EWORKSPACE
+    assert call(shape=tw.ffn_shape(T, d, F, tw.TWELL_F32, tw.TWELL_F32)) == tw.TWELL_EUNSUPPORTED
