@@ -342,7 +342,10 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool, 
         dbg = torch.empty((f,), dtype=torch.float32, device=dev)
         nD = torch.empty((1,), dtype=torch.int32, device=dev)
         ws_bwd_bytes = tw.twell_ffn_bwd_workspace(shape, tau)
-        wsb = torch.empty(max(1, ws_bwd_bytes), dtype=torch.uint8, device=dev)
+        # the forward's workspace is free once it returns: one buffer serves both calls
+        if ws_bwd_bytes > ws_fwd_bytes:
+            wsf = torch.empty(ws_bwd_bytes, dtype=torch.uint8, device=dev)
+        wsb = wsf
 
     def step(evs=None):
         if evs is None:
@@ -432,7 +435,7 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool, 
             out["dense_vs_sparse_rel_diff"] = (y - yd).norm().item() / max(yd.norm().item(), 1e-30)
         out["speedup_vs_dense"] = dms / ms_step
         # device memory the step needs beyond its inputs and outputs
-        twell_ws = ws_fwd_bytes + (tw.twell_mat_bytes(T, f)[0] + ws_bwd_bytes if training else 0)
+        twell_ws = (max(ws_fwd_bytes, ws_bwd_bytes) + tw.twell_mat_bytes(T, f)[0]) if training else ws_fwd_bytes
         out["workspace_bytes"] = {"twell": int(twell_ws), "own_dense": int(dense_ws)}
 
     caps = None if args.no_bounded else BOUNDED_CAPS.get(name)
@@ -479,11 +482,11 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool, 
         c = tw.alloc_twell_cmat(T, f, W, device=dev)
         fws = tw.twell_ffn_fwd_compact_workspace(shape, W)
         bws = tw.twell_ffn_bwd_compact_workspace(shape, tau, W)
-        wfc = torch.empty(max(1, fws), dtype=torch.uint8, device=dev)
-        wsc = torch.empty(max(1, bws), dtype=torch.uint8, device=dev)
+        # the forward's workspace is free once it returns: one buffer serves both calls
+        wsc = torch.empty(max(1, fws, bws), dtype=torch.uint8, device=dev)
 
         def compact_step():
-            tw.twell_ffn_fwd_compact(shape, x, WgT, bg, WuT, Wd, y, c, tau, wfc, stream)
+            tw.twell_ffn_fwd_compact(shape, x, WgT, bg, WuT, Wd, y, c, tau, wsc, stream)
             tw.twell_ffn_bwd_hybrid_compact(shape, x, WgT, bg, WuT, Wd, dY, c, tau, 0.0, False, dX, dW[0], dW[1],
                                             dW[2], dbg, nD, wsc, stream)
         cms = _timed(compact_step, steps, warmup, stream, warm_s)
@@ -493,14 +496,14 @@ def measure(args, name: str, decode: bool, steps: int, warmup: int, full: bool, 
             "overflow_rows": int(c.ovf.to(torch.int64).sum().item()), "dense_rows": int(nD.item()),
             "saved_state_bytes": saved_c,
             "full_saved_state_bytes": tw.twell_mat_bytes(T, f)[0],
-            "workspace_bytes": {"forward": int(fws), "backward": int(bws), "saved_state": int(saved_c),
-                                "total": int(fws + bws + saved_c)},
+            "workspace_bytes": {"forward": int(fws), "backward": int(bws), "shared": int(max(fws, bws)),
+                                "saved_state": int(saved_c), "peak": int(max(fws, bws) + saved_c)},
         }
         if "dense_baseline" in out:
             out["compact_twell"]["speedup_vs_dense"] = out["dense_baseline"]["ms_per_step"] / cms
-            out["compact_twell"]["workspace_vs_own_dense"] = (fws + bws + saved_c) / max(
+            out["compact_twell"]["workspace_vs_own_dense"] = (max(fws, bws) + saved_c) / max(
                 1, out["workspace_bytes"]["own_dense"])
-        del wfc, wsc
+        del wsc
     out["_workload"] = w
     if not full:
         return out
