@@ -147,6 +147,19 @@ size_t fwd_layout(const twell_ffn_shape* sh, bool training, void* ws, FwdWs* out
   mat_parts(sh->T, sh->F, GPU_R, GPU_C, TWELL_F32, parts);
   Carver c(ws);
   FwdWs w{};
+  if (training) {
+    w.flag = (uint8_t*)c.take((size_t)sh->T);
+    w.list = (int*)c.take((size_t)sh->T * 4);
+    w.nD = (int*)c.take(4);
+  }
+  // the dense rows' activation buffer overlays the sparse phases' buffers:
+  // the dense-row forward runs after the down-projection, on the same stream
+  size_t act_end = 0;
+  if (training) {
+    Carver dn(ws ? (char*)ws + c.off : nullptr);
+    w.act = (float*)dn.take((size_t)sh->T * sh->F * 4);
+    act_end = c.off + dn.off;
+  }
   TwellView& v = w.h;
   v.T = sh->T; v.F = sh->F; v.NT = sh->F / GPU_C; v.NR = (sh->T + GPU_R - 1) / GPU_R;
   v.cnt = (uint8_t*)c.take(parts[0]);
@@ -154,19 +167,13 @@ size_t fwd_layout(const twell_ffn_shape* sh, bool training, void* ws, FwdWs* out
   v.val = c.take(parts[2]);
   v.idx = (uint8_t*)c.take(parts[3]);
   v.mask = (uint64_t*)c.take(parts[4]);
-  if (training) {
-    w.flag = (uint8_t*)c.take((size_t)sh->T);
-    w.list = (int*)c.take((size_t)sh->T * 4);
-    w.nD = (int*)c.take(4);
-    w.act = (float*)c.take((size_t)sh->T * sh->F * 4);
-  }
   if (few_token_path(sh, training)) {
     w.dec = c.take(decode_ws_bytes(sh->T, sh->d, sh->F));
   } else if (sh->in_dt == TWELL_BF16) {
     w.uni = c.take(union_ws_bytes(sh->T, sh->d, sh->F));
   }
   if (out) *out = w;
-  return c.off;
+  return c.off > act_end ? c.off : act_end;
 }
 
 // Workspace of the capacity-bounded forward (T > DECODE_T_MAX): the TwELL of
@@ -222,8 +229,13 @@ size_t bwd_layout(const twell_ffn_shape* sh, int32_t tau, void* ws, BwdWs* out, 
   w.flag = (uint8_t*)c.take((size_t)T);
   w.list = (int*)c.take((size_t)T * 4);
   w.nD = (int*)c.take(4);
-  w.buf3 = (float*)c.take((size_t)(T * 3 * F) * 4);
-  w.dbg_part = (float*)c.take((size_t)(((T + 63) / 64) * F) * 4);
+  // the dense-row branch runs to its end before the sparse branch starts (one
+  // stream), so the sparse branch's buffers overlay the dense branch's
+  Carver dn(ws ? (char*)ws + c.off : nullptr);
+  dn.off = 0;
+  w.buf3 = (float*)dn.take((size_t)(T * 3 * F) * 4);
+  w.dbg_part = (float*)dn.take((size_t)(((T + 63) / 64) * F) * 4);
+  const size_t dense_end = c.off + dn.off;
   w.aval = (float*)c.take(slots * 4);
   w.dgval = (float*)c.take(slots * 4);
   w.duval = (float*)c.take(slots * 4);
@@ -232,7 +244,7 @@ size_t bwd_layout(const twell_ffn_shape* sh, int32_t tau, void* ws, BwdWs* out, 
   w.entries = (uint32_t*)c.take((size_t)(T * per_row) * 4);
   if (sh->in_dt == TWELL_BF16) w.uni = c.take(union_bwd_ws_bytes((int)T, sh->d, (int)F));
   if (out) *out = w;
-  return c.off;
+  return c.off > dense_end ? c.off : dense_end;
 }
 
 }  // namespace
@@ -595,7 +607,11 @@ static size_t fwd_compact_layout(const twell_ffn_shape* sh, int32_t W, void* ws,
   w.flag = (uint8_t*)c.take((size_t)sh->T);
   w.list = (int*)c.take((size_t)sh->T * 4);
   w.nD = (int*)c.take(4);
-  w.act = (float*)c.take((size_t)sh->T * sh->F * 4);
+  // the dense rows' activation buffer overlays the sparse phases' buffers
+  // (the dense-row forward runs after the down-projection, on the same stream)
+  Carver dn(ws ? (char*)ws + c.off : nullptr);
+  w.act = (float*)dn.take((size_t)sh->T * sh->F * 4);
+  const size_t act_end = c.off + dn.off;
   float* av = nullptr;
   if (sh->in_dt == TWELL_BF16) {
     w.uni = c.take(union_ws_bytes(sh->T, sh->d, sh->F));
@@ -606,7 +622,7 @@ static size_t fwd_compact_layout(const twell_ffn_shape* sh, int32_t W, void* ws,
   }
   if (out) *out = w;
   if (aval) *aval = av;
-  return c.off;
+  return c.off > act_end ? c.off : act_end;
 }
 
 size_t twell_ffn_fwd_compact_workspace(const twell_ffn_shape* sh, int32_t W) {

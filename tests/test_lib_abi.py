@@ -205,7 +205,10 @@ def test_bwd_compact_argument_errors():
     full = tw.twell_ffn_bwd_workspace(sh, 51)
     assert tw.twell_ffn_bwd_compact_workspace(sh, 51, 64) == full
     slots = 4 * 8 * 16 * 4                         # NR * NT * 16 rows, per slot of a tile, fp32
-    assert abs((full - need) - 3 * slots * (64 - 4)) <= 3 * 256
+    # at most that much smaller (the sparse branch's buffers overlay the dense
+    # branch's [T][3F] fp32-sized buffer, which may then set the size)
+    assert 0 < full - need <= 3 * slots * (64 - 4) + 3 * 256
+    assert need >= 64 * 3 * 512 * 4
     assert tw.twell_ffn_bwd_compact_workspace(sh, 51, 0) == 0
     assert tw.twell_ffn_bwd_compact_workspace(sh, 51, 65) == 0
 
