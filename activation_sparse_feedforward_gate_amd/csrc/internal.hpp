@@ -111,6 +111,15 @@ hipError_t launch_compact_finish(const CompactArgs& a, hipStream_t s);
 hipError_t launch_classify(const TwellView& h, int tau, uint8_t* flag, int* list, int* n_out, int* n_copy,
                            hipStream_t s, const uint8_t* force = nullptr);
 
+// Rows per round of the dense-row branch: its buffers hold this many rows and
+// it runs in ceil(T / cap) rounds over the dense-row list (all of T up to
+// 1024 tokens, else half of T rounded up to 128 rows: two rounds at most).
+inline int dense_row_cap(int T) {
+  if (T <= 1024) return T;
+  const int h = (T + 1) / 2;
+  return (h + 127) / 128 * 128;
+}
+
 // Dense-branch forward on the listed rows: actbuf [T][F] (rows < n used)
 // receives ReLU(g)*u, then y[list[r]] = actbuf[r].Wd.
 hipError_t launch_dense_rows_fwd(int in_dt, const void* x, const void* WgT, const void* bg, const void* WuT,

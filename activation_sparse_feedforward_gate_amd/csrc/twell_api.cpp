@@ -157,7 +157,7 @@ size_t fwd_layout(const twell_ffn_shape* sh, bool training, void* ws, FwdWs* out
   size_t act_end = 0;
   if (training) {
     Carver dn(ws ? (char*)ws + c.off : nullptr);
-    w.act = (float*)dn.take((size_t)sh->T * sh->F * 4);
+    w.act = (float*)dn.take((size_t)dense_row_cap(sh->T) * sh->F * 4);   // one round of dense rows
     act_end = c.off + dn.off;
   }
   TwellView& v = w.h;
@@ -233,8 +233,10 @@ size_t bwd_layout(const twell_ffn_shape* sh, int32_t tau, void* ws, BwdWs* out, 
   // stream), so the sparse branch's buffers overlay the dense branch's
   Carver dn(ws ? (char*)ws + c.off : nullptr);
   dn.off = 0;
-  w.buf3 = (float*)dn.take((size_t)(T * 3 * F) * 4);
-  w.dbg_part = (float*)dn.take((size_t)(((T + 63) / 64) * F) * 4);
+  // the dense rows go in rounds of dense_row_cap(T) rows
+  const int64_t DC = dense_row_cap((int)T);
+  w.buf3 = (float*)dn.take((size_t)(DC * 3 * F) * 4);
+  w.dbg_part = (float*)dn.take((size_t)(((DC + 63) / 64) * F) * 4);
   const size_t dense_end = c.off + dn.off;
   w.aval = (float*)c.take(slots * 4);
   w.dgval = (float*)c.take(slots * 4);
@@ -610,7 +612,7 @@ static size_t fwd_compact_layout(const twell_ffn_shape* sh, int32_t W, void* ws,
   // the dense rows' activation buffer overlays the sparse phases' buffers
   // (the dense-row forward runs after the down-projection, on the same stream)
   Carver dn(ws ? (char*)ws + c.off : nullptr);
-  w.act = (float*)dn.take((size_t)sh->T * sh->F * 4);
+  w.act = (float*)dn.take((size_t)dense_row_cap(sh->T) * sh->F * 4);    // one round of dense rows
   const size_t act_end = c.off + dn.off;
   float* av = nullptr;
   if (sh->in_dt == TWELL_BF16) {

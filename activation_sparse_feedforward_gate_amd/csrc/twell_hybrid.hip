@@ -103,7 +103,16 @@ struct DenseRowsArgs {
   float* dbg;
   int dbg_rows;       // rows per dbg partial
   float l1;           // backward: added to dG where g > 0 (activation penalty)
+  // rounds: the launch covers list entries [r0, r0 + cap) (rows already points
+  // at entry r0; buf and dbg_part hold cap rows), accum: add the weight and
+  // bias gradients to those of the earlier rounds
+  int r0, cap, accum;
 };
+
+// dense rows of this round
+__device__ __forceinline__ int round_rows(const DenseRowsArgs& a) {
+  return min(max(*a.n_rows - a.r0, 0), a.cap);
+}
 
 template <bool BF16IN>
 __device__ __forceinline__ float ld_bias(const void* b, int n) {
@@ -117,7 +126,7 @@ __device__ __forceinline__ float ld_bias(const void* b, int n) {
 template <class Cfg2, class Cfg1, bool BF16IN, bool BWD>
 __global__ __launch_bounds__(Cfg2::NTH) void dense_rows_act_kernel(DenseRowsArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg2::LDS_BYTES];
-  const int nD = *a.n_rows;
+  const int nD = round_rows(a);
   const int nbn = a.F / Cfg2::BN;
   const int bm = blockIdx.x / nbn, bn = blockIdx.x % nbn;
   const int m0 = bm * Cfg2::BM, n0 = bn * Cfg2::BN;
@@ -167,7 +176,7 @@ template <class Cfg2, class Cfg1, bool BWD>
 __global__ __launch_bounds__(Cfg2::NTH, WavesPerEU<Cfg2>::value) void dense_rows_act_dma_kernel(DenseRowsArgs a) {
   static_assert(Cfg2::SINGLE && Cfg1::SINGLE && Cfg2::STAGE >= Cfg1::STAGE, "one stage buffer for both GEMMs");
   __shared__ __attribute__((aligned(1024))) char st[Cfg2::STAGE];
-  const int nD = *a.n_rows;
+  const int nD = round_rows(a);
   const int nbn = a.F / Cfg2::BN;
   const int bm = blockIdx.x / nbn, bn = blockIdx.x % nbn;
   const int m0 = bm * Cfg2::BM, n0 = bn * Cfg2::BN;
@@ -259,7 +268,7 @@ __global__ __launch_bounds__(Cfg2::NTH, WavesPerEU<Cfg2>::value) void dense_rows
 template <class Cfg, bool BWD>
 __global__ __launch_bounds__(Cfg::NTH) void dense_rows_out16_kernel(DenseRowsArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
-  const int nD = *a.n_rows;
+  const int nD = round_rows(a);
   const int nbn = a.d / Cfg::BN;
   const int bm = blockIdx.x / nbn, bn = blockIdx.x % nbn;
   const int m0 = bm * Cfg::BM, n0 = bn * Cfg::BN;
@@ -310,7 +319,7 @@ template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTH) void dense_rows_wgrad16_kernel(DenseRowsArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE];
-  const int nD = *a.n_rows;
+  const int nD = round_rows(a);
   const int nbn = a.d / Cfg::BN;
   const int tl = xcd_remap(blockIdx.x, gridDim.x);
   const int bm = tl / nbn, bn = tl % nbn;
@@ -322,6 +331,7 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_rows_wgrad16_kernel(DenseRowsA
   const void* V = part == 2 ? a.dY : a.x;
   typedef DmaTile<Cfg> Tile;
   Tile g;
+  if (nD == 0 && a.accum) return;                   // nothing to add in this round
   if (nD == 0) {
     const Operand A{b16, ld16, nullptr, 0};
     const Operand B{V, a.d, a.rows, a.T};
@@ -343,7 +353,10 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_rows_wgrad16_kernel(DenseRowsA
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) out[(int64_t)(mp + Tile::row_of(i, e)) * a.d + col] = g.acc[0][i][j][e];
+      for (int e = 0; e < 16; ++e) {
+        float* o = out + (int64_t)(mp + Tile::row_of(i, e)) * a.d + col;
+        *o = a.accum ? *o + g.acc[0][i][j][e] : g.acc[0][i][j][e];
+      }
   }
 }
 
@@ -352,7 +365,7 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_rows_wgrad16_kernel(DenseRowsA
 template <class Cfg, bool BWD>
 __global__ __launch_bounds__(Cfg::NTH) void dense_rows_out_kernel(DenseRowsArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
-  const int nD = *a.n_rows;
+  const int nD = round_rows(a);
   const int nbn = a.d / Cfg::BN;
   const int bm = blockIdx.x / nbn, bn = blockIdx.x % nbn;
   const int m0 = bm * Cfg::BM, n0 = bn * Cfg::BN;
@@ -401,11 +414,12 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_rows_out_kernel(DenseRowsArgs 
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTH) void dense_rows_wgrad_kernel(DenseRowsArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
-  const int nD = *a.n_rows;
+  const int nD = round_rows(a);
   const int nbn = a.d / Cfg::BN;
   const int bm = blockIdx.x / nbn, bn = blockIdx.x % nbn;
   const int m0 = bm * Cfg::BM, n0 = bn * Cfg::BN;
   const int part = m0 / a.F;                      // 0: dWgT, 1: dWuT, 2: dWd (tiles never straddle)
+  if (nD == 0 && a.accum) return;                 // nothing to add in this round
   GemmTile<Cfg> g;
   const Operand A{a.buf, 3 * (int64_t)a.F, nullptr, 3 * a.F};
   const Operand B{part == 2 ? a.dY : a.x, a.d, a.rows, a.T};
@@ -420,7 +434,8 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_rows_wgrad_kernel(DenseRowsArg
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int m = mrow0 + GemmTile<Cfg>::row_of(i, e);
-        out[(int64_t)m * a.d + col] = g.acc[0][i][j][e];
+        float* o = out + (int64_t)m * a.d + col;
+        *o = a.accum ? *o + g.acc[0][i][j][e] : g.acc[0][i][j][e];
       }
   }
 }
@@ -428,7 +443,7 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_rows_wgrad_kernel(DenseRowsArg
 // dbg over the dense rows: per 64-row chunk partial column sums of dG, then
 // a fixed-order sum of the partials (written, not accumulated).
 __global__ __launch_bounds__(256) void dense_rows_dbg_part_kernel(DenseRowsArgs a) {
-  const int nD = *a.n_rows;
+  const int nD = round_rows(a);
   const int n = blockIdx.x * 256 + threadIdx.x;
   const int c = blockIdx.y;
   if (c * 64 >= nD || n >= a.F) return;
@@ -439,13 +454,14 @@ __global__ __launch_bounds__(256) void dense_rows_dbg_part_kernel(DenseRowsArgs 
 }
 
 __global__ __launch_bounds__(256) void dense_rows_dbg_sum_kernel(DenseRowsArgs a) {
-  const int nD = *a.n_rows;
+  const int nD = round_rows(a);
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= a.F) return;
+  if (nD == 0 && a.accum) return;
   const int nc = (nD + a.dbg_rows - 1) / a.dbg_rows;
   float s = 0.f;
   for (int c = 0; c < nc; ++c) s += a.dbg_part[(int64_t)c * a.F + n];
-  a.dbg[n] = s;
+  a.dbg[n] = a.accum ? a.dbg[n] + s : s;
 }
 
 // Configurations.  act: 128x128 block, 4 waves, gate+up (2 B operands) then dA.
@@ -580,26 +596,43 @@ static hipError_t dense_rows_t(const DenseRowsArgs& a, hipStream_t s) {
   else return dense_rows_f32<BWD>(a, s);
 }
 
+// The dense rows go in rounds of dense_row_cap(T) list entries, each through
+// the whole branch with buffers of that many rows (the count is known only on
+// the device: a round past it does nothing).
 hipError_t launch_dense_rows_fwd(int in_dt, const void* x, const void* WgT, const void* bg, const void* WuT,
                                  const void* Wd, int T, int d, int F, const int* rows, const int* n_rows,
                                  float* actbuf, int out_dt, void* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  DenseRowsArgs a{};
-  a.x = x; a.WgT = WgT; a.bg = bg; a.WuT = WuT; a.Wd = Wd; a.T = T; a.d = d; a.F = F;
-  a.rows = rows; a.n_rows = n_rows; a.buf = actbuf; a.y = y; a.out_bf16 = out_dt == DT_BF16;
-  return in_dt == DT_BF16 ? dense_rows_t<true, false>(a, s) : dense_rows_t<false, false>(a, s);
+  const int cap = dense_row_cap(T);
+  hipError_t e = hipSuccess;
+  for (int r0 = 0; r0 < T && e == hipSuccess; r0 += cap) {
+    DenseRowsArgs a{};
+    a.x = x; a.WgT = WgT; a.bg = bg; a.WuT = WuT; a.Wd = Wd; a.T = cap; a.d = d; a.F = F;
+    a.rows = rows + r0; a.n_rows = n_rows; a.buf = actbuf; a.y = y; a.out_bf16 = out_dt == DT_BF16;
+    a.r0 = r0; a.cap = cap; a.accum = r0 > 0;
+    e = in_dt == DT_BF16 ? dense_rows_t<true, false>(a, s) : dense_rows_t<false, false>(a, s);
+  }
+  return e;
 }
 
 hipError_t launch_dense_rows_bwd(int in_dt, const void* x, const void* WgT, const void* bg, const void* WuT,
                                  const void* Wd, const void* dY, int T, int d, int F, const int* rows,
                                  const int* n_rows, float* buf3, float* dbg_part, float* dX, float* dWgT,
                                  float* dWuT, float* dWd, float* dbg, hipStream_t s, float l1) {
-  DenseRowsArgs a{};
-  a.l1 = l1;
-  a.x = x; a.WgT = WgT; a.bg = bg; a.WuT = WuT; a.Wd = Wd; a.dY = dY; a.T = T; a.d = d; a.F = F;
-  a.rows = rows; a.n_rows = n_rows; a.buf = buf3; a.dX = dX; a.dWgT = dWgT; a.dWuT = dWuT; a.dWd = dWd;
-  a.dbg_part = dbg_part; a.dbg = dbg;
-  return in_dt == DT_BF16 ? dense_rows_t<true, true>(a, s) : dense_rows_t<false, true>(a, s);
+  const int cap = dense_row_cap(T);
+  hipError_t e = hipSuccess;
+  // T == 0: one round with no rows writes zero weight gradients
+  for (int r0 = 0; (r0 < T || r0 == 0) && e == hipSuccess; r0 += cap) {
+    DenseRowsArgs a{};
+    a.l1 = l1;
+    a.x = x; a.WgT = WgT; a.bg = bg; a.WuT = WuT; a.Wd = Wd; a.dY = dY; a.T = cap; a.d = d; a.F = F;
+    a.rows = rows + r0; a.n_rows = n_rows; a.buf = buf3; a.dX = dX; a.dWgT = dWgT; a.dWuT = dWuT; a.dWd = dWd;
+    a.dbg_part = dbg_part; a.dbg = dbg;
+    a.r0 = r0; a.cap = cap; a.accum = r0 > 0;
+    e = in_dt == DT_BF16 ? dense_rows_t<true, true>(a, s) : dense_rows_t<false, true>(a, s);
+    if (cap == 0) break;
+  }
+  return e;
 }
 
 // ------------------------------------------------------------------ sparse-branch weight gradients

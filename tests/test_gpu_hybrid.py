@@ -124,12 +124,16 @@ def test_hybrid_threshold_limits(torch, tw, tau_kind):
     check_full(w, got, tau)
 
 
-@pytest.mark.parametrize("d,f", [(128, 640), (256, 1280)], ids=["d128-f640", "d256-f1280"])
-def test_hybrid_all_dense_many_rows(torch, tw, d, f):
-    """Every row dense with more than 1024 of them: the dense-row weight
-    gradients run their K loop over the rows in two chunks (1024 + 76), on
-    the 64x64 (d = 128) and the 256x256 (d = 256, F = 1280) tiles."""
-    w = make_workload("hybrid", T=1100, d=d, f=f)
+@pytest.mark.parametrize("T,d,f", [(1100, 128, 640), (2200, 128, 640), (2200, 256, 1280)],
+                         ids=["1100-d128", "2200-d128", "2200-d256"])
+def test_hybrid_all_dense_many_rows(torch, tw, T, d, f):
+    """Every row dense with more than 1024 of them: the dense-row branch runs
+    in two rounds of half the rows (640 + 460 at T = 1100; 1152 + 1048 at
+    T = 2200, where each round's weight gradients run their K loop in two
+    chunks of at most 1024 rows), the second adding its weight and bias
+    gradients to the first's, on the 64x64 (d = 128) and the 256x256
+    (d = 256, F = 1280) tiles."""
+    w = make_workload("hybrid", T=T, d=d, f=f)
     log(f"[hybrid] all dense T={w.T} d={w.d} f={w.f}")
     got = run_train(torch, tw, w, -1)
     assert got["nD"] == w.T
@@ -243,3 +247,14 @@ def test_hybrid_fp16_overflow_falls_back(torch, tw):
     log("[hybrid] fp16 overflow in the backward")
     got = run_train(torch, tw, w, w.tau)
     check_full(w, got, w.tau)
+
+
+def test_hybrid_all_dense_rounds_fp32(torch, tw):
+    """fp32 inputs, every row dense, T = 1100: the register-staged dense-row
+    kernels in two rounds (the weight and bias gradients of the second added
+    to the first's)."""
+    w = make_workload("tiny_f32", T=1100, d=128, f=512, grad=True)
+    log(f"[hybrid] fp32 all dense T={w.T} d={w.d} f={w.f}")
+    got = run_train(torch, tw, w, -1)
+    assert got["nD"] == w.T
+    check_full(w, got, -1)
