@@ -148,7 +148,10 @@ twell_status twell_ffn_fwd(const twell_ffn_shape *sh, const void *x, const void 
 
 /* Workspace bytes for twell_ffn_bwd_hybrid with this shape and threshold
  * (the sparse branch's pair index is sized by min(F, threshold) pairs per
- * row).  0 for an invalid shape. */
+ * row; the dense rows go in rounds of half the tokens, all of them up to
+ * 1024, and the sparse branch's buffers reuse the dense branch's memory).
+ * 0 for an invalid shape.  The forward's workspace is free once it returns,
+ * so one buffer of the larger size serves both calls. */
 size_t twell_ffn_bwd_workspace(const twell_ffn_shape *sh, int32_t dense_row_threshold);
 
 /*
