@@ -123,8 +123,9 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_down_kernel(DenseArgs a) {
         const int row = m0 + Tile::row_of(i, e);
         if (row < a.T) {
           const float v = g.acc[0][i][j][e];
-          if (a.out_bf16) ((uint16_t*)a.y)[(int64_t)row * a.d + col] = (uint16_t)f32_to_bf16_bits(v);
-          else ((float*)a.y)[(int64_t)row * a.d + col] = v;
+          // y streams past the caches, as the TwELL path's does
+          if (a.out_bf16) __builtin_nontemporal_store((uint16_t)f32_to_bf16_bits(v), (uint16_t*)a.y + (int64_t)row * a.d + col);
+          else __builtin_nontemporal_store(v, (float*)a.y + (int64_t)row * a.d + col);
         }
       }
   }
