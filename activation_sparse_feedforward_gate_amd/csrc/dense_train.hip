@@ -189,7 +189,7 @@ __global__ __launch_bounds__(Cfg::NTH) void train_dx_kernel(TrainArgs a, float* 
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = m0 + Tile::row_of(i, e);
-        if (row < a.T) dX[(int64_t)row * a.d + col] = g.acc[0][i][j][e];
+        if (row < a.T) __builtin_nontemporal_store(g.acc[0][i][j][e], dX + (int64_t)row * a.d + col);   // streamed, as the TwELL step's
       }
   }
 }

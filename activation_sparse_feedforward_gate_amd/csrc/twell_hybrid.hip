@@ -297,7 +297,7 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_rows_out16_kernel(DenseRowsArg
           const int64_t t = a.rows[r];
           const float v = g.acc[0][i][j][e];
           if constexpr (BWD) {
-            a.dX[t * a.d + col] = v;
+            __builtin_nontemporal_store(v, a.dX + t * a.d + col);   // streamed like the sparse rows' dX
           } else {
             if (a.out_bf16) ((uint16_t*)a.y)[t * a.d + col] = (uint16_t)f32_to_bf16_bits(v);
             else ((float*)a.y)[t * a.d + col] = v;
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(Cfg::NTH) void dense_rows_out_kernel(DenseRowsArgs 
           const int64_t t = a.rows[r];
           const float v = g.acc[0][i][j][e];
           if constexpr (BWD) {
-            a.dX[t * a.d + col] = v;
+            __builtin_nontemporal_store(v, a.dX + t * a.d + col);   // streamed like the sparse rows' dX
           } else {
             if (a.out_bf16) ((uint16_t*)a.y)[t * a.d + col] = (uint16_t)f32_to_bf16_bits(v);
             else ((float*)a.y)[t * a.d + col] = v;
